@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Throughput of the device-wide chained scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the library entry point over the whole input resident
+in HBM (workspace clear + the single-pass kernel).  W untimed steps, then K
+steps timed with the wall clock between two device synchronisations; HIP
+events that the library records around its main kernel on the same stream
+give that kernel's average duration for the roofline figure.  Prints one JSON
+line.
+
+Workloads (default: u32x): the headline is the uint32 exclusive sum scan of
+2^28 elements, values uniform in [0, 255] (seed 2).  The others time the
+remaining kernels on their configurations:
+  u32x-ragged  same, n = 2^28 - 12345            u32i  inclusive, n = 2^28
+  f32          fp32 inclusive sum, n = 2^27, N(0,1)  f32max  fp32 inclusive max
+  segmented    segmented u32 exclusive, 2^26 values, 2^16 Zipf(1.2) segments
+  compact      2^26 16-byte records, Bernoulli(0.3) keep flags
+  copy         plain 1 GiB copy (the practical bandwidth ceiling)
+
+Only the cpu_baseline leg runs the oracle: the sequential C scan, one host
+thread, timed on the same input, and its output is compared with the GPU's.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+METRIC = "Gelem/s and % of HBM peak GB/s, 2^28 uint32 exclusive scan on 1 MI355X"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "device_wide_prefix_chained_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, launch_bytes_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None when absent or taken on different kernel sources."""
+    path = os.path.join(PROFILES, "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return float(t["hbm_bytes_per_launch"])
+
+
+def build_workload(name: str):
+    """Return (description, dtype, n, algorithmic bytes per call, host inputs, runner factory)."""
+    import torch
+
+    import device_wide_prefix_chained_amd as dw
+    import workloads as wl
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint32:
+            a = a.view(np.int32)
+        return torch.from_numpy(a).to("cuda")
+
+    if name in ("u32x", "u32x-ragged", "u32i", "copy"):
+        n = wl.N_RAGGED_U32 if name == "u32x-ragged" else wl.N_LARGE_U32
+        x = wl.large_u32()[:n]
+        d_in, d_out = dev(x), torch.empty(n, dtype=torch.int32, device="cuda")
+        total = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if name == "copy":
+            desc = "plain copy of 2^28 uint32 (1 GiB read + 1 GiB written)"
+            run = lambda: dw.ps_copy_u32(d_in, d_out)  # noqa: E731
+        else:
+            incl = name == "u32i"
+            fn = "ps_scan_inclusive_u32" if incl else "ps_scan_exclusive_u32"
+            ws = torch.empty(dw.workspace_bytes(fn, None, None, n, None, None), dtype=torch.uint8, device="cuda")
+            f = getattr(dw, fn)
+            run = lambda: f(d_in, d_out, total, workspace=ws)  # noqa: E731
+            desc = "u32 %s sum scan, n=%s, values uniform in [0,255], seed 2" % (
+                "inclusive" if incl else "exclusive", "2^28-12345" if name == "u32x-ragged" else "2^28")
+        return dict(desc=desc, dtype="u32", n=n, bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out,
+                    inclusive=(name == "u32i"), kind="copy" if name == "copy" else "u32")
+    if name in ("f32", "f32max"):
+        n = wl.N_F32
+        x = wl.f32_normal()
+        d_in, d_out = dev(x), torch.empty(n, dtype=torch.float32, device="cuda")
+        op = "sum" if name == "f32" else "max"
+        ws = torch.empty(dw.workspace_bytes("ps_scan", None, None, 0, 1, 1, None, None, n, None, None),
+                         dtype=torch.uint8, device="cuda")
+        run = lambda: dw.ps_scan(op, True, d_in, d_out, workspace=ws)  # noqa: E731
+        return dict(desc="fp32 inclusive %s scan, n=2^27, N(0,1), seed 3" % op, dtype="f32", n=n,
+                    bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=True, kind="f32" + op)
+    if name == "segmented":
+        values, off = wl.zipf_segments()
+        n = values.size
+        d_v, d_o = dev(values), dev(off)
+        d_out = torch.empty(n, dtype=torch.int32, device="cuda")
+        ws = torch.empty(dw.workspace_bytes("ps_segmented_scan_u32", None, n, None, off.size - 1, None, 0, None),
+                         dtype=torch.uint8, device="cuda")
+        run = lambda: dw.ps_segmented_scan_u32(d_v, d_o, d_out, inclusive=False, workspace=ws)  # noqa: E731
+        return dict(desc="segmented u32 exclusive sum scan, 2^26 values U[0,1023], 2^16 CSR segments "
+                         "(10% empty, one with 25% of the elements, rank-size Zipf(1.2)), seed 5",
+                    dtype="u32", n=n, bytes=8.0 * n + 4.0 * off.size, inputs=dict(x=values, off=off),
+                    run=run, out=d_out, inclusive=False, kind="segmented")
+    if name == "compact":
+        rec, flags = wl.compaction_records()
+        n = flags.size
+        kept = int(flags.sum())
+        d_r, d_f = dev(rec), dev(flags)
+        d_out = torch.empty_like(d_r)
+        cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
+        ws = torch.empty(dw.workspace_bytes("ps_compact", None, 16, None, n, None, None, None),
+                         dtype=torch.uint8, device="cuda")
+        run = lambda: dw.ps_compact(d_r, d_f, d_out, cnt, workspace=ws)  # noqa: E731
+        return dict(desc="stream compaction of 2^26 16-byte records {u32 id, u32 key, f32 a, f32 b}, "
+                         "keep ~ Bernoulli(0.3), seed 4", dtype="u32", n=n,
+                    bytes=17.0 * n + 16.0 * kept + 8.0, inputs=dict(rec=rec, flags=flags), run=run,
+                    out=d_out, count=cnt, inclusive=False, kind="compact")
+    raise SystemExit("unknown workload %r" % name)
+
+
+def cpu_baseline(w, gpu_out, min_seconds: float):
+    """Time the oracle (single-threaded C loop) on the same input; compare."""
+    import oracle
+    orc = oracle.default()
+    kind = w["kind"]
+    times = []
+    ref = None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        if kind == "u32" or kind == "copy":
+            ref = orc.scan_u32(w["inputs"]["x"], "sum", w["inclusive"])[0]
+        elif kind == "f32sum":
+            ref = orc.scan_f32_sum(w["inputs"]["x"], True, want_abs=True)
+        elif kind == "f32max":
+            ref = orc.scan_f32_minmax(w["inputs"]["x"], "max", True)[0]
+        elif kind == "segmented":
+            ref = orc.segmented_scan_u32(w["inputs"]["x"], w["inputs"]["off"], False)
+        elif kind == "compact":
+            ref = orc.compact(w["inputs"]["rec"], w["inputs"]["flags"])
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 and time.perf_counter() - t_start >= min_seconds:
+            break
+    med = statistics.median(times)
+    gelems = w["n"] / med / 1e9
+    parity = None
+    if kind == "u32" or kind == "segmented":
+        parity = "bit-exact" if np.array_equal(gpu_out, ref) else "MISMATCH"
+    elif kind == "f32max":
+        parity = "bit-exact" if np.array_equal(gpu_out.view(np.uint32), ref.view(np.uint32)) else "MISMATCH"
+    elif kind == "f32sum":
+        y, ab, _ = ref
+        ok = bool(np.all(np.abs(gpu_out.astype(np.float64) - y) <= 1e-5 * ab))
+        parity = "within 1e-5*sum|x|" if ok else "MISMATCH"
+    elif kind == "compact":
+        out, count = ref
+        parity = "bit-exact" if (count == gpu_out[1] and np.array_equal(gpu_out[0][:count], out[:count])) \
+            else "MISMATCH"
+    sample = "the full %d-element input, %d repetitions (median)" % (w["n"], len(times))
+    return {"value": round(gelems, 4), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds_per_rep": round(med, 4)}, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="u32x")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum oracle time of the cpu_baseline leg (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import device_wide_prefix_chained_amd as dw
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dw.lib()
+
+    print("[bench] building workload %s" % args.workload, file=sys.stderr, flush=True)
+    w = build_workload(args.workload)
+    run = w["run"]
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    print("[bench] warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    dw.ps_kernel_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms_total, launches = dw.ps_kernel_timing_read()
+    dw.ps_kernel_timing(False)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    kernel_ms = kernel_ms_total / max(launches, 1)
+    n = w["n"]
+    value = n / (ms_per_step * 1e-3) / 1e9
+    call_gbs = w["bytes"] / (ms_per_step * 1e-3) / 1e9
+    achieved = w["bytes"] / (kernel_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, w["bytes"])
+
+    gpu_out = None
+    cpu = None
+    parity = None
+    if args.cpu_seconds > 0:
+        if w["kind"] == "compact":
+            gpu_out = (w["out"].cpu().numpy().view(np.uint32), int(w["count"].cpu().item()))
+        else:
+            o = w["out"].cpu().numpy()
+            gpu_out = o.view(np.uint32) if o.dtype == np.int32 else o
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu, parity = cpu_baseline(w, gpu_out, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC if args.workload == "u32x" else "Gelem/s, " + w["desc"],
+        "value": round(value, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": w["desc"], "n": n, "algorithmic_bytes_per_step": w["bytes"],
+                   "tile_elements": dw.ps_tile_elements(0)},
+        "gbs_per_step": round(call_gbs, 1),
+        "pct_hbm_peak_per_step": round(100.0 * call_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(round(traffic)),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+                     "kernel_ms": round(kernel_ms, 5), "timed_launches": launches},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

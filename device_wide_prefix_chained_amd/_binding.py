@@ -1,0 +1,290 @@
+"""ctypes binding of libdwps.so: argument marshalling only.
+
+Each Python function has the name of the C entry point it wraps (see
+``include/dwps.h`` for the contract).  Tensors are PyTorch CUDA (HIP) tensors;
+PyTorch supplies device memory (outputs and workspaces the caller does not
+pass are allocated with ``torch.empty``) and the current stream.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libdwps.so")
+
+# enum values of include/dwps.h
+PS_OK = 0
+PS_U32, PS_F32 = 0, 1
+PS_OP_SUM, PS_OP_MAX, PS_OP_MIN, PS_OP_AND, PS_OP_OR, PS_OP_XOR, PS_OP_AFFINE16 = range(7)
+OPS = {"sum": PS_OP_SUM, "max": PS_OP_MAX, "min": PS_OP_MIN, "and": PS_OP_AND,
+       "or": PS_OP_OR, "xor": PS_OP_XOR, "affine16": PS_OP_AFFINE16}
+
+_U32_DTYPES = (torch.uint32, torch.int32)
+
+_lib = None
+
+
+class DwpsError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdwps.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise ImportError("libdwps.so is not built (%s); run "
+                          "`python -m device_wide_prefix_chained_amd.build`" % LIBRARY)
+    L = ctypes.CDLL(LIBRARY)
+    vp, sz, u64, u32, i32 = (ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t), ctypes.c_uint64,
+                             ctypes.c_uint32, ctypes.c_int)
+    flat = [vp, sz, vp, vp, u64, vp, vp]
+    for name in ("ps_scan_exclusive_u32", "ps_scan_inclusive_u32",
+                 "ps_scan_exclusive_f32", "ps_scan_inclusive_f32"):
+        getattr(L, name).argtypes = flat
+        getattr(L, name).restype = i32
+    L.ps_scan.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
+    L.ps_scan.restype = i32
+    L.ps_segmented_scan_u32.argtypes = [vp, sz, vp, u64, vp, u32, vp, i32, vp]
+    L.ps_segmented_scan_u32.restype = i32
+    L.ps_validate_offsets.argtypes = [vp, u32, u64, vp, vp]
+    L.ps_validate_offsets.restype = i32
+    L.ps_compact.argtypes = [vp, sz, vp, u32, vp, u64, vp, vp, vp]
+    L.ps_compact.restype = i32
+    L.ps_copy_u32.argtypes = [vp, vp, u64, vp]
+    L.ps_copy_u32.restype = i32
+    L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
+    L.ps_lookback_stats_u32.restype = i32
+    L.ps_lookback_tiles.argtypes = [u64]
+    L.ps_lookback_tiles.restype = u64
+    L.ps_kernel_timing.argtypes = [i32]
+    L.ps_kernel_timing.restype = i32
+    L.ps_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]
+    L.ps_kernel_timing_read.restype = i32
+    L.ps_tile_elements.argtypes = [i32]
+    L.ps_tile_elements.restype = u32
+    L.ps_version.argtypes = []
+    L.ps_version.restype = ctypes.c_char_p
+    L.ps_status_string.argtypes = [i32]
+    L.ps_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PS_OK:
+        raise DwpsError(fn, status, lib().ps_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev_tensor(name, t, dtypes=None, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, needs %d" % (name, t.numel(), numel))
+    return t
+
+
+def _workspace(fn: str, call, device, workspace):
+    """CUB-style size query, then a torch byte buffer when none is given."""
+    need = ctypes.c_size_t(0)
+    _check(fn, call(None, ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=device)
+    else:
+        _dev_tensor("workspace", workspace)
+    have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    return workspace, have
+
+
+# ---------------------------------------------------------------------------
+# flat scans
+# ---------------------------------------------------------------------------
+def _flat(fn: str, inp, out, total, workspace, stream, dtypes):
+    _dev_tensor("inp", inp, dtypes)
+    _dev_tensor("out", out, dtypes, inp.numel())
+    if total is not None:
+        _dev_tensor("total", total, dtypes, 1)
+    f = getattr(lib(), fn)
+    n = inp.numel()
+    s = _stream(inp, stream)
+    call = lambda ws, wsb: f(ws, wsb, _ptr(inp), _ptr(out), n, _ptr(total), s)  # noqa: E731
+    ws, have = _workspace(fn, call, inp.device, workspace)
+    _check(fn, call(_ptr(ws), ctypes.byref(have)))
+    return out
+
+
+def ps_scan_exclusive_u32(inp, out, total=None, workspace=None, stream=None):
+    return _flat("ps_scan_exclusive_u32", inp, out, total, workspace, stream, _U32_DTYPES)
+
+
+def ps_scan_inclusive_u32(inp, out, total=None, workspace=None, stream=None):
+    return _flat("ps_scan_inclusive_u32", inp, out, total, workspace, stream, _U32_DTYPES)
+
+
+def ps_scan_exclusive_f32(inp, out, total=None, workspace=None, stream=None):
+    return _flat("ps_scan_exclusive_f32", inp, out, total, workspace, stream, (torch.float32,))
+
+
+def ps_scan_inclusive_f32(inp, out, total=None, workspace=None, stream=None):
+    return _flat("ps_scan_inclusive_f32", inp, out, total, workspace, stream, (torch.float32,))
+
+
+def ps_scan(op, inclusive, inp, out, total=None, workspace=None, stream=None, dtype=None):
+    """Generic associative-operator scan; ``op`` is a PS_OP_* code or a name
+    ('sum', 'max', 'min', 'and', 'or', 'xor', 'affine16')."""
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    if dtype is None:
+        dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
+    dtypes = (torch.float32,) if dtype == PS_F32 else _U32_DTYPES
+    _dev_tensor("inp", inp, dtypes)
+    _dev_tensor("out", out, dtypes, inp.numel())
+    if total is not None:
+        _dev_tensor("total", total, dtypes, 1)
+    n = inp.numel()
+    s = _stream(inp, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_scan(ws, wsb, opc, dtype, int(bool(inclusive)), _ptr(inp),  # noqa: E731
+                                     _ptr(out), n, _ptr(total), s)
+    ws, have = _workspace("ps_scan", call, inp.device, workspace)
+    _check("ps_scan", call(_ptr(ws), ctypes.byref(have)))
+    return out
+
+
+def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None, stream=None):
+    _dev_tensor("inp", inp, _U32_DTYPES)
+    _dev_tensor("out", out, _U32_DTYPES, inp.numel())
+    n = inp.numel()
+    _dev_tensor("stats", stats, _U32_DTYPES, 4 * ps_lookback_tiles(n))
+    s = _stream(inp, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_lookback_stats_u32(ws, wsb, _ptr(inp), _ptr(out), n,  # noqa: E731
+                                                   _ptr(stats), int(bool(aggregate_only)), s)
+    ws, have = _workspace("ps_lookback_stats_u32", call, inp.device, workspace)
+    _check("ps_lookback_stats_u32", call(_ptr(ws), ctypes.byref(have)))
+    return stats
+
+
+def ps_lookback_tiles(n: int) -> int:
+    return int(lib().ps_lookback_tiles(n))
+
+
+# ---------------------------------------------------------------------------
+# segmented scan
+# ---------------------------------------------------------------------------
+def ps_segmented_scan_u32(values, offsets, out, inclusive=False, workspace=None, stream=None):
+    _dev_tensor("values", values, _U32_DTYPES)
+    _dev_tensor("offsets", offsets, _U32_DTYPES)
+    _dev_tensor("out", out, _U32_DTYPES, values.numel())
+    if offsets.numel() < 1:
+        raise ValueError("offsets needs num_segments + 1 >= 1 entries")
+    n = values.numel()
+    nseg = offsets.numel() - 1
+    s = _stream(values, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_segmented_scan_u32(ws, wsb, _ptr(values), n, _ptr(offsets),  # noqa: E731
+                                                   nseg, _ptr(out), int(bool(inclusive)), s)
+    ws, have = _workspace("ps_segmented_scan_u32", call, values.device, workspace)
+    _check("ps_segmented_scan_u32", call(_ptr(ws), ctypes.byref(have)))
+    return out
+
+
+def ps_validate_offsets(offsets, n, result, stream=None):
+    _dev_tensor("offsets", offsets, _U32_DTYPES)
+    _dev_tensor("result", result, (torch.int64,), 1)
+    _check("ps_validate_offsets", lib().ps_validate_offsets(
+        _ptr(offsets), offsets.numel() - 1, int(n), _ptr(result), _stream(offsets, stream)))
+    return result
+
+
+# ---------------------------------------------------------------------------
+# compaction
+# ---------------------------------------------------------------------------
+def ps_compact(records, flags, out, num_selected, workspace=None, stream=None):
+    """records: (n,) or (n, k) tensor whose rows are the records (4, 8 or 16
+    bytes); flags: (n,) uint8/bool; out: same shape as records;
+    num_selected: one int64/uint64 element on the device."""
+    _dev_tensor("records", records)
+    _dev_tensor("flags", flags, (torch.uint8, torch.bool))
+    _dev_tensor("out", out)
+    _dev_tensor("num_selected", num_selected, (torch.int64, torch.uint64), 1)
+    n = flags.numel()
+    if records.shape[0] != n or (records.dim() > 1 and out.shape[1:] != records.shape[1:]):
+        raise ValueError("records must have one row per flag and out the same row shape")
+    if out.shape[0] < n:
+        raise ValueError("out needs room for n records")
+    rb = records.element_size() * (records[0].numel() if records.dim() > 1 else 1)
+    s = _stream(flags, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_compact(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa: E731
+                                        _ptr(out), _ptr(num_selected), s)
+    ws, have = _workspace("ps_compact", call, flags.device, workspace)
+    _check("ps_compact", call(_ptr(ws), ctypes.byref(have)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# measurement helpers
+# ---------------------------------------------------------------------------
+def ps_copy_u32(inp, out, stream=None):
+    _dev_tensor("inp", inp, _U32_DTYPES)
+    _dev_tensor("out", out, _U32_DTYPES, inp.numel())
+    _check("ps_copy_u32", lib().ps_copy_u32(_ptr(inp), _ptr(out), inp.numel(), _stream(inp, stream)))
+    return out
+
+
+def ps_kernel_timing(enable: bool) -> None:
+    _check("ps_kernel_timing", lib().ps_kernel_timing(int(bool(enable))))
+
+
+def ps_kernel_timing_read():
+    """Return (total milliseconds, number of timed launches)."""
+    ms = ctypes.c_double(0.0)
+    cnt = ctypes.c_uint64(0)
+    _check("ps_kernel_timing_read", lib().ps_kernel_timing_read(ctypes.byref(ms), ctypes.byref(cnt)))
+    return ms.value, cnt.value
+
+
+def ps_tile_elements(dtype=PS_U32) -> int:
+    return int(lib().ps_tile_elements(dtype))
+
+
+def ps_version() -> str:
+    return lib().ps_version().decode()
+
+
+def ps_status_string(status: int) -> str:
+    return lib().ps_status_string(status).decode()
+
+
+def workspace_bytes(fn: str, *args) -> int:
+    """Size query of entry point ``fn`` for the given scalar arguments
+    (as in the C call, with device pointers given as None)."""
+    need = ctypes.c_size_t(0)
+    _check(fn, getattr(lib(), fn)(None, ctypes.byref(need), *args))
+    return int(need.value)

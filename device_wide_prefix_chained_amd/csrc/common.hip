@@ -1,0 +1,180 @@
+// common.hip -- workspace clearing, the calibration copy kernel, the offsets
+// validator, kernel-timing events and the status/version strings.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "host_common.hpp"
+
+namespace dwps {
+
+__global__ void clear_kernel(uint4 *p, uint64_t n16) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_clear(void *p, size_t bytes, hipStream_t stream) {
+    const uint64_t n16 = bytes / 16;
+    if (!n16) return hipSuccess;
+    const uint64_t blocks = ceil_div(n16, 256);
+    const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
+    hipLaunchKernelGGL(clear_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint4 *>(p), n16);
+    return hipGetLastError();
+}
+
+// Streaming copy: each thread moves 4 x 16 bytes per iteration, coalesced
+// across the wave; the scalar tail is handled by the first threads.
+__global__ __launch_bounds__(256) void copy_vec_kernel(const uint4 *in, uint4 *out, uint64_t n16) {
+    const uint64_t base = ((uint64_t)blockIdx.x * 256 * 4) + threadIdx.x;
+    uint4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint64_t i = base + (uint64_t)k * 256;
+        if (i < n16) r[k] = in[i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint64_t i = base + (uint64_t)k * 256;
+        if (i < n16) out[i] = r[k];
+    }
+}
+__global__ void copy_scalar_kernel(const uint32_t *in, uint32_t *out, uint64_t begin, uint64_t n) {
+    const uint64_t i = begin + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = in[i];
+}
+
+// offsets validator: result = -1, or the first offending index (atomic min).
+__global__ void validate_offsets_kernel(const uint32_t *offsets, uint32_t num_segments, uint64_t n,
+                                        unsigned long long *result) {
+    const uint64_t s = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s > num_segments) return;
+    bool bad;
+    if (s < num_segments)
+        bad = offsets[s] > offsets[s + 1];
+    else
+        bad = (uint64_t)offsets[s] > n;
+    if (bad) atomicMin(result, (unsigned long long)s);
+}
+__global__ void init_i64_kernel(unsigned long long *p, unsigned long long v) { *p = v; }
+__global__ void finish_validate_kernel(unsigned long long *p) {
+    if (*p == ~0ull) *p = (unsigned long long)(-1ll);
+}
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+namespace {
+std::mutex g_timing_mu;
+std::atomic<bool> g_timing_on{false};
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timing_events;
+thread_local hipEvent_t t_pending_start = nullptr;
+}  // namespace
+
+void timing_begin(hipStream_t stream) {
+    if (!g_timing_on.load(std::memory_order_relaxed)) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, stream);
+    t_pending_start = e;
+}
+
+void timing_end(hipStream_t stream) {
+    if (!g_timing_on.load(std::memory_order_relaxed) || !t_pending_start) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEventRecord(e, stream);
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing_events.emplace_back(t_pending_start, e);
+    t_pending_start = nullptr;
+}
+
+}  // namespace dwps
+
+using namespace dwps;
+
+extern "C" ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *stream) {
+    if (n == 0) return PS_OK;
+    if (!in || !out) return PS_ERR_NULL;
+    if (n >= (1ull << 32)) return PS_ERR_SIZE;
+    if (!aligned(in, 4) || !aligned(out, 4)) return PS_ERR_ALIGNMENT;
+    if (ranges_overlap(in, n * 4, out, n * 4)) return PS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint64_t done = 0;
+    timing_begin(s);
+    if (aligned(in, 16) && aligned(out, 16)) {
+        const uint64_t n16 = n / 4;
+        if (n16) {
+            const uint64_t blocks = ceil_div(n16, 1024);
+            hipLaunchKernelGGL(copy_vec_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                               reinterpret_cast<const uint4 *>(in), reinterpret_cast<uint4 *>(out), n16);
+        }
+        done = n16 * 4;
+    }
+    if (done < n) {
+        const uint64_t rest = n - done;
+        hipLaunchKernelGGL(copy_scalar_kernel, dim3((unsigned)ceil_div(rest, 256)), dim3(256), 0, s, in, out,
+                           done, n);
+    }
+    timing_end(s);
+    return launch_status();
+}
+
+extern "C" ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_segments, uint64_t n,
+                                         int64_t *result, void *stream) {
+    if (!offsets || !result) return PS_ERR_NULL;
+    if (!aligned(offsets, 4) || !aligned(result, 8)) return PS_ERR_ALIGNMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto *r = reinterpret_cast<unsigned long long *>(result);
+    hipLaunchKernelGGL(init_i64_kernel, dim3(1), dim3(1), 0, s, r, ~0ull);
+    const uint64_t count = (uint64_t)num_segments + 1;
+    hipLaunchKernelGGL(validate_offsets_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, offsets,
+                       num_segments, n, r);
+    hipLaunchKernelGGL(finish_validate_kernel, dim3(1), dim3(1), 0, s, r);
+    return launch_status();
+}
+
+extern "C" ps_status ps_kernel_timing(int enable) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    for (auto &pr : g_timing_events) {
+        hipEventDestroy(pr.first);
+        hipEventDestroy(pr.second);
+    }
+    g_timing_events.clear();
+    g_timing_on.store(enable != 0);
+    return PS_OK;
+}
+
+extern "C" ps_status ps_kernel_timing_read(double *total_ms, uint64_t *launches) {
+    if (!total_ms || !launches) return PS_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    double sum = 0.0;
+    for (auto &pr : g_timing_events) {
+        if (hipEventSynchronize(pr.second) != hipSuccess) return PS_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return PS_ERR_HIP;
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = g_timing_events.size();
+    return PS_OK;
+}
+
+extern "C" const char *ps_status_string(ps_status status) {
+    switch (status) {
+    case PS_OK: return "ok";
+    case PS_ERR_NULL: return "a required pointer is NULL";
+    case PS_ERR_ALIAS: return "input and output overlap in a way this call forbids";
+    case PS_ERR_SIZE: return "size out of the supported range (n must be below 2^32)";
+    case PS_ERR_WORKSPACE: return "workspace smaller than the size query reported";
+    case PS_ERR_UNSUPPORTED: return "operator, dtype or record size not supported";
+    case PS_ERR_HIP: return "a HIP launch failed";
+    case PS_ERR_ALIGNMENT: return "a pointer is not aligned to its element size";
+    }
+    return "unknown status";
+}
+
+extern "C" const char *ps_version(void) { return "dwps 0.1 (gfx950)"; }

@@ -1,0 +1,221 @@
+// dwps_device.hpp -- device building blocks of the chained scan for gfx950.
+//
+// Layers, bottom to top (the warp / block / grid composition of
+// "Parallel Prefix Sum (Scan), in depth", section "A CUDA scan: warp, block,
+// grid", and "Prefix scans and compaction", section "Warp, block, and grid
+// composition"), re-built for 64-lane CDNA4 wavefronts:
+//   * thread-serial fold of the elements a lane holds in registers;
+//   * wave64 Hillis-Steele scan with DPP row shifts and row broadcasts (no
+//     LDS traffic, no barrier: the 64 lanes execute in lockstep);
+//   * block scan over the per-wave totals staged in LDS;
+//   * grid level: per-tile 64-bit descriptors with the three states of
+//     "Single-Pass Prefix Scan with Decoupled Look-Back", section "Three
+//     states in a per-block descriptor", published and read as single
+//     agent-scope atomic words (section "The publication protocol in code"),
+//     with a look-back that reads 64 predecessors per poll, one per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dwps {
+
+// ---------------------------------------------------------------------------
+// Operators: op(a, b) with a the EARLIER and b the LATER operand.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t to_bits(uint32_t v) { return v; }
+__device__ __forceinline__ uint32_t to_bits(float v) { return __float_as_uint(v); }
+template <class T> __device__ __forceinline__ T from_bits(uint32_t b);
+template <> __device__ __forceinline__ uint32_t from_bits<uint32_t>(uint32_t b) { return b; }
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
+
+struct SumU32 {
+    using T = uint32_t;
+    __device__ static T id() { return 0u; }
+    __device__ static T op(T a, T b) { return a + b; }
+};
+struct MaxU32 {
+    using T = uint32_t;
+    __device__ static T id() { return 0u; }
+    __device__ static T op(T a, T b) { return (b > a) ? b : a; }
+};
+struct MinU32 {
+    using T = uint32_t;
+    __device__ static T id() { return 0xFFFFFFFFu; }
+    __device__ static T op(T a, T b) { return (b < a) ? b : a; }
+};
+struct AndU32 {
+    using T = uint32_t;
+    __device__ static T id() { return 0xFFFFFFFFu; }
+    __device__ static T op(T a, T b) { return a & b; }
+};
+struct OrU32 {
+    using T = uint32_t;
+    __device__ static T id() { return 0u; }
+    __device__ static T op(T a, T b) { return a | b; }
+};
+struct XorU32 {
+    using T = uint32_t;
+    __device__ static T id() { return 0u; }
+    __device__ static T op(T a, T b) { return a ^ b; }
+};
+// h -> a*h + b over Z/2^16, packed (a << 16) | b; a first, then b:
+// h -> a_b*(a_a*h + b_a) + b_b.
+struct Affine16 {
+    using T = uint32_t;
+    __device__ static T id() { return 0x00010000u; }
+    __device__ static T op(T x, T y) {
+        const uint32_t xa = x >> 16, xb = x & 0xFFFFu;
+        const uint32_t ya = y >> 16, yb = y & 0xFFFFu;
+        return (((xa * ya) & 0xFFFFu) << 16) | ((ya * xb + yb) & 0xFFFFu);
+    }
+};
+struct SumF32 {
+    using T = float;
+    __device__ static T id() { return 0.0f; }
+    __device__ static T op(T a, T b) { return a + b; }
+};
+struct MaxF32 {
+    using T = float;
+    __device__ static T id() { return -__builtin_huge_valf(); }
+    __device__ static T op(T a, T b) { return (b > a) ? b : a; }
+};
+struct MinF32 {
+    using T = float;
+    __device__ static T id() { return __builtin_huge_valf(); }
+    __device__ static T op(T a, T b) { return (b < a) ? b : a; }
+};
+
+// ---------------------------------------------------------------------------
+// Wave64 primitives (DPP).  DPP control codes of the GFX9 ISA:
+//   0x111..0x11F row_shr:1..15   (within each row of 16 lanes)
+//   0x138        wave_shr:1      (whole wave, lane i <- lane i-1)
+//   0x142        row_bcast:15    (lane 15 of a row -> every lane of the next row)
+//   0x143        row_bcast:31    (lane 31 -> rows 2 and 3)
+// A lane whose source is outside the row/wave, or that row_mask disables,
+// keeps `old`, which is always the operator's identity here.
+// ---------------------------------------------------------------------------
+template <class Op, int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ typename Op::T dpp_from(typename Op::T x) {
+    using T = typename Op::T;
+    return from_bits<T>((uint32_t)__builtin_amdgcn_update_dpp(
+        (int)to_bits(Op::id()), (int)to_bits(x), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive scan across the 64 lanes, lane order = element order.
+template <class Op>
+__device__ __forceinline__ typename Op::T wave_inclusive(typename Op::T x) {
+    x = Op::op(dpp_from<Op, 0x111>(x), x);
+    x = Op::op(dpp_from<Op, 0x112>(x), x);
+    x = Op::op(dpp_from<Op, 0x114>(x), x);
+    x = Op::op(dpp_from<Op, 0x118>(x), x);
+    x = Op::op(dpp_from<Op, 0x142, 0xA>(x), x);
+    x = Op::op(dpp_from<Op, 0x143, 0xC>(x), x);
+    return x;
+}
+
+// Inclusive -> exclusive: lane i takes lane i-1's value, lane 0 the identity.
+template <class Op>
+__device__ __forceinline__ typename Op::T wave_shift_right(typename Op::T x) {
+    return dpp_from<Op, 0x138>(x);
+}
+
+template <class T>
+__device__ __forceinline__ T read_lane(T x, int lane) {
+    return from_bits<T>((uint32_t)__builtin_amdgcn_readlane((int)to_bits(x), lane));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// ---------------------------------------------------------------------------
+// Tile descriptors: state in the high 32 bits, payload in the low 32 bits,
+// so one atomic store publishes both and one atomic load reads a consistent
+// pair.  Agent (device) scope: readers are on other XCDs of the same GPU,
+// never on the host or a peer device.  The ordering that matters -- the tile's
+// own LDS/register scan before its publication -- is program order within the
+// publishing lane after a workgroup barrier, so relaxed ordering suffices;
+// no other memory is handed over through a descriptor.
+// ---------------------------------------------------------------------------
+constexpr uint32_t ST_INVALID = 0u;    // nothing published
+constexpr uint32_t ST_AGGREGATE = 1u;  // payload = the tile's own fold
+constexpr uint32_t ST_PREFIX = 2u;     // payload = fold of tiles 0..t (inclusive)
+
+__device__ __forceinline__ uint64_t desc_word(uint32_t state, uint32_t payload) {
+    return ((uint64_t)state << 32) | (uint64_t)payload;
+}
+__device__ __forceinline__ void desc_publish(uint64_t *d, uint64_t w) {
+    __hip_atomic_store(d, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t desc_poll(const uint64_t *d) {
+    return __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr) {
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct LookbackStats {
+    uint32_t polls = 0;    // poll rounds (64 descriptor reads each)
+    uint32_t windows = 0;  // windows of 64 predecessors folded
+    uint32_t stalls = 0;   // polls that found an unpublished predecessor
+};
+
+// Safety net of the spin: a wave that finds an unpublished predecessor this
+// many times in a row (seconds of waiting; a healthy chain needs a few) gives
+// up, raises the workspace error word and continues with a wrong prefix
+// instead of hanging the GPU.  Progress is guaranteed by the protocol, so the
+// limit only trips on a broken workspace or a faulting predecessor.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// Decoupled look-back, executed by one full wave.  Lane k of a poll reads the
+// descriptor of tile (nearest - 63 + k), so lane 63 holds the nearest
+// predecessor and lower lanes hold earlier tiles (lane order = element
+// order).  Indices below 0 read as a PREFIX carrying the identity.  Let p be
+// the highest lane in PREFIX state: if some lane at or above p is still
+// INVALID the window is polled again (each poll reloads every word); else the
+// payloads of lanes p..63 are folded in order and, if p exists, the fold is
+// final; otherwise the window slides 64 tiles back.  (After kSpinLimit
+// consecutive stalls the unpublished lanes are folded as they are and *err is
+// set.)  Returns the exclusive
+// prefix of `tile` (the fold of every earlier tile).  Terminates because tile
+// 0 publishes PREFIX without waiting and every tile only waits on tiles that
+// took their ticket earlier, hence are resident or finished
+// ("Single-Pass Prefix Scan with Decoupled Look-Back", sections "Three states
+// in a per-block descriptor", "Why the work stays linear" and "Where the
+// algorithm meets the hardware").
+template <class Op, bool STATS>
+__device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_t tile,
+                                                   uint32_t lane, LookbackStats &st,
+                                                   uint32_t *err) {
+    using T = typename Op::T;
+    T acc = Op::id();
+    int64_t nearest = (int64_t)tile - 1;
+    uint32_t spins = 0;
+    const uint64_t pad = desc_word(ST_PREFIX, to_bits(Op::id()));
+    for (;;) {
+        const int64_t idx = nearest - 63 + (int64_t)lane;
+        const uint64_t w = (idx >= 0) ? desc_poll(desc + idx) : pad;
+        const uint32_t state = (uint32_t)(w >> 32);
+        const uint64_t pm = ballot(state == ST_PREFIX);
+        const uint64_t im = ballot(state == ST_INVALID);
+        const uint32_t lim = pm ? 63u - (uint32_t)__builtin_clzll(pm) : 0u;
+        if (STATS) st.polls++;
+        if (im & (~0ull << lim)) {
+            if (STATS) st.stalls++;
+            if (++spins < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        spins = 0;
+        T v = (lane >= lim) ? from_bits<T>((uint32_t)w) : Op::id();
+        v = wave_inclusive<Op>(v);
+        acc = Op::op(read_lane(v, 63), acc);
+        if (STATS) st.windows++;
+        if (pm) break;
+        nearest -= 64;
+    }
+    return acc;
+}
+
+}  // namespace dwps

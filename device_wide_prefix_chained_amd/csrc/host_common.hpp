@@ -1,0 +1,61 @@
+// host_common.hpp -- host-side helpers shared by the entry points of the
+// library: workspace layout, argument checks, launch error mapping and the
+// optional kernel-timing events.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dwps.h"
+
+namespace dwps {
+
+// Workspace: a 256-byte header (word 0 = tile-ticket counter, word 1 = error
+// word, nonzero when a look-back hit its spin limit) followed by one 64-bit
+// descriptor per tile.  Everything is cleared to zero (counter 0, all
+// descriptors INVALID) on the caller's stream before each scan launch.
+constexpr size_t kWsHeader = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+inline size_t ws_bytes_for_tiles(uint64_t tiles) { return kWsHeader + round_up(tiles * 8, 256); }
+inline uint32_t *ws_counter(void *ws) { return static_cast<uint32_t *>(ws); }
+inline uint64_t *ws_desc(void *ws) {
+    return reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + kWsHeader);
+}
+
+inline bool ranges_overlap(const void *a, size_t abytes, const void *b, size_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return abytes && bbytes && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Size query / workspace check of the CUB two-call pattern.  Returns PS_OK
+// with *done = true when the call was a size query.
+inline ps_status workspace_protocol(void *ws, size_t *ws_bytes, size_t need, bool *done) {
+    *done = false;
+    if (!ws_bytes) return PS_ERR_NULL;
+    if (!ws) {
+        *ws_bytes = need;
+        *done = true;
+        return PS_OK;
+    }
+    if (*ws_bytes < need) return PS_ERR_WORKSPACE;
+    return PS_OK;
+}
+
+// Zero-fill `bytes` (a multiple of 16) at `p` on `stream` with a small kernel
+// (not hipMemsetAsync, so that a caller may capture the call in a graph).
+hipError_t launch_clear(void *p, size_t bytes, hipStream_t stream);
+
+inline ps_status launch_status() {
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+// Kernel timing hooks: when enabled (ps_kernel_timing), timing_begin/end
+// record a HIP event pair around the main kernel of the call on `stream`.
+void timing_begin(hipStream_t stream);
+void timing_end(hipStream_t stream);
+
+}  // namespace dwps

@@ -1,0 +1,222 @@
+/*
+ * dwps.h -- device-wide prefix scan for AMD Instinct MI355X (gfx950).
+ *
+ * A single-pass chained scan with decoupled look-back, its CSR-segmented
+ * variant and flag-driven stable stream compaction, behind a plain C ABI.
+ *
+ * Sources (page title, section):
+ *   [P1] "Single-Pass Prefix Scan with Decoupled Look-Back": lead section
+ *        (what an exclusive/inclusive prefix sum is); "Three states in a
+ *        per-block descriptor"; "The publication protocol in code";
+ *        "Where the algorithm meets the hardware".
+ *   [P2] "Parallel Prefix Sum (Scan), in depth": "Inclusive, exclusive and
+ *        associative"; "Scanning a whole array: three grid strategies";
+ *        "Use the library" (size query with a null temporary buffer);
+ *        "What scan builds" (compaction); "Failure modes".
+ *   [P3] "Prefix scans and compaction": "Scan as an index generator";
+ *        "Worked example: Stable stream compaction".
+ *   [P5] "GPUSegmentedScan": "Prefix scans and segmented scans", "Contract",
+ *        "Limitations".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named in/out/values/offsets/records/flags/total/num_selected
+ *    are DEVICE pointers (hipMalloc'd or torch CUDA tensors) unless stated.
+ *    `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Calls only enqueue work on `stream` and return at once; results are
+ *    visible in stream order.  The library never synchronises and never
+ *    allocates device memory.
+ *  - Workspace (the CUB-style two-call pattern of [P2] "Use the library"):
+ *    call with ws == NULL to receive the byte count in *ws_bytes (nothing is
+ *    launched, no GPU is touched); then call again with a device buffer of at
+ *    least that many bytes.  The caller owns it; its contents need no
+ *    initialisation (the library clears it on `stream` each call).  Two calls
+ *    in flight at once must not share a workspace.
+ *  - Argument errors are returned synchronously before anything is
+ *    launched: PS_ERR_NULL (a required pointer is NULL while n > 0),
+ *    PS_ERR_SIZE (n >= 2^32, or offsets beyond the supported range),
+ *    PS_ERR_WORKSPACE (*ws_bytes smaller than required), PS_ERR_UNSUPPORTED
+ *    (operator / dtype / record size not provided), PS_ERR_ALIAS (forbidden
+ *    overlap of input and output), PS_ERR_ALIGNMENT (a pointer is not
+ *    aligned to its element size).  A failed launch returns PS_ERR_HIP.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - n == 0 is valid: nothing is written except *total (the identity) or
+ *    *num_selected (0).
+ *  - Arithmetic: uint32 sums wrap modulo 2^32.  fp32 operations use IEEE
+ *    fp32 round-to-nearest with an fp32 accumulator; the grouping of a
+ *    floating-point sum depends on run-time scheduling, so fp32 sums are not
+ *    bitwise reproducible ([P1] "When not to use it").  Integer results,
+ *    max/min and compaction are exact and deterministic.
+ */
+#ifndef DWPS_H
+#define DWPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ps_status {
+    PS_OK = 0,
+    PS_ERR_NULL = 1,
+    PS_ERR_ALIAS = 2,
+    PS_ERR_SIZE = 3,
+    PS_ERR_WORKSPACE = 4,
+    PS_ERR_UNSUPPORTED = 5,
+    PS_ERR_HIP = 6,
+    PS_ERR_ALIGNMENT = 7
+} ps_status;
+
+typedef enum ps_dtype { PS_U32 = 0, PS_F32 = 1 } ps_dtype;
+
+/* Associative operators ([P2] "Inclusive, exclusive and associative": any
+ * associative operator, commutativity not required).  Operands are always
+ * combined as (earlier) (+) (later).
+ *   SUM      u32: a + b mod 2^32, identity 0;  f32: a + b, identity +0.0f
+ *   MAX      u32: identity 0;          f32: identity -inf
+ *   MIN      u32: identity 0xFFFFFFFF; f32: identity +inf
+ *            (max/min keep the earlier operand on ties; f32 inputs must not
+ *             hold NaN)
+ *   AND/OR/XOR  u32 only; identities 0xFFFFFFFF / 0 / 0
+ *   AFFINE16 u32 only: the linear-recurrence pair of [P2] "What scan builds"
+ *            over the integers mod 2^16, packed (a << 16) | b:
+ *            (a1,b1) (+) (a2,b2) = (a1*a2, a2*b1 + b2); identity 0x00010000.
+ *            Not commutative. */
+typedef enum ps_op {
+    PS_OP_SUM = 0,
+    PS_OP_MAX = 1,
+    PS_OP_MIN = 2,
+    PS_OP_AND = 3,
+    PS_OP_OR = 4,
+    PS_OP_XOR = 5,
+    PS_OP_AFFINE16 = 6
+} ps_op;
+
+/* ---------------------------------------------------------------------------
+ * Flat scans.  [P2] "Inclusive, exclusive and associative":
+ *   inclusive  out[i] = in[0] (+) ... (+) in[i]
+ *   exclusive  out[0] = identity, out[i] = in[0] (+) ... (+) in[i-1]
+ * computed in one pass by the chained scan with decoupled look-back
+ * ([P1] "Three states in a per-block descriptor"; [P2] "Scanning a whole
+ * array: three grid strategies").
+ *   in, out : n elements each; in == out (exact in-place) is allowed, any
+ *             other overlap returns PS_ERR_ALIAS.  4-byte alignment
+ *             required; 16-byte alignment of both selects the vector path.
+ *   n       : element count, 0 <= n < 2^32.
+ *   total   : optional (may be NULL) device pointer to ONE element that
+ *             receives the fold of all n inputs (identity when n == 0) --
+ *             the allocation size when offsets are built from lengths
+ *             ([P3] "Scan as an index generator").
+ * ------------------------------------------------------------------------- */
+ps_status ps_scan_exclusive_u32(void *ws, size_t *ws_bytes, const uint32_t *in,
+                                uint32_t *out, uint64_t n, uint32_t *total,
+                                void *stream);
+ps_status ps_scan_inclusive_u32(void *ws, size_t *ws_bytes, const uint32_t *in,
+                                uint32_t *out, uint64_t n, uint32_t *total,
+                                void *stream);
+ps_status ps_scan_exclusive_f32(void *ws, size_t *ws_bytes, const float *in,
+                                float *out, uint64_t n, float *total,
+                                void *stream);
+ps_status ps_scan_inclusive_f32(void *ws, size_t *ws_bytes, const float *in,
+                                float *out, uint64_t n, float *total,
+                                void *stream);
+
+/* Generic associative-operator scan: the same pass for any (op, dtype) pair
+ * listed under ps_op.  `in`, `out` and `total` point to elements of `dtype`
+ * (uint32_t or float); inclusive != 0 selects the inclusive form.  Pairs not
+ * listed return PS_ERR_UNSUPPORTED. */
+ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
+                  int inclusive, const void *in, void *out, uint64_t n,
+                  void *total, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Segmented uint32 sum scan over CSR offsets ([P5] "Prefix scans and
+ * segmented scans", "Contract", "Limitations"; the carried segment flag of
+ * [P2] "What scan builds").
+ *   values       : n uint32 inputs.
+ *   offsets      : num_segments + 1 uint32 offsets; segment s is
+ *                  [offsets[s], offsets[s+1]).  The terminal offset is
+ *                  mandatory; repeated offsets are empty segments.  Offsets
+ *                  must be non-decreasing with offsets[num_segments] <= n:
+ *                  this is ASSUMED, not checked, on this hot path (use
+ *                  ps_validate_offsets when unsure).
+ *   out          : n uint32 outputs.  For every row i of segment s:
+ *                  exclusive  out[i] = sum of values[offsets[s] .. i-1]
+ *                  inclusive  out[i] = sum of values[offsets[s] .. i]
+ *                  (mod 2^32).  Rows outside [offsets[0],
+ *                  offsets[num_segments]) belong to no segment and are NOT
+ *                  written; empty segments write nothing.
+ *   inclusive    : nonzero for the inclusive form.
+ * Any overlap of out with values or offsets returns PS_ERR_ALIAS.
+ * num_segments may be 0 (nothing is written). */
+ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes,
+                                const uint32_t *values, uint64_t n,
+                                const uint32_t *offsets, uint32_t num_segments,
+                                uint32_t *out, int inclusive, void *stream);
+
+/* Optional check of the offsets contract above, on the device.  Writes to
+ * *result (device int64): -1 when valid, else the first index s with
+ * offsets[s] > offsets[s+1], or num_segments when offsets[num_segments] > n.
+ * Needs no workspace. */
+ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_segments,
+                              uint64_t n, int64_t *result, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Stable stream compaction ([P3] "Worked example: Stable stream compaction";
+ * [P2] "What scan builds"): every record whose flag is nonzero is copied,
+ * bitwise and in input order, to out[0], out[1], ...  The positions are the
+ * exclusive scan of the flags, fused into the same pass (never materialised);
+ * *num_selected (device uint64) receives the count = last offset + last flag.
+ * Slots of out at or past the count are not touched.
+ *   records      : n records of record_bytes bytes each (4, 8 or 16),
+ *                  aligned to record_bytes.
+ *   flags        : n bytes, 0 = drop, anything else = keep.
+ *   out          : room for n records (the count is not known in advance).
+ * out must not overlap records or flags (PS_ERR_ALIAS). */
+ps_status ps_compact(void *ws, size_t *ws_bytes, const void *records,
+                     uint32_t record_bytes, const uint8_t *flags, uint64_t n,
+                     void *out, uint64_t *num_selected, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement and diagnostics (not part of the scan itself).
+ * ------------------------------------------------------------------------- */
+
+/* Plain streaming copy of n uint32 (16-byte vector path when aligned): the
+ * practical HBM ceiling next to which the scans are read, and the reference
+ * kernel of known size used to scale the hardware byte counters. */
+ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *stream);
+
+/* Exclusive uint32 sum scan (same kernel as ps_scan_exclusive_u32, built
+ * with per-tile instrumentation of the look-back of [P1] "Why the work
+ * stays linear").  stats: device buffer of 4 * tiles uint32, tiles reported
+ * by ps_lookback_tiles(n); per tile: [0] poll rounds, [1] windows of 64
+ * predecessors walked, [2] look-back time in 100 MHz ticks (low 32 bits),
+ * [3] number of polls that found an unpublished predecessor.
+ * aggregate_only != 0 (a test of the sliding window): tiles after tile 0
+ * never publish their inclusive prefix, so every look-back walks back to
+ * tile 0 -- quadratic in the tile count, meant for small n only. */
+ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uint32_t *in,
+                                uint32_t *out, uint64_t n, uint32_t *stats,
+                                int aggregate_only, void *stream);
+uint64_t ps_lookback_tiles(uint64_t n);
+
+/* Kernel timing with HIP events placed around the main scan kernel of every
+ * call (the workspace clear is outside the pair).  enable != 0 starts a new
+ * measurement; ps_kernel_timing_read synchronises on the recorded events and
+ * returns the summed milliseconds and the number of timed launches. */
+ps_status ps_kernel_timing(int enable);
+ps_status ps_kernel_timing_read(double *total_ms, uint64_t *launches);
+
+/* Elements per tile of the flat scan kernel for `dtype`, and the library
+ * version string. */
+uint32_t ps_tile_elements(ps_dtype dtype);
+const char *ps_version(void);
+const char *ps_status_string(ps_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWPS_H */

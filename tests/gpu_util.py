@@ -1,0 +1,68 @@
+"""Helpers of the GPU parity tests: device transfer, workspace error word,
+and the fp32 tolerance of the flat sum scan."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+TILE = 4096  # elements per tile of the flat and segmented kernels
+
+
+def require_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import device_wide_prefix_chained_amd as dw
+    dw.lib()  # raises when the HIP library is missing: no silent fallback
+    return dw
+
+
+def say(*args):
+    """Name the case on stdout before a GPU step (flushed, so that it survives
+    a crash of the process)."""
+    print("[gpu-case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    """Host array -> device tensor.  uint32 data travels as bit-identical int32
+    tensors (PyTorch's uint32 support is minimal; the library reads bits)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to("cuda")
+
+
+def host(t):
+    """Device tensor -> host array; int32 tensors come back as uint32."""
+    import torch
+    torch.cuda.synchronize()
+    a = t.cpu().numpy()
+    return a.view(np.uint32) if a.dtype == np.int32 else a
+
+
+def filled_dev(like, fill):
+    """A device array shaped like the host array ``like``, every element = fill."""
+    return dev(np.full_like(like, fill))
+
+
+def ws_error_word(ws) -> int:
+    """Word 1 of a workspace header: nonzero when a look-back hit its spin limit."""
+    return int(host(ws[4:8].clone()).view(np.uint32)[0])
+
+
+def assert_f32_sum_close(gpu, ref64, absprefix, exclusive):
+    """|gpu_i - ref_i| <= 1e-5 * sum_{j<=i} |x_j| at every index; exclusive
+    output 0 must be exactly +0.0."""
+    gpu64 = gpu.astype(np.float64)
+    err = np.abs(gpu64 - ref64)
+    tol = 1e-5 * absprefix
+    bad = np.nonzero(err > tol)[0]
+    assert bad.size == 0, ("fp32 tolerance broken at %d indices, first %d: gpu %r ref %r tol %r"
+                           % (bad.size, bad[0], gpu[bad[0]], ref64[bad[0]], tol[bad[0]]))
+    if exclusive and gpu.size:
+        assert gpu[0] == 0.0 and not np.signbit(gpu[0])
+    return float((err / np.maximum(tol, 1e-300)).max()) if gpu.size else 0.0

@@ -1,0 +1,154 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares (and the binding wraps each), answers size queries and rejects bad
+arguments before anything is launched.  No compute call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dwps.h")
+
+
+def _lib():
+    import device_wide_prefix_chained_amd as d
+    if not os.path.exists(os.path.join(ROOT, "device_wide_prefix_chained_amd", "libdwps.so")):
+        from device_wide_prefix_chained_amd import build
+        build.build()
+    return d.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ps_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_lists_the_boundary():
+    names = header_functions()
+    for required in ("ps_scan_exclusive_u32", "ps_scan_inclusive_u32", "ps_scan_exclusive_f32",
+                     "ps_scan_inclusive_f32", "ps_scan", "ps_segmented_scan_u32", "ps_compact"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    so = lib._name
+    out = subprocess.run(["nm", "-D", "--defined-only", so], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ps_\w+)", out))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name), name
+
+
+def test_binding_wraps_every_declared_symbol():
+    import device_wide_prefix_chained_amd as d
+    for name in header_functions():
+        assert callable(getattr(d, name, None)), name
+
+
+def _wsq(lib, fn, *args):
+    need = ctypes.c_size_t(0)
+    st = getattr(lib, fn)(None, ctypes.byref(need), *args)
+    return st, need.value
+
+
+def test_size_queries():
+    lib = _lib()
+    tile = lib.ps_tile_elements(0)
+    assert tile == 4096
+    for n in (0, 1, tile - 1, tile, tile + 1, 1 << 20, (1 << 28) - 12345, 1 << 28):
+        st, need = _wsq(lib, "ps_scan_exclusive_u32", None, None, n, None, None)
+        tiles = -(-n // tile)
+        assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256, n
+        st2, need2 = _wsq(lib, "ps_scan", 3, 0, 1, None, None, n, None, None)
+        assert st2 == 0 and need2 == need
+        assert lib.ps_lookback_tiles(n) == tiles
+    st, need = _wsq(lib, "ps_segmented_scan_u32", None, 1 << 26, None, 1 << 16, None, 0, None)
+    assert st == 0 and need >= 256 + 8 * ((1 << 26) // 4096)
+    for rb in (4, 8, 16):
+        st, need = _wsq(lib, "ps_compact", None, rb, None, 1 << 26, None, None, None)
+        assert st == 0 and need > 256
+
+
+FAKE_WS = 0x10000000
+A = 0x20000000          # fake, 256-byte aligned "device" addresses: never dereferenced
+B = 0x40000000
+
+
+def _call_flat(lib, fn, ws_bytes, inp, out, n, total=None):
+    wsb = ctypes.c_size_t(ws_bytes)
+    return getattr(lib, fn)(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), ctypes.c_void_p(inp) if inp else None,
+                            ctypes.c_void_p(out) if out else None, n,
+                            ctypes.c_void_p(total) if total else None, None)
+
+
+def test_argument_errors_flat():
+    lib = _lib()
+    PS_ERR_NULL, PS_ERR_ALIAS, PS_ERR_SIZE, PS_ERR_WORKSPACE, PS_ERR_UNSUPPORTED, PS_ERR_ALIGNMENT = 1, 2, 3, 4, 5, 7
+    big = 1 << 30
+    for fn in ("ps_scan_exclusive_u32", "ps_scan_inclusive_u32", "ps_scan_exclusive_f32", "ps_scan_inclusive_f32"):
+        assert _call_flat(lib, fn, big, A, B, 1 << 32) == PS_ERR_SIZE
+        assert _call_flat(lib, fn, 16, A, B, 100000) == PS_ERR_WORKSPACE
+        assert _call_flat(lib, fn, big, None, B, 10) == PS_ERR_NULL
+        assert _call_flat(lib, fn, big, A, None, 10) == PS_ERR_NULL
+        assert _call_flat(lib, fn, big, A + 2, B, 10) == PS_ERR_ALIGNMENT
+        assert _call_flat(lib, fn, big, A, B + 1, 10) == PS_ERR_ALIGNMENT
+        assert _call_flat(lib, fn, big, A, A + 4, 10) == PS_ERR_ALIAS       # partial overlap
+        assert _call_flat(lib, fn, big, A + 36, A, 10) == PS_ERR_ALIAS
+        # n == 0 without a total launches nothing and succeeds
+        assert _call_flat(lib, fn, big, None, None, 0) == 0
+    # ws_bytes == NULL
+    assert lib.ps_scan_exclusive_u32(None, None, None, None, 5, None, None) == PS_ERR_NULL
+    # unsupported operator / dtype pairs
+    wsb = ctypes.c_size_t(big)
+    for op, dt in ((3, 1), (4, 1), (5, 1), (6, 1), (7, 0), (99, 0), (0, 2)):
+        st = lib.ps_scan(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), op, dt, 0, ctypes.c_void_p(A),
+                         ctypes.c_void_p(B), 10, None, None)
+        assert st == PS_ERR_UNSUPPORTED, (op, dt)
+
+
+def test_argument_errors_segmented_and_compact():
+    lib = _lib()
+    big = ctypes.c_size_t(1 << 30)
+    ws = ctypes.c_void_p(FAKE_WS)
+    seg = lib.ps_segmented_scan_u32
+    # out overlapping values or offsets
+    assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 4, ctypes.c_void_p(A), 0, None) == 2
+    assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 4, ctypes.c_void_p(B - 16), 0, None) == 2
+    assert seg(ws, ctypes.byref(big), None, 100, ctypes.c_void_p(B), 4, ctypes.c_void_p(A), 0, None) == 1
+    assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 1 << 32, ctypes.c_void_p(B), 4, ctypes.c_void_p(A), 0, None) == 3
+    assert seg(ws, ctypes.byref(ctypes.c_size_t(8)), ctypes.c_void_p(A), 100000, ctypes.c_void_p(B), 4,
+               ctypes.c_void_p(A + (1 << 20)), 0, None) == 4
+    # zero segments or n == 0: nothing to do
+    assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 0, ctypes.c_void_p(B + 4096), 0, None) == 0
+    comp = lib.ps_compact
+    C = 0x60000000
+    for rb in (1, 2, 3, 12, 32):
+        assert comp(ws, ctypes.byref(big), ctypes.c_void_p(A), rb, ctypes.c_void_p(B), 10, ctypes.c_void_p(C),
+                    ctypes.c_void_p(C + 4096), None) == 5
+    assert comp(ws, ctypes.byref(big), ctypes.c_void_p(A), 16, ctypes.c_void_p(B), 10, ctypes.c_void_p(A + 32),
+                ctypes.c_void_p(C), None) == 2
+    assert comp(ws, ctypes.byref(big), ctypes.c_void_p(A), 16, ctypes.c_void_p(B), 10, ctypes.c_void_p(C),
+                None, None) == 1
+    assert comp(ws, ctypes.byref(big), ctypes.c_void_p(A + 8), 16, ctypes.c_void_p(B), 10, ctypes.c_void_p(C),
+                ctypes.c_void_p(C + 4096), None) == 7
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in range(8):
+        s = lib.ps_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.ps_status_string(1234).decode() == "unknown status"
+    assert b"gfx950" in lib.ps_version()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import device_wide_prefix_chained_amd as d
+    x = torch.zeros(8, dtype=torch.uint32)
+    with pytest.raises(ValueError):
+        d.ps_scan_exclusive_u32(x, x.clone())

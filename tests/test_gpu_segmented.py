@@ -1,0 +1,124 @@
+"""Parity of the segmented scan (HIP, through the C ABI) with the oracle:
+bit-exact, including the rows that belong to no segment (left untouched)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import TILE, dev, host, require_gpu, say, ws_error_word
+from pins import golden
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xDEADBEEF
+
+
+@pytest.fixture(scope="module")
+def dw():
+    return require_gpu()
+
+
+def _run(dw, x, offsets, inclusive, workspace=None):
+    d_out = dev(np.full(x.size, SENTINEL, np.uint32))
+    dw.ps_segmented_scan_u32(dev(x), dev(offsets), d_out, inclusive=inclusive, workspace=workspace)
+    return host(d_out)
+
+
+def _check(dw, orc, x, offsets, inclusive):
+    got = _run(dw, x, offsets, inclusive)
+    ref = orc.segmented_scan_u32(x, offsets, inclusive, sentinel=SENTINEL)
+    if not np.array_equal(got, ref):
+        bad = np.nonzero(got != ref)[0]
+        raise AssertionError("%d rows differ, first %d: gpu %d oracle %d"
+                             % (bad.size, bad[0], got[bad[0]], ref[bad[0]]))
+
+
+def test_worked_example(dw, orc):
+    g = golden("p5_segmented_example.json")
+    x = np.array(g["values"], np.uint32)
+    off = np.array(g["offsets"], np.uint32)
+    for inclusive, key in ((False, "exclusive"), (True, "inclusive")):
+        say("segmented worked example", key)
+        assert _run(dw, x, off, inclusive).tolist() == g[key]
+
+
+@pytest.mark.parametrize("n", [1, 5, 100, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, 100_003, 1_000_003])
+@pytest.mark.parametrize("nseg", [1, 2, 17, 1000])
+@pytest.mark.parametrize("cover", [True, False])
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_random_segmentations(dw, orc, n, nseg, cover, inclusive):
+    x = wl.full_range_u32(n, seed=n + nseg)
+    off = wl.random_segments(n, nseg, seed=n * 7 + nseg, cover=cover)
+    say("segmented", n, nseg, cover, inclusive)
+    _check(dw, orc, x, off, inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_special_segmentations(dw, orc, inclusive):
+    n = 50_000
+    x = wl.full_range_u32(n, seed=3)
+    cases = {
+        "unit segments": np.arange(n + 1, dtype=np.uint32),
+        "one segment": np.array([0, n], np.uint32),
+        "all empty at 0": np.zeros(9, np.uint32),
+        "all empty inside": np.full(5, 777, np.uint32),
+        "zero segments": np.array([0], np.uint32),
+        "heads on tile edges": np.arange(0, n + 1, TILE, dtype=np.uint32),
+        "heads one past tile edges": np.concatenate(([0], np.arange(1, n, TILE), [n])).astype(np.uint32),
+        "empties between": np.array([0, 10, 10, 10, TILE, TILE, 3 * TILE, n, n], np.uint32),
+        "gap at both ends": np.array([TILE + 5, 2 * TILE, 3 * TILE + 1, n - 100], np.uint32),
+    }
+    for name, off in cases.items():
+        say("segmented special", name, inclusive)
+        _check(dw, orc, x, off, inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_long_segments_chain(dw, orc, inclusive):
+    """Segments much longer than a tile: head-free tiles must chain through
+    the look-back, and the chain must stop at every head."""
+    n = 400 * TILE + 33
+    x = wl.full_range_u32(n, seed=4)
+    off = np.array([0, 3, 150 * TILE + 1, 150 * TILE + 2, 399 * TILE, n], np.uint32)
+    say("long segments", inclusive)
+    _check(dw, orc, x, off, inclusive)
+
+
+def test_repeated_runs_stay_exact(dw, orc):
+    import torch
+    values, off = wl.zipf_segments(n=1 << 22, num_segments=1 << 12, seed=12)
+    ref = orc.segmented_scan_u32(values, off, False, sentinel=SENTINEL)
+    ws = torch.empty(dw.workspace_bytes("ps_segmented_scan_u32", None, values.size, None, off.size - 1,
+                                        None, 0, None), dtype=torch.uint8, device="cuda")
+    for it in range(20):
+        say("segmented repeat", it)
+        got = _run(dw, values, off, False, workspace=ws)
+        assert np.array_equal(got, ref), it
+        assert ws_error_word(ws) == 0
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_skewed_config(dw, orc, inclusive):
+    """2^26 values in [0, 1023] over 2^16 CSR segments: 10% empty, one holding
+    25% of the elements, the rest with rank-size Zipf(1.2) lengths."""
+    values, off = wl.zipf_segments()
+    say("segmented config", inclusive)
+    _check(dw, orc, values, off, inclusive)
+
+
+def test_validate_offsets(dw, orc):
+    import torch
+    r = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cases = [
+        (np.array([0, 2, 5, 6], np.uint32), 6),
+        (np.array([0, 0, 0], np.uint32), 0),
+        (np.array([0, 3, 2, 6], np.uint32), 6),
+        (np.array([0, 2, 5, 7], np.uint32), 6),
+        (np.array([5], np.uint32), 4),
+        (wl.zipf_segments(n=1 << 20, num_segments=1 << 10, seed=2)[1], 1 << 20),
+    ]
+    bad = wl.zipf_segments(n=1 << 20, num_segments=1 << 10, seed=2)[1].copy()
+    bad[700], bad[701] = bad[701] + 1, bad[700]
+    cases.append((bad, 1 << 20))
+    for off, n in cases:
+        dw.ps_validate_offsets(dev(off), n, r)
+        assert int(host(r)[0]) == orc.validate_offsets(off, n)
