@@ -101,7 +101,7 @@ def build_workload(name: str):
         x = wl.f32_normal()
         d_in, d_out = dev(x), torch.empty(n, dtype=torch.float32, device="cuda")
         op = "sum" if name == "f32" else "max"
-        ws = torch.empty(dw.workspace_bytes("ps_scan", None, None, 0, 1, 1, None, None, n, None, None),
+        ws = torch.empty(dw.workspace_bytes("ps_scan", 0, 1, 1, None, None, n, None, None),
                          dtype=torch.uint8, device="cuda")
         run = lambda: dw.ps_scan(op, True, d_in, d_out, workspace=ws)  # noqa: E731
         return dict(desc="fp32 inclusive %s scan, n=2^27, N(0,1), seed 3" % op, dtype="f32", n=n,

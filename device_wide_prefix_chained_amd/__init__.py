@@ -22,7 +22,9 @@ from ._binding import (  # noqa: F401
     ps_kernel_timing,
     ps_kernel_timing_read,
     ps_lookback_stats_u32,
+    ps_lookback_group,
     ps_lookback_tiles,
+    ps_lookback_window,
     ps_scan,
     ps_scan_exclusive_f32,
     ps_scan_exclusive_u32,

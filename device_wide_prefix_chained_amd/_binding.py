@@ -69,6 +69,10 @@ def lib() -> ctypes.CDLL:
     L.ps_kernel_timing.restype = i32
     L.ps_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64)]
     L.ps_kernel_timing_read.restype = i32
+    L.ps_lookback_window.argtypes = []
+    L.ps_lookback_window.restype = u32
+    L.ps_lookback_group.argtypes = []
+    L.ps_lookback_group.restype = u32
     L.ps_tile_elements.argtypes = [i32]
     L.ps_tile_elements.restype = u32
     L.ps_version.argtypes = []
@@ -238,7 +242,10 @@ def ps_compact(records, flags, out, num_selected, workspace=None, stream=None):
         raise ValueError("records must have one row per flag and out the same row shape")
     if out.shape[0] < n:
         raise ValueError("out needs room for n records")
-    rb = records.element_size() * (records[0].numel() if records.dim() > 1 else 1)
+    row = 1
+    for d in records.shape[1:]:
+        row *= int(d)
+    rb = records.element_size() * row
     s = _stream(flags, stream)
     L = lib()
     call = lambda ws, wsb: L.ps_compact(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa: E731
@@ -268,6 +275,14 @@ def ps_kernel_timing_read():
     cnt = ctypes.c_uint64(0)
     _check("ps_kernel_timing_read", lib().ps_kernel_timing_read(ctypes.byref(ms), ctypes.byref(cnt)))
     return ms.value, cnt.value
+
+
+def ps_lookback_window() -> int:
+    return int(lib().ps_lookback_window())
+
+
+def ps_lookback_group() -> int:
+    return int(lib().ps_lookback_group())
 
 
 def ps_tile_elements(dtype=PS_U32) -> int:

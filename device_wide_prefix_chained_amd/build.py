@@ -26,6 +26,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep single-lane atomics as written: the wave-wide rewrite consumes the
+    # returned ticket at once, which serialises it with the look-back polls
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

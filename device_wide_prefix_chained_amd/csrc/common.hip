@@ -65,6 +65,36 @@ __global__ void finish_validate_kernel(unsigned long long *p) {
 }
 
 // ---------------------------------------------------------------------------
+// persistent grids
+// ---------------------------------------------------------------------------
+namespace {
+std::mutex g_grid_mu;
+std::vector<std::pair<std::pair<const void *, int>, uint32_t>> g_grid_cache;
+}  // namespace
+
+uint32_t persistent_grid(const void *kernel, int block_threads, uint32_t work_items) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    uint32_t resident = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_grid_mu);
+        for (auto &e : g_grid_cache)
+            if (e.first.first == kernel && e.first.second == dev) resident = e.second;
+    }
+    if (!resident) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess)
+            return 0;
+        if (per_cu < 1) per_cu = 1;
+        resident = (uint32_t)cus * (uint32_t)per_cu;
+        std::lock_guard<std::mutex> lk(g_grid_mu);
+        g_grid_cache.push_back({{kernel, dev}, resident});
+    }
+    return resident < work_items ? resident : work_items;
+}
+
+// ---------------------------------------------------------------------------
 // kernel timing
 // ---------------------------------------------------------------------------
 namespace {
@@ -78,7 +108,7 @@ void timing_begin(hipStream_t stream) {
     if (!g_timing_on.load(std::memory_order_relaxed)) return;
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return;
-    hipEventRecord(e, stream);
+    (void)hipEventRecord(e, stream);
     t_pending_start = e;
 }
 
@@ -86,7 +116,7 @@ void timing_end(hipStream_t stream) {
     if (!g_timing_on.load(std::memory_order_relaxed) || !t_pending_start) return;
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return;
-    hipEventRecord(e, stream);
+    (void)hipEventRecord(e, stream);
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_events.emplace_back(t_pending_start, e);
     t_pending_start = nullptr;
@@ -140,8 +170,8 @@ extern "C" ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_s
 extern "C" ps_status ps_kernel_timing(int enable) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     for (auto &pr : g_timing_events) {
-        hipEventDestroy(pr.first);
-        hipEventDestroy(pr.second);
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
     }
     g_timing_events.clear();
     g_timing_on.store(enable != 0);

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(NT) void compact_kernel(const Rec *records, const u
             if (lane == 0) desc_publish(desc, desc_word(ST_PREFIX, count));
         } else {
             if (lane == 0) desc_publish(desc + tile, desc_word(ST_AGGREGATE, count));
-            excl = lookback<SumU32, false>(desc, tile, lane, st, ctr + 1);
+            excl = lookback<SumU32, DWPS_LOOKBACK_K, false>(desc, tile, lane, st, ctr + 1);
             if (lane == 0) desc_publish(desc + tile, desc_word(ST_PREFIX, excl + count));
         }
         if (lane == 0) {

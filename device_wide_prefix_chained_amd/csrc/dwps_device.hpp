@@ -166,23 +166,31 @@ struct LookbackStats {
 // limit only trips on a broken workspace or a faulting predecessor.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-// Decoupled look-back, executed by one full wave.  Lane k of a poll reads the
-// descriptor of tile (nearest - 63 + k), so lane 63 holds the nearest
-// predecessor and lower lanes hold earlier tiles (lane order = element
-// order).  Indices below 0 read as a PREFIX carrying the identity.  Let p be
-// the highest lane in PREFIX state: if some lane at or above p is still
-// INVALID the window is polled again (each poll reloads every word); else the
-// payloads of lanes p..63 are folded in order and, if p exists, the fold is
-// final; otherwise the window slides 64 tiles back.  (After kSpinLimit
-// consecutive stalls the unpublished lanes are folded as they are and *err is
-// set.)  Returns the exclusive
-// prefix of `tile` (the fold of every earlier tile).  Terminates because tile
-// 0 publishes PREFIX without waiting and every tile only waits on tiles that
-// took their ticket earlier, hence are resident or finished
+// Descriptors read per lane per poll (the look-back window is 64 * K tiles).
+#ifndef DWPS_LOOKBACK_K
+#define DWPS_LOOKBACK_K 2
+#endif
+
+// Decoupled look-back, executed by one full wave, reading K descriptors per
+// lane per poll, i.e. a window of 64*K predecessors.  Lane l holds tiles
+// (base + l*K) .. (base + l*K + K-1) of the window, where base =
+// nearest - 64*K + 1, so lane 63's last word is the nearest predecessor and
+// (lane, word) order is tile order.  Indices below 0 read as a PREFIX
+// carrying the identity.  Let p be the nearest word in PREFIX state: if any
+// word nearer than p is still INVALID the whole window is polled again (each
+// poll reloads every word); otherwise the payloads from p to the nearest
+// predecessor are folded in tile order (each lane folds its own words, then
+// one wave scan joins the lanes) and, if p exists, the fold is final; else
+// the window slides 64*K tiles back.  After kSpinLimit consecutive stalls the
+// unpublished words are folded as they are and *err is set.  Returns the
+// exclusive prefix of `tile` (the fold of every earlier tile).  Terminates
+// because tile 0 publishes PREFIX without waiting and every tile only waits
+// on tiles that took their ticket earlier, hence are resident or finished
 // ("Single-Pass Prefix Scan with Decoupled Look-Back", sections "Three states
 // in a per-block descriptor", "Why the work stays linear" and "Where the
-// algorithm meets the hardware").
-template <class Op, bool STATS>
+// algorithm meets the hardware"; the window of 64*K words read at once is
+// this implementation's answer to the latency of a long dependent chain).
+template <class Op, int K, bool STATS>
 __device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_t tile,
                                                    uint32_t lane, LookbackStats &st,
                                                    uint32_t *err) {
@@ -192,14 +200,29 @@ __device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_
     uint32_t spins = 0;
     const uint64_t pad = desc_word(ST_PREFIX, to_bits(Op::id()));
     for (;;) {
-        const int64_t idx = nearest - 63 + (int64_t)lane;
-        const uint64_t w = (idx >= 0) ? desc_poll(desc + idx) : pad;
-        const uint32_t state = (uint32_t)(w >> 32);
-        const uint64_t pm = ballot(state == ST_PREFIX);
-        const uint64_t im = ballot(state == ST_INVALID);
-        const uint32_t lim = pm ? 63u - (uint32_t)__builtin_clzll(pm) : 0u;
+        const int64_t first = nearest - 64 * K + 1 + (int64_t)lane * K;
+        uint64_t w[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const int64_t idx = first + j;
+            w[j] = (idx >= 0) ? desc_poll(desc + idx) : pad;
+        }
+        // nearest PREFIX word of this lane (-1 if none), and whether a word
+        // nearer than it (in this lane) is INVALID
+        int jp = -1;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            if ((uint32_t)(w[j] >> 32) == ST_PREFIX) jp = j;
+        bool inv_after = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            if (j > jp && (uint32_t)(w[j] >> 32) == ST_INVALID) inv_after = true;
+        const uint64_t pm = ballot(jp >= 0);
+        const uint32_t lp = pm ? 63u - (uint32_t)__builtin_clzll(pm) : 0u;
+        // lanes above lp count entirely; lane lp counts from its PREFIX word
+        const bool relevant = pm ? (lane >= lp) : true;
         if (STATS) st.polls++;
-        if (im & (~0ull << lim)) {
+        if (ballot(relevant && inv_after)) {
             if (STATS) st.stalls++;
             if (++spins < kSpinLimit) {
                 __builtin_amdgcn_s_sleep(1);
@@ -208,12 +231,18 @@ __device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_
             if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         spins = 0;
-        T v = (lane >= lim) ? from_bits<T>((uint32_t)w) : Op::id();
+        T v = Op::id();
+        if (relevant) {
+            const int jfrom = (pm && lane == lp) ? jp : 0;
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (j >= jfrom) v = Op::op(v, from_bits<T>((uint32_t)w[j]));
+        }
         v = wave_inclusive<Op>(v);
         acc = Op::op(read_lane(v, 63), acc);
         if (STATS) st.windows++;
         if (pm) break;
-        nearest -= 64;
+        nearest -= 64 * K;
     }
     return acc;
 }

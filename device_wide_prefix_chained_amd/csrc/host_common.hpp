@@ -53,6 +53,11 @@ inline ps_status launch_status() {
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
 }
 
+// Grid of a persistent kernel: the number of its workgroups the current
+// device keeps resident (occupancy x compute units, cached per kernel and
+// device), capped at `work_items`.  0 on a HIP error.
+uint32_t persistent_grid(const void *kernel, int block_threads, uint32_t work_items);
+
 // Kernel timing hooks: when enabled (ps_kernel_timing), timing_begin/end
 // record a HIP event pair around the main kernel of the call on `stream`.
 void timing_begin(hipStream_t stream);

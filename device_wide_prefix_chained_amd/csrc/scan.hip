@@ -3,158 +3,250 @@
 // Prefix Sum (Scan), in depth", section "Scanning a whole array: three grid
 // strategies").
 //
-// One workgroup of NT threads scans one tile of NT * Q * 4 elements.
-//   1. Ticket: thread 0 takes the tile index from an atomic counter, so every
-//      tile it may wait on was handed out earlier and is already resident or
-//      finished (blockIdx order is not a dispatch guarantee).
-//   2. Load: wave w of the tile owns Q * 256 consecutive elements; load q of
-//      lane l is the 16-byte group at element q*256 + 4*l of that span, so each
-//      wave-wide load instruction reads 1 KiB of contiguous memory.
-//   3. Thread-serial inclusive scan of each group of four, wave64 DPP scan of
-//      the Q group totals, LDS scan of the NT/64 wave totals -> the tile
-//      aggregate.
-//   4. Wave 0 publishes the aggregate (tile 0: its inclusive prefix), looks
-//      back over the predecessors' descriptors, publishes the tile's inclusive
-//      prefix, and hands the exclusive prefix to the other waves through LDS.
-//   5. Every lane combines tile prefix (+) wave prefix (+) group prefix (+)
-//      lane prefix (+) its element prefix and stores 16 bytes per group.
+// Persistent, wave-specialised workgroups.  The grid holds as many
+// workgroups as the GPU keeps resident; each one loops over tiles of
+// D * Q * 256 elements taken from the atomic tile counter.  A workgroup has
+// one control wave and D data waves.  A tile passes through three phases:
+//   phase k-1  its loads are issued (into a register buffer);
+//   phase k    it is scanned, its aggregate is published, and its
+//              tile-relative outputs are parked in LDS, which frees the
+//              register buffer for the loads of the tile two ahead;
+//   phase k+1  its look-back runs -- one phase after its aggregate went out,
+//              like the aggregates of the tiles around it, so the poll
+//              normally finds every word it needs -- and the data waves add
+//              the prefix to the parked outputs and store them.
+// Control wave (per phase): publish the current tile's aggregate, take the
+// ticket of the tile three ahead, look back for the previous tile, publish
+// its inclusive prefix.  Its vector-memory queue holds only descriptor
+// traffic, so a poll never waits behind a tile load.
+// Data waves (per phase): finalize the current tile into LDS, issue the loads
+// of the tile two ahead; after the barrier, store the previous tile from LDS,
+// then scan the next tile.  Up to two tiles of loads per workgroup are in
+// flight while look-backs are resolved a phase behind (a persistent
+// grid-stride loop, as in "Where the algorithm meets the hardware", with the
+// look-back joining the tiles inside one launch).  Tickets come from an
+// atomic counter, so every tile a look-back can wait on was handed out
+// earlier to a running workgroup, which finishes it without waiting on
+// anything later ("Scanning a whole array: three grid strategies"); forward
+// progress follows by induction on the smallest unfinished tile.
 #include <hip/hip_runtime.h>
 
 #include "dwps_device.hpp"
 #include "host_common.hpp"
+#include "tile_io.hpp"
 
 namespace dwps {
 
-template <class Op, int NT, int Q, bool INCL, bool VEC, bool STATS>
-__global__ __launch_bounds__(NT) void scan_kernel(const typename Op::T *in, typename Op::T *out,
-                                                  uint32_t n, uint32_t num_tiles, uint32_t *ctr,
-                                                  uint64_t *desc, typename Op::T *total,
-                                                  uint32_t *stats, int aggregate_only) {
+constexpr int kParkSlots = 3;
+
+template <class Op, int D, int Q>
+struct ScanShared {
     using T = typename Op::T;
-    constexpr int NW = NT / 64;
-    constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
-    constexpr uint32_t TILE = (uint32_t)NT * (uint32_t)Q * 4u;
+    v4u park[kParkSlots][D * Q * 64];  // tile-relative outputs, 16 bytes per lane-group
+    uint32_t t0;
+    uint32_t next;
+    T wt[2][D];  // wave totals, double-buffered by phase parity
+    T prefix;
+};
 
-    __shared__ uint32_t s_tile;
-    __shared__ T s_wave[NW];
-    __shared__ T s_prefix;
+// Tile ids of the pipeline, identical in every wave of the workgroup
+// (num_tiles = none): prev2 waits for its prefix, prev and cur are parked or
+// being parked, f1 and f2 are in flight.  Every value comes from LDS through
+// readfirstlane, so the compiler keeps them in scalar registers and branches
+// on them with scalar branches.
+struct PipeTiles {
+    uint32_t prev2, prev, cur, f1, f2;
+    __device__ __forceinline__ bool drained(uint32_t num_tiles) const {
+        return prev < num_tiles ? false : (cur >= num_tiles && f1 >= num_tiles && f2 >= num_tiles);
+    }
+    __device__ __forceinline__ void advance(uint32_t after, uint32_t num_tiles) {
+        prev2 = prev;
+        prev = cur;
+        cur = f1;
+        f1 = f2;
+        f2 = (f2 < num_tiles) ? after : num_tiles;
+    }
+};
 
-    const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & 63u;
-    const uint32_t wave = tid >> 6;
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-    if (tid == 0) s_tile = take_ticket(ctr);
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint64_t tile_base = (uint64_t)tile * TILE;
-    const uint64_t span = tile_base + (uint64_t)wave * WAVE_ELEMS + 4u * lane;
-    const bool full = tile_base + TILE <= (uint64_t)n;
-
-    // ---- 2. load -----------------------------------------------------------
-    T v[Q][4];
-    if (VEC && full) {
+// Control wave: aggregates, look-back, prefixes.  Phase k runs between
+// barriers A_k and B_k, while the data waves work on their side.  The
+// look-back of a tile runs two phases after its aggregate went out, so the
+// aggregates of its neighbours and the prefixes of the tiles one generation
+// older are already published: one poll, off the critical path.  The wave
+// issues its descriptor stores only after the poll has returned, so the only
+// thing it ever waits for is its own poll.
+template <class Op, int D, int Q, int LB_K, int G, bool STATS>
+__device__ __forceinline__ void control_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, uint32_t num_tiles,
+                                             uint32_t *ctr, uint64_t *desc, typename Op::T *total,
+                                             uint32_t *stats, int aggregate_only, uint32_t lane) {
+    using T = typename Op::T;
+    T agg_prev = Op::id(), agg_prev2 = Op::id();
+    T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
+    for (int par = 0;; par ^= 1) {
+        T agg = Op::id();
+        if (pt.cur < num_tiles) {
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const uint4 r = *reinterpret_cast<const uint4 *>(in + span + (uint64_t)q * 256u);
-            v[q][0] = from_bits<T>(r.x);
-            v[q][1] = from_bits<T>(r.y);
-            v[q][2] = from_bits<T>(r.z);
-            v[q][3] = from_bits<T>(r.w);
+            for (int w = 0; w < D; ++w) agg = Op::op(agg, sh.wt[par][w]);
         }
-    } else {
-#pragma unroll
-        for (int q = 0; q < Q; ++q)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t i = span + (uint64_t)q * 256u + k;
-                v[q][k] = (i < n) ? in[i] : Op::id();
-            }
-    }
-
-    // ---- 3. thread-serial, wave and block scans ---------------------------------
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        v[q][1] = Op::op(v[q][0], v[q][1]);
-        v[q][2] = Op::op(v[q][1], v[q][2]);
-        v[q][3] = Op::op(v[q][2], v[q][3]);
-    }
-    T lane_excl[Q];
-    T group_prefix[Q];
-    T run = Op::id();
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const T inc = wave_inclusive<Op>(v[q][3]);
-        lane_excl[q] = wave_shift_right<Op>(inc);
-        group_prefix[q] = run;
-        run = Op::op(run, read_lane(inc, 63));
-    }
-    if (lane == 0) s_wave[wave] = run;
-    __syncthreads();
-    T wave_prefix = Op::id();
-    T agg = Op::id();
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const T t = s_wave[w];
-        if ((uint32_t)w < wave) wave_prefix = Op::op(wave_prefix, t);
-        agg = Op::op(agg, t);
-    }
-
-    // ---- 4. publish, look back, publish -------------------------------------
-    if (wave == 0) {
+        // Only the first tile of a group looks back; the next ones of the
+        // group follow it through this wave's own registers.
         LookbackStats st;
         uint64_t t0 = 0;
         if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
         T excl = Op::id();
-        if (tile == 0) {
-            if (lane == 0) desc_publish(desc, desc_word(ST_PREFIX, to_bits(agg)));
-        } else {
-            if (lane == 0) desc_publish(desc + tile, desc_word(ST_AGGREGATE, to_bits(agg)));
-            excl = lookback<Op, STATS>(desc, tile, lane, st, ctr + 1);
-            // (diagnostic build only: aggregate_only keeps every later tile in
-            // AGGREGATE state so that each look-back walks back to tile 0)
-            if (lane == 0 && !(STATS && aggregate_only))
-                desc_publish(desc + tile, desc_word(ST_PREFIX, to_bits(Op::op(excl, agg))));
-        }
+        const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
+        const bool look = have_prev2 && (pt.prev2 % G == 0u || (STATS && aggregate_only));
+        if (look)
+            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr + 1);
+        else if (have_prev2)
+            excl = incl_last;
         if (lane == 0) {
-            s_prefix = excl;
-            if (total && tile == num_tiles - 1) *total = Op::op(excl, agg);
-            if (STATS) {
-                const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-                uint4 rec = make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
-                reinterpret_cast<uint4 *>(stats)[tile] = rec;
+            sh.prefix = excl;
+            if (pt.prev2 < num_tiles) {
+                if (total && pt.prev2 == num_tiles - 1) *total = Op::op(excl, agg_prev2);
+                if (STATS) {
+                    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+                    reinterpret_cast<uint4 *>(stats)[pt.prev2] =
+                        make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
+                }
             }
+            if (have_prev2 && !(STATS && aggregate_only))
+                desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, to_bits(Op::op(excl, agg_prev2))));
+            if (pt.cur < num_tiles)
+                desc_publish(desc + pt.cur, desc_word(pt.cur == 0 ? ST_PREFIX : ST_AGGREGATE, to_bits(agg)));
         }
+        incl_last = Op::op(excl, agg_prev2);
+        agg_prev2 = agg_prev;
+        agg_prev = agg;
+        __syncthreads();  // B: prefix of prev2 is in LDS
+        if (pt.drained(num_tiles)) break;
+        __syncthreads();  // A: the next tile id is in LDS
+        pt.advance(uniform(sh.next), num_tiles);
     }
-    __syncthreads();
+}
 
-    // ---- 5. combine and store -------------------------------------------------
-    const T base = Op::op(s_prefix, wave_prefix);
+// One phase of a data wave: `cur` holds the scanned current tile (its wave
+// totals in wt[par]), `f1` the next tile (loads in flight).  cur is parked
+// in LDS slot `slot`; slot (slot+1) % 3 holds prev2.  Data wave 0 also takes
+// the tickets: the atomic goes out at the start of the phase, ahead of the
+// wave's tile loads, and its value is needed only after barrier B.
+template <class Op, int D, int Q, int G, bool INCL, bool VEC>
+__device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q> &f1, int par, uint32_t &slot,
+                                           PipeTiles &pt, typename Op::T (&lane_excl)[Q],
+                                           typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
+                                           const typename Op::T *in, typename Op::T *out, uint32_t n,
+                                           uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
+                                           uint64_t lane_off) {
+    using T = typename Op::T;
+    constexpr uint32_t TILE = (uint32_t)D * (uint32_t)Q * 256u;
+    // the tile after f2: the next one of its group, or the first of a new
+    // group taken from the ticket counter
+    const bool need_ticket = pt.f2 < num_tiles && (pt.f2 + 1u) % G == 0u;
+    uint32_t ticket = 0;
+    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
+    const uint32_t old_slot = (slot == kParkSlots - 1) ? 0u : slot + 1u;
+    v4u *mine = &sh.park[slot][(uint32_t)d * Q * 64u + lane];
+    const v4u *theirs = &sh.park[old_slot][(uint32_t)d * Q * 64u + lane];
+    // Straight-line code whether or not the tiles exist (absent tiles are
+    // dummy loads of the first group and harmless arithmetic), so that the
+    // compiler sees one fixed sequence of loads and keeps two tiles in flight.
+    // Make cur tile-relative and park it.
+    T wave_prefix = Op::id();
+#pragma unroll
+    for (int w = 0; w < D; ++w)
+        if ((uint32_t)w < d) wave_prefix = Op::op(wave_prefix, sh.wt[par][w]);
+    finalize_span<Op, Q, INCL>(cur, lane_excl, row_prefix, wave_prefix);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const T c = Op::op(Op::op(base, group_prefix[q]), lane_excl[q]);
-        T o[4];
-        if (INCL) {
-            o[0] = Op::op(c, v[q][0]);
-            o[1] = Op::op(c, v[q][1]);
-            o[2] = Op::op(c, v[q][2]);
-            o[3] = Op::op(c, v[q][3]);
-        } else {
-            o[0] = c;
-            o[1] = Op::op(c, v[q][0]);
-            o[2] = Op::op(c, v[q][1]);
-            o[3] = Op::op(c, v[q][2]);
-        }
-        if (VEC && full) {
-            *reinterpret_cast<uint4 *>(out + span + (uint64_t)q * 256u) =
-                make_uint4(to_bits(o[0]), to_bits(o[1]), to_bits(o[2]), to_bits(o[3]));
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t i = span + (uint64_t)q * 256u + k;
-                if (i < n) out[i] = o[k];
-            }
-        }
+        v4u w;
+        w.x = to_bits(cur.v[q][0]);
+        w.y = to_bits(cur.v[q][1]);
+        w.z = to_bits(cur.v[q][2]);
+        w.w = to_bits(cur.v[q][3]);
+        mine[q * 64] = w;
     }
+    // the freed registers take the tile two ahead
+    const uint64_t b2 = (uint64_t)pt.f2 * TILE;
+    cur.template load<VEC>(in, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
+    // scan the next tile while the control wave looks back
+    const uint64_t b1 = (uint64_t)pt.f1 * TILE;
+    f1.pad(b1 + lane_off, n, b1 + TILE <= n);
+    const T wt = scan_span<Op, Q>(f1, lane_excl, row_prefix);
+    if (lane == 0) sh.wt[par ^ 1][d] = wt;
+    __syncthreads();  // B
+    if (pt.prev2 < num_tiles) {
+        const uint64_t bp = (uint64_t)pt.prev2 * TILE;
+        WaveSpan<Op, Q> old;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const v4u w = theirs[q * 64];
+            old.v[q][0] = from_bits<T>(w.x);
+            old.v[q][1] = from_bits<T>(w.y);
+            old.v[q][2] = from_bits<T>(w.z);
+            old.v[q][3] = from_bits<T>(w.w);
+        }
+        store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, bp + TILE <= n);
+    }
+    if (pt.drained(num_tiles)) return true;
+    if (d == 0 && lane == 0) {
+        uint32_t after = num_tiles;
+        if (need_ticket)
+            after = (ticket < (num_tiles + G - 1u) / G) ? ticket * G : num_tiles;
+        else if (pt.f2 < num_tiles && pt.f2 + 1u < num_tiles)
+            after = pt.f2 + 1u;
+        sh.next = after;
+    }
+    slot = old_slot;  // the slot just emptied takes the next tile
+    __syncthreads();  // A
+    pt.advance(uniform(sh.next), num_tiles);
+    return false;
+}
+
+template <class Op, int D, int Q, int G, bool INCL, bool VEC>
+__device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, const typename Op::T *in,
+                                          typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+                                          uint32_t lane, uint32_t d) {
+    using T = typename Op::T;
+    constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
+    const uint64_t lane_off = (uint64_t)d * WAVE_ELEMS + 4u * lane;
+    // Two register buffers with alternating roles.  The pipeline starts
+    // empty: the first two phases only load (prev, cur and f1 are absent),
+    // so the loop is entered with no load in flight and every phase is the
+    // same instruction sequence.
+    WaveSpan<Op, Q> x, y;
+    T lane_excl[Q], row_prefix[Q];
+    uint32_t slot = 0;
+    for (;;) {
+        if (data_phase<Op, D, Q, G, INCL, VEC>(x, y, 0, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                               num_tiles, ctr, lane, d, lane_off))
+            break;
+        if (data_phase<Op, D, Q, G, INCL, VEC>(y, x, 1, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                               num_tiles, ctr, lane, d, lane_off))
+            break;
+    }
+}
+
+template <class Op, int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
+__global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
+    const typename Op::T *in, typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+    uint64_t *desc, typename Op::T *total, uint32_t *stats, int aggregate_only) {
+    __shared__ ScanShared<Op, D, Q> sh;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+
+    if (threadIdx.x == 0) {
+        const uint32_t g = take_ticket(ctr);
+        sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
+    }
+    __syncthreads();
+    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
+    if (pt.f2 >= num_tiles) return;
+    if (wave == 0)
+        control_loop<Op, D, Q, LB_K, G, STATS>(pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, lane);
+    else
+        data_loop<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
 }
 
 template <class T>
@@ -162,10 +254,25 @@ __global__ void write_one(T *p, T v) {
     *p = v;
 }
 
-// Flat scan tile shape: 256 threads (4 waves) x 16 elements.
-constexpr int kFlatNT = 256;
-constexpr int kFlatQ = 4;
-constexpr uint32_t kFlatTile = kFlatNT * kFlatQ * 4;
+// Flat scan shape: D data waves x Q groups of four elements per lane, plus
+// the control wave; look-back width 64 * K predecessors per poll.
+#ifndef DWPS_FLAT_D
+#define DWPS_FLAT_D 8
+#endif
+#ifndef DWPS_FLAT_Q
+#define DWPS_FLAT_Q 6
+#endif
+constexpr int kFlatD = DWPS_FLAT_D;
+constexpr int kFlatQ = DWPS_FLAT_Q;
+constexpr int kLookbackK = DWPS_LOOKBACK_K;
+// Tiles claimed per ticket: a workgroup scans G consecutive tiles in
+// consecutive phases, and only the first of them looks back.
+#ifndef DWPS_TILES_PER_TICKET
+#define DWPS_TILES_PER_TICKET 2
+#endif
+constexpr int kTilesPerTicket = DWPS_TILES_PER_TICKET;
+constexpr int kFlatThreads = (kFlatD + 1) * 64;
+constexpr uint32_t kFlatTile = kFlatD * kFlatQ * 256;
 
 inline uint64_t flat_tiles(uint64_t n) { return ceil_div(n, kFlatTile); }
 
@@ -194,26 +301,25 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
     if (in != (const void *)out && ranges_overlap(in, n * 4, out, n * 4)) return PS_ERR_ALIAS;
     if (launch_clear(ws, ws_bytes_for_tiles(tiles), s) != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(in, 16) && aligned(out, 16);
-    const dim3 grid((unsigned)tiles), block(kFlatNT);
     uint32_t *ctr = ws_counter(ws);
     uint64_t *desc = ws_desc(ws);
     const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
-    timing_begin(s);
-    if (inclusive) {
-        if (vec)
-            hipLaunchKernelGGL((scan_kernel<Op, kFlatNT, kFlatQ, true, true, STATS>), grid, block, 0, s, in, out,
-                               n32, nt, ctr, desc, total, stats, aggregate_only);
-        else
-            hipLaunchKernelGGL((scan_kernel<Op, kFlatNT, kFlatQ, true, false, STATS>), grid, block, 0, s, in, out,
-                               n32, nt, ctr, desc, total, stats, aggregate_only);
-    } else {
-        if (vec)
-            hipLaunchKernelGGL((scan_kernel<Op, kFlatNT, kFlatQ, false, true, STATS>), grid, block, 0, s, in, out,
-                               n32, nt, ctr, desc, total, stats, aggregate_only);
-        else
-            hipLaunchKernelGGL((scan_kernel<Op, kFlatNT, kFlatQ, false, false, STATS>), grid, block, 0, s, in,
-                               out, n32, nt, ctr, desc, total, stats, aggregate_only);
-    }
+    auto launch = [&](auto kernel) -> ps_status {
+        const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kFlatThreads, nt);
+        if (!grid) return PS_ERR_HIP;
+        timing_begin(s);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFlatThreads), 0, s, in, out, n32, nt, ctr, desc, total,
+                           stats, aggregate_only);
+        return PS_OK;
+    };
+    ps_status r;
+    if (inclusive)
+        r = vec ? launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, true, true, STATS>)
+                : launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, true, false, STATS>);
+    else
+        r = vec ? launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, false, true, STATS>)
+                : launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, false, false, STATS>);
+    if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
 }
@@ -287,6 +393,10 @@ extern "C" ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uin
 }
 
 extern "C" uint64_t ps_lookback_tiles(uint64_t n) { return flat_tiles(n); }
+
+extern "C" uint32_t ps_lookback_window(void) { return 64u * (uint32_t)kLookbackK; }
+
+extern "C" uint32_t ps_lookback_group(void) { return (uint32_t)kTilesPerTicket; }
 
 extern "C" uint32_t ps_tile_elements(ps_dtype dtype) {
     (void)dtype;

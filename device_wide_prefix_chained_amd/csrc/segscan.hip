@@ -195,10 +195,10 @@ __global__ __launch_bounds__(NT) void segscan_kernel(const uint32_t *values, uin
             if (lane == 0) desc_publish(desc, desc_word(ST_PREFIX, agg.v));
         } else if (agg.f) {
             if (lane == 0) desc_publish(desc + tile, desc_word(ST_PREFIX, agg.v));
-            if (!first_is_head) carry = lookback<SumU32, false>(desc, tile, lane, st, ctr + 1);
+            if (!first_is_head) carry = lookback<SumU32, DWPS_LOOKBACK_K, false>(desc, tile, lane, st, ctr + 1);
         } else {
             if (lane == 0) desc_publish(desc + tile, desc_word(ST_AGGREGATE, agg.v));
-            carry = lookback<SumU32, false>(desc, tile, lane, st, ctr + 1);
+            carry = lookback<SumU32, DWPS_LOOKBACK_K, false>(desc, tile, lane, st, ctr + 1);
             if (lane == 0) desc_publish(desc + tile, desc_word(ST_PREFIX, carry + agg.v));
         }
         if (lane == 0) s_carry = carry;

@@ -191,8 +191,8 @@ ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *strea
 /* Exclusive uint32 sum scan (same kernel as ps_scan_exclusive_u32, built
  * with per-tile instrumentation of the look-back of [P1] "Why the work
  * stays linear").  stats: device buffer of 4 * tiles uint32, tiles reported
- * by ps_lookback_tiles(n); per tile: [0] poll rounds, [1] windows of 64
- * predecessors walked, [2] look-back time in 100 MHz ticks (low 32 bits),
+ * by ps_lookback_tiles(n); per tile: [0] poll rounds, [1] windows of
+ * ps_lookback_window() predecessors walked, [2] look-back time in 100 MHz ticks (low 32 bits),
  * [3] number of polls that found an unpublished predecessor.
  * aggregate_only != 0 (a test of the sliding window): tiles after tile 0
  * never publish their inclusive prefix, so every look-back walks back to
@@ -201,6 +201,13 @@ ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uint32_t *in,
                                 uint32_t *out, uint64_t n, uint32_t *stats,
                                 int aggregate_only, void *stream);
 uint64_t ps_lookback_tiles(uint64_t n);
+/* Predecessor descriptors read per look-back poll (64 lanes x K words). */
+uint32_t ps_lookback_window(void);
+/* Tiles claimed per ticket of the flat scan: a workgroup scans that many
+ * consecutive tiles, and only the first of each group looks back (the others
+ * take the inclusive prefix of the tile before them, which the same
+ * workgroup computed); their stats rows show zero polls. */
+uint32_t ps_lookback_group(void);
 
 /* Kernel timing with HIP events placed around the main scan kernel of every
  * call (the workspace clear is outside the pair).  enable != 0 starts a new

@@ -58,7 +58,7 @@ def _wsq(lib, fn, *args):
 def test_size_queries():
     lib = _lib()
     tile = lib.ps_tile_elements(0)
-    assert tile == 4096
+    assert tile == 12288
     for n in (0, 1, tile - 1, tile, tile + 1, 1 << 20, (1 << 28) - 12345, 1 << 28):
         st, need = _wsq(lib, "ps_scan_exclusive_u32", None, None, n, None, None)
         tiles = -(-n // tile)

@@ -7,20 +7,26 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_util import TILE, assert_f32_sum_close, dev, host, require_gpu, say, ws_error_word
+from gpu_util import FLAT_GROUP, FLAT_TILE, TILE, assert_f32_sum_close, dev, host, require_gpu, say, ws_error_word
 from pins import golden
 
 pytestmark = pytest.mark.gpu
 
-EDGE_SIZES = [1, 2, 3, 4, 5, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025,
-              TILE - 1, TILE, TILE + 1, 2 * TILE - 1, 2 * TILE + 1, 3 * TILE + 17,
-              64 * TILE + 5, 65 * TILE - 3, 1_000_003]
+FT = FLAT_TILE
+EDGE_SIZES = [1, 2, 3, 4, 5, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, 1536, 1537,
+              TILE - 1, TILE, TILE + 1, FT - 1, FT, FT + 1, 2 * FT - 1, 2 * FT, 2 * FT + 1,
+              3 * FT - 1, 3 * FT + 17, 64 * FT + 5, 65 * FT - 3, 257 * FT, 513 * FT + 1, 1_000_003]
 U32_OPS = ["sum", "max", "min", "and", "or", "xor", "affine16"]
 
 
 @pytest.fixture(scope="module")
 def dw():
     return require_gpu()
+
+
+def test_tile_shape_matches_the_library(dw):
+    assert dw.ps_tile_elements(0) == FLAT_TILE
+    assert dw.ps_lookback_group() == FLAT_GROUP
 
 
 def _run_u32(dw, x, op="sum", inclusive=False, with_total=True):
@@ -58,7 +64,7 @@ def test_u32_sum_edge_sizes(dw, orc, n, inclusive):
 
 
 @pytest.mark.parametrize("op", U32_OPS)
-@pytest.mark.parametrize("n", [1000, 3 * TILE + 17, 300 * TILE + 1])
+@pytest.mark.parametrize("n", [1000, 3 * FT + 17, 300 * FT + 1])
 @pytest.mark.parametrize("inclusive", [False, True])
 def test_u32_all_operators(dw, orc, op, n, inclusive):
     r = np.random.default_rng(n + 17)
@@ -75,7 +81,7 @@ def test_u32_all_operators(dw, orc, op, n, inclusive):
     assert total == ref_total
 
 
-@pytest.mark.parametrize("n", [1, 33, TILE + 1, 100_003, 3_000_001])
+@pytest.mark.parametrize("n", [1, 33, FT + 1, 100_003, 3_000_001])
 @pytest.mark.parametrize("inclusive", [False, True])
 def test_f32_sum_tolerance(dw, orc, n, inclusive):
     import torch
@@ -90,7 +96,7 @@ def test_f32_sum_tolerance(dw, orc, n, inclusive):
     assert abs(float(host(tot)[0]) - ref_total) <= 1e-5 * ab[-1]
 
 
-@pytest.mark.parametrize("n", [7, TILE * 5 + 3, 1_000_003])
+@pytest.mark.parametrize("n", [7, FT * 5 + 3, 1_000_003])
 def test_f32_small_integers_are_exact(dw, orc, n):
     """fp32 inputs that are small integers stay exact under any grouping while
     every partial sum is below 2^24, so the result equals the integer scan."""
@@ -105,7 +111,7 @@ def test_f32_small_integers_are_exact(dw, orc, n):
 
 
 @pytest.mark.parametrize("op", ["max", "min"])
-@pytest.mark.parametrize("n", [5, TILE + 3, 1_000_003])
+@pytest.mark.parametrize("n", [5, FT + 3, 1_000_003])
 @pytest.mark.parametrize("inclusive", [False, True])
 def test_f32_minmax_bit_exact(dw, orc, op, n, inclusive):
     import torch
@@ -122,7 +128,7 @@ def test_f32_minmax_bit_exact(dw, orc, op, n, inclusive):
 
 def test_f32_signed_zero_ties(dw, orc):
     import torch
-    z = np.tile(np.array([0.0, -0.0, 0.0, -0.0], np.float32), 3 * TILE)
+    z = np.tile(np.array([0.0, -0.0, 0.0, -0.0], np.float32), 3 * FT)
     for op in ("max", "min"):
         for src in (z, -z):
             d_in = dev(src)
@@ -136,7 +142,7 @@ def test_f32_signed_zero_ties(dw, orc):
 def test_unaligned_pointers(dw, orc, shift):
     """4-byte but not 16-byte aligned input/output take the scalar path."""
     import torch
-    n = 3 * TILE + 11
+    n = 7 * FT + 11
     x = wl.full_range_u32(n + shift, seed=shift)
     d_all = dev(x)
     d_in = d_all[shift:]
@@ -150,7 +156,7 @@ def test_unaligned_pointers(dw, orc, shift):
 
 
 def test_in_place(dw, orc):
-    n = 5 * TILE + 123
+    n = 5 * FT + 123
     x = wl.full_range_u32(n, seed=99)
     for inclusive in (False, True):
         d = dev(x)
@@ -179,7 +185,7 @@ def test_workspace_reuse_and_error_word(dw, orc):
     import torch
     ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, 1 << 22, None, None),
                      dtype=torch.uint8, device="cuda")
-    for n in (1 << 22, 5, TILE * 7 + 1, 1 << 22):
+    for n in (1 << 22, 5, FT * 7 + 1, 1 << 22):
         x = wl.full_range_u32(n, seed=n + 3)
         d_in = dev(x)
         d_out = torch.empty_like(d_in)
@@ -192,7 +198,7 @@ def test_workspace_reuse_and_error_word(dw, orc):
 def test_torch_uint32_tensors(dw, orc):
     """The binding also takes torch.uint32 tensors (created and copied only)."""
     import torch
-    x = wl.full_range_u32(TILE * 3 + 5, seed=8)
+    x = wl.full_range_u32(FT * 3 + 5, seed=8)
     d_in = torch.from_numpy(x).to("cuda")
     assert d_in.dtype == torch.uint32
     d_out = torch.empty_like(d_in)
@@ -242,7 +248,8 @@ def test_lookback_instrumented(dw, orc, aggregate_only):
     """The instrumented kernel gives the same result; with aggregate_only every
     look-back has to slide its 64-wide window back to tile 0."""
     import torch
-    n = 300 * TILE + 77
+    tile = dw.ps_tile_elements(0)
+    n = 1100 * tile + 77
     x = wl.full_range_u32(n, seed=21)
     tiles = dw.ps_lookback_tiles(n)
     stats = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
@@ -254,10 +261,16 @@ def test_lookback_instrumented(dw, orc, aggregate_only):
     assert np.array_equal(host(d_out), ref)
     st = host(stats).reshape(tiles, 4).astype(np.int64)
     assert st[0, 0] == 0 and st[0, 1] == 0  # tile 0 never looks back
-    assert np.all(st[1:, 1] >= 1) and np.all(st[1:, 0] >= st[1:, 1])
+    assert np.all(st[1:, 0] >= st[1:, 1])
+    t = np.arange(tiles)
+    first = (t % dw.ps_lookback_group() == 0) & (t > 0)
+    if not aggregate_only:
+        # the first tile of each group looks back, the others follow it
+        assert np.all(st[first, 1] >= 1) and np.all(st[~first, 0] == 0)
     if aggregate_only:
         t = np.arange(1, tiles)
-        assert np.array_equal(st[1:, 1], (t + 63) // 64)
+        win = dw.ps_lookback_window()
+        assert np.array_equal(st[1:, 1], (t + win - 1) // win)
 
 
 def test_small_config_u32(dw, orc):
