@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     ps_scan_inclusive_f32,
     ps_scan_inclusive_u32,
     ps_segmented_scan_u32,
+    ps_segmented_tile_elements,
     ps_status_string,
     ps_tile_elements,
     ps_validate_offsets,

@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.ps_lookback_group.restype = u32
     L.ps_tile_elements.argtypes = [i32]
     L.ps_tile_elements.restype = u32
+    L.ps_segmented_tile_elements.argtypes = []
+    L.ps_segmented_tile_elements.restype = u32
     L.ps_version.argtypes = []
     L.ps_version.restype = ctypes.c_char_p
     L.ps_status_string.argtypes = [i32]
@@ -287,6 +289,10 @@ def ps_lookback_group() -> int:
 
 def ps_tile_elements(dtype=PS_U32) -> int:
     return int(lib().ps_tile_elements(dtype))
+
+
+def ps_segmented_tile_elements() -> int:
+    return int(lib().ps_segmented_tile_elements())
 
 
 def ps_version() -> str:

@@ -33,11 +33,10 @@
 
 #include "dwps_device.hpp"
 #include "host_common.hpp"
+#include "pipeline.hpp"
 #include "tile_io.hpp"
 
 namespace dwps {
-
-constexpr int kParkSlots = 3;
 
 template <class Op, int D, int Q>
 struct ScanShared {
@@ -48,27 +47,6 @@ struct ScanShared {
     T wt[2][D];  // wave totals, double-buffered by phase parity
     T prefix;
 };
-
-// Tile ids of the pipeline, identical in every wave of the workgroup
-// (num_tiles = none): prev2 waits for its prefix, prev and cur are parked or
-// being parked, f1 and f2 are in flight.  Every value comes from LDS through
-// readfirstlane, so the compiler keeps them in scalar registers and branches
-// on them with scalar branches.
-struct PipeTiles {
-    uint32_t prev2, prev, cur, f1, f2;
-    __device__ __forceinline__ bool drained(uint32_t num_tiles) const {
-        return prev < num_tiles ? false : (cur >= num_tiles && f1 >= num_tiles && f2 >= num_tiles);
-    }
-    __device__ __forceinline__ void advance(uint32_t after, uint32_t num_tiles) {
-        prev2 = prev;
-        prev = cur;
-        cur = f1;
-        f1 = f2;
-        f2 = (f2 < num_tiles) ? after : num_tiles;
-    }
-};
-
-__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Control wave: aggregates, look-back, prefixes.  Phase k runs between
 // barriers A_k and B_k, while the data waves work on their side.  The
@@ -143,10 +121,10 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
     constexpr uint32_t TILE = (uint32_t)D * (uint32_t)Q * 256u;
     // the tile after f2: the next one of its group, or the first of a new
     // group taken from the ticket counter
-    const bool need_ticket = pt.f2 < num_tiles && (pt.f2 + 1u) % G == 0u;
+    const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
     if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
-    const uint32_t old_slot = (slot == kParkSlots - 1) ? 0u : slot + 1u;
+    const uint32_t old_slot = next_slot(slot);
     v4u *mine = &sh.park[slot][(uint32_t)d * Q * 64u + lane];
     const v4u *theirs = &sh.park[old_slot][(uint32_t)d * Q * 64u + lane];
     // Straight-line code whether or not the tiles exist (absent tiles are
@@ -190,14 +168,7 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
         store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, bp + TILE <= n);
     }
     if (pt.drained(num_tiles)) return true;
-    if (d == 0 && lane == 0) {
-        uint32_t after = num_tiles;
-        if (need_ticket)
-            after = (ticket < (num_tiles + G - 1u) / G) ? ticket * G : num_tiles;
-        else if (pt.f2 < num_tiles && pt.f2 + 1u < num_tiles)
-            after = pt.f2 + 1u;
-        sh.next = after;
-    }
+    if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
     slot = old_slot;  // the slot just emptied takes the next tile
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);

@@ -3,30 +3,39 @@
 // Contract: "GPUSegmentedScan", sections "Prefix scans and segmented scans",
 // "Contract" and "Limitations" (segment s is [offsets[s], offsets[s+1]), the
 // running total restarts at every segment, empty segments write nothing,
-// offsets are trusted on the hot path).  The scan itself is the flat chained
-// scan with the operator of the carried segment flag ("Parallel Prefix Sum
-// (Scan), in depth", section "What scan builds"):
+// offsets are trusted on the hot path).  The scan itself is the chained scan
+// with the operator of the carried segment flag ("Parallel Prefix Sum (Scan),
+// in depth", section "What scan builds"):
 //     (f1, v1) (+) (f2, v2) = (f1 | f2,  f2 ? v2 : v1 + v2).
 //
-// Strategy selection by segment size, inside one launch (the page's
-// "Performance notes" call for it without building it):
+// Strategy selection by segment size, inside one pass (the segmented-scan
+// page's "Performance notes" call for it without building it):
 //   * a segment that starts and ends inside one lane's 4 elements, one wave's
 //     span or one tile is finished by the lane-serial, DPP wave or LDS block
 //     layer -- it never waits on another workgroup;
-//   * a tile that contains a segment head knows its carry-out without looking
-//     back (the sum since its last head), so it publishes PREFIX at once and
-//     cuts every look-back chain that reaches it;
-//   * only tiles without a head (inside a segment longer than a tile) publish
-//     AGGREGATE and wait, exactly like the flat scan; a tile whose first
-//     element is a head needs no carry and does not look back at all.
-// Heads are found per tile without host readback: two 64-way searches of the
-// offsets give the range of segment starts inside the tile, and those starts
-// set bits in an LDS bitmap (duplicate offsets -- empty segments -- set the
-// same bit).
+//   * a tile that contains a segment start knows its carry-out without
+//     looking back (the sum since its last start), so it publishes PREFIX
+//     together with its aggregate and cuts every look-back chain that
+//     reaches it;
+//   * only a tile whose first element is not a segment start needs a carry,
+//     and only the first tile of a ticket group looks back for it -- long
+//     segments chain through start-free tiles exactly like the flat scan.
+//
+// Two launches per call:
+//   1. a pre-pass, one wave per tile, clears the tile's descriptor and writes
+//      the tile's segment starts as a bitmap into the workspace: two 64-way
+//      searches of the offsets bound the starts inside the tile, and those
+//      starts set bits in LDS (repeated offsets -- empty segments -- set the
+//      same bit);
+//   2. the persistent, wave-specialised pipeline of the flat scan (one
+//      control wave, D data waves, look-back two phases behind the
+//      aggregate), streaming the values and their bitmap words.
 #include <hip/hip_runtime.h>
 
 #include "dwps_device.hpp"
 #include "host_common.hpp"
+#include "pipeline.hpp"
+#include "tile_io.hpp"
 
 namespace dwps {
 
@@ -54,8 +63,8 @@ __device__ __forceinline__ uint32_t wave_lower_bound(const uint32_t *a, uint32_t
 }
 
 struct SegPair {
-    uint32_t f;  // 1 if the covered range contains a segment head
-    uint32_t v;  // sum since the last head in the range (the whole range if none)
+    uint32_t f;  // 1 if the covered range contains a segment start
+    uint32_t v;  // sum since the last start in the range (the whole range if none)
 };
 __device__ __forceinline__ SegPair seg_op(SegPair a, SegPair b) {
     return SegPair{a.f | b.f, b.f ? b.v : a.v + b.v};
@@ -79,142 +88,176 @@ __device__ __forceinline__ void wave_seg_inclusive(uint32_t &f, uint32_t &v) {
     seg_dpp_step<0x143, 0xC>(f, v);
 }
 
-template <int NT, int Q, bool INCL, bool VEC>
-__global__ __launch_bounds__(NT) void segscan_kernel(const uint32_t *values, uint32_t *out, uint32_t n,
-                                                     const uint32_t *offsets, uint32_t num_segments,
-                                                     uint32_t *ctr, uint64_t *desc) {
-    static_assert(NT >= 128, "two waves run the two offset searches");
-    constexpr int NW = NT / 64;
-    constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
-    constexpr uint32_t TILE = (uint32_t)NT * (uint32_t)Q * 4u;
-    constexpr uint32_t BITWORDS = TILE / 32u;
+// Segmented tile shape: D data waves x Q groups of four elements per lane.
+#ifndef DWPS_SEG_D
+#define DWPS_SEG_D 8
+#endif
+#ifndef DWPS_SEG_Q
+#define DWPS_SEG_Q 6
+#endif
+constexpr int kSegD = DWPS_SEG_D;
+constexpr int kSegQ = DWPS_SEG_Q;
+constexpr int kSegG = 2;  // tiles claimed per ticket
+constexpr int kSegThreads = (kSegD + 1) * 64;
+constexpr uint32_t kSegTile = (uint32_t)kSegD * kSegQ * 256u;
+constexpr uint32_t kSegWords = kSegTile / 32u;  // bitmap words per tile
 
-    __shared__ uint32_t s_tile, s_lo, s_hi, s_carry;
-    __shared__ uint32_t s_heads[BITWORDS];
-    __shared__ uint32_t s_wf[NW], s_wv[NW];
-
-    const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & 63u;
-    const uint32_t wave = tid >> 6;
-
-    if (tid == 0) s_tile = take_ticket(ctr);
-    for (uint32_t i = tid; i < BITWORDS; i += NT) s_heads[i] = 0u;
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint64_t tile_base = (uint64_t)tile * TILE;
-    const uint32_t tb = (uint32_t)tile_base;  // < n < 2^32
-    const uint64_t tile_end64 = tile_base + TILE;
-    const uint32_t te = tile_end64 < (uint64_t)n ? (uint32_t)tile_end64 : n;
-    const bool full = tile_end64 <= (uint64_t)n;
-    const uint64_t span = tile_base + (uint64_t)wave * WAVE_ELEMS + 4u * lane;
-
-    // values first, so their latency overlaps the offset searches
-    uint32_t x[Q][4];
-    if (VEC && full) {
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const uint4 r = *reinterpret_cast<const uint4 *>(values + span + (uint64_t)q * 256u);
-            x[q][0] = r.x;
-            x[q][1] = r.y;
-            x[q][2] = r.z;
-            x[q][3] = r.w;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < Q; ++q)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t i = span + (uint64_t)q * 256u + k;
-                x[q][k] = (i < n) ? values[i] : 0u;
-            }
-    }
-    uint32_t row_lo = offsets[0];
-    uint32_t row_hi = offsets[num_segments];
-    row_lo = row_lo < n ? row_lo : n;
-    row_hi = row_hi < n ? row_hi : n;
-
-    if (wave == 0) {
-        const uint32_t r = wave_lower_bound(offsets, num_segments + 1u, tb, lane);
-        if (lane == 0) s_lo = r;
-    } else if (wave == 1) {
-        const uint32_t r = wave_lower_bound(offsets, num_segments + 1u, te, lane);
-        if (lane == 0) s_hi = r;
-    }
-    __syncthreads();
-    {
-        const uint32_t lo = s_lo, hi = s_hi;
-        for (uint32_t s = lo + tid; s < hi; s += NT) {
-            const uint32_t o = offsets[s];
-            if (o >= tb && o < te) atomicOr(&s_heads[(o - tb) >> 5], 1u << ((o - tb) & 31u));
-        }
-    }
-    __syncthreads();
-
-    // lane-serial segmented scan of each group of four
-    uint32_t fl[Q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const uint32_t li = wave * WAVE_ELEMS + (uint32_t)q * 256u + 4u * lane;
-        fl[q] = (s_heads[li >> 5] >> (li & 31u)) & 0xFu;
-        x[q][1] = (fl[q] & 2u) ? x[q][1] : x[q][0] + x[q][1];
-        x[q][2] = (fl[q] & 4u) ? x[q][2] : x[q][1] + x[q][2];
-        x[q][3] = (fl[q] & 8u) ? x[q][3] : x[q][2] + x[q][3];
-    }
-    // wave scans of the group pairs, then the wave pairs through LDS
-    SegPair lane_excl[Q], group_prefix[Q];
-    SegPair run{0u, 0u};
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        uint32_t f = fl[q] ? 1u : 0u, v = x[q][3];
-        wave_seg_inclusive(f, v);
-        lane_excl[q].f = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)f, 0x138, 0xF, 0xF, false);
-        lane_excl[q].v = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);
-        group_prefix[q] = run;
-        run = seg_op(run, SegPair{(uint32_t)__builtin_amdgcn_readlane((int)f, 63),
-                                  (uint32_t)__builtin_amdgcn_readlane((int)v, 63)});
-    }
+// ---------------------------------------------------------------------------
+// 1. pre-pass: descriptors cleared, per-tile segment-start bitmaps written
+// ---------------------------------------------------------------------------
+template <uint32_t TILE>
+__global__ __launch_bounds__(64) void seg_prepass_kernel(const uint32_t *offsets, uint32_t num_segments,
+                                                         uint32_t n, uint32_t *ctr, uint64_t *desc,
+                                                         uint32_t *heads) {
+    constexpr uint32_t WORDS = TILE / 32u;
+    __shared__ uint32_t bits[WORDS];
+    const uint32_t lane = threadIdx.x;
+    const uint32_t t = blockIdx.x;
+    const uint32_t tb = t * TILE;  // t * TILE <= n - 1
+    const uint64_t tile_end = (uint64_t)tb + TILE;
+    const uint32_t te = tile_end < (uint64_t)n ? (uint32_t)tile_end : n;
     if (lane == 0) {
-        s_wf[wave] = run.f;
-        s_wv[wave] = run.v;
-    }
-    __syncthreads();
-    SegPair wave_prefix{0u, 0u}, agg{0u, 0u};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const SegPair t{s_wf[w], s_wv[w]};
-        if ((uint32_t)w < wave) wave_prefix = seg_op(wave_prefix, t);
-        agg = seg_op(agg, t);
-    }
-
-    // grid level: heads publish at once; head-free tiles chain like the flat scan
-    if (wave == 0) {
-        LookbackStats st;
-        uint32_t carry = 0u;
-        const bool first_is_head = (s_heads[0] & 1u) != 0u;
-        if (tile == 0) {
-            if (lane == 0) desc_publish(desc, desc_word(ST_PREFIX, agg.v));
-        } else if (agg.f) {
-            if (lane == 0) desc_publish(desc + tile, desc_word(ST_PREFIX, agg.v));
-            if (!first_is_head) carry = lookback<SumU32, DWPS_LOOKBACK_K, false>(desc, tile, lane, st, ctr + 1);
-        } else {
-            if (lane == 0) desc_publish(desc + tile, desc_word(ST_AGGREGATE, agg.v));
-            carry = lookback<SumU32, DWPS_LOOKBACK_K, false>(desc, tile, lane, st, ctr + 1);
-            if (lane == 0) desc_publish(desc + tile, desc_word(ST_PREFIX, carry + agg.v));
+        desc[t] = 0ull;
+        if (t == 0) {
+            ctr[0] = 0u;  // ticket counter
+            ctr[1] = 0u;  // error word
         }
-        if (lane == 0) s_carry = carry;
+    }
+    for (uint32_t i = lane; i < WORDS; i += 64) bits[i] = 0u;
+    const uint32_t lo = wave_lower_bound(offsets, num_segments + 1u, tb, lane);
+    const uint32_t hi = wave_lower_bound(offsets, num_segments + 1u, te, lane);
+    __syncthreads();
+    for (uint32_t s = lo + lane; s < hi; s += 64) {
+        const uint32_t o = offsets[s];
+        if (o >= tb && o < te) atomicOr(&bits[(o - tb) >> 5], 1u << ((o - tb) & 31u));
     }
     __syncthreads();
+    uint32_t *dst = heads + (uint64_t)t * WORDS;
+    for (uint32_t i = lane; i < WORDS; i += 64) dst[i] = bits[i];
+}
 
-    const SegPair base = seg_op(SegPair{0u, s_carry}, wave_prefix);
-    const bool vec_store = VEC && full && tb >= row_lo && tile_end64 <= (uint64_t)row_hi;
+// ---------------------------------------------------------------------------
+// 2. the persistent pipeline
+// ---------------------------------------------------------------------------
+template <int D, int Q>
+struct SegShared {
+    v4u park[kParkSlots][D * Q * 64];  // tile-relative outputs (carry into the tile = 0)
+    uint32_t park_first[kParkSlots];   // first segment start of each parked tile (tile-local; TILE if none)
+    uint32_t wf[2][D], wv[2][D];       // wave totals (pairs), double-buffered by phase parity
+    uint32_t wfirst[2][D];             // first segment start in each wave's span (TILE if none)
+    uint32_t t0;
+    uint32_t next;
+    uint32_t carry;                    // carry into prev2
+};
+
+// Register state of one wave's span: the values and the bitmap words that
+// cover them (one word per group-row; 8 lanes share a word).
+template <int Q>
+struct SegSpan {
+    WaveSpan<SumU32, Q> x;
+    uint32_t hw[Q];
+    template <bool VEC>
+    __device__ __forceinline__ void load(const uint32_t *values, const uint32_t *heads, uint32_t tile,
+                                         uint64_t lane_off, uint32_t word_off, uint32_t n, bool valid) {
+        const uint64_t base = (uint64_t)tile * kSegTile;
+        x.template load<VEC>(values, base + lane_off, n, base + kSegTile <= n, valid);
+        const uint64_t wb = valid ? (uint64_t)tile * kSegWords + word_off : (uint64_t)word_off;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) hw[q] = heads[wb + (uint64_t)q * 8u];
+    }
+};
+
+// Control wave.  Phase k: combine the wave pairs of cur into its aggregate
+// and first start; find the carry into prev2 (a look-back only when prev2
+// heads a ticket group and its first element is not a segment start; the
+// second tile of a group takes the carry-out of the first from this wave's
+// registers); publish PREFIX for prev2 if it had no start, and cur's
+// descriptor -- PREFIX at once when cur holds a start (or is tile 0),
+// AGGREGATE otherwise.  Descriptor stores go out after the poll returned.
+template <int D, int Q, int LB_K, int G>
+__device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles,
+                                                 uint32_t *ctr, uint64_t *desc, uint32_t lane) {
+    SegPair a_prev{0u, 0u}, a_prev2{0u, 0u};
+    uint32_t fh_prev = kSegTile, fh_prev2 = kSegTile;
+    uint32_t carry_out_last = 0;  // carry out of the tile handled one phase ago
+    for (int par = 0;; par ^= 1) {
+        SegPair agg{0u, 0u};
+        uint32_t fh = kSegTile;
+        if (pt.cur < num_tiles) {
+#pragma unroll
+            for (int w = 0; w < D; ++w) {
+                agg = seg_op(agg, SegPair{sh.wf[par][w], sh.wv[par][w]});
+                fh = min(fh, sh.wfirst[par][w]);
+            }
+        }
+        uint32_t carry = 0;
+        const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
+        if (have_prev2) {
+            if (pt.prev2 % G != 0u) {
+                carry = carry_out_last;
+            } else if (fh_prev2 != 0u) {
+                LookbackStats st;
+                carry = lookback<SumU32, LB_K, false>(desc, pt.prev2, lane, st, ctr + 1);
+            }
+        }
+        if (lane == 0) {
+            sh.carry = carry;
+            if (have_prev2 && !a_prev2.f)
+                desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, carry + a_prev2.v));
+            if (pt.cur < num_tiles)
+                desc_publish(desc + pt.cur, desc_word((pt.cur == 0 || agg.f) ? ST_PREFIX : ST_AGGREGATE, agg.v));
+        }
+        carry_out_last = a_prev2.f ? a_prev2.v : carry + a_prev2.v;
+        a_prev2 = a_prev;
+        fh_prev2 = fh_prev;
+        a_prev = agg;
+        fh_prev = fh;
+        __syncthreads();  // B: the carry of prev2 is in LDS
+        if (pt.drained(num_tiles)) break;
+        __syncthreads();  // A: the next tile id is in LDS
+        pt.advance(uniform(sh.next), num_tiles);
+    }
+}
+
+// One phase of a data wave (the flat scan's phase with segment flags):
+// finalize cur into LDS slot `slot` with carry 0, load the tile two ahead
+// into the freed registers, scan f1; after barrier B add the carry to the
+// elements of prev2 before its first segment start and store prev2.
+template <int D, int Q, int G, bool INCL, bool VEC>
+__device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, int par, uint32_t &slot,
+                                               PipeTiles &pt, uint32_t (&pre)[Q], uint32_t (&fl)[Q],
+                                               SegShared<D, Q> &sh, const uint32_t *values,
+                                               const uint32_t *heads, uint32_t *out, uint32_t n,
+                                               uint32_t row_lo, uint32_t row_hi, uint32_t num_tiles,
+                                               uint32_t *ctr, uint32_t lane, uint32_t d, uint64_t lane_off,
+                                               uint32_t word_off) {
+    constexpr uint32_t TILE = kSegTile;
+    constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
+    const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
+    uint32_t ticket = 0;
+    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
+    const uint32_t old_slot = next_slot(slot);
+    v4u *mine = &sh.park[slot][d * Q * 64u + lane];
+    const v4u *theirs = &sh.park[old_slot][d * Q * 64u + lane];
+
+    // cur: tile-relative segmented outputs, parked
+    SegPair wave_prefix{0u, 0u};
+    uint32_t first = TILE;
+#pragma unroll
+    for (int w = 0; w < D; ++w) {
+        if ((uint32_t)w < d) wave_prefix = seg_op(wave_prefix, SegPair{sh.wf[par][w], sh.wv[par][w]});
+        first = min(first, sh.wfirst[par][w]);
+    }
+    if (d == 0 && lane == 0) sh.park_first[slot] = first;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const uint32_t c = seg_op(seg_op(base, group_prefix[q]), lane_excl[q]).v;
+        // the lane's prefix inside the wave, then the earlier waves' pair
+        const uint32_t c = (fl[q] & 16u) ? pre[q] : wave_prefix.v + pre[q];
         uint32_t inc[4], o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const bool seen = (fl[q] & ((2u << k) - 1u)) != 0u;  // a head among elements 0..k
-            inc[k] = seen ? x[q][k] : c + x[q][k];
+            const bool seen = (fl[q] & ((2u << k) - 1u)) != 0u;  // a start among elements 0..k
+            inc[k] = seen ? cur.x.v[q][k] : c + cur.x.v[q][k];
         }
         if (INCL) {
 #pragma unroll
@@ -224,21 +267,146 @@ __global__ __launch_bounds__(NT) void segscan_kernel(const uint32_t *values, uin
 #pragma unroll
             for (int k = 1; k < 4; ++k) o[k] = (fl[q] & (1u << k)) ? 0u : inc[k - 1];
         }
-        if (vec_store) {
-            *reinterpret_cast<uint4 *>(out + span + (uint64_t)q * 256u) = make_uint4(o[0], o[1], o[2], o[3]);
-        } else {
+        v4u w;
+        w.x = o[0];
+        w.y = o[1];
+        w.z = o[2];
+        w.w = o[3];
+        mine[q * 64] = w;
+    }
+    // the freed registers take the tile two ahead
+    cur.template load<VEC>(values, heads, pt.f2, lane_off, word_off, n, pt.f2 < num_tiles);
+    // scan the next tile while the control wave looks back
+    {
+        const uint64_t b1 = (uint64_t)pt.f1 * TILE;
+        f1.x.pad(b1 + lane_off, n, b1 + TILE <= n);
+        const uint32_t sh4 = 4u * (lane & 7u);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t i = span + (uint64_t)q * 256u + k;
-                if (i >= row_lo && i < row_hi) out[i] = o[k];
+        for (int q = 0; q < Q; ++q) {
+            fl[q] = (f1.hw[q] >> sh4) & 0xFu;
+            f1.x.v[q][1] = (fl[q] & 2u) ? f1.x.v[q][1] : f1.x.v[q][0] + f1.x.v[q][1];
+            f1.x.v[q][2] = (fl[q] & 4u) ? f1.x.v[q][2] : f1.x.v[q][1] + f1.x.v[q][2];
+            f1.x.v[q][3] = (fl[q] & 8u) ? f1.x.v[q][3] : f1.x.v[q][2] + f1.x.v[q][3];
+        }
+        SegPair run{0u, 0u};
+        uint32_t wave_first = TILE;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            uint32_t f = fl[q] ? 1u : 0u, v = f1.x.v[q][3];
+            const uint64_t m = ballot(f != 0u);
+            if (m != 0u && wave_first == TILE) {
+                const uint32_t l0 = (uint32_t)__builtin_ctzll(m);
+                const uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)fl[q], (int)l0);
+                wave_first = d * WAVE_ELEMS + (uint32_t)q * 256u + 4u * l0 + (uint32_t)__builtin_ctz(bits);
+            }
+            wave_seg_inclusive(f, v);
+            // lane-exclusive pair within the row, combined at once with the
+            // pair of the earlier rows of the span: bit 4 of fl marks a start
+            // before the lane, pre holds the sum since it (or since the span
+            // start)
+            const uint32_t ef = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)f, 0x138, 0xF, 0xF, false);
+            const uint32_t ev = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);
+            const SegPair e = seg_op(run, SegPair{ef, ev});
+            fl[q] |= e.f << 4;
+            pre[q] = e.v;
+            run = seg_op(run, SegPair{(uint32_t)__builtin_amdgcn_readlane((int)f, 63),
+                                      (uint32_t)__builtin_amdgcn_readlane((int)v, 63)});
+        }
+        if (lane == 0) {
+            sh.wf[par ^ 1][d] = run.f;
+            sh.wv[par ^ 1][d] = run.v;
+            sh.wfirst[par ^ 1][d] = wave_first;
+        }
+    }
+    __syncthreads();  // B
+    if (pt.prev2 < num_tiles) {
+        const uint64_t bp = (uint64_t)pt.prev2 * TILE;
+        const uint32_t carry = sh.carry;
+        const uint32_t first_start = sh.park_first[old_slot];
+        const uint32_t span_local = d * WAVE_ELEMS + 4u * lane;
+        const bool vec_store = VEC && bp >= row_lo && bp + TILE <= (uint64_t)row_hi;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const v4u w = theirs[q * 64];
+            const uint32_t li = span_local + (uint32_t)q * 256u;
+            uint32_t o[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = (li + k < first_start) ? o[k] + carry : o[k];
+            if (vec_store) {
+                v4u r;
+                r.x = o[0];
+                r.y = o[1];
+                r.z = o[2];
+                r.w = o[3];
+                store16(out + bp + li, r);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint64_t i = bp + li + k;
+                    if (i >= row_lo && i < row_hi) out[i] = o[k];
+                }
             }
         }
     }
+    if (pt.drained(num_tiles)) return true;
+    if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
+    slot = old_slot;  // the slot just emptied takes the next tile
+    __syncthreads();  // A
+    pt.advance(uniform(sh.next), num_tiles);
+    return false;
 }
 
-constexpr int kSegNT = 256;
-constexpr int kSegQ = 4;
-constexpr uint32_t kSegTile = kSegNT * kSegQ * 4;
+template <int D, int Q, int G, bool INCL, bool VEC>
+__device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh, const uint32_t *values,
+                                              const uint32_t *heads, uint32_t *out, uint32_t n, uint32_t row_lo,
+                                              uint32_t row_hi, uint32_t num_tiles, uint32_t *ctr, uint32_t lane,
+                                              uint32_t d) {
+    const uint64_t lane_off = (uint64_t)d * Q * 256u + 4u * lane;
+    const uint32_t word_off = d * Q * 8u + (lane >> 3);
+    // two register buffers with alternating roles; the first two phases only
+    // load, so every phase of the loop is the same instruction sequence
+    SegSpan<Q> x, y;
+    uint32_t pre[Q], fl[Q];
+    uint32_t slot = 0;
+    for (;;) {
+        if (seg_data_phase<D, Q, G, INCL, VEC>(x, y, 0, slot, pt, pre, fl, sh, values, heads,
+                                               out, n, row_lo, row_hi, num_tiles, ctr, lane, d, lane_off,
+                                               word_off))
+            break;
+        if (seg_data_phase<D, Q, G, INCL, VEC>(y, x, 1, slot, pt, pre, fl, sh, values, heads,
+                                               out, n, row_lo, row_hi, num_tiles, ctr, lane, d, lane_off,
+                                               word_off))
+            break;
+    }
+}
+
+template <int D, int Q, int LB_K, int G, bool INCL, bool VEC>
+__global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *values, const uint32_t *heads,
+                                                               uint32_t *out, uint32_t n,
+                                                               const uint32_t *offsets, uint32_t num_segments,
+                                                               uint32_t num_tiles, uint32_t *ctr, uint64_t *desc) {
+    __shared__ SegShared<D, Q> sh;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    if (threadIdx.x == 0) {
+        const uint32_t g = take_ticket(ctr);
+        sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
+    }
+    __syncthreads();
+    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
+    if (pt.f2 >= num_tiles) return;
+    if (wave == 0) {
+        seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, ctr, desc, lane);
+    } else {
+        // rows outside [offsets[0], offsets[N]) belong to no segment
+        const uint32_t lo = offsets[0], hi = offsets[num_segments];
+        seg_data_loop<D, Q, G, INCL, VEC>(pt, sh, values, heads, out, n, uniform(lo < n ? lo : n),
+                                          uniform(hi < n ? hi : n), num_tiles, ctr, lane, wave - 1);
+    }
+}
+
+// Workspace: header and descriptors as for the flat scan, then the bitmaps.
+inline size_t seg_ws_bytes(uint64_t tiles) { return ws_bytes_for_tiles(tiles) + tiles * kSegWords * 4u; }
 
 }  // namespace dwps
 
@@ -250,7 +418,7 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
     const uint64_t tiles = ceil_div(n, kSegTile);
     bool query = false;
-    ps_status st = workspace_protocol(ws, ws_bytes, ws_bytes_for_tiles(tiles), &query);
+    ps_status st = workspace_protocol(ws, ws_bytes, seg_ws_bytes(tiles), &query);
     if (st != PS_OK || query) return st;
     if (n == 0 || num_segments == 0) return PS_OK;
     if (!values || !offsets || !out) return PS_ERR_NULL;
@@ -259,28 +427,32 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
         ranges_overlap(out, n * 4, offsets, ((size_t)num_segments + 1) * 4))
         return PS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_clear(ws, ws_bytes_for_tiles(tiles), s) != hipSuccess) return PS_ERR_HIP;
-    const bool vec = aligned(values, 16) && aligned(out, 16);
-    const dim3 grid((unsigned)tiles), block(kSegNT);
     uint32_t *ctr = ws_counter(ws);
     uint64_t *desc = ws_desc(ws);
-    const uint32_t n32 = (uint32_t)n;
-    timing_begin(s);
-    if (inclusive) {
-        if (vec)
-            hipLaunchKernelGGL((segscan_kernel<kSegNT, kSegQ, true, true>), grid, block, 0, s, values, out, n32,
-                               offsets, num_segments, ctr, desc);
-        else
-            hipLaunchKernelGGL((segscan_kernel<kSegNT, kSegQ, true, false>), grid, block, 0, s, values, out, n32,
-                               offsets, num_segments, ctr, desc);
-    } else {
-        if (vec)
-            hipLaunchKernelGGL((segscan_kernel<kSegNT, kSegQ, false, true>), grid, block, 0, s, values, out, n32,
-                               offsets, num_segments, ctr, desc);
-        else
-            hipLaunchKernelGGL((segscan_kernel<kSegNT, kSegQ, false, false>), grid, block, 0, s, values, out,
-                               n32, offsets, num_segments, ctr, desc);
-    }
+    uint32_t *heads = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + ws_bytes_for_tiles(tiles));
+    const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
+    hipLaunchKernelGGL(seg_prepass_kernel<kSegTile>, dim3(nt), dim3(64), 0, s, offsets, num_segments, n32, ctr,
+                       desc, heads);
+    if (hipGetLastError() != hipSuccess) return PS_ERR_HIP;
+    const bool vec = aligned(values, 16) && aligned(out, 16);
+    auto launch = [&](auto kernel) -> ps_status {
+        const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kSegThreads, nt);
+        if (!grid) return PS_ERR_HIP;
+        timing_begin(s);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSegThreads), 0, s, values, heads, out, n32, offsets,
+                           num_segments, nt, ctr, desc);
+        return PS_OK;
+    };
+    ps_status r;
+    if (inclusive)
+        r = vec ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, true>)
+                : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, false>);
+    else
+        r = vec ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, true>)
+                : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, false>);
+    if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
 }
+
+extern "C" uint32_t ps_segmented_tile_elements(void) { return kSegTile; }

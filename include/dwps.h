@@ -150,7 +150,11 @@ ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
  *                  written; empty segments write nothing.
  *   inclusive    : nonzero for the inclusive form.
  * Any overlap of out with values or offsets returns PS_ERR_ALIAS.
- * num_segments may be 0 (nothing is written). */
+ * num_segments may be 0 (nothing is written).
+ * Two kernels run per call: a pre-pass that writes a bitmap of the segment
+ * starts of every tile into the workspace (n/8 bytes, beside the tile
+ * descriptors), then the single-pass scan, which reads the values once and
+ * writes every row of a segment once. */
 ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes,
                                 const uint32_t *values, uint64_t n,
                                 const uint32_t *offsets, uint32_t num_segments,
@@ -216,9 +220,10 @@ uint32_t ps_lookback_group(void);
 ps_status ps_kernel_timing(int enable);
 ps_status ps_kernel_timing_read(double *total_ms, uint64_t *launches);
 
-/* Elements per tile of the flat scan kernel for `dtype`, and the library
- * version string. */
+/* Elements per tile of the flat scan kernel for `dtype`, of the segmented
+ * scan kernel, and the library version string. */
 uint32_t ps_tile_elements(ps_dtype dtype);
+uint32_t ps_segmented_tile_elements(void);
 const char *ps_version(void);
 const char *ps_status_string(ps_status status);
 

@@ -7,7 +7,7 @@ import sys
 import numpy as np
 import pytest
 
-TILE = 4096          # elements per tile of the segmented kernel
+TILE = 12288         # elements per tile of the segmented kernel (8 data waves x 6 x 256)
 FLAT_TILE = 12288    # elements per tile of the flat scan (8 data waves x 6 x 256)
 FLAT_GROUP = 2       # consecutive flat tiles claimed per ticket
 

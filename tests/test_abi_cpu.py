@@ -66,8 +66,13 @@ def test_size_queries():
         st2, need2 = _wsq(lib, "ps_scan", 3, 0, 1, None, None, n, None, None)
         assert st2 == 0 and need2 == need
         assert lib.ps_lookback_tiles(n) == tiles
-    st, need = _wsq(lib, "ps_segmented_scan_u32", None, 1 << 26, None, 1 << 16, None, 0, None)
-    assert st == 0 and need >= 256 + 8 * ((1 << 26) // 4096)
+    stile = lib.ps_segmented_tile_elements()
+    assert stile == 12288
+    for n in (0, 1, stile, stile + 1, 1 << 26, (1 << 32) - 1):
+        st, need = _wsq(lib, "ps_segmented_scan_u32", None, n, None, 1 << 16, None, 0, None)
+        tiles = -(-n // stile)
+        # header, one descriptor per tile, then a bitmap of segment starts
+        assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256 + tiles * (stile // 8), n
     for rb in (4, 8, 16):
         st, need = _wsq(lib, "ps_compact", None, rb, None, 1 << 26, None, None, None)
         assert st == 0 and need > 256

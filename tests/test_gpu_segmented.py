@@ -83,6 +83,57 @@ def test_long_segments_chain(dw, orc, inclusive):
     _check(dw, orc, x, off, inclusive)
 
 
+def test_tile_shape(dw):
+    assert dw.ps_segmented_tile_elements() == TILE
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tile_level_patterns(dw, orc, inclusive, seed):
+    """Every tile gets one of: no start, a start on its first element, one in
+    its middle, one on its last element, several, a run of empty segments --
+    so that every pairing of neighbours (and of the two tiles of a ticket
+    group) occurs, including head-free runs that chain across groups."""
+    rng = np.random.default_rng(seed)
+    tiles = 97
+    n = tiles * TILE - 1234
+    starts = []
+    for t in range(tiles):
+        b = t * TILE
+        kind = int(rng.integers(0, 6))
+        if kind == 1:
+            starts.append(b)
+        elif kind == 2:
+            starts.append(b + int(rng.integers(1, TILE - 1)))
+        elif kind == 3:
+            starts.append(b + TILE - 1)
+        elif kind == 4:
+            starts.extend(sorted(b + rng.choice(TILE, 5, replace=False)))
+        elif kind == 5:
+            starts.extend([b + 100] * 3)
+    # repeated offsets (kind 5, or a start at 0) are empty segments
+    off = np.array(sorted([0] + [s for s in starts if s < n] + [n]), np.uint32)
+    x = wl.full_range_u32(n, seed=seed + 50)
+    say("segmented tile patterns", seed, inclusive, off.size - 1)
+    _check(dw, orc, x, off, inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_unaligned_buffers(dw, orc, inclusive):
+    """values and out one element past a 16-byte boundary: the 4-byte path."""
+    import torch
+    n = 7 * TILE + 11
+    x = wl.full_range_u32(n, seed=8)
+    off = wl.random_segments(n, 40, seed=9, cover=False)
+    vx = dev(np.concatenate(([0], x)).astype(np.uint32))[1:]
+    vo = dev(np.full(n + 1, SENTINEL, np.uint32))[1:]
+    assert vx.data_ptr() % 16 != 0 and vo.data_ptr() % 16 != 0
+    say("segmented unaligned", inclusive)
+    dw.ps_segmented_scan_u32(vx, dev(off), vo, inclusive=inclusive)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(vo), orc.segmented_scan_u32(x, off, inclusive, sentinel=SENTINEL))
+
+
 def test_repeated_runs_stay_exact(dw, orc):
     import torch
     values, off = wl.zipf_segments(n=1 << 22, num_segments=1 << 12, seed=12)
