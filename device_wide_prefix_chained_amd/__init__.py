@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     DwpsError,
     lib,
     ps_compact,
+    ps_compact_tile_records,
     ps_copy_u32,
     ps_kernel_timing,
     ps_kernel_timing_read,

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.ps_tile_elements.restype = u32
     L.ps_segmented_tile_elements.argtypes = []
     L.ps_segmented_tile_elements.restype = u32
+    L.ps_compact_tile_records.argtypes = [u32]
+    L.ps_compact_tile_records.restype = u32
     L.ps_version.argtypes = []
     L.ps_version.restype = ctypes.c_char_p
     L.ps_status_string.argtypes = [i32]
@@ -293,6 +295,10 @@ def ps_tile_elements(dtype=PS_U32) -> int:
 
 def ps_segmented_tile_elements() -> int:
     return int(lib().ps_segmented_tile_elements())
+
+
+def ps_compact_tile_records(record_bytes: int) -> int:
+    return int(lib().ps_compact_tile_records(record_bytes))
 
 
 def ps_version() -> str:

@@ -6,107 +6,280 @@
 // the exclusive scan of the keep flags at its position, so kept records land
 // densely and in input order; the count is the last offset plus the last
 // flag.  The offsets are never written to memory (the page's advice to avoid
-// materialising the flags and prefixes): each tile scans its flags in
-// registers, takes its output base from the chained look-back over per-tile
-// counts, and writes its kept records straight to their destinations.
+// materialising the flags and prefixes).
 //
-// Tile: NT threads x R records.  Wave w owns 64*R consecutive records; step r
-// of lane l handles record (w*64*R + r*64 + l), so every step of a wave reads
-// 64 consecutive flag bytes and up to 64 consecutive records.  Within a step
-// the flag scan is a ballot plus a lane-masked popcount (v_mbcnt), the
-// rank of a kept record among the kept records of earlier lanes.
+// The flat scan's persistent, wave-specialised pipeline with a count as the
+// scanned value: a tile is D waves x Q loads of 16 bytes per lane (E = 16 /
+// record_bytes records per load), 48 KiB of records.  Per phase a data wave
+//   * parks the kept records of the current tile, compacted, at their
+//     tile-relative positions in LDS (the rank of a record is a ballot plus a
+//     lane-masked popcount, v_mbcnt, over its row of 64 lanes);
+//   * issues the loads of the tile two ahead into the freed registers;
+//   * ranks the next tile (its wave count goes to the control wave);
+//   * after the look-back of the tile parked two phases earlier has returned
+//     its output base, copies that tile's run of kept records from LDS to
+//     out[base ...] -- contiguous, so every store instruction of the wave
+//     writes 64 consecutive records.
+// The control wave is the flat scan's (tile counts instead of sums).
 #include <hip/hip_runtime.h>
 
 #include "dwps_device.hpp"
 #include "host_common.hpp"
+#include "pipeline.hpp"
+#include "tile_io.hpp"
 
 namespace dwps {
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-template <class Rec, int NT, int R>
-__global__ __launch_bounds__(NT) void compact_kernel(const Rec *records, const uint8_t *flags, uint32_t n,
-                                                     Rec *out, uint64_t *num_selected, uint32_t num_tiles,
-                                                     uint32_t *ctr, uint64_t *desc) {
-    constexpr int NW = NT / 64;
-    constexpr uint32_t WAVE_RECS = (uint32_t)R * 64u;
-    constexpr uint32_t TILE = (uint32_t)NT * (uint32_t)R;
+// Record k of a 16-byte load, for each record width.
+template <class Rec>
+__device__ __forceinline__ Rec record_at(const v4u &raw, int k);
+template <>
+__device__ __forceinline__ uint32_t record_at<uint32_t>(const v4u &raw, int k) {
+    return raw[k];
+}
+template <>
+__device__ __forceinline__ v2u record_at<v2u>(const v4u &raw, int k) {
+    v2u r;
+    r.x = raw[2 * k];
+    r.y = raw[2 * k + 1];
+    return r;
+}
+template <>
+__device__ __forceinline__ v4u record_at<v4u>(const v4u &raw, int k) {
+    (void)k;
+    return raw;
+}
 
-    __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_wave[NW];
-    __shared__ uint32_t s_base;
+// Register state of one wave's span of a tile: Q 16-byte loads per lane and
+// the keep flags of their records (byte k of fw[q] is the flag of record k).
+// Load q of lane l covers records q*64*E + l*E ... + E-1 of the span, so one
+// load instruction of the wave reads 1 KiB of consecutive records and the
+// flags it needs are 64*E consecutive bytes.
+template <class Rec, int Q>
+struct RecSpan {
+    static constexpr int E = 16 / (int)sizeof(Rec);
+    v4u raw[Q];
+    uint32_t fw[Q];
 
-    const uint32_t tid = threadIdx.x;
-    const uint32_t lane = tid & 63u;
-    const uint32_t wave = tid >> 6;
-
-    if (tid == 0) s_tile = take_ticket(ctr);
-    __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint64_t first = (uint64_t)tile * TILE + (uint64_t)wave * WAVE_RECS + lane;
-
-    bool keep[R];
-    Rec rec[R];
+    // Straight-line loads as in the flat scan: past-the-end groups are
+    // clamped to the last group that starts below n (it never leaves the page
+    // of record n-1, nor does the flag word of that group), !valid reads the
+    // first group again; pad() drops the flags at or past n.
+    // VEC: records 16-byte aligned and flags E-byte aligned -- one 16-byte
+    // record load and one E-byte flag load per group; otherwise one load per
+    // record and flag byte.
+    template <bool VEC>
+    __device__ __forceinline__ void load(const Rec *records, const uint8_t *flags, uint64_t span, uint32_t n,
+                                         bool full, bool valid) {
+        if (VEC) {
+            const uint64_t last_group = ((uint64_t)n - 1u) / E * E;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint64_t i = first + (uint64_t)r * 64u;
-        keep[r] = (i < n) && flags[i] != 0;
-    }
+            for (int q = 0; q < Q; ++q) {
+                uint64_t g = span + (uint64_t)q * 64u * E;
+                if (!full) g = g < last_group ? g : last_group;
+                if (!valid) g = 0;
+                raw[q] = load16(records + g);
+                if (E == 4)
+                    fw[q] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(flags + g));
+                else if (E == 2)
+                    fw[q] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(flags + g));
+                else
+                    fw[q] = __builtin_nontemporal_load(flags + g);
+            }
+        } else {
+            const uint64_t last = (uint64_t)n - 1u;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint64_t i = first + (uint64_t)r * 64u;
-        if (keep[r]) rec[r] = records[i];
-    }
-    uint32_t rank[R], step_prefix[R];
-    uint32_t run = 0u;
+            for (int q = 0; q < Q; ++q) {
+                uint32_t w[4];
+                uint32_t f = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint64_t m = ballot(keep[r]);
-        rank[r] = lane_rank(m);
-        step_prefix[r] = run;
-        run += (uint32_t)__builtin_popcountll(m);
+                for (int k = 0; k < E; ++k) {
+                    uint64_t i = span + (uint64_t)q * 64u * E + k;
+                    i = i < last ? i : last;
+                    if (!valid) i = 0;
+                    const uint32_t *r = reinterpret_cast<const uint32_t *>(records + i);
+#pragma unroll
+                    for (int j = 0; j < 4 / E; ++j) w[k * (4 / E) + j] = r[j];
+                    f |= (uint32_t)flags[i] << (8 * k);
+                }
+                raw[q].x = w[0];
+                raw[q].y = w[1];
+                raw[q].z = w[2];
+                raw[q].w = w[3];
+                fw[q] = f;
+            }
+        }
     }
-    if (lane == 0) s_wave[wave] = run;
-    __syncthreads();
+
+    __device__ __forceinline__ void pad(uint64_t span, uint32_t n, bool full) {
+        if (full) return;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const uint64_t i = span + (uint64_t)q * 64u * E + k;
+                fw[q] = (i < n) ? fw[q] : (fw[q] & ~(0xFFu << (8 * k)));
+            }
+    }
+};
+
+template <int D, int Q>
+struct CompactShared {
+    v4u park[kParkSlots][D * Q * 64];  // kept records of a tile, compacted
+    uint32_t park_cnt[kParkSlots];     // number of kept records of each parked tile
+    uint32_t wt[2][D];                 // wave counts, double-buffered by phase parity
+    uint32_t t0;
+    uint32_t next;
+    uint32_t prefix;                   // output base of prev2
+};
+
+// One phase of a data wave (see the file comment).  kb[q] holds the keep
+// bits of the lane's E records of row q of cur, pos[q] the wave-relative
+// position of the first of them; both come from the ranking of the previous
+// phase.
+template <class Rec, int D, int Q, int G, bool VEC>
+__device__ __forceinline__ bool compact_phase(RecSpan<Rec, Q> &cur, RecSpan<Rec, Q> &f1, int par, uint32_t &slot,
+                                              PipeTiles &pt, uint32_t (&kb)[Q], uint32_t (&pos)[Q],
+                                              CompactShared<D, Q> &sh, const Rec *records, const uint8_t *flags,
+                                              Rec *out, uint64_t *num_selected, uint32_t n, uint32_t num_tiles,
+                                              uint32_t *ctr, uint32_t lane, uint32_t d, uint64_t lane_off) {
+    constexpr int E = RecSpan<Rec, Q>::E;
+    constexpr uint32_t TILE = (uint32_t)D * Q * 64u * E;
+    const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
+    uint32_t ticket = 0;
+    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
+    const uint32_t old_slot = next_slot(slot);
+
+    // park the kept records of cur at their tile-relative positions
     uint32_t wave_prefix = 0u, count = 0u;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t t = s_wave[w];
-        if ((uint32_t)w < wave) wave_prefix += t;
-        count += t;
+    for (int w = 0; w < D; ++w) {
+        const uint32_t c = sh.wt[par][w];
+        wave_prefix += ((uint32_t)w < d) ? c : 0u;
+        count += c;
     }
-    if (wave == 0) {
-        LookbackStats st;
-        uint32_t excl = 0u;
-        if (tile == 0) {
-            if (lane == 0) desc_publish(desc, desc_word(ST_PREFIX, count));
-        } else {
-            if (lane == 0) desc_publish(desc + tile, desc_word(ST_AGGREGATE, count));
-            excl = lookback<SumU32, DWPS_LOOKBACK_K, false>(desc, tile, lane, st, ctr + 1);
-            if (lane == 0) desc_publish(desc + tile, desc_word(ST_PREFIX, excl + count));
+    if (d == 0 && lane == 0) sh.park_cnt[slot] = count;
+    Rec *mine = reinterpret_cast<Rec *>(&sh.park[slot][0]);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const uint32_t p = wave_prefix + pos[q];
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if ((kb[q] >> k) & 1u) mine[p + (uint32_t)__builtin_popcount(kb[q] & ((1u << k) - 1u))] =
+                record_at<Rec>(cur.raw[q], k);
+    }
+    // the freed registers take the tile two ahead
+    const uint64_t b2 = (uint64_t)pt.f2 * TILE;
+    cur.template load<VEC>(records, flags, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
+    // rank the next tile while the control wave looks back
+    {
+        const uint64_t b1 = (uint64_t)pt.f1 * TILE;
+        f1.pad(b1 + lane_off, n, b1 + TILE <= n);
+        uint32_t run = 0u;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int k = 0; k < E; ++k) bits |= ((f1.fw[q] >> (8 * k)) & 0xFFu) ? (1u << k) : 0u;
+            kb[q] = bits;
+            uint32_t before = 0u, total = 0u;
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const uint64_t m = ballot(((bits >> k) & 1u) != 0u);
+                before += lane_rank(m);
+                total += (uint32_t)__builtin_popcountll(m);
+            }
+            pos[q] = run + before;
+            run += total;
         }
-        if (lane == 0) {
-            s_base = excl;
-            if (tile == num_tiles - 1) *num_selected = (uint64_t)(excl + count);
-        }
+        if (lane == 0) sh.wt[par ^ 1][d] = run;
+    }
+    __syncthreads();  // B
+    if (pt.prev2 < num_tiles) {
+        const uint32_t cnt = sh.park_cnt[old_slot];
+        const uint32_t base = sh.prefix;
+        const Rec *theirs = reinterpret_cast<const Rec *>(&sh.park[old_slot][0]);
+        for (uint32_t j = d * 64u + lane; j < cnt; j += (uint32_t)D * 64u)
+            __builtin_nontemporal_store(theirs[j], out + (uint64_t)base + j);
+        if (pt.prev2 == num_tiles - 1u && d == 0 && lane == 0) *num_selected = (uint64_t)base + cnt;
+    }
+    if (pt.drained(num_tiles)) return true;
+    if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
+    slot = old_slot;  // the slot just emptied takes the next tile
+    __syncthreads();  // A
+    pt.advance(uniform(sh.next), num_tiles);
+    return false;
+}
+
+template <class Rec, int D, int Q, int G, bool VEC>
+__device__ __forceinline__ void compact_data_loop(PipeTiles pt, CompactShared<D, Q> &sh, const Rec *records,
+                                                  const uint8_t *flags, Rec *out, uint64_t *num_selected,
+                                                  uint32_t n, uint32_t num_tiles, uint32_t *ctr, uint32_t lane,
+                                                  uint32_t d) {
+    constexpr int E = RecSpan<Rec, Q>::E;
+    const uint64_t lane_off = (uint64_t)d * Q * 64u * E + (uint64_t)lane * E;
+    RecSpan<Rec, Q> x, y;
+    // no keep bits before the first ranking: the first phases park nothing
+    uint32_t kb[Q], pos[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) kb[q] = pos[q] = 0u;
+    uint32_t slot = 0;
+    for (;;) {
+        if (compact_phase<Rec, D, Q, G, VEC>(x, y, 0, slot, pt, kb, pos, sh, records, flags, out, num_selected, n,
+                                             num_tiles, ctr, lane, d, lane_off))
+            break;
+        if (compact_phase<Rec, D, Q, G, VEC>(y, x, 1, slot, pt, kb, pos, sh, records, flags, out, num_selected, n,
+                                             num_tiles, ctr, lane, d, lane_off))
+            break;
+    }
+}
+
+template <class Rec, int D, int Q, int LB_K, int G, bool VEC>
+__global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *records, const uint8_t *flags,
+                                                               uint32_t n, Rec *out, uint64_t *num_selected,
+                                                               uint32_t num_tiles, uint32_t *ctr, uint64_t *desc) {
+    __shared__ CompactShared<D, Q> sh;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = uniform(threadIdx.x >> 6);
+    if (threadIdx.x == 0) {
+        const uint32_t g = take_ticket(ctr);
+        sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
     }
     __syncthreads();
-    const uint32_t base = s_base + wave_prefix;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (keep[r]) out[base + step_prefix[r] + rank[r]] = rec[r];
+    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
+    if (pt.f2 >= num_tiles) return;
+    if (wave == 0)
+        control_loop<SumU32, D, LB_K, G, false>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr, nullptr, 0,
+                                                lane);
+    else
+        compact_data_loop<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
+                                             wave - 1);
 }
 
 __global__ void write_count_zero(uint64_t *p) { *p = 0ull; }
 
-constexpr int kCompactNT = 256;
+// Compaction tile shape: D data waves x Q 16-byte loads per lane.
+#ifndef DWPS_COMPACT_D
+#define DWPS_COMPACT_D 8
+#endif
+#ifndef DWPS_COMPACT_Q
+#define DWPS_COMPACT_Q 6
+#endif
+constexpr int kCompactD = DWPS_COMPACT_D;
+constexpr int kCompactQ = DWPS_COMPACT_Q;
+constexpr int kCompactG = 2;
+constexpr int kCompactThreads = (kCompactD + 1) * 64;
 
-template <class Rec, int R>
+template <class Rec>
 ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const uint8_t *flags, uint64_t n,
                          void *out, uint64_t *num_selected, hipStream_t s) {
-    constexpr uint32_t TILE = kCompactNT * R;
+    constexpr uint32_t TILE = (uint32_t)kCompactD * kCompactQ * 64u * (16u / sizeof(Rec));
     const uint64_t tiles = ceil_div(n, TILE);
     bool query = false;
     ps_status st = workspace_protocol(ws, ws_bytes, ws_bytes_for_tiles(tiles), &query);
@@ -124,10 +297,23 @@ ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const 
         ranges_overlap(num_selected, 8, out, bytes))
         return PS_ERR_ALIAS;
     if (launch_clear(ws, ws_bytes_for_tiles(tiles), s) != hipSuccess) return PS_ERR_HIP;
-    timing_begin(s);
-    hipLaunchKernelGGL((compact_kernel<Rec, kCompactNT, R>), dim3((unsigned)tiles), dim3(kCompactNT), 0, s,
-                       static_cast<const Rec *>(records), flags, (uint32_t)n, static_cast<Rec *>(out),
-                       num_selected, (uint32_t)tiles, ws_counter(ws), ws_desc(ws));
+    const bool vec = aligned(records, 16) && aligned(flags, 16 / sizeof(Rec));
+    const Rec *rin = static_cast<const Rec *>(records);
+    Rec *rout = static_cast<Rec *>(out);
+    const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
+    uint32_t *ctr = ws_counter(ws);
+    uint64_t *desc = ws_desc(ws);
+    auto launch = [&](auto kernel) -> ps_status {
+        const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kCompactThreads, nt);
+        if (!grid) return PS_ERR_HIP;
+        timing_begin(s);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCompactThreads), 0, s, rin, flags, n32, rout, num_selected,
+                           nt, ctr, desc);
+        return PS_OK;
+    };
+    const ps_status r = vec ? launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, true>)
+                            : launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, false>);
+    if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
 }
@@ -142,9 +328,14 @@ extern "C" ps_status ps_compact(void *ws, size_t *ws_bytes, const void *records,
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (record_bytes) {
-    case 4: return launch_compact<uint32_t, 16>(ws, ws_bytes, records, flags, n, out, num_selected, s);
-    case 8: return launch_compact<uint2, 16>(ws, ws_bytes, records, flags, n, out, num_selected, s);
-    case 16: return launch_compact<uint4, 8>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    case 4: return launch_compact<uint32_t>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    case 8: return launch_compact<v2u>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    case 16: return launch_compact<v4u>(ws, ws_bytes, records, flags, n, out, num_selected, s);
     default: return PS_ERR_UNSUPPORTED;
     }
+}
+
+extern "C" uint32_t ps_compact_tile_records(uint32_t record_bytes) {
+    if (record_bytes != 4 && record_bytes != 8 && record_bytes != 16) return 0;
+    return (uint32_t)kCompactD * kCompactQ * 64u * (16u / record_bytes);
 }

@@ -48,63 +48,6 @@ struct ScanShared {
     T prefix;
 };
 
-// Control wave: aggregates, look-back, prefixes.  Phase k runs between
-// barriers A_k and B_k, while the data waves work on their side.  The
-// look-back of a tile runs two phases after its aggregate went out, so the
-// aggregates of its neighbours and the prefixes of the tiles one generation
-// older are already published: one poll, off the critical path.  The wave
-// issues its descriptor stores only after the poll has returned, so the only
-// thing it ever waits for is its own poll.
-template <class Op, int D, int Q, int LB_K, int G, bool STATS>
-__device__ __forceinline__ void control_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, uint32_t num_tiles,
-                                             uint32_t *ctr, uint64_t *desc, typename Op::T *total,
-                                             uint32_t *stats, int aggregate_only, uint32_t lane) {
-    using T = typename Op::T;
-    T agg_prev = Op::id(), agg_prev2 = Op::id();
-    T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
-    for (int par = 0;; par ^= 1) {
-        T agg = Op::id();
-        if (pt.cur < num_tiles) {
-#pragma unroll
-            for (int w = 0; w < D; ++w) agg = Op::op(agg, sh.wt[par][w]);
-        }
-        // Only the first tile of a group looks back; the next ones of the
-        // group follow it through this wave's own registers.
-        LookbackStats st;
-        uint64_t t0 = 0;
-        if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
-        T excl = Op::id();
-        const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
-        const bool look = have_prev2 && (pt.prev2 % G == 0u || (STATS && aggregate_only));
-        if (look)
-            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr + 1);
-        else if (have_prev2)
-            excl = incl_last;
-        if (lane == 0) {
-            sh.prefix = excl;
-            if (pt.prev2 < num_tiles) {
-                if (total && pt.prev2 == num_tiles - 1) *total = Op::op(excl, agg_prev2);
-                if (STATS) {
-                    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-                    reinterpret_cast<uint4 *>(stats)[pt.prev2] =
-                        make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
-                }
-            }
-            if (have_prev2 && !(STATS && aggregate_only))
-                desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, to_bits(Op::op(excl, agg_prev2))));
-            if (pt.cur < num_tiles)
-                desc_publish(desc + pt.cur, desc_word(pt.cur == 0 ? ST_PREFIX : ST_AGGREGATE, to_bits(agg)));
-        }
-        incl_last = Op::op(excl, agg_prev2);
-        agg_prev2 = agg_prev;
-        agg_prev = agg;
-        __syncthreads();  // B: prefix of prev2 is in LDS
-        if (pt.drained(num_tiles)) break;
-        __syncthreads();  // A: the next tile id is in LDS
-        pt.advance(uniform(sh.next), num_tiles);
-    }
-}
-
 // One phase of a data wave: `cur` holds the scanned current tile (its wave
 // totals in wt[par]), `f1` the next tile (loads in flight).  cur is parked
 // in LDS slot `slot`; slot (slot+1) % 3 holds prev2.  Data wave 0 also takes
@@ -215,7 +158,7 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0)
-        control_loop<Op, D, Q, LB_K, G, STATS>(pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, lane);
+        control_loop<Op, D, LB_K, G, STATS>(pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, lane);
     else
         data_loop<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
 }

@@ -182,6 +182,9 @@ ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_segments,
 ps_status ps_compact(void *ws, size_t *ws_bytes, const void *records,
                      uint32_t record_bytes, const uint8_t *flags, uint64_t n,
                      void *out, uint64_t *num_selected, void *stream);
+/* Records per tile of the compaction kernel for a record width (4, 8 or
+ * 16 bytes; 0 for any other width). */
+uint32_t ps_compact_tile_records(uint32_t record_bytes);
 
 /* ---------------------------------------------------------------------------
  * Measurement and diagnostics (not part of the scan itself).

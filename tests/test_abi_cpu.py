@@ -74,8 +74,13 @@ def test_size_queries():
         # header, one descriptor per tile, then a bitmap of segment starts
         assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256 + tiles * (stile // 8), n
     for rb in (4, 8, 16):
-        st, need = _wsq(lib, "ps_compact", None, rb, None, 1 << 26, None, None, None)
-        assert st == 0 and need > 256
+        ctile = lib.ps_compact_tile_records(rb)
+        assert ctile == 8 * 6 * 64 * (16 // rb)
+        for n in (0, 1, ctile, ctile + 1, 1 << 26):
+            st, need = _wsq(lib, "ps_compact", None, rb, None, n, None, None, None)
+            tiles = -(-n // ctile)
+            assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256, (rb, n)
+    assert lib.ps_compact_tile_records(12) == 0
 
 
 FAKE_WS = 0x10000000

@@ -66,6 +66,55 @@ def test_edge_lengths(dw, orc, n, width, kind):
     _check(dw, orc, rec, flags)
 
 
+def test_tile_shape(dw):
+    for rb in (4, 8, 16):
+        assert dw.ps_compact_tile_records(rb) == 8 * 6 * 64 * (16 // rb)
+    assert dw.ps_compact_tile_records(12) == 0
+
+
+@pytest.mark.parametrize("width", [1, 2, 4])
+@pytest.mark.parametrize("rel", [(1, -1), (1, 0), (1, 1), (2, -1), (2, 0), (2, 1), (3, 5), (64, 7), (301, 0)])
+@pytest.mark.parametrize("kind", ["none", "all", "random", "clustered"])
+def test_tile_relative_lengths(dw, orc, width, rel, kind):
+    """Lengths around whole tiles and ticket groups of the compaction kernel
+    for each record width (its tile holds 48 KiB of records)."""
+    tile = dw.ps_compact_tile_records(4 * width)
+    n = rel[0] * tile + rel[1]
+    rec = wl.full_range_u32(n * width, seed=n + 3 * width).reshape(n, width)
+    if width == 1:
+        rec = rec.reshape(n)
+    flags = wl.flag_pattern(n, kind, seed=n + 5, run=tile // 3 + 1)
+    say("compact tile-relative", width, rel, kind)
+    _check(dw, orc, rec, flags)
+
+
+@pytest.mark.parametrize("width", [1, 2, 4])
+def test_unaligned_buffers(dw, orc, width):
+    """Flags one byte past an aligned address, and for 4- and 8-byte records
+    records that are not 16-byte aligned: the per-record load path."""
+    import torch
+    n = 3 * dw.ps_compact_tile_records(4 * width) + 77
+    rec = wl.full_range_u32(n * width, seed=21 + width).reshape(n, width)
+    flags = wl.flag_pattern(n, "random", seed=22 + width)
+    d_flags = dev(np.concatenate(([7], flags)).astype(np.uint8))[1:]
+    shift = 0 if width == 4 else 1
+    full = np.concatenate((np.zeros((shift, width), np.uint32), rec))
+    d_rec = dev(full)[shift:]
+    d_out = dev(np.full((n + shift, width), FILL, np.uint32))[shift:]
+    if width == 1:
+        d_rec, d_out = d_rec.reshape(n), d_out.reshape(n)
+    assert d_flags.data_ptr() % 2 == 1
+    if width < 4:
+        assert d_rec.data_ptr() % 16 != 0
+    cnt = torch.full((1,), -7, dtype=torch.int64, device="cuda")
+    say("compact unaligned", width)
+    dw.ps_compact(d_rec, d_flags, d_out, cnt)
+    ref, ref_count = orc.compact(rec.reshape(n) if width == 1 else rec, flags,
+                                 out=np.full((n,) if width == 1 else (n, width), FILL, np.uint32))
+    assert int(host(cnt)[0]) == ref_count
+    assert np.array_equal(host(d_out), ref)
+
+
 def test_empty(dw):
     import torch
     cnt = torch.full((1,), 99, dtype=torch.int64, device="cuda")
