@@ -28,18 +28,23 @@ hipError_t launch_clear(void *p, size_t bytes, hipStream_t stream) {
 
 // Streaming copy: each thread moves 4 x 16 bytes per iteration, coalesced
 // across the wave; the scalar tail is handled by the first threads.
-__global__ __launch_bounds__(256) void copy_vec_kernel(const uint4 *in, uint4 *out, uint64_t n16) {
+typedef unsigned int copy_v4u __attribute__((ext_vector_type(4)));
+
+// Streaming copy, 4 x 16 bytes per thread, non-temporal loads and stores
+// (the fastest plain copy found on MI355X: it is the practical HBM ceiling
+// the scans are compared with).
+__global__ __launch_bounds__(256) void copy_vec_kernel(const copy_v4u *in, copy_v4u *out, uint64_t n16) {
     const uint64_t base = ((uint64_t)blockIdx.x * 256 * 4) + threadIdx.x;
-    uint4 r[4];
+    copy_v4u r[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint64_t i = base + (uint64_t)k * 256;
-        if (i < n16) r[k] = in[i];
+        if (i < n16) r[k] = __builtin_nontemporal_load(in + i);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint64_t i = base + (uint64_t)k * 256;
-        if (i < n16) out[i] = r[k];
+        if (i < n16) __builtin_nontemporal_store(r[k], out + i);
     }
 }
 __global__ void copy_scalar_kernel(const uint32_t *in, uint32_t *out, uint64_t begin, uint64_t n) {
@@ -140,7 +145,7 @@ extern "C" ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, 
         if (n16) {
             const uint64_t blocks = ceil_div(n16, 1024);
             hipLaunchKernelGGL(copy_vec_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                               reinterpret_cast<const uint4 *>(in), reinterpret_cast<uint4 *>(out), n16);
+                               reinterpret_cast<const copy_v4u *>(in), reinterpret_cast<copy_v4u *>(out), n16);
         }
         done = n16 * 4;
     }

@@ -22,11 +22,11 @@
 //     segments chain through start-free tiles exactly like the flat scan.
 //
 // Two launches per call:
-//   1. a pre-pass, one wave per tile, clears the tile's descriptor and writes
-//      the tile's segment starts as a bitmap into the workspace: two 64-way
-//      searches of the offsets bound the starts inside the tile, and those
-//      starts set bits in LDS (repeated offsets -- empty segments -- set the
-//      same bit);
+//   1. a pre-pass, one wave per tile (four per workgroup), clears the tile's
+//      descriptor and writes the tile's segment starts as a bitmap into the
+//      workspace: two 64-way searches of the offsets, run side by side, bound
+//      the starts inside the tile, and those starts set bits in LDS (repeated
+//      offsets -- empty segments -- set the same bit);
 //   2. the persistent, wave-specialised pipeline of the flat scan (one
 //      control wave, D data waves, look-back two phases behind the
 //      aggregate), streaming the values and their bitmap words.
@@ -39,27 +39,51 @@
 
 namespace dwps {
 
-// First index s in [0, count) with a[s] >= key (count if none), searched by
-// one full wave: 64 probes per round narrow the range 64-fold, so 65 537
-// offsets take three dependent rounds.  Reads stay inside [0, count) even if
-// `a` is not sorted.
-__device__ __forceinline__ uint32_t wave_lower_bound(const uint32_t *a, uint32_t count, uint32_t key,
-                                                     uint32_t lane) {
-    uint32_t lo = 0, hi = count;
-    while (hi - lo > 64u) {
-        const uint32_t step = (hi - lo + 63u) / 64u;
-        const uint32_t p = lo + lane * step;
-        const bool less = (p < hi) && (a[p] < key);
-        const uint32_t c = (uint32_t)__builtin_popcountll(ballot(less));
-        if (c == 0) return lo;
-        const uint32_t old_lo = lo;
-        lo = old_lo + (c - 1u) * step + 1u;
-        const uint32_t next_probe = old_lo + c * step;
-        hi = next_probe < hi ? next_probe : hi;
+// Lower bounds of two keys in one sorted array (first index s in [0, count)
+// with a[s] >= key, count if none), searched by one full wave: per round each
+// search probes 64 evenly spaced entries of its range and keeps the stretch
+// between the last probe below its key and the next one, so 65 537 offsets
+// take three rounds.  The probes of both searches are issued together, so a
+// round costs one memory latency.  Reads stay inside [0, count) even if `a`
+// is not sorted.
+__device__ __forceinline__ void wave_lower_bound2(const uint32_t *a, uint32_t count, uint32_t key0, uint32_t key1,
+                                                  uint32_t lane, uint32_t &r0, uint32_t &r1) {
+    // [lo, hi] brackets the answer; probes stay below hi
+    uint32_t lo0 = 0, hi0 = count, lo1 = 0, hi1 = count;
+    for (;;) {
+        const uint32_t w0 = hi0 - lo0, w1 = hi1 - lo1;
+        const uint32_t s0 = w0 > 64u ? (w0 + 63u) / 64u : 1u;
+        const uint32_t s1 = w1 > 64u ? (w1 + 63u) / 64u : 1u;
+        const uint32_t p0 = lo0 + lane * s0, p1 = lo1 + lane * s1;
+        const bool in0 = p0 < hi0, in1 = p1 < hi1;
+        const uint32_t v0 = in0 ? a[p0] : 0u;
+        const uint32_t v1 = in1 ? a[p1] : 0u;
+        const uint32_t c0 = (uint32_t)__builtin_popcountll(ballot(in0 && v0 < key0));
+        const uint32_t c1 = (uint32_t)__builtin_popcountll(ballot(in1 && v1 < key1));
+        if (w0 <= 64u) {
+            lo0 += c0;  // every entry of the range was probed
+            hi0 = lo0;
+        } else if (c0 == 0u) {
+            hi0 = lo0;  // a[lo0] >= key0
+        } else {
+            const uint32_t b = lo0;
+            lo0 = b + (c0 - 1u) * s0 + 1u;
+            hi0 = min(hi0, b + c0 * s0);
+        }
+        if (w1 <= 64u) {
+            lo1 += c1;
+            hi1 = lo1;
+        } else if (c1 == 0u) {
+            hi1 = lo1;
+        } else {
+            const uint32_t b = lo1;
+            lo1 = b + (c1 - 1u) * s1 + 1u;
+            hi1 = min(hi1, b + c1 * s1);
+        }
+        if (lo0 == hi0 && lo1 == hi1) break;
     }
-    const uint32_t p = lo + lane;
-    const bool less = (p < hi) && (a[p] < key);
-    return lo + (uint32_t)__builtin_popcountll(ballot(less));
+    r0 = lo0;
+    r1 = lo1;
 }
 
 struct SegPair {
@@ -105,18 +129,22 @@ constexpr uint32_t kSegWords = kSegTile / 32u;  // bitmap words per tile
 // ---------------------------------------------------------------------------
 // 1. pre-pass: descriptors cleared, per-tile segment-start bitmaps written
 // ---------------------------------------------------------------------------
-template <uint32_t TILE>
-__global__ __launch_bounds__(64) void seg_prepass_kernel(const uint32_t *offsets, uint32_t num_segments,
-                                                         uint32_t n, uint32_t *ctr, uint64_t *desc,
-                                                         uint32_t *heads) {
+// W waves per workgroup, one tile per wave.
+template <uint32_t TILE, int W>
+__global__ __launch_bounds__(W * 64) void seg_prepass_kernel(const uint32_t *offsets, uint32_t num_segments,
+                                                             uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+                                                             uint64_t *desc, uint32_t *heads) {
     constexpr uint32_t WORDS = TILE / 32u;
-    __shared__ uint32_t bits[WORDS];
-    const uint32_t lane = threadIdx.x;
-    const uint32_t t = blockIdx.x;
-    const uint32_t tb = t * TILE;  // t * TILE <= n - 1
+    __shared__ uint32_t bits_all[W][WORDS];
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t w = threadIdx.x >> 6;
+    uint32_t *bits = bits_all[w];
+    const uint32_t t = blockIdx.x * W + w;
+    const bool live = t < num_tiles;  // the last workgroup may hold fewer tiles
+    const uint32_t tb = live ? t * TILE : 0u;  // t * TILE <= n - 1
     const uint64_t tile_end = (uint64_t)tb + TILE;
     const uint32_t te = tile_end < (uint64_t)n ? (uint32_t)tile_end : n;
-    if (lane == 0) {
+    if (live && lane == 0) {
         desc[t] = 0ull;
         if (t == 0) {
             ctr[0] = 0u;  // ticket counter
@@ -124,16 +152,18 @@ __global__ __launch_bounds__(64) void seg_prepass_kernel(const uint32_t *offsets
         }
     }
     for (uint32_t i = lane; i < WORDS; i += 64) bits[i] = 0u;
-    const uint32_t lo = wave_lower_bound(offsets, num_segments + 1u, tb, lane);
-    const uint32_t hi = wave_lower_bound(offsets, num_segments + 1u, te, lane);
+    uint32_t lo = 0, hi = 0;
+    if (live) wave_lower_bound2(offsets, num_segments + 1u, tb, te, lane, lo, hi);
     __syncthreads();
     for (uint32_t s = lo + lane; s < hi; s += 64) {
         const uint32_t o = offsets[s];
         if (o >= tb && o < te) atomicOr(&bits[(o - tb) >> 5], 1u << ((o - tb) & 31u));
     }
     __syncthreads();
-    uint32_t *dst = heads + (uint64_t)t * WORDS;
-    for (uint32_t i = lane; i < WORDS; i += 64) dst[i] = bits[i];
+    if (live) {
+        uint32_t *dst = heads + (uint64_t)t * WORDS;
+        for (uint32_t i = lane; i < WORDS; i += 64) dst[i] = bits[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -431,8 +461,9 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
     uint64_t *desc = ws_desc(ws);
     uint32_t *heads = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + ws_bytes_for_tiles(tiles));
     const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
-    hipLaunchKernelGGL(seg_prepass_kernel<kSegTile>, dim3(nt), dim3(64), 0, s, offsets, num_segments, n32, ctr,
-                       desc, heads);
+    constexpr int kPreWaves = 4;
+    hipLaunchKernelGGL((seg_prepass_kernel<kSegTile, kPreWaves>), dim3((unsigned)ceil_div(nt, kPreWaves)),
+                       dim3(kPreWaves * 64), 0, s, offsets, num_segments, n32, nt, ctr, desc, heads);
     if (hipGetLastError() != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(values, 16) && aligned(out, 16);
     auto launch = [&](auto kernel) -> ps_status {

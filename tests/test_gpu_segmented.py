@@ -134,6 +134,34 @@ def test_unaligned_buffers(dw, orc, inclusive):
     assert np.array_equal(host(vo), orc.segmented_scan_u32(x, off, inclusive, sentinel=SENTINEL))
 
 
+@pytest.mark.parametrize("inclusive", [False, True])
+@pytest.mark.parametrize("nseg", [131071, 131072])
+def test_many_segments(dw, orc, inclusive, nseg):
+    """2^17 segments over 2^22 + 5 values: three-round offset searches in the
+    pre-pass, about 32 elements per segment."""
+    n = 32 * 131072 + 5
+    x = wl.full_range_u32(n, seed=nseg)
+    off = wl.random_segments(n, nseg, seed=nseg + 1, cover=True)
+    say("segmented many segments", nseg, inclusive)
+    _check(dw, orc, x, off, inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_dense_cluster_in_sparse_offsets(dw, orc, inclusive):
+    """Mostly long segments with a run of 5000 unit segments and a run of 3000
+    two-element segments: tiles holding thousands of starts next to tiles
+    holding none."""
+    n = 1 << 22
+    starts = list(range(0, 700_000, 997))
+    starts += list(range(700_000, 705_000))                 # unit segments
+    starts += list(range(705_000, 711_000, 2))              # two-element segments
+    starts += list(range(711_000, n - 20_000, 1531))
+    off = np.array(starts + [n - 20_000], np.uint32)
+    x = wl.full_range_u32(n, seed=77)
+    say("segmented dense cluster", inclusive)
+    _check(dw, orc, x, off, inclusive)
+
+
 def test_repeated_runs_stay_exact(dw, orc):
     import torch
     values, off = wl.zipf_segments(n=1 << 22, num_segments=1 << 12, seed=12)
