@@ -135,6 +135,17 @@ def build_workload(name: str):
     raise SystemExit("unknown workload %r" % name)
 
 
+def tile_elements(dw, w):
+    """Elements (records) per tile of the workload's main kernel."""
+    if w["kind"] == "segmented":
+        return dw.ps_segmented_tile_elements()
+    if w["kind"] == "compact":
+        return dw.ps_compact_tile_records(16)
+    if w["kind"] == "copy":
+        return None
+    return dw.ps_tile_elements(1 if w["dtype"] == "f32" else 0)
+
+
 def cpu_baseline(w, gpu_out, min_seconds: float):
     """Time the oracle (single-threaded C loop) on the same input; compare."""
     import oracle
@@ -253,7 +264,7 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic",
         "config": {"workload": w["desc"], "n": n, "algorithmic_bytes_per_step": w["bytes"],
-                   "tile_elements": dw.ps_tile_elements(0)},
+                   "tile_elements": tile_elements(dw, w)},
         "gbs_per_step": round(call_gbs, 1),
         "pct_hbm_peak_per_step": round(100.0 * call_gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
