@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     ps_kernel_timing,
     ps_kernel_timing_read,
     ps_lookback_stats_u32,
+    ps_lookback_config,
+    ps_lookback_config_get,
     ps_lookback_group,
     ps_lookback_tiles,
     ps_lookback_window,

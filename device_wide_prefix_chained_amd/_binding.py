@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.ps_lookback_window.restype = u32
     L.ps_lookback_group.argtypes = []
     L.ps_lookback_group.restype = u32
+    L.ps_lookback_config.argtypes = [u32, u32]
+    L.ps_lookback_config.restype = i32
+    L.ps_lookback_config_get.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
+    L.ps_lookback_config_get.restype = None
     L.ps_tile_elements.argtypes = [i32]
     L.ps_tile_elements.restype = u32
     L.ps_segmented_tile_elements.argtypes = []
@@ -287,6 +291,21 @@ def ps_lookback_window() -> int:
 
 def ps_lookback_group() -> int:
     return int(lib().ps_lookback_group())
+
+
+def ps_lookback_config(fallback_polls: int, partial_windows: int) -> None:
+    """Look-back settings of every later call: fallback after this many
+    stalled polls (0 = never); PARTIAL descriptors after this many windows
+    walked without an inclusive prefix (0 = never)."""
+    _check("ps_lookback_config", lib().ps_lookback_config(int(fallback_polls), int(partial_windows)))
+
+
+def ps_lookback_config_get():
+    """Current (fallback_polls, partial_windows) settings."""
+    f = ctypes.c_uint32(0)
+    p = ctypes.c_uint32(0)
+    lib().ps_lookback_config_get(ctypes.byref(f), ctypes.byref(p))
+    return int(f.value), int(p.value)
 
 
 def ps_tile_elements(dtype=PS_U32) -> int:

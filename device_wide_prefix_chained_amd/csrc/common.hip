@@ -172,6 +172,27 @@ extern "C" ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_s
     return launch_status();
 }
 
+namespace {
+std::atomic<uint32_t> g_fallback_after{4096u};
+std::atomic<uint32_t> g_partial{4u};
+}  // namespace
+
+namespace dwps {
+uint32_t lookback_fallback_after() { return g_fallback_after.load(std::memory_order_relaxed); }
+uint32_t lookback_partial() { return g_partial.load(std::memory_order_relaxed); }
+}  // namespace dwps
+
+extern "C" ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows) {
+    g_fallback_after.store(fallback_polls, std::memory_order_relaxed);
+    g_partial.store(partial_windows, std::memory_order_relaxed);
+    return PS_OK;
+}
+
+extern "C" void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows) {
+    if (fallback_polls) *fallback_polls = g_fallback_after.load(std::memory_order_relaxed);
+    if (partial_windows) *partial_windows = g_partial.load(std::memory_order_relaxed);
+}
+
 extern "C" ps_status ps_kernel_timing(int enable) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
     for (auto &pr : g_timing_events) {

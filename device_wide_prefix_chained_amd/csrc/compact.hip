@@ -240,10 +240,37 @@ __device__ __forceinline__ void compact_data_loop(PipeTiles pt, CompactShared<D,
     }
 }
 
+// A look-back's fallback: count the kept flags of tile p from scratch (rows
+// of 64 flags, a ballot each) and return the descriptor word its owner
+// publishes first.  Runs on the control wave, rarely.
+template <uint32_t TILE>
+struct CompactFallback {
+    const uint8_t *flags;
+    uint32_t n;
+    __device__ uint64_t operator()(uint32_t p, uint32_t lane) const {
+        constexpr uint32_t ROWS = TILE / 64u, BATCH = 8u;
+        static_assert(ROWS % BATCH == 0, "whole batches of rows");
+        const uint64_t base = (uint64_t)p * TILE + lane;
+        uint32_t count = 0;
+        for (uint32_t r = 0; r < ROWS; r += BATCH) {
+            uint32_t f[BATCH];
+#pragma unroll
+            for (uint32_t k = 0; k < BATCH; ++k) {
+                const uint64_t i = base + (uint64_t)(r + k) * 64u;
+                f[k] = i < n ? flags[i] : 0u;
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < BATCH; ++k) count += (uint32_t)__builtin_popcountll(ballot(f[k] != 0u));
+        }
+        return desc_word(p == 0 ? ST_PREFIX : ST_AGGREGATE, count);
+    }
+};
+
 template <class Rec, int D, int Q, int LB_K, int G, bool VEC>
 __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *records, const uint8_t *flags,
                                                                uint32_t n, Rec *out, uint64_t *num_selected,
-                                                               uint32_t num_tiles, uint32_t *ctr, uint64_t *desc) {
+                                                               uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
+                                                               LookbackCfg cfg) {
     __shared__ CompactShared<D, Q> sh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -255,7 +282,8 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0)
-        control_loop<SumU32, D, LB_K, G, false>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr, nullptr, 0,
+        control_loop<SumU32, D, LB_K, G, false>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr, nullptr, 0, cfg,
+                                                CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>{flags, n},
                                                 lane);
     else
         compact_data_loop<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
@@ -307,8 +335,9 @@ ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const 
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kCompactThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
+        const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCompactThreads), 0, s, rin, flags, n32, rout, num_selected,
-                           nt, ctr, desc);
+                           nt, ctr, desc, cfg);
         return PS_OK;
     };
     const ps_status r = vec ? launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, true>)

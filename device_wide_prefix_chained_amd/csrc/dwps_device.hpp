@@ -135,28 +135,62 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 // own LDS/register scan before its publication -- is program order within the
 // publishing lane after a workgroup barrier, so relaxed ordering suffices;
 // no other memory is handed over through a descriptor.
+// High word: bits 1..0 the state, bits 31..2 the distance of a PARTIAL.
 // ---------------------------------------------------------------------------
 constexpr uint32_t ST_INVALID = 0u;    // nothing published
 constexpr uint32_t ST_AGGREGATE = 1u;  // payload = the tile's own fold
 constexpr uint32_t ST_PREFIX = 2u;     // payload = fold of tiles 0..t (inclusive)
+constexpr uint32_t ST_PARTIAL = 3u;    // payload = fold of tiles t-d+1..t, d in the high bits
 
 __device__ __forceinline__ uint64_t desc_word(uint32_t state, uint32_t payload) {
     return ((uint64_t)state << 32) | (uint64_t)payload;
 }
+__device__ __forceinline__ uint64_t desc_partial(uint32_t dist, uint32_t payload) {
+    return ((uint64_t)((dist << 2) | ST_PARTIAL) << 32) | (uint64_t)payload;
+}
+__device__ __forceinline__ uint32_t desc_state(uint64_t w) { return (uint32_t)(w >> 32) & 3u; }
+__device__ __forceinline__ uint32_t desc_dist(uint64_t w) { return (uint32_t)(w >> 34); }
 __device__ __forceinline__ void desc_publish(uint64_t *d, uint64_t w) {
     __hip_atomic_store(d, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t desc_poll(const uint64_t *d) {
     return __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Install a descriptor computed by another tile's fallback: only over
+// INVALID, so a word the owner (or an earlier fallback) published stays.
+__device__ __forceinline__ bool desc_install(uint64_t *d, uint64_t w) {
+    uint64_t expected = 0ull;
+    return __hip_atomic_compare_exchange_strong(d, &expected, w, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr) {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void count_event(uint32_t *word) {
+    __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct LookbackStats {
-    uint32_t polls = 0;    // poll rounds (64 descriptor reads each)
-    uint32_t windows = 0;  // windows of 64 predecessors folded
+    uint32_t polls = 0;    // poll rounds (64*K descriptor reads each)
+    uint32_t windows = 0;  // windows of predecessors folded
     uint32_t stalls = 0;   // polls that found an unpublished predecessor
+};
+
+// Workspace header words (32-bit): [0] ticket counter, [1] error word,
+// [2] fallbacks performed, [3] PARTIAL descriptors published (counted by the
+// instrumented scan only).
+constexpr int kHdrError = 1;
+constexpr int kHdrFallbacks = 2;
+constexpr int kHdrPartials = 3;
+
+// What a look-back may do besides waiting: after `fallback_after` stalled
+// polls in a row (0 = never) reduce the stalled predecessor's input itself;
+// once it has walked `partial` windows without reaching an inclusive prefix
+// (0 = never), publish a PARTIAL descriptor for its own tile after every
+// further window.
+struct LookbackCfg {
+    uint32_t fallback_after;
+    uint32_t partial;
 };
 
 // Safety net of the spin: a wave that finds an unpublished predecessor this
@@ -171,33 +205,57 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 #define DWPS_LOOKBACK_K 2
 #endif
 
+// A look-back that never computes a predecessor itself.
+struct NoFallback {
+    __device__ __forceinline__ uint64_t operator()(uint32_t, uint32_t) const { return 0ull; }
+};
+
 // Decoupled look-back, executed by one full wave, reading K descriptors per
 // lane per poll, i.e. a window of 64*K predecessors.  Lane l holds tiles
 // (base + l*K) .. (base + l*K + K-1) of the window, where base =
 // nearest - 64*K + 1, so lane 63's last word is the nearest predecessor and
 // (lane, word) order is tile order.  Indices below 0 read as a PREFIX
-// carrying the identity.  Let p be the nearest word in PREFIX state: if any
-// word nearer than p is still INVALID the whole window is polled again (each
-// poll reloads every word); otherwise the payloads from p to the nearest
+// carrying the identity.
+//
+// Walking back from the nearest predecessor, an AGGREGATE adds its payload
+// and steps one tile, a PARTIAL adds its payload and jumps over the d tiles
+// it covers, a PREFIX adds its payload and ends the walk, an INVALID waits.
+// In a window: let s be the nearest word in PREFIX or PARTIAL state; if a
+// word nearer than s is INVALID the window is polled again (each poll
+// reloads every word); otherwise the payloads from s to the nearest
 // predecessor are folded in tile order (each lane folds its own words, then
-// one wave scan joins the lanes) and, if p exists, the fold is final; else
-// the window slides 64*K tiles back.  After kSpinLimit consecutive stalls the
-// unpublished words are folded as they are and *err is set.  Returns the
-// exclusive prefix of `tile` (the fold of every earlier tile).  Terminates
-// because tile 0 publishes PREFIX without waiting and every tile only waits
-// on tiles that took their ticket earlier, hence are resident or finished
-// ("Single-Pass Prefix Scan with Decoupled Look-Back", sections "Three states
-// in a per-block descriptor", "Why the work stays linear" and "Where the
-// algorithm meets the hardware"; the window of 64*K words read at once is
-// this implementation's answer to the latency of a long dependent chain).
-template <class Op, int K, bool STATS>
-__device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_t tile,
-                                                   uint32_t lane, LookbackStats &st,
-                                                   uint32_t *err) {
+// one wave scan joins the lanes).  At a PREFIX the fold is final; at a
+// PARTIAL the next window ends just before the tiles it covers; with neither,
+// the window slides 64*K tiles back.  Each time the walk continues, the
+// tile's own descriptor becomes a PARTIAL covering everything folded so far
+// and itself (once cfg.partial windows were walked, and when may_publish),
+// so later look-backs over
+// the same stretch jump it in one read -- the bounded-window variant of
+// "Single-Pass Prefix Scan with Decoupled Look-Back", section "Why the work
+// stays linear", with W = cfg.partial windows of 64*K predecessors.
+//
+// After cfg.fallback_after stalled polls in a row the wave reduces the
+// nearest unpublished predecessor from its input (fb(tile, lane) returns the
+// descriptor word that tile's owner would publish first) and installs it
+// over INVALID with a compare-and-swap, so the first of several fallbacks on
+// one tile wins and the owner's own later stores agree with it
+// ("GPUPrefixSums", section "Decoupled Fallback").  After kSpinLimit stalled
+// polls the unpublished words are folded as they are and the error word is
+// set.  Returns the exclusive prefix of `tile` (the fold of every earlier
+// tile).  Terminates because tile 0 publishes PREFIX without waiting and
+// every tile only waits on tiles that took their ticket earlier, hence are
+// resident or finished ("Single-Pass Prefix Scan with Decoupled Look-Back",
+// sections "Three states in a per-block descriptor" and "Where the algorithm
+// meets the hardware").
+template <class Op, int K, bool STATS, class FB = NoFallback>
+__device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile, uint32_t lane, LookbackStats &st,
+                                                   uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u},
+                                                   typename Op::T own = Op::id(), bool may_publish = false,
+                                                   const FB &fb = FB{}) {
     using T = typename Op::T;
     T acc = Op::id();
     int64_t nearest = (int64_t)tile - 1;
-    uint32_t spins = 0;
+    uint32_t spins = 0, stalled = 0, walked = 0;
     const uint64_t pad = desc_word(ST_PREFIX, to_bits(Op::id()));
     for (;;) {
         const int64_t first = nearest - 64 * K + 1 + (int64_t)lane * K;
@@ -207,30 +265,41 @@ __device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_
             const int64_t idx = first + j;
             w[j] = (idx >= 0) ? desc_poll(desc + idx) : pad;
         }
-        // nearest PREFIX word of this lane (-1 if none), and whether a word
-        // nearer than it (in this lane) is INVALID
+        // nearest PREFIX/PARTIAL word of this lane (-1 if none), and whether
+        // a word nearer than it (in this lane) is INVALID
         int jp = -1;
 #pragma unroll
         for (int j = 0; j < K; ++j)
-            if ((uint32_t)(w[j] >> 32) == ST_PREFIX) jp = j;
-        bool inv_after = false;
+            if (desc_state(w[j]) >= ST_PREFIX) jp = j;
+        int ji = -1;
 #pragma unroll
         for (int j = 0; j < K; ++j)
-            if (j > jp && (uint32_t)(w[j] >> 32) == ST_INVALID) inv_after = true;
+            if (j > jp && desc_state(w[j]) == ST_INVALID) ji = j;
         const uint64_t pm = ballot(jp >= 0);
         const uint32_t lp = pm ? 63u - (uint32_t)__builtin_clzll(pm) : 0u;
-        // lanes above lp count entirely; lane lp counts from its PREFIX word
+        // lanes above lp count entirely; lane lp counts from its stopper word
         const bool relevant = pm ? (lane >= lp) : true;
         if (STATS) st.polls++;
-        if (ballot(relevant && inv_after)) {
+        const uint64_t im = ballot(relevant && ji >= 0);
+        if (im) {
             if (STATS) st.stalls++;
+            if (cfg.fallback_after && ++stalled >= cfg.fallback_after) {
+                // reduce the nearest unpublished predecessor ourselves
+                const uint32_t li = 63u - (uint32_t)__builtin_clzll(im);
+                const int64_t p = nearest - 64 * K + 1 + (int64_t)li * K + __builtin_amdgcn_readlane(ji, (int)li);
+                const uint64_t word = fb((uint32_t)p, lane);
+                if (lane == 0 && desc_install(desc + p, word)) count_event(hdr + kHdrFallbacks);
+                stalled = 0;
+                continue;
+            }
             if (++spins < kSpinLimit) {
                 __builtin_amdgcn_s_sleep(1);
                 continue;
             }
-            if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_store(hdr + kHdrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         spins = 0;
+        stalled = 0;
         T v = Op::id();
         if (relevant) {
             const int jfrom = (pm && lane == lp) ? jp : 0;
@@ -241,8 +310,26 @@ __device__ __forceinline__ typename Op::T lookback(const uint64_t *desc, uint32_
         v = wave_inclusive<Op>(v);
         acc = Op::op(read_lane(v, 63), acc);
         if (STATS) st.windows++;
-        if (pm) break;
-        nearest -= 64 * K;
+        if (pm) {
+            // the stopper word, uniform
+            uint64_t ws = w[0];
+#pragma unroll
+            for (int j = 1; j < K; ++j) ws = (j == jp) ? w[j] : ws;
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ws >> 32), (int)lp);
+            if ((hi & 3u) == ST_PREFIX) break;
+            const int64_t s = nearest - 64 * K + 1 + (int64_t)lp * K +
+                              __builtin_amdgcn_readlane(jp, (int)lp);
+            nearest = s - (int64_t)(hi >> 2);
+        } else {
+            nearest -= 64 * K;
+        }
+        if (nearest < 0) break;  // a PARTIAL reaching back to tile 0 ends the walk
+        if (cfg.partial && ++walked >= cfg.partial && may_publish && lane == 0) {
+            desc_publish(desc + tile, desc_partial((uint32_t)((int64_t)tile - nearest), to_bits(Op::op(acc, own))));
+            // counted by the instrumented build only: an atomic on one shared
+            // word would queue ahead of this wave's next poll
+            if (STATS) count_event(hdr + kHdrPartials);
+        }
     }
     return acc;
 }

@@ -58,6 +58,12 @@ inline ps_status launch_status() {
 // device), capped at `work_items`.  0 on a HIP error.
 uint32_t persistent_grid(const void *kernel, int block_threads, uint32_t work_items);
 
+// Process-wide look-back settings (ps_lookback_config), read at launch:
+// stalled polls in a row before a fallback (0 = never) and whether tiles
+// publish PARTIAL descriptors.
+uint32_t lookback_fallback_after();
+uint32_t lookback_partial();
+
 // Kernel timing hooks: when enabled (ps_kernel_timing), timing_begin/end
 // record a HIP event pair around the main kernel of the call on `stream`.
 void timing_begin(hipStream_t stream);

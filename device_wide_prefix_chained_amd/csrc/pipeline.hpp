@@ -61,11 +61,13 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
 // thing it ever waits for is its own poll.  Shared (the workgroup's LDS
 // block) provides wt[2][D] (the data waves' tile totals, by phase parity),
 // prefix (the exclusive prefix of prev2, read by the data waves after B) and
-// next (the tile after f2, written by data wave 0 before A).
-template <class Op, int D, int LB_K, int G, bool STATS, class Shared>
+// next (the tile after f2, written by data wave 0 before A).  fb reduces a
+// tile from its input when a look-back falls back on it (see lookback).
+template <class Op, int D, int LB_K, int G, bool STATS, class Shared, class FB>
 __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t num_tiles,
                                              uint32_t *ctr, uint64_t *desc, typename Op::T *total,
-                                             uint32_t *stats, int aggregate_only, uint32_t lane) {
+                                             uint32_t *stats, int aggregate_only, LookbackCfg cfg,
+                                             const FB &fb, uint32_t lane) {
     using T = typename Op::T;
     T agg_prev = Op::id(), agg_prev2 = Op::id();
     T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
@@ -84,7 +86,7 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
         const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
         const bool look = have_prev2 && (pt.prev2 % G == 0u || (STATS && aggregate_only));
         if (look)
-            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr + 1);
+            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb);
         else if (have_prev2)
             excl = incl_last;
         if (lane == 0) {

@@ -142,10 +142,43 @@ __device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh
     }
 }
 
+// A look-back's fallback: reduce tile p of the input from scratch, in tile
+// order (rows of 256 elements; each lane folds its four, the wave scan joins
+// the lanes, the rows are folded in order), and return the descriptor word
+// its owner publishes first.  Runs on the control wave, rarely.
+template <class Op, uint32_t TILE>
+struct FlatFallback {
+    const typename Op::T *in;
+    uint32_t n;
+    __device__ uint64_t operator()(uint32_t p, uint32_t lane) const {
+        using T = typename Op::T;
+        constexpr uint32_t ROWS = TILE / 256u, BATCH = 8u;
+        static_assert(ROWS % BATCH == 0, "whole batches of rows");
+        const uint64_t base = (uint64_t)p * TILE + 4u * lane;
+        T acc = Op::id();
+        for (uint32_t r = 0; r < ROWS; r += BATCH) {
+            T part[BATCH];
+#pragma unroll
+            for (uint32_t k = 0; k < BATCH; ++k) {
+                T v = Op::id();
+#pragma unroll
+                for (uint32_t e = 0; e < 4; ++e) {
+                    const uint64_t i = base + (uint64_t)(r + k) * 256u + e;
+                    v = Op::op(v, i < n ? in[i] : Op::id());
+                }
+                part[k] = v;
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < BATCH; ++k) acc = Op::op(acc, read_lane(wave_inclusive<Op>(part[k]), 63));
+        }
+        return desc_word(p == 0 ? ST_PREFIX : ST_AGGREGATE, to_bits(acc));
+    }
+};
+
 template <class Op, int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
     const typename Op::T *in, typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
-    uint64_t *desc, typename Op::T *total, uint32_t *stats, int aggregate_only) {
+    uint64_t *desc, typename Op::T *total, uint32_t *stats, int aggregate_only, LookbackCfg cfg) {
     __shared__ ScanShared<Op, D, Q> sh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -158,7 +191,8 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0)
-        control_loop<Op, D, LB_K, G, STATS>(pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, lane);
+        control_loop<Op, D, LB_K, G, STATS>(pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, cfg,
+                                            FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
     else
         data_loop<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
 }
@@ -222,8 +256,9 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kFlatThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
+        const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFlatThreads), 0, s, in, out, n32, nt, ctr, desc, total,
-                           stats, aggregate_only);
+                           stats, aggregate_only, cfg);
         return PS_OK;
     };
     ps_status r;

@@ -197,6 +197,49 @@ struct SegSpan {
     }
 };
 
+// A look-back's fallback: reduce tile p from scratch -- values and start
+// bits, rows of 256 elements, lane-serial pairs of four, the DPP pair scan
+// across the lanes, rows folded in order -- and return the descriptor word
+// its owner publishes first: PREFIX with the carry-out when the tile holds a
+// start (or is tile 0), AGGREGATE with its sum otherwise.  Control wave,
+// rarely.
+struct SegFallback {
+    const uint32_t *values;
+    const uint32_t *heads;
+    uint32_t n;
+    __device__ uint64_t operator()(uint32_t p, uint32_t lane) const {
+        constexpr uint32_t ROWS = kSegTile / 256u, BATCH = 8u;
+        static_assert(ROWS % BATCH == 0, "whole batches of rows");
+        const uint64_t base = (uint64_t)p * kSegTile + 4u * lane;
+        const uint64_t wbase = (uint64_t)p * kSegWords + (lane >> 3);
+        const uint32_t sh4 = 4u * (lane & 7u);
+        SegPair acc{0u, 0u};
+        for (uint32_t r = 0; r < ROWS; r += BATCH) {
+            uint32_t x[BATCH][4], fl[BATCH];
+#pragma unroll
+            for (uint32_t k = 0; k < BATCH; ++k) {
+                fl[k] = (heads[wbase + (uint64_t)(r + k) * 8u] >> sh4) & 0xFu;
+#pragma unroll
+                for (uint32_t e = 0; e < 4; ++e) {
+                    const uint64_t i = base + (uint64_t)(r + k) * 256u + e;
+                    x[k][e] = i < n ? values[i] : 0u;
+                }
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < BATCH; ++k) {
+                uint32_t v = 0u;
+#pragma unroll
+                for (uint32_t e = 0; e < 4; ++e) v = ((fl[k] >> e) & 1u) ? x[k][e] : v + x[k][e];
+                uint32_t f = fl[k] ? 1u : 0u;
+                wave_seg_inclusive(f, v);
+                acc = seg_op(acc, SegPair{(uint32_t)__builtin_amdgcn_readlane((int)f, 63),
+                                          (uint32_t)__builtin_amdgcn_readlane((int)v, 63)});
+            }
+        }
+        return desc_word((acc.f || p == 0) ? ST_PREFIX : ST_AGGREGATE, acc.v);
+    }
+};
+
 // Control wave.  Phase k: combine the wave pairs of cur into its aggregate
 // and first start; find the carry into prev2 (a look-back only when prev2
 // heads a ticket group and its first element is not a segment start; the
@@ -206,7 +249,8 @@ struct SegSpan {
 // AGGREGATE otherwise.  Descriptor stores go out after the poll returned.
 template <int D, int Q, int LB_K, int G>
 __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles,
-                                                 uint32_t *ctr, uint64_t *desc, uint32_t lane) {
+                                                 uint32_t *ctr, uint64_t *desc, LookbackCfg cfg,
+                                                 const SegFallback &fb, uint32_t lane) {
     SegPair a_prev{0u, 0u}, a_prev2{0u, 0u};
     uint32_t fh_prev = kSegTile, fh_prev2 = kSegTile;
     uint32_t carry_out_last = 0;  // carry out of the tile handled one phase ago
@@ -227,7 +271,9 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
                 carry = carry_out_last;
             } else if (fh_prev2 != 0u) {
                 LookbackStats st;
-                carry = lookback<SumU32, LB_K, false>(desc, pt.prev2, lane, st, ctr + 1);
+                // only a start-free tile's descriptor may turn PARTIAL (a
+                // tile holding a start published PREFIX already)
+                carry = lookback<SumU32, LB_K, false>(desc, pt.prev2, lane, st, ctr, cfg, a_prev2.v, !a_prev2.f, fb);
             }
         }
         if (lane == 0) {
@@ -414,7 +460,8 @@ template <int D, int Q, int LB_K, int G, bool INCL, bool VEC>
 __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *values, const uint32_t *heads,
                                                                uint32_t *out, uint32_t n,
                                                                const uint32_t *offsets, uint32_t num_segments,
-                                                               uint32_t num_tiles, uint32_t *ctr, uint64_t *desc) {
+                                                               uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
+                                                               LookbackCfg cfg) {
     __shared__ SegShared<D, Q> sh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
@@ -426,7 +473,7 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0) {
-        seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, ctr, desc, lane);
+        seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, ctr, desc, cfg, SegFallback{values, heads, n}, lane);
     } else {
         // rows outside [offsets[0], offsets[N]) belong to no segment
         const uint32_t lo = offsets[0], hi = offsets[num_segments];
@@ -470,8 +517,9 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kSegThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
+        const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSegThreads), 0, s, values, heads, out, n32, offsets,
-                           num_segments, nt, ctr, desc);
+                           num_segments, nt, ctr, desc, cfg);
         return PS_OK;
     };
     ps_status r;

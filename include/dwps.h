@@ -31,7 +31,12 @@
  *    launched, no GPU is touched); then call again with a device buffer of at
  *    least that many bytes.  The caller owns it; its contents need no
  *    initialisation (the library clears it on `stream` each call).  Two calls
- *    in flight at once must not share a workspace.
+ *    in flight at once must not share a workspace.  After a call its first
+ *    four uint32 words hold diagnostics: [0] tiles handed out (+ one ticket
+ *    per workgroup), [1] error word (nonzero: a look-back hit its spin limit
+ *    and the results are not valid), [2] look-back fallbacks performed,
+ *    [3] PARTIAL descriptors published (counted by ps_lookback_stats_u32
+ *    only; see ps_lookback_config).
  *  - Argument errors are returned synchronously before anything is
  *    launched: PS_ERR_NULL (a required pointer is NULL while n > 0),
  *    PS_ERR_SIZE (n >= 2^32, or offsets beyond the supported range),
@@ -215,6 +220,33 @@ uint32_t ps_lookback_window(void);
  * take the inclusive prefix of the tile before them, which the same
  * workgroup computed); their stats rows show zero polls. */
 uint32_t ps_lookback_group(void);
+
+/* Look-back settings of every later call of this process (calls already
+ * enqueued keep theirs); not synchronised with calls made at the same time
+ * from other threads.
+ *   fallback_polls  : after this many polls in a row that find an
+ *                     unpublished predecessor, the waiting tile reduces that
+ *                     predecessor's input itself and installs the result
+ *                     with a compare-and-swap, so the first of several such
+ *                     tiles wins ([P4] "Decoupled Fallback").  0 = never.
+ *                     Default 4096 (milliseconds of waiting; the protocol
+ *                     already guarantees progress on this GPU, so the
+ *                     fallback is a safety valve).
+ *   partial_windows : a tile whose look-back has walked this many windows of
+ *                     ps_lookback_window() predecessors without reaching an
+ *                     inclusive prefix publishes a PARTIAL descriptor after
+ *                     every further window -- the fold of the tiles it has
+ *                     covered, itself included, and their count -- which
+ *                     later look-backs jump in one read ([P1] "Why the work
+ *                     stays linear", the bounded-window variant with W =
+ *                     partial_windows windows).  0 = never.  Default 4:
+ *                     ordinary look-backs end within two windows and never
+ *                     publish; a threshold of 1 would publish on ordinary
+ *                     walks, and the extra store and the short jumps it
+ *                     offers slow the scans by 10-20%.
+ * Results do not depend on either setting. */
+ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows);
+void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows);
 
 /* Kernel timing with HIP events placed around the main scan kernel of every
  * call (the workspace clear is outside the pair).  enable != 0 starts a new

@@ -162,3 +162,18 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(8, dtype=torch.uint32)
     with pytest.raises(ValueError):
         d.ps_scan_exclusive_u32(x, x.clone())
+
+
+def test_lookback_config_roundtrip():
+    """Host-side setting only: no GPU is touched."""
+    import device_wide_prefix_chained_amd as d
+    old = d.ps_lookback_config_get()
+    assert old == (4096, 4)
+    try:
+        d.ps_lookback_config(0, 0)
+        assert d.ps_lookback_config_get() == (0, 0)
+        d.ps_lookback_config(12345, 3)
+        assert d.ps_lookback_config_get() == (12345, 3)
+    finally:
+        d.ps_lookback_config(*old)
+    assert d.ps_lookback_config_get() == old

@@ -256,7 +256,12 @@ def test_lookback_instrumented(dw, orc, aggregate_only):
     d_in = dev(x)
     d_out = torch.empty_like(d_in)
     say("lookback stats", aggregate_only)
-    dw.ps_lookback_stats_u32(d_in, d_out, stats, aggregate_only=aggregate_only)
+    old = dw.ps_lookback_config_get()
+    dw.ps_lookback_config(old[0], 0)  # no PARTIAL shortcuts: the plain sliding window
+    try:
+        dw.ps_lookback_stats_u32(d_in, d_out, stats, aggregate_only=aggregate_only)
+    finally:
+        dw.ps_lookback_config(*old)
     ref, _ = orc.scan_u32(x, "sum", False)
     assert np.array_equal(host(d_out), ref)
     st = host(stats).reshape(tiles, 4).astype(np.int64)
