@@ -60,6 +60,8 @@ class Oracle:
         vp, u64, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int
         lib.oracle_scan_u32.argtypes = [i32, i32, vp, vp, u64, vp]
         lib.oracle_scan_u32.restype = i32
+        lib.oracle_scan_u32_u64.argtypes = [i32, vp, vp, u64, vp]
+        lib.oracle_scan_u32_u64.restype = i32
         lib.oracle_scan_f32_sum.argtypes = [i32, vp, vp, vp, u64, vp]
         lib.oracle_scan_f32_sum.restype = i32
         lib.oracle_scan_f32_minmax.argtypes = [i32, i32, vp, vp, u64, vp]
@@ -82,6 +84,14 @@ class Oracle:
                                       x.size, _ptr(total))
         if rc != 0:
             raise ValueError("oracle_scan_u32: unknown operator %r" % op)
+        return y, int(total[0])
+
+    def scan_u32_u64(self, x, inclusive: bool = False):
+        """Return (y uint64, total) for the widening uint32 -> uint64 sum scan."""
+        x = np.ascontiguousarray(x, dtype=np.uint32)
+        y = np.empty(x.size, dtype=np.uint64)
+        total = np.zeros(1, dtype=np.uint64)
+        self.lib.oracle_scan_u32_u64(int(bool(inclusive)), _ptr(x), _ptr(y), x.size, _ptr(total))
         return y, int(total[0])
 
     def scan_f32_sum(self, x, inclusive: bool = False, want_abs: bool = True):

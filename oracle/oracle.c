@@ -145,6 +145,32 @@ int oracle_scan_u32(int op, int inclusive, const uint32_t *x, uint32_t *y,
 }
 
 /*
+ * Widening sum scan: uint32 inputs, uint64 running sums ([P2] "Failure modes":
+ * a 32-bit accumulator overflows on long inputs; [P3] "Scan as an index
+ * generator": offsets over billions of flags need 64 bits).  The same running
+ * accumulator as above, 64 bits wide, so no sum below 2^64 wraps.  *total
+ * (optional) receives the sum of the whole input (0 when n == 0).
+ */
+int oracle_scan_u32_u64(int inclusive, const uint32_t *x, uint64_t *y,
+                        uint64_t n, uint64_t *total)
+{
+    uint64_t acc = 0u;
+    for (uint64_t i = 0; i < n; ++i) {
+        uint64_t xi = (uint64_t)x[i];
+        if (inclusive) {
+            acc = acc + xi;
+            y[i] = acc;
+        } else {
+            y[i] = acc;
+            acc = acc + xi;
+        }
+    }
+    if (total)
+        *total = acc;
+    return 0;
+}
+
+/*
  * fp32 sum scan, accumulated in fp64 from the fp32 inputs ([P2] "Numerics and
  * determinism": keep the accumulator in float32 or wider; the float64 answer
  * is the reference).  Also returns absprefix[i] = sum_{j<=i} |x[j]| in fp64,

@@ -94,6 +94,12 @@ def brute_force_scan(x, op, inclusive):
     return [fold(x[: i + 1] if inclusive else x[:i]) for i in range(n)]
 
 
+def brute_force_wide(x, inclusive):
+    """O(n^2) with Python integers (no wrap at all): output i sums x[0..i] or
+    x[0..i-1] anew."""
+    return [sum(int(v) for v in (x[: i + 1] if inclusive else x[:i])) for i in range(len(x))]
+
+
 def blelloch_exclusive(x, op):
     """Work-efficient scan from its description ("Blelloch: work-efficient
     up-sweep and down-sweep"; "Work-efficient tree scan"): pad to a power of
@@ -246,6 +252,60 @@ def pin_closed_forms(orc):
     assert np.array_equal(inc, srt)
     inc, _ = orc.scan_u32(srt[::-1].copy(), "min", inclusive=True)
     assert np.array_equal(inc, srt[::-1])
+
+
+# --------------------------------------------------------------------------
+# Widening uint32 -> uint64 sum scan
+# --------------------------------------------------------------------------
+@pin
+def pin_widening_worked_examples(orc):
+    for name in ("p1_lead_scan.json", "p3_inclusive_exclusive.json", "p5_flat_example.json",
+                 "p3_lengths_offsets.json"):
+        g = golden(name)
+        x = _u32(g["input"] if "input" in g else g["lengths"])
+        ex, tex = orc.scan_u32_u64(x, inclusive=False)
+        ref_ex = g["exclusive"] if "exclusive" in g else g["offsets"]
+        assert ex.tolist() == ref_ex, name
+        if "inclusive" in g:
+            inc, tin = orc.scan_u32_u64(x, inclusive=True)
+            assert inc.tolist() == g["inclusive"] and tin == tex == g["inclusive"][-1], name
+
+
+@pin
+def pin_widening_brute_force_and_numpy(orc):
+    r = np.random.default_rng(505)
+    for n in (0, 1, 2, 5, 64, 1000):
+        x = r.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+        for inclusive in (False, True):
+            y, total = orc.scan_u32_u64(x, inclusive)
+            assert y.dtype == np.uint64
+            assert y.tolist() == brute_force_wide(x.tolist(), inclusive), (n, inclusive)
+            assert total == sum(int(v) for v in x.tolist())
+    n = 200_003  # full-range values: the sums pass 2^32 after a couple of elements
+    x = r.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    ref_inc = np.cumsum(x.astype(np.uint64), dtype=np.uint64)
+    inc, tin = orc.scan_u32_u64(x, inclusive=True)
+    ex, tex = orc.scan_u32_u64(x, inclusive=False)
+    assert np.array_equal(inc, ref_inc) and ex[0] == 0 and np.array_equal(ex[1:], ref_inc[:-1])
+    assert tin == tex == int(ref_inc[-1]) == sum(int(v) for v in x.tolist())
+
+
+@pin
+def pin_widening_closed_forms(orc):
+    n = 1 << 17
+    for c in (1, 0x9E3779B9, M32):  # constant input: exclusive[i] = c * i, no wrap below 2^64
+        ex, total = orc.scan_u32_u64(np.full(n, c, np.uint32), inclusive=False)
+        assert ex.tolist() == [c * i for i in range(n)], c
+        assert total == c * n
+    ex, total = orc.scan_u32_u64(np.arange(n, dtype=np.uint32), inclusive=False)  # iota
+    assert ex.tolist() == [i * (i - 1) // 2 for i in range(n)]
+    assert total == n * (n - 1) // 2
+    # the low 32 bits are the wrapping uint32 scan
+    x = np.random.default_rng(606).integers(0, 1 << 32, size=50_000, dtype=np.uint64).astype(np.uint32)
+    for inclusive in (False, True):
+        wide, _ = orc.scan_u32_u64(x, inclusive)
+        narrow, _ = orc.scan_u32(x, "sum", inclusive)
+        assert np.array_equal((wide & np.uint64(M32)).astype(np.uint32), narrow)
 
 
 @pin

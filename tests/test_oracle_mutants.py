@@ -26,6 +26,14 @@ MUTANTS = [
      "acc = u32_combine(op, acc, xi);", "acc = u32_combine(op, xi, acc);"),
     ("scan: total is the last output", "int oracle_scan_u32(",
      "        *total = acc;", "        *total = n ? y[n - 1] : acc;"),
+    ("widening: 32-bit accumulator", "int oracle_scan_u32_u64(",
+     "    uint64_t acc = 0u;", "    uint32_t acc = 0u;"),
+    ("widening: exclusive writes after adding", "int oracle_scan_u32_u64(",
+     "            y[i] = acc;\n            acc = acc + xi;", "            acc = acc + xi;\n            y[i] = acc;"),
+    ("widening: input truncated to 16 bits", "int oracle_scan_u32_u64(",
+     "        uint64_t xi = (uint64_t)x[i];", "        uint64_t xi = (uint64_t)(x[i] & 0xFFFFu);"),
+    ("widening: total misses the last element", "int oracle_scan_u32_u64(",
+     "        *total = acc;", "        *total = n ? y[n - 1] : acc;"),
     ("sum: xor instead of add", "case ORC_SUM:", "return a + b;", "return a ^ b;"),
     ("max: picks the smaller", "case ORC_MAX:", "return (b > a) ? b : a;", "return (b > a) ? a : b;"),
     ("min: identity zero", "static uint32_t u32_identity", "    case ORC_MIN:\n        return 0xFFFFFFFFu;",
