@@ -17,6 +17,7 @@ remaining kernels on their configurations:
   f32          fp32 inclusive sum, n = 2^27, N(0,1)  f32max  fp32 inclusive max
   segmented    segmented u32 exclusive, 2^26 values, 2^16 Zipf(1.2) segments
   compact      2^26 16-byte records, Bernoulli(0.3) keep flags
+  u64x         widening u32 -> u64 exclusive sum scan, n = 2^28 (12 B/element)
   copy         plain 1 GiB copy (the practical bandwidth ceiling)
 
 Only the cpu_baseline leg runs the oracle: the sequential C scan, one host
@@ -96,6 +97,17 @@ def build_workload(name: str):
                 "inclusive" if incl else "exclusive", "2^28-12345" if name == "u32x-ragged" else "2^28")
         return dict(desc=desc, dtype="u32", n=n, bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out,
                     inclusive=(name == "u32i"), kind="copy" if name == "copy" else "u32")
+    if name == "u64x":
+        n = wl.N_LARGE_U32
+        x = wl.large_u32()
+        d_in, d_out = dev(x), torch.empty(n, dtype=torch.int64, device="cuda")
+        total = torch.zeros(1, dtype=torch.int64, device="cuda")
+        ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None),
+                         dtype=torch.uint8, device="cuda")
+        run = lambda: dw.ps_scan_exclusive_u32_u64(d_in, d_out, total, workspace=ws)  # noqa: E731
+        return dict(desc="widening u32 -> u64 exclusive sum scan, n=2^28, values uniform in [0,255], seed 2",
+                    dtype="u64", n=n, bytes=12.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=False,
+                    kind="u64")
     if name in ("f32", "f32max"):
         n = wl.N_F32
         x = wl.f32_normal()
@@ -143,7 +155,7 @@ def tile_elements(dw, w):
         return dw.ps_compact_tile_records(16)
     if w["kind"] == "copy":
         return None
-    return dw.ps_tile_elements(1 if w["dtype"] == "f32" else 0)
+    return dw.ps_tile_elements({"f32": 1, "u64": 2}.get(w["dtype"], 0))
 
 
 def cpu_baseline(w, gpu_out, min_seconds: float):
@@ -158,6 +170,8 @@ def cpu_baseline(w, gpu_out, min_seconds: float):
         t0 = time.perf_counter()
         if kind == "u32" or kind == "copy":
             ref = orc.scan_u32(w["inputs"]["x"], "sum", w["inclusive"])[0]
+        elif kind == "u64":
+            ref = orc.scan_u32_u64(w["inputs"]["x"], w["inclusive"])[0]
         elif kind == "f32sum":
             ref = orc.scan_f32_sum(w["inputs"]["x"], True, want_abs=True)
         elif kind == "f32max":
@@ -172,7 +186,7 @@ def cpu_baseline(w, gpu_out, min_seconds: float):
     med = statistics.median(times)
     gelems = w["n"] / med / 1e9
     parity = None
-    if kind == "u32" or kind == "segmented":
+    if kind in ("u32", "segmented", "u64"):
         parity = "bit-exact" if np.array_equal(gpu_out, ref) else "MISMATCH"
     elif kind == "f32max":
         parity = "bit-exact" if np.array_equal(gpu_out.view(np.uint32), ref.view(np.uint32)) else "MISMATCH"
@@ -246,7 +260,7 @@ def main():
             gpu_out = (w["out"].cpu().numpy().view(np.uint32), int(w["count"].cpu().item()))
         else:
             o = w["out"].cpu().numpy()
-            gpu_out = o.view(np.uint32) if o.dtype == np.int32 else o
+            gpu_out = o.view(np.uint32) if o.dtype == np.int32 else (o.view(np.uint64) if o.dtype == np.int64 else o)
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         cpu, parity = cpu_baseline(w, gpu_out, args.cpu_seconds)
 

@@ -19,12 +19,13 @@ LIBRARY = os.path.join(PKG, "libdwps.so")
 
 # enum values of include/dwps.h
 PS_OK = 0
-PS_U32, PS_F32 = 0, 1
+PS_U32, PS_F32, PS_U64 = 0, 1, 2
 PS_OP_SUM, PS_OP_MAX, PS_OP_MIN, PS_OP_AND, PS_OP_OR, PS_OP_XOR, PS_OP_AFFINE16 = range(7)
 OPS = {"sum": PS_OP_SUM, "max": PS_OP_MAX, "min": PS_OP_MIN, "and": PS_OP_AND,
        "or": PS_OP_OR, "xor": PS_OP_XOR, "affine16": PS_OP_AFFINE16}
 
 _U32_DTYPES = (torch.uint32, torch.int32)
+_U64_DTYPES = (torch.uint64, torch.int64)
 
 _lib = None
 
@@ -48,7 +49,8 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_uint32, ctypes.c_int)
     flat = [vp, sz, vp, vp, u64, vp, vp]
     for name in ("ps_scan_exclusive_u32", "ps_scan_inclusive_u32",
-                 "ps_scan_exclusive_f32", "ps_scan_inclusive_f32"):
+                 "ps_scan_exclusive_f32", "ps_scan_inclusive_f32",
+                 "ps_scan_exclusive_u32_u64", "ps_scan_inclusive_u32_u64"):
         getattr(L, name).argtypes = flat
         getattr(L, name).restype = i32
     L.ps_scan.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
@@ -137,11 +139,12 @@ def _workspace(fn: str, call, device, workspace):
 # ---------------------------------------------------------------------------
 # flat scans
 # ---------------------------------------------------------------------------
-def _flat(fn: str, inp, out, total, workspace, stream, dtypes):
+def _flat(fn: str, inp, out, total, workspace, stream, dtypes, out_dtypes=None):
+    out_dtypes = dtypes if out_dtypes is None else out_dtypes
     _dev_tensor("inp", inp, dtypes)
-    _dev_tensor("out", out, dtypes, inp.numel())
+    _dev_tensor("out", out, out_dtypes, inp.numel())
     if total is not None:
-        _dev_tensor("total", total, dtypes, 1)
+        _dev_tensor("total", total, out_dtypes, 1)
     f = getattr(lib(), fn)
     n = inp.numel()
     s = _stream(inp, stream)
@@ -167,6 +170,15 @@ def ps_scan_inclusive_f32(inp, out, total=None, workspace=None, stream=None):
     return _flat("ps_scan_inclusive_f32", inp, out, total, workspace, stream, (torch.float32,))
 
 
+def ps_scan_exclusive_u32_u64(inp, out, total=None, workspace=None, stream=None):
+    """Widening sum: uint32 (or bit-identical int32) in, uint64/int64 out."""
+    return _flat("ps_scan_exclusive_u32_u64", inp, out, total, workspace, stream, _U32_DTYPES, _U64_DTYPES)
+
+
+def ps_scan_inclusive_u32_u64(inp, out, total=None, workspace=None, stream=None):
+    return _flat("ps_scan_inclusive_u32_u64", inp, out, total, workspace, stream, _U32_DTYPES, _U64_DTYPES)
+
+
 def ps_scan(op, inclusive, inp, out, total=None, workspace=None, stream=None, dtype=None):
     """Generic associative-operator scan; ``op`` is a PS_OP_* code or a name
     ('sum', 'max', 'min', 'and', 'or', 'xor', 'affine16')."""
@@ -174,10 +186,11 @@ def ps_scan(op, inclusive, inp, out, total=None, workspace=None, stream=None, dt
     if dtype is None:
         dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
     dtypes = (torch.float32,) if dtype == PS_F32 else _U32_DTYPES
+    out_dtypes = _U64_DTYPES if dtype == PS_U64 else dtypes
     _dev_tensor("inp", inp, dtypes)
-    _dev_tensor("out", out, dtypes, inp.numel())
+    _dev_tensor("out", out, out_dtypes, inp.numel())
     if total is not None:
-        _dev_tensor("total", total, dtypes, 1)
+        _dev_tensor("total", total, out_dtypes, 1)
     n = inp.numel()
     s = _stream(inp, stream)
     L = lib()

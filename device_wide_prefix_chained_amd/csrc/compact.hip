@@ -247,7 +247,7 @@ template <uint32_t TILE>
 struct CompactFallback {
     const uint8_t *flags;
     uint32_t n;
-    __device__ uint64_t operator()(uint32_t p, uint32_t lane) const {
+    __device__ DescVal<uint32_t> operator()(uint32_t p, uint32_t lane) const {
         constexpr uint32_t ROWS = TILE / 64u, BATCH = 8u;
         static_assert(ROWS % BATCH == 0, "whole batches of rows");
         const uint64_t base = (uint64_t)p * TILE + lane;
@@ -262,7 +262,7 @@ struct CompactFallback {
 #pragma unroll
             for (uint32_t k = 0; k < BATCH; ++k) count += (uint32_t)__builtin_popcountll(ballot(f[k] != 0u));
         }
-        return desc_word(p == 0 ? ST_PREFIX : ST_AGGREGATE, count);
+        return DescVal<uint32_t>{p == 0 ? ST_PREFIX : ST_AGGREGATE, count};
     }
 };
 

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dwps {
 
 // ---------------------------------------------------------------------------
@@ -70,6 +72,13 @@ struct Affine16 {
         return (((xa * ya) & 0xFFFFu) << 16) | ((ya * xb + yb) & 0xFFFFu);
     }
 };
+// Widening sum: uint32 inputs, uint64 running sums (no wrap below 2^64).
+struct SumU32toU64 {
+    using T = uint64_t;
+    using In = uint32_t;
+    __device__ static T id() { return 0ull; }
+    __device__ static T op(T a, T b) { return a + b; }
+};
 struct SumF32 {
     using T = float;
     __device__ static T id() { return 0.0f; }
@@ -86,6 +95,16 @@ struct MinF32 {
     __device__ static T op(T a, T b) { return (b < a) ? b : a; }
 };
 
+// Element type of an operator's input: Op::In when it widens, else Op::T.
+template <class Op, class = void>
+struct InputOf {
+    using type = typename Op::T;
+};
+template <class Op>
+struct InputOf<Op, decltype((void)sizeof(typename Op::In))> {
+    using type = typename Op::In;
+};
+
 // ---------------------------------------------------------------------------
 // Wave64 primitives (DPP).  DPP control codes of the GFX9 ISA:
 //   0x111..0x11F row_shr:1..15   (within each row of 16 lanes)
@@ -95,11 +114,22 @@ struct MinF32 {
 // A lane whose source is outside the row/wave, or that row_mask disables,
 // keeps `old`, which is always the operator's identity here.
 // ---------------------------------------------------------------------------
+// 64-bit values move as two 32-bit halves.
 template <class Op, int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ typename Op::T dpp_from(typename Op::T x) {
     using T = typename Op::T;
-    return from_bits<T>((uint32_t)__builtin_amdgcn_update_dpp(
-        (int)to_bits(Op::id()), (int)to_bits(x), CTRL, ROW_MASK, 0xF, false));
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t id = (uint64_t)Op::id(), v = (uint64_t)x;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)id, (int)(uint32_t)v, CTRL,
+                                                                  ROW_MASK, 0xF, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(id >> 32),
+                                                                  (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF,
+                                                                  false);
+        return (T)(((uint64_t)hi << 32) | lo);
+    } else {
+        return from_bits<T>((uint32_t)__builtin_amdgcn_update_dpp((int)to_bits(Op::id()), (int)to_bits(x), CTRL,
+                                                                  ROW_MASK, 0xF, false));
+    }
 }
 
 // Inclusive scan across the 64 lanes, lane order = element order.
@@ -122,7 +152,14 @@ __device__ __forceinline__ typename Op::T wave_shift_right(typename Op::T x) {
 
 template <class T>
 __device__ __forceinline__ T read_lane(T x, int lane) {
-    return from_bits<T>((uint32_t)__builtin_amdgcn_readlane((int)to_bits(x), lane));
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t v = (uint64_t)x;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+        return (T)(((uint64_t)hi << 32) | lo);
+    } else {
+        return from_bits<T>((uint32_t)__builtin_amdgcn_readlane((int)to_bits(x), lane));
+    }
 }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
@@ -145,11 +182,6 @@ constexpr uint32_t ST_PARTIAL = 3u;    // payload = fold of tiles t-d+1..t, d in
 __device__ __forceinline__ uint64_t desc_word(uint32_t state, uint32_t payload) {
     return ((uint64_t)state << 32) | (uint64_t)payload;
 }
-__device__ __forceinline__ uint64_t desc_partial(uint32_t dist, uint32_t payload) {
-    return ((uint64_t)((dist << 2) | ST_PARTIAL) << 32) | (uint64_t)payload;
-}
-__device__ __forceinline__ uint32_t desc_state(uint64_t w) { return (uint32_t)(w >> 32) & 3u; }
-__device__ __forceinline__ uint32_t desc_dist(uint64_t w) { return (uint32_t)(w >> 34); }
 __device__ __forceinline__ void desc_publish(uint64_t *d, uint64_t w) {
     __hip_atomic_store(d, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -169,6 +201,70 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr) {
 __device__ __forceinline__ void count_event(uint32_t *word) {
     __hip_atomic_fetch_add(word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// A descriptor's content: the state word (state in bits 1..0, a PARTIAL's
+// distance in bits 31..2) and the payload.
+template <class T>
+struct DescVal {
+    uint32_t state;
+    T value;
+};
+
+// One 64-bit word per tile: state word high, 32-bit payload low.
+template <class Op>
+struct Words1 {
+    using T = typename Op::T;
+    static constexpr int WORDS = 1;
+    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t &state, T &v) {
+        const uint64_t w = desc_poll(desc + tile);
+        state = (uint32_t)(w >> 32);
+        v = from_bits<T>((uint32_t)w);
+    }
+    __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
+        desc_publish(desc + tile, ((uint64_t)state << 32) | to_bits(v));
+    }
+    __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
+        return desc_install(desc + tile, ((uint64_t)state << 32) | to_bits(v));
+    }
+};
+
+// Two 64-bit words per tile for a 64-bit payload: word 0 = state word | low
+// half, word 1 = state word | high half, each one atomic store.  A reader
+// takes the tile only when both state words agree.  Every state word
+// (state and distance) is published with one payload only, so agreeing
+// words hold the two halves of one value; a read that meets a publication
+// half done sees two different state words and polls again.
+template <class Op>
+struct Words2 {
+    using T = typename Op::T;
+    static constexpr int WORDS = 2;
+    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t &state, T &v) {
+        const uint64_t w0 = desc_poll(desc + 2 * tile), w1 = desc_poll(desc + 2 * tile + 1);
+        const uint32_t s0 = (uint32_t)(w0 >> 32), s1 = (uint32_t)(w1 >> 32);
+        state = (s0 == s1) ? s0 : ST_INVALID;
+        v = (T)(((uint64_t)(uint32_t)w1 << 32) | (uint32_t)w0);
+    }
+    __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
+        const uint64_t b = (uint64_t)v, sw = (uint64_t)state << 32;
+        desc_publish(desc + 2 * (uint64_t)tile, sw | (uint32_t)b);
+        desc_publish(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32));
+    }
+    __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
+        const uint64_t b = (uint64_t)v, sw = (uint64_t)state << 32;
+        const bool lo = desc_install(desc + 2 * (uint64_t)tile, sw | (uint32_t)b);
+        const bool hi = desc_install(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32));
+        return lo || hi;
+    }
+};
+
+template <class Op>
+using WordsFor = typename std::conditional<sizeof(typename Op::T) == 8, Words2<Op>, Words1<Op>>::type;
+
+// A look-back that never computes a predecessor itself.
+template <class T>
+struct NoFallback {
+    __device__ DescVal<T> operator()(uint32_t, uint32_t) const { return DescVal<T>{ST_INVALID, T{}}; }
+};
 
 struct LookbackStats {
     uint32_t polls = 0;    // poll rounds (64*K descriptor reads each)
@@ -204,11 +300,6 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 #ifndef DWPS_LOOKBACK_K
 #define DWPS_LOOKBACK_K 2
 #endif
-
-// A look-back that never computes a predecessor itself.
-struct NoFallback {
-    __device__ __forceinline__ uint64_t operator()(uint32_t, uint32_t) const { return 0ull; }
-};
 
 // Decoupled look-back, executed by one full wave, reading K descriptors per
 // lane per poll, i.e. a window of 64*K predecessors.  Lane l holds tiles
@@ -247,7 +338,7 @@ struct NoFallback {
 // resident or finished ("Single-Pass Prefix Scan with Decoupled Look-Back",
 // sections "Three states in a per-block descriptor" and "Where the algorithm
 // meets the hardware").
-template <class Op, int K, bool STATS, class FB = NoFallback>
+template <class Op, int K, bool STATS, class FB = NoFallback<typename Op::T>, class W = WordsFor<Op>>
 __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile, uint32_t lane, LookbackStats &st,
                                                    uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u},
                                                    typename Op::T own = Op::id(), bool may_publish = false,
@@ -256,25 +347,34 @@ __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile
     T acc = Op::id();
     int64_t nearest = (int64_t)tile - 1;
     uint32_t spins = 0, stalled = 0, walked = 0;
-    const uint64_t pad = desc_word(ST_PREFIX, to_bits(Op::id()));
     for (;;) {
         const int64_t first = nearest - 64 * K + 1 + (int64_t)lane * K;
-        uint64_t w[K];
+        uint32_t sw[K];  // state words
+        T val[K];
+        // every load is issued before any is used (no branch around a load,
+        // so one poll costs one round trip); words before tile 0 read
+        // tile 0's and are then replaced by a PREFIX carrying the identity
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const int64_t idx = first + j;
-            w[j] = (idx >= 0) ? desc_poll(desc + idx) : pad;
+            W::read(desc, idx >= 0 ? idx : 0, sw[j], val[j]);
         }
-        // nearest PREFIX/PARTIAL word of this lane (-1 if none), and whether
-        // a word nearer than it (in this lane) is INVALID
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const bool before = first + j < 0;
+            sw[j] = before ? ST_PREFIX : sw[j];
+            val[j] = before ? Op::id() : val[j];
+        }
+        // nearest PREFIX/PARTIAL word of this lane (-1 if none), and the
+        // nearest INVALID word nearer than it (-1 if none)
         int jp = -1;
 #pragma unroll
         for (int j = 0; j < K; ++j)
-            if (desc_state(w[j]) >= ST_PREFIX) jp = j;
+            if ((sw[j] & 3u) >= ST_PREFIX) jp = j;
         int ji = -1;
 #pragma unroll
         for (int j = 0; j < K; ++j)
-            if (j > jp && desc_state(w[j]) == ST_INVALID) ji = j;
+            if (j > jp && (sw[j] & 3u) == ST_INVALID) ji = j;
         const uint64_t pm = ballot(jp >= 0);
         const uint32_t lp = pm ? 63u - (uint32_t)__builtin_clzll(pm) : 0u;
         // lanes above lp count entirely; lane lp counts from its stopper word
@@ -287,8 +387,8 @@ __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile
                 // reduce the nearest unpublished predecessor ourselves
                 const uint32_t li = 63u - (uint32_t)__builtin_clzll(im);
                 const int64_t p = nearest - 64 * K + 1 + (int64_t)li * K + __builtin_amdgcn_readlane(ji, (int)li);
-                const uint64_t word = fb((uint32_t)p, lane);
-                if (lane == 0 && desc_install(desc + p, word)) count_event(hdr + kHdrFallbacks);
+                const DescVal<T> dv = fb((uint32_t)p, lane);
+                if (lane == 0 && W::install(desc, (uint32_t)p, dv.state, dv.value)) count_event(hdr + kHdrFallbacks);
                 stalled = 0;
                 continue;
             }
@@ -305,27 +405,26 @@ __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile
             const int jfrom = (pm && lane == lp) ? jp : 0;
 #pragma unroll
             for (int j = 0; j < K; ++j)
-                if (j >= jfrom) v = Op::op(v, from_bits<T>((uint32_t)w[j]));
+                if (j >= jfrom) v = Op::op(v, val[j]);
         }
         v = wave_inclusive<Op>(v);
         acc = Op::op(read_lane(v, 63), acc);
         if (STATS) st.windows++;
         if (pm) {
-            // the stopper word, uniform
-            uint64_t ws = w[0];
+            // the stopper's state word, uniform
+            uint32_t ss = sw[0];
 #pragma unroll
-            for (int j = 1; j < K; ++j) ws = (j == jp) ? w[j] : ws;
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(ws >> 32), (int)lp);
+            for (int j = 1; j < K; ++j) ss = (j == jp) ? sw[j] : ss;
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)ss, (int)lp);
             if ((hi & 3u) == ST_PREFIX) break;
-            const int64_t s = nearest - 64 * K + 1 + (int64_t)lp * K +
-                              __builtin_amdgcn_readlane(jp, (int)lp);
+            const int64_t s = nearest - 64 * K + 1 + (int64_t)lp * K + __builtin_amdgcn_readlane(jp, (int)lp);
             nearest = s - (int64_t)(hi >> 2);
         } else {
             nearest -= 64 * K;
         }
         if (nearest < 0) break;  // a PARTIAL reaching back to tile 0 ends the walk
         if (cfg.partial && ++walked >= cfg.partial && may_publish && lane == 0) {
-            desc_publish(desc + tile, desc_partial((uint32_t)((int64_t)tile - nearest), to_bits(Op::op(acc, own))));
+            W::publish(desc, tile, ((uint32_t)((int64_t)tile - nearest) << 2) | ST_PARTIAL, Op::op(acc, own));
             // counted by the instrumented build only: an atomic on one shared
             // word would queue ahead of this wave's next poll
             if (STATS) count_event(hdr + kHdrPartials);

@@ -69,6 +69,7 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
                                              uint32_t *stats, int aggregate_only, LookbackCfg cfg,
                                              const FB &fb, uint32_t lane) {
     using T = typename Op::T;
+    using W = WordsFor<Op>;
     T agg_prev = Op::id(), agg_prev2 = Op::id();
     T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
     for (int par = 0;; par ^= 1) {
@@ -100,9 +101,8 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
                 }
             }
             if (have_prev2 && !(STATS && aggregate_only))
-                desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, to_bits(Op::op(excl, agg_prev2))));
-            if (pt.cur < num_tiles)
-                desc_publish(desc + pt.cur, desc_word(pt.cur == 0 ? ST_PREFIX : ST_AGGREGATE, to_bits(agg)));
+                W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
+            if (pt.cur < num_tiles) W::publish(desc, pt.cur, pt.cur == 0 ? ST_PREFIX : ST_AGGREGATE, agg);
         }
         incl_last = Op::op(excl, agg_prev2);
         agg_prev2 = agg_prev;

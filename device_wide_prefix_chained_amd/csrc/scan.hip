@@ -41,7 +41,8 @@ namespace dwps {
 template <class Op, int D, int Q>
 struct ScanShared {
     using T = typename Op::T;
-    v4u park[kParkSlots][D * Q * 64];  // tile-relative outputs, 16 bytes per lane-group
+    static constexpr int PW = (int)sizeof(T) / 4;  // 16-byte vectors per group of four outputs
+    v4u park[kParkSlots][D * Q * 64 * PW];       // tile-relative outputs
     uint32_t t0;
     uint32_t next;
     T wt[2][D];  // wave totals, double-buffered by phase parity
@@ -57,7 +58,7 @@ template <class Op, int D, int Q, int G, bool INCL, bool VEC>
 __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q> &f1, int par, uint32_t &slot,
                                            PipeTiles &pt, typename Op::T (&lane_excl)[Q],
                                            typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
-                                           const typename Op::T *in, typename Op::T *out, uint32_t n,
+                                           const typename InputOf<Op>::type *in, typename Op::T *out, uint32_t n,
                                            uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
                                            uint64_t lane_off) {
     using T = typename Op::T;
@@ -67,9 +68,11 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
     if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
+    constexpr int PW = ScanShared<Op, D, Q>::PW;
     const uint32_t old_slot = next_slot(slot);
-    v4u *mine = &sh.park[slot][(uint32_t)d * Q * 64u + lane];
-    const v4u *theirs = &sh.park[old_slot][(uint32_t)d * Q * 64u + lane];
+    // group (q, lane) of wave d parks as PW vectors at ((d*Q + q)*PW + h)*64 + lane
+    v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
+    const v4u *theirs = &sh.park[old_slot][(uint32_t)d * Q * PW * 64u + lane];
     // Straight-line code whether or not the tiles exist (absent tiles are
     // dummy loads of the first group and harmless arithmetic), so that the
     // compiler sees one fixed sequence of loads and keeps two tiles in flight.
@@ -81,12 +84,10 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
     finalize_span<Op, Q, INCL>(cur, lane_excl, row_prefix, wave_prefix);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        v4u w;
-        w.x = to_bits(cur.v[q][0]);
-        w.y = to_bits(cur.v[q][1]);
-        w.z = to_bits(cur.v[q][2]);
-        w.w = to_bits(cur.v[q][3]);
-        mine[q * 64] = w;
+        v4u w[PW];
+        pack16<T>(cur.v[q], w);
+#pragma unroll
+        for (int h = 0; h < PW; ++h) mine[(q * PW + h) * 64] = w[h];
     }
     // the freed registers take the tile two ahead
     const uint64_t b2 = (uint64_t)pt.f2 * TILE;
@@ -99,16 +100,45 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
     __syncthreads();  // B
     if (pt.prev2 < num_tiles) {
         const uint64_t bp = (uint64_t)pt.prev2 * TILE;
-        WaveSpan<Op, Q> old;
+        const bool full = bp + TILE <= n;
+        bool stored = false;
+        if constexpr (PW == 2 && VEC) {
+            if (full) {
+                // 8-byte outputs, read back regrouped: lane l takes elements
+                // 2l and 2l+1 of each half row of 128 (they were parked by
+                // lane l/2, in its half l%2), so every 16-byte store
+                // instruction of the wave writes 1 KiB contiguous
+                const v4u *wp = &sh.park[old_slot][(uint32_t)d * Q * PW * 64u];
+                T *row = out + bp + (uint64_t)d * Q * 256u + 2u * lane;
+                const T pre = sh.prefix;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            const v4u w = theirs[q * 64];
-            old.v[q][0] = from_bits<T>(w.x);
-            old.v[q][1] = from_bits<T>(w.y);
-            old.v[q][2] = from_bits<T>(w.z);
-            old.v[q][3] = from_bits<T>(w.w);
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const v4u w = wp[(q * 2 + (int)(lane & 1u)) * 64 + h * 32 + (int)(lane >> 1)];
+                        const T a = Op::op(pre, (T)(((uint64_t)w.y << 32) | w.x));
+                        const T b = Op::op(pre, (T)(((uint64_t)w.w << 32) | w.z));
+                        v4u r;
+                        r.x = (uint32_t)a;
+                        r.y = (uint32_t)((uint64_t)a >> 32);
+                        r.z = (uint32_t)b;
+                        r.w = (uint32_t)((uint64_t)b >> 32);
+                        store16(row + q * 256 + h * 128, r);
+                    }
+                stored = true;
+            }
         }
-        store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, bp + TILE <= n);
+        if (!stored) {
+            WaveSpan<Op, Q> old;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                v4u w[PW];
+#pragma unroll
+                for (int h = 0; h < PW; ++h) w[h] = theirs[(q * PW + h) * 64];
+                unpack16<T>(w, old.v[q]);
+            }
+            store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, full);
+        }
     }
     if (pt.drained(num_tiles)) return true;
     if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
@@ -119,7 +149,7 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
 }
 
 template <class Op, int D, int Q, int G, bool INCL, bool VEC>
-__device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, const typename Op::T *in,
+__device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, const typename InputOf<Op>::type *in,
                                           typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
                                           uint32_t lane, uint32_t d) {
     using T = typename Op::T;
@@ -148,9 +178,9 @@ __device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh
 // its owner publishes first.  Runs on the control wave, rarely.
 template <class Op, uint32_t TILE>
 struct FlatFallback {
-    const typename Op::T *in;
+    const typename InputOf<Op>::type *in;
     uint32_t n;
-    __device__ uint64_t operator()(uint32_t p, uint32_t lane) const {
+    __device__ DescVal<typename Op::T> operator()(uint32_t p, uint32_t lane) const {
         using T = typename Op::T;
         constexpr uint32_t ROWS = TILE / 256u, BATCH = 8u;
         static_assert(ROWS % BATCH == 0, "whole batches of rows");
@@ -164,20 +194,20 @@ struct FlatFallback {
 #pragma unroll
                 for (uint32_t e = 0; e < 4; ++e) {
                     const uint64_t i = base + (uint64_t)(r + k) * 256u + e;
-                    v = Op::op(v, i < n ? in[i] : Op::id());
+                    v = Op::op(v, i < n ? (T)in[i] : Op::id());
                 }
                 part[k] = v;
             }
 #pragma unroll
             for (uint32_t k = 0; k < BATCH; ++k) acc = Op::op(acc, read_lane(wave_inclusive<Op>(part[k]), 63));
         }
-        return desc_word(p == 0 ? ST_PREFIX : ST_AGGREGATE, to_bits(acc));
+        return DescVal<T>{p == 0 ? ST_PREFIX : ST_AGGREGATE, acc};
     }
 };
 
 template <class Op, int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
-    const typename Op::T *in, typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+    const typename InputOf<Op>::type *in, typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
     uint64_t *desc, typename Op::T *total, uint32_t *stats, int aggregate_only, LookbackCfg cfg) {
     __shared__ ScanShared<Op, D, Q> sh;
     const uint32_t lane = threadIdx.x & 63u;
@@ -222,32 +252,61 @@ constexpr int kTilesPerTicket = DWPS_TILES_PER_TICKET;
 constexpr int kFlatThreads = (kFlatD + 1) * 64;
 constexpr uint32_t kFlatTile = kFlatD * kFlatQ * 256;
 
+// 8-byte outputs take half the groups per lane, so a parked tile keeps the
+// same LDS footprint (48 KiB).
+template <class Op>
+constexpr int flat_q() {
+    return sizeof(typename Op::T) == 8 ? kFlatQ / 2 : kFlatQ;
+}
+// Look-back width: every lane reads kLookbackK descriptor words per poll, so
+// with two words per tile (64-bit payloads) a poll covers half as many tiles.
+template <class Op>
+constexpr int flat_k() {
+    return kLookbackK / WordsFor<Op>::WORDS > 0 ? kLookbackK / WordsFor<Op>::WORDS : 1;
+}
+template <class Op>
+constexpr uint32_t flat_tile() {
+    return (uint32_t)kFlatD * (uint32_t)flat_q<Op>() * 256u;
+}
 inline uint64_t flat_tiles(uint64_t n) { return ceil_div(n, kFlatTile); }
+
+// Workspace: header + descriptor words (one or two per tile).
+template <class Op>
+inline size_t flat_ws_bytes(uint64_t tiles) {
+    return kWsHeader + round_up(tiles * 8u * (uint64_t)WordsFor<Op>::WORDS, 256);
+}
 
 template <class Op, bool STATS>
 ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v, uint64_t n, void *total_v,
                       bool inclusive, uint32_t *stats, hipStream_t s, typename Op::T identity,
                       int aggregate_only = 0) {
     using T = typename Op::T;
+    using In = typename InputOf<Op>::type;
+    constexpr int Q = flat_q<Op>();
+    constexpr int K = flat_k<Op>();
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
-    const uint64_t tiles = flat_tiles(n);
+    const uint64_t tiles = ceil_div(n, flat_tile<Op>());
+    const size_t ws_need = flat_ws_bytes<Op>(tiles);
     bool query = false;
-    ps_status st = workspace_protocol(ws, ws_bytes, ws_bytes_for_tiles(tiles), &query);
+    ps_status st = workspace_protocol(ws, ws_bytes, ws_need, &query);
     if (st != PS_OK || query) return st;
-    const T *in = static_cast<const T *>(in_v);
+    const In *in = static_cast<const In *>(in_v);
     T *out = static_cast<T *>(out_v);
     T *total = static_cast<T *>(total_v);
     if (n == 0) {
         if (!total) return PS_OK;
-        if (!aligned(total, 4)) return PS_ERR_ALIGNMENT;
+        if (!aligned(total, sizeof(T))) return PS_ERR_ALIGNMENT;
         hipLaunchKernelGGL(write_one<T>, dim3(1), dim3(1), 0, s, total, identity);
         return launch_status();
     }
     if (!in || !out) return PS_ERR_NULL;
     if (STATS && !stats) return PS_ERR_NULL;
-    if (!aligned(in, 4) || !aligned(out, 4) || (total && !aligned(total, 4))) return PS_ERR_ALIGNMENT;
-    if (in != (const void *)out && ranges_overlap(in, n * 4, out, n * 4)) return PS_ERR_ALIAS;
-    if (launch_clear(ws, ws_bytes_for_tiles(tiles), s) != hipSuccess) return PS_ERR_HIP;
+    if (!aligned(in, sizeof(In)) || !aligned(out, sizeof(T)) || (total && !aligned(total, sizeof(T))))
+        return PS_ERR_ALIGNMENT;
+    // exact in-place is allowed when input and output elements have one size
+    const bool in_place = sizeof(In) == sizeof(T) && in_v == (const void *)out_v;
+    if (!in_place && ranges_overlap(in, n * sizeof(In), out, n * sizeof(T))) return PS_ERR_ALIAS;
+    if (launch_clear(ws, ws_need, s) != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(in, 16) && aligned(out, 16);
     uint32_t *ctr = ws_counter(ws);
     uint64_t *desc = ws_desc(ws);
@@ -263,11 +322,11 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
     };
     ps_status r;
     if (inclusive)
-        r = vec ? launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, true, true, STATS>)
-                : launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, true, false, STATS>);
+        r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, true, STATS>)
+                : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, false, STATS>);
     else
-        r = vec ? launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, false, true, STATS>)
-                : launch(chained_scan_kernel<Op, kFlatD, kFlatQ, kLookbackK, kTilesPerTicket, false, false, STATS>);
+        r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, true, STATS>)
+                : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, false, STATS>);
     if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
@@ -287,6 +346,18 @@ extern "C" ps_status ps_scan_inclusive_u32(void *ws, size_t *ws_bytes, const uin
                                            uint64_t n, uint32_t *total, void *stream) {
     return launch_flat<SumU32, false>(ws, ws_bytes, in, out, n, total, true, nullptr,
                                       static_cast<hipStream_t>(stream), 0u);
+}
+
+extern "C" ps_status ps_scan_exclusive_u32_u64(void *ws, size_t *ws_bytes, const uint32_t *in, uint64_t *out,
+                                               uint64_t n, uint64_t *total, void *stream) {
+    return launch_flat<SumU32toU64, false>(ws, ws_bytes, in, out, n, total, false, nullptr,
+                                           static_cast<hipStream_t>(stream), 0ull);
+}
+
+extern "C" ps_status ps_scan_inclusive_u32_u64(void *ws, size_t *ws_bytes, const uint32_t *in, uint64_t *out,
+                                               uint64_t n, uint64_t *total, void *stream) {
+    return launch_flat<SumU32toU64, false>(ws, ws_bytes, in, out, n, total, true, nullptr,
+                                           static_cast<hipStream_t>(stream), 0ull);
 }
 
 extern "C" ps_status ps_scan_exclusive_f32(void *ws, size_t *ws_bytes, const float *in, float *out, uint64_t n,
@@ -320,6 +391,10 @@ extern "C" ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtyp
         }
         return PS_ERR_UNSUPPORTED;
     }
+    if (dtype == PS_U64) {
+        if (op != PS_OP_SUM) return PS_ERR_UNSUPPORTED;
+        return launch_flat<SumU32toU64, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0ull);
+    }
     if (dtype == PS_F32) {
         switch (op) {
         case PS_OP_SUM: return launch_flat<SumF32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0.0f);
@@ -348,6 +423,5 @@ extern "C" uint32_t ps_lookback_window(void) { return 64u * (uint32_t)kLookbackK
 extern "C" uint32_t ps_lookback_group(void) { return (uint32_t)kTilesPerTicket; }
 
 extern "C" uint32_t ps_tile_elements(ps_dtype dtype) {
-    (void)dtype;
-    return kFlatTile;
+    return dtype == PS_U64 ? flat_tile<SumU32toU64>() : kFlatTile;
 }

@@ -207,7 +207,7 @@ struct SegFallback {
     const uint32_t *values;
     const uint32_t *heads;
     uint32_t n;
-    __device__ uint64_t operator()(uint32_t p, uint32_t lane) const {
+    __device__ DescVal<uint32_t> operator()(uint32_t p, uint32_t lane) const {
         constexpr uint32_t ROWS = kSegTile / 256u, BATCH = 8u;
         static_assert(ROWS % BATCH == 0, "whole batches of rows");
         const uint64_t base = (uint64_t)p * kSegTile + 4u * lane;
@@ -236,7 +236,7 @@ struct SegFallback {
                                           (uint32_t)__builtin_amdgcn_readlane((int)v, 63)});
             }
         }
-        return desc_word((acc.f || p == 0) ? ST_PREFIX : ST_AGGREGATE, acc.v);
+        return DescVal<uint32_t>{(acc.f || p == 0) ? ST_PREFIX : ST_AGGREGATE, acc.v};
     }
 };
 

@@ -40,6 +40,8 @@ __device__ __forceinline__ void store16(void *p, v4u v) {
 template <class Op, int Q>
 struct WaveSpan {
     using T = typename Op::T;
+    using In = typename InputOf<Op>::type;  // 4-byte input elements, widened to T on load
+    static_assert(sizeof(In) == 4, "16-byte loads carry four input elements");
     T v[Q][4];  // elements, then their lane-local inclusive prefixes
 
     // Issue the loads of the span starting at element `span` (= tile base +
@@ -53,7 +55,7 @@ struct WaveSpan {
     // VEC: 16-byte aligned input, one 16-byte load per group; otherwise one
     // 4-byte load per element.
     template <bool VEC>
-    __device__ __forceinline__ void load(const T *in, uint64_t span, uint32_t n, bool full, bool valid) {
+    __device__ __forceinline__ void load(const In *in, uint64_t span, uint32_t n, bool full, bool valid) {
         if (VEC) {
             const uint64_t last_group = ((uint64_t)n - 1u) & ~(uint64_t)3u;
 #pragma unroll
@@ -62,10 +64,10 @@ struct WaveSpan {
                 if (!full) g = g < last_group ? g : last_group;
                 if (!valid) g = 0;
                 const v4u r = load16(in + g);
-                v[q][0] = from_bits<T>(r.x);
-                v[q][1] = from_bits<T>(r.y);
-                v[q][2] = from_bits<T>(r.z);
-                v[q][3] = from_bits<T>(r.w);
+                v[q][0] = (T)from_bits<In>(r.x);
+                v[q][1] = (T)from_bits<In>(r.y);
+                v[q][2] = (T)from_bits<In>(r.z);
+                v[q][3] = (T)from_bits<In>(r.w);
             }
         } else {
             const uint64_t last = (uint64_t)n - 1u;
@@ -76,7 +78,7 @@ struct WaveSpan {
                     uint64_t i = span + (uint64_t)q * 256u + k;
                     i = i < last ? i : last;
                     if (!valid) i = 0;
-                    v[q][k] = in[i];
+                    v[q][k] = (T)in[i];
                 }
         }
     }
@@ -144,62 +146,56 @@ __device__ __forceinline__ void finalize_span(WaveSpan<Op, Q> &s, const typename
     }
 }
 
+// Four elements as 16-byte vectors: one for 4-byte T, two for 8-byte T.
+template <class T>
+__device__ __forceinline__ void pack16(const T (&o)[4], v4u (&w)[sizeof(T) / 4]) {
+    if constexpr (sizeof(T) == 8) {
+        w[0].x = (uint32_t)o[0];
+        w[0].y = (uint32_t)(o[0] >> 32);
+        w[0].z = (uint32_t)o[1];
+        w[0].w = (uint32_t)(o[1] >> 32);
+        w[1].x = (uint32_t)o[2];
+        w[1].y = (uint32_t)(o[2] >> 32);
+        w[1].z = (uint32_t)o[3];
+        w[1].w = (uint32_t)(o[3] >> 32);
+    } else {
+        w[0].x = to_bits(o[0]);
+        w[0].y = to_bits(o[1]);
+        w[0].z = to_bits(o[2]);
+        w[0].w = to_bits(o[3]);
+    }
+}
+template <class T>
+__device__ __forceinline__ void unpack16(const v4u (&w)[sizeof(T) / 4], T (&o)[4]) {
+    if constexpr (sizeof(T) == 8) {
+        o[0] = (T)(((uint64_t)w[0].y << 32) | w[0].x);
+        o[1] = (T)(((uint64_t)w[0].w << 32) | w[0].z);
+        o[2] = (T)(((uint64_t)w[1].y << 32) | w[1].x);
+        o[3] = (T)(((uint64_t)w[1].w << 32) | w[1].z);
+    } else {
+        o[0] = from_bits<T>(w[0].x);
+        o[1] = from_bits<T>(w[0].y);
+        o[2] = from_bits<T>(w[0].z);
+        o[3] = from_bits<T>(w[0].w);
+    }
+}
+
 // Store a finalized span: out = prefix (+) v.
 template <class Op, int Q, bool VEC>
 __device__ __forceinline__ void store_final(const WaveSpan<Op, Q> &s, typename Op::T prefix, typename Op::T *out,
                                             uint64_t span, uint32_t n, bool full) {
     using T = typename Op::T;
+    constexpr int PW = (int)sizeof(T) / 4;  // 16-byte vectors per group of four
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         T o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = Op::op(prefix, s.v[q][k]);
         if (VEC && full) {
-            v4u w;
-            w.x = to_bits(o[0]);
-            w.y = to_bits(o[1]);
-            w.z = to_bits(o[2]);
-            w.w = to_bits(o[3]);
-            store16(out + span + (uint64_t)q * 256u, w);
-        } else {
+            v4u w[PW];
+            pack16<T>(o, w);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t i = span + (uint64_t)q * 256u + k;
-                if (i < n) out[i] = o[k];
-            }
-        }
-    }
-}
-
-// Combine base (+) row prefix (+) lane prefix (+) element prefix and store
-// the span (inclusive or exclusive form).
-template <class Op, int Q, bool INCL, bool VEC>
-__device__ __forceinline__ void store_span(const WaveSpan<Op, Q> &s, const typename Op::T (&lane_excl)[Q],
-                                           const typename Op::T (&row_prefix)[Q], typename Op::T base,
-                                           typename Op::T *out, uint64_t span, uint32_t n, bool full) {
-    using T = typename Op::T;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const T c = Op::op(Op::op(base, row_prefix[q]), lane_excl[q]);
-        T o[4];
-        if (INCL) {
-            o[0] = Op::op(c, s.v[q][0]);
-            o[1] = Op::op(c, s.v[q][1]);
-            o[2] = Op::op(c, s.v[q][2]);
-            o[3] = Op::op(c, s.v[q][3]);
-        } else {
-            o[0] = c;
-            o[1] = Op::op(c, s.v[q][0]);
-            o[2] = Op::op(c, s.v[q][1]);
-            o[3] = Op::op(c, s.v[q][2]);
-        }
-        if (VEC && full) {
-            v4u w;
-            w.x = to_bits(o[0]);
-            w.y = to_bits(o[1]);
-            w.z = to_bits(o[2]);
-            w.w = to_bits(o[3]);
-            store16(out + span + (uint64_t)q * 256u, w);
+            for (int h = 0; h < PW; ++h) store16(out + span + (uint64_t)q * 256u + 4 / PW * h, w[h]);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

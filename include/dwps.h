@@ -74,7 +74,9 @@ typedef enum ps_status {
     PS_ERR_ALIGNMENT = 7
 } ps_status;
 
-typedef enum ps_dtype { PS_U32 = 0, PS_F32 = 1 } ps_dtype;
+/* Element types.  PS_U64 names the widening sum: uint32 inputs, uint64
+ * outputs and total (ps_scan with PS_OP_SUM only). */
+typedef enum ps_dtype { PS_U32 = 0, PS_F32 = 1, PS_U64 = 2 } ps_dtype;
 
 /* Associative operators ([P2] "Inclusive, exclusive and associative": any
  * associative operator, commutativity not required).  Operands are always
@@ -128,10 +130,30 @@ ps_status ps_scan_inclusive_f32(void *ws, size_t *ws_bytes, const float *in,
                                 float *out, uint64_t n, float *total,
                                 void *stream);
 
+/* Widening uint32 -> uint64 sum scan (the 64-bit results [P2] "Failure
+ * modes" asks for when 32-bit sums overflow; [P3] "Scan as an index
+ * generator": offsets over billions of flags).  Same contract as the flat
+ * scans, except:
+ *   in    : n uint32 values (4-byte aligned);
+ *   out   : n uint64 sums, exact (no wrap below 2^64), 8-byte aligned; out
+ *           must not overlap in at all (the element sizes differ);
+ *   total : optional, one uint64.
+ * Each tile's 64-bit aggregate and prefix travel as two descriptor words
+ * that both carry the state; a reader takes a tile only when the two agree.
+ * Tiles hold 6144 elements (ps_tile_elements(PS_U64)), so the parked
+ * 64-bit outputs fit the same LDS as the 32-bit scans'. */
+ps_status ps_scan_exclusive_u32_u64(void *ws, size_t *ws_bytes, const uint32_t *in,
+                                    uint64_t *out, uint64_t n, uint64_t *total,
+                                    void *stream);
+ps_status ps_scan_inclusive_u32_u64(void *ws, size_t *ws_bytes, const uint32_t *in,
+                                    uint64_t *out, uint64_t n, uint64_t *total,
+                                    void *stream);
+
 /* Generic associative-operator scan: the same pass for any (op, dtype) pair
- * listed under ps_op.  `in`, `out` and `total` point to elements of `dtype`
- * (uint32_t or float); inclusive != 0 selects the inclusive form.  Pairs not
- * listed return PS_ERR_UNSUPPORTED. */
+ * listed under ps_op, and (PS_OP_SUM, PS_U64) for the widening sum.  `in`,
+ * `out` and `total` point to elements of `dtype` (uint32_t or float; for
+ * PS_U64 uint32_t in, uint64_t out and total); inclusive != 0 selects the
+ * inclusive form.  Pairs not listed return PS_ERR_UNSUPPORTED. */
 ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
                   int inclusive, const void *in, void *out, uint64_t n,
                   void *total, void *stream);
@@ -255,7 +277,8 @@ void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows)
 ps_status ps_kernel_timing(int enable);
 ps_status ps_kernel_timing_read(double *total_ms, uint64_t *launches);
 
-/* Elements per tile of the flat scan kernel for `dtype`, of the segmented
+/* Elements per tile of the flat scan kernel for `dtype` (PS_U64: the
+ * widening scan), of the segmented
  * scan kernel, and the library version string. */
 uint32_t ps_tile_elements(ps_dtype dtype);
 uint32_t ps_segmented_tile_elements(void);

@@ -66,6 +66,15 @@ def test_size_queries():
         st2, need2 = _wsq(lib, "ps_scan", 3, 0, 1, None, None, n, None, None)
         assert st2 == 0 and need2 == need
         assert lib.ps_lookback_tiles(n) == tiles
+    wtile = lib.ps_tile_elements(2)
+    assert wtile == 6144
+    for n in (0, 1, wtile, wtile + 1, 1 << 28):
+        st, need = _wsq(lib, "ps_scan_exclusive_u32_u64", None, None, n, None, None)
+        tiles = -(-n // wtile)
+        # two descriptor words per tile for the 64-bit payload
+        assert st == 0 and need == 256 + -(-tiles * 16 // 256) * 256, n
+        st2, need2 = _wsq(lib, "ps_scan", 0, 2, 0, None, None, n, None, None)
+        assert st2 == 0 and need2 == need
     stile = lib.ps_segmented_tile_elements()
     assert stile == 12288
     for n in (0, 1, stile, stile + 1, 1 << 26, (1 << 32) - 1):
@@ -114,10 +123,23 @@ def test_argument_errors_flat():
     assert lib.ps_scan_exclusive_u32(None, None, None, None, 5, None, None) == PS_ERR_NULL
     # unsupported operator / dtype pairs
     wsb = ctypes.c_size_t(big)
-    for op, dt in ((3, 1), (4, 1), (5, 1), (6, 1), (7, 0), (99, 0), (0, 2)):
+    for op, dt in ((3, 1), (4, 1), (5, 1), (6, 1), (7, 0), (99, 0), (0, 3), (1, 2), (6, 2)):
         st = lib.ps_scan(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), op, dt, 0, ctypes.c_void_p(A),
                          ctypes.c_void_p(B), 10, None, None)
         assert st == PS_ERR_UNSUPPORTED, (op, dt)
+
+
+def test_argument_errors_widening():
+    lib = _lib()
+    PS_ERR_ALIAS, PS_ERR_ALIGNMENT, PS_ERR_SIZE = 2, 7, 3
+    big = 1 << 30
+    for fn in ("ps_scan_exclusive_u32_u64", "ps_scan_inclusive_u32_u64"):
+        assert _call_flat(lib, fn, big, A, B, 1 << 32) == PS_ERR_SIZE
+        assert _call_flat(lib, fn, big, A, A, 10) == PS_ERR_ALIAS        # no in-place: sizes differ
+        assert _call_flat(lib, fn, big, A, A + 32, 10) == PS_ERR_ALIAS   # out overlaps in's tail
+        assert _call_flat(lib, fn, big, A + 48, A, 10) == PS_ERR_ALIAS   # in inside out
+        assert _call_flat(lib, fn, big, A, B + 4, 10) == PS_ERR_ALIGNMENT  # out not 8-byte aligned
+        assert _call_flat(lib, fn, big, A, B, 10, total=B + 4096 + 4) == PS_ERR_ALIGNMENT
 
 
 def test_argument_errors_segmented_and_compact():
