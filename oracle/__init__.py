@@ -62,6 +62,8 @@ class Oracle:
         lib.oracle_scan_u32.restype = i32
         lib.oracle_scan_u32_u64.argtypes = [i32, vp, vp, u64, vp]
         lib.oracle_scan_u32_u64.restype = i32
+        lib.oracle_scan_linrec_f32.argtypes = [i32, vp, vp, vp, vp, vp, u64, vp, vp]
+        lib.oracle_scan_linrec_f32.restype = i32
         lib.oracle_scan_f32_sum.argtypes = [i32, vp, vp, vp, u64, vp]
         lib.oracle_scan_f32_sum.restype = i32
         lib.oracle_scan_f32_minmax.argtypes = [i32, i32, vp, vp, u64, vp]
@@ -93,6 +95,22 @@ class Oracle:
         total = np.zeros(1, dtype=np.uint64)
         self.lib.oracle_scan_u32_u64(int(bool(inclusive)), _ptr(x), _ptr(y), x.size, _ptr(total))
         return y, int(total[0])
+
+    def scan_linrec_f32(self, ab, inclusive: bool = True, want_abs: bool = True):
+        """Scan of (a, b) pairs under (a1,b1) then (a2,b2) = (a1 a2, a2 b1 + b2).
+        ab: (n, 2) float32.  Returns (A, B, SA, SB, (ta, tb)) in fp64; SA/SB are
+        the same scan over (|a|, |b|) (None unless want_abs)."""
+        ab = np.ascontiguousarray(ab, dtype=np.float32).reshape(-1, 2)
+        n = ab.shape[0]
+        A = np.empty(n, np.float64)
+        B = np.empty(n, np.float64)
+        sa = np.empty(n, np.float64) if want_abs else None
+        sb = np.empty(n, np.float64) if want_abs else None
+        ta = np.zeros(1, np.float64)
+        tb = np.zeros(1, np.float64)
+        self.lib.oracle_scan_linrec_f32(int(bool(inclusive)), _ptr(ab), _ptr(A), _ptr(B), _ptr(sa), _ptr(sb), n,
+                                        _ptr(ta), _ptr(tb))
+        return A, B, sa, sb, (float(ta[0]), float(tb[0]))
 
     def scan_f32_sum(self, x, inclusive: bool = False, want_abs: bool = True):
         """Return (y_fp64, absprefix_fp64 or None, total_fp64) for an fp32 sum scan."""

@@ -171,6 +171,49 @@ int oracle_scan_u32_u64(int inclusive, const uint32_t *x, uint64_t *y,
 }
 
 /*
+ * Linear recurrence h[t] = a[t] h[t-1] + b[t] as a scan of (a, b) pairs
+ * ([P2] "What scan builds": (a1, b1) then (a2, b2) combine to
+ * (a1 a2, a2 b1 + b2); identity (1, 0); not commutative).  fp32 inputs,
+ * fp64 accumulation, one running pair in index order:
+ *   inclusive  out[t] = (a_0, b_0) (+) ... (+) (a_t, b_t)
+ *   exclusive  out[0] = (1, 0), out[t] = (a_0, b_0) (+) ... (+) (a_{t-1}, b_{t-1})
+ * so with h[-1] = 0 the second component of the inclusive pair is h[t].
+ * ab holds n interleaved pairs; A, B receive the two components (fp64).
+ * sa, sb (optional) receive the same scan over (|a|, |b|): the magnitudes
+ * that scale the tolerance of an fp32 evaluation in any grouping.
+ * *ta, *tb (optional) receive the fold of all n pairs.
+ */
+int oracle_scan_linrec_f32(int inclusive, const float *ab, double *A, double *B,
+                           double *sa, double *sb, uint64_t n, double *ta, double *tb)
+{
+    double pa = 1.0, pb = 0.0;   /* running pair */
+    double qa = 1.0, qb = 0.0;   /* running pair of magnitudes */
+    for (uint64_t t = 0; t < n; ++t) {
+        double at = (double)ab[2 * t], bt = (double)ab[2 * t + 1];
+        if (!inclusive) {
+            A[t] = pa;
+            B[t] = pb;
+            if (sa) sa[t] = qa;
+            if (sb) sb[t] = qb;
+        }
+        /* (pa, pb) then (at, bt) */
+        pb = at * pb + bt;
+        pa = pa * at;
+        qb = fabs(at) * qb + fabs(bt);
+        qa = qa * fabs(at);
+        if (inclusive) {
+            A[t] = pa;
+            B[t] = pb;
+            if (sa) sa[t] = qa;
+            if (sb) sb[t] = qb;
+        }
+    }
+    if (ta) *ta = pa;
+    if (tb) *tb = pb;
+    return 0;
+}
+
+/*
  * fp32 sum scan, accumulated in fp64 from the fp32 inputs ([P2] "Numerics and
  * determinism": keep the accumulator in float32 or wider; the float64 answer
  * is the reference).  Also returns absprefix[i] = sum_{j<=i} |x[j]| in fp64,

@@ -16,6 +16,8 @@ from the oracle itself:
 * a Blelloch up-sweep/down-sweep written here from its description (a
   reduction tree, then prefixes pushed from the root to the leaves);
 * a Hillis-Steele scan written here from its description;
+* for the recurrence pair, exact rational arithmetic: the maps h -> a h + b
+  composed on numbers, the closed-form sums of products, a tree grouping;
 * invariants (last inclusive value = total, differences of the exclusive
   scan = input, reset at every segment start, untouched rows outside).
 
@@ -28,6 +30,7 @@ import functools
 import json
 import math
 import operator
+from fractions import Fraction
 from pathlib import Path
 
 import numpy as np
@@ -413,6 +416,147 @@ def pin_f32_minmax(orc):
         assert np.signbit(inc).tolist() == [False, False, False], op
         inc, _ = orc.scan_f32_minmax(-z, op, inclusive=True)
         assert np.signbit(inc).tolist() == [True, True, True], op
+
+
+# --------------------------------------------------------------------------
+# Linear recurrence h[t] = a[t] h[t-1] + b[t] as a scan of (a, b) pairs
+# ("Parallel Prefix Sum (Scan), in depth", section "What scan builds")
+# --------------------------------------------------------------------------
+def _maps_fold_exact(pairs):
+    """Compose the maps h -> a h + b of `pairs` in order with exact rationals
+    and read the composition back as (A, B) by evaluating it at h = 0 (B) and
+    h = 1 (A + B).  No use of the pair formula."""
+    def apply(h):
+        for a, b in pairs:
+            h = Fraction(a) * h + Fraction(b)
+        return h
+    f0, f1 = apply(Fraction(0)), apply(Fraction(1))
+    return f1 - f0, f0
+
+
+def _linrec_closed_exact(a, b, t):
+    """A_t = prod_{k<=t} a_k, B_t = sum_j b_j prod_{j<k<=t} a_k (exact), and
+    the same sums over |a|, |b|."""
+    A = math.prod((Fraction(float(v)) for v in a[: t + 1]), start=Fraction(1))
+    B = Fraction(0)
+    SB = Fraction(0)
+    for j in range(t + 1):
+        tail = math.prod((Fraction(float(v)) for v in a[j + 1: t + 1]), start=Fraction(1))
+        B += Fraction(float(b[j])) * tail
+        SB += abs(Fraction(float(b[j]))) * abs(tail)
+    return A, B, abs(A), SB
+
+
+def _linrec_tree_exact(pairs):
+    """Inclusive scan by a balanced tree: each output folds a left and a right
+    subtree's compositions, each computed by _maps_fold_exact.  Exact, so it
+    must agree with any correct grouping."""
+    out = []
+    for t in range(len(pairs)):
+        mid = (t + 1) // 2
+        la, lb = _maps_fold_exact(pairs[:mid])
+        ra, rb = _maps_fold_exact(pairs[mid: t + 1])
+        out.append(_maps_fold_exact([(la, lb), (ra, rb)]))
+    return out
+
+
+@pin
+def pin_linrec_page_example(orc):
+    g = golden("p2_recurrence_example.json")
+    ab = np.stack([np.array(g["a"], np.float32), np.array(g["b"], np.float32)], axis=1)
+    A, B, sa, sb, tot = orc.scan_linrec_f32(ab, inclusive=True)
+    # the page's decimals are the recurrence on a = 0.9, 0.1 exactly; the
+    # float32 inputs differ from them by < 2^-24 relative
+    assert np.allclose(B, g["h"], rtol=3e-7, atol=0), B
+    assert np.allclose(A, np.cumprod(np.array(g["a"], np.float64)), rtol=3e-7, atol=0)
+    pairs = [(float(x), float(y)) for x, y in ab]
+    for t in range(len(pairs)):
+        ea, eb = _maps_fold_exact(pairs[: t + 1])
+        assert abs(B[t] - eb) <= 1e-15 * abs(eb) and abs(A[t] - ea) <= 1e-15 * abs(ea), t
+    assert tot == (A[-1], B[-1])
+    E_A, E_B, _, _, etot = orc.scan_linrec_f32(ab, inclusive=False)
+    assert (E_A[0], E_B[0]) == (1.0, 0.0)
+    assert np.array_equal(E_A[1:], A[:-1]) and np.array_equal(E_B[1:], B[:-1]) and etot == tot
+
+
+@pin
+def pin_linrec_brute_force_exact(orc):
+    """Against exact closed forms and an exact tree grouping; the fp64 oracle
+    must sit within the rounding bound 4 (t+1) 2^-53 of the magnitude sum."""
+    r = np.random.default_rng(1301)
+    for n in (0, 1, 2, 3, 7, 33, 70):
+        a = r.uniform(-1.25, 1.25, size=n).astype(np.float32)
+        b = r.standard_normal(n).astype(np.float32)
+        ab = np.stack([a, b], axis=1).reshape(n, 2)
+        A, B, sa, sb, (ta, tb) = orc.scan_linrec_f32(ab, inclusive=True)
+        E_A, E_B, esa, esb, etot = orc.scan_linrec_f32(ab, inclusive=False)
+        tree = _linrec_tree_exact([(float(x), float(y)) for x, y in ab])
+        for t in range(n):
+            xa, xb, xsa, xsb = _linrec_closed_exact(a, b, t)
+            eps = 4 * (t + 1) * 2.0 ** -53
+            assert tree[t] == (xa, xb), (n, t)
+            assert abs(Fraction(A[t]) - xa) <= eps * xsa, (n, t)
+            assert abs(Fraction(B[t]) - xb) <= eps * xsb, (n, t)
+            assert abs(Fraction(sa[t]) - xsa) <= eps * xsa and abs(Fraction(sb[t]) - xsb) <= eps * xsb, (n, t)
+            if t + 1 < n:
+                assert (E_A[t + 1], E_B[t + 1], esa[t + 1], esb[t + 1]) == (A[t], B[t], sa[t], sb[t])
+        if n:
+            assert (E_A[0], E_B[0], esa[0], esb[0]) == (1.0, 0.0, 1.0, 0.0)
+            assert (ta, tb) == etot == (A[-1], B[-1])
+        else:
+            assert (ta, tb) == etot == (1.0, 0.0)
+
+
+@pin
+def pin_linrec_closed_forms(orc):
+    r = np.random.default_rng(1302)
+    n = 100_000
+    b = r.standard_normal(n).astype(np.float32)
+    a = r.uniform(0.5, 1.0, size=n).astype(np.float32)
+    # a = 1: plain prefix sums of b; products stay 1
+    A, B, _, sb, _ = orc.scan_linrec_f32(np.stack([np.ones(n, np.float32), b], 1))
+    assert np.array_equal(B, np.cumsum(b.astype(np.float64))) and np.all(A == 1.0)
+    assert np.array_equal(sb, np.cumsum(np.abs(b.astype(np.float64))))
+    # b = 0: h stays 0, A = prefix products of a
+    A, B, sa, _, _ = orc.scan_linrec_f32(np.stack([a, np.zeros(n, np.float32)], 1))
+    assert np.all(B == 0.0) and np.array_equal(A, np.cumprod(a.astype(np.float64)))
+    assert np.array_equal(sa, A)
+    # a = 0: the recurrence forgets, h[t] = b[t]
+    A, B, _, _, _ = orc.scan_linrec_f32(np.stack([np.zeros(n, np.float32), b], 1))
+    assert np.array_equal(B, b.astype(np.float64)) and np.all(A == 0.0)
+    # constant (c, beta): geometric series beta (1 - c^(t+1)) / (1 - c)
+    for c, beta in ((0.5, 1.0), (0.99951171875, -3.0), (-0.75, 2.0)):
+        m = 5000
+        A, B, _, _, _ = orc.scan_linrec_f32(np.tile(np.array([[c, beta]], np.float32), (m, 1)))
+        t = np.arange(1, m + 1, dtype=np.float64)
+        geo = beta * (1.0 - c ** t) / (1.0 - c)
+        assert np.allclose(B, geo, rtol=1e-12, atol=1e-12 * abs(beta)), c
+        assert np.allclose(A, c ** t, rtol=1e-11, atol=1e-300), c
+    # nonnegative pairs: the magnitude scan is the scan itself
+    ab = np.stack([a, np.abs(b)], 1)
+    A, B, sa, sb, _ = orc.scan_linrec_f32(ab)
+    assert np.array_equal(A, sa) and np.array_equal(B, sb)
+    # signed inputs: the magnitude scan bounds the scan
+    A, B, sa, sb, _ = orc.scan_linrec_f32(np.stack([-a, b], 1))
+    assert np.all(np.abs(B) <= sb) and np.all(np.abs(A) <= sa)
+
+
+@pin
+def pin_linrec_order(orc):
+    """The pair operator is associative but not commutative: folding two
+    pairs must compose their maps in index order."""
+    r = np.random.default_rng(1303)
+    differ = 0
+    for _ in range(100):
+        x = r.uniform(-2, 2, size=2).astype(np.float32)
+        y = r.uniform(-2, 2, size=2).astype(np.float32)
+        _, _, _, _, xy = orc.scan_linrec_f32(np.stack([x, y]), want_abs=False)
+        _, _, _, _, yx = orc.scan_linrec_f32(np.stack([y, x]), want_abs=False)
+        ea, eb = _maps_fold_exact([(float(x[0]), float(x[1])), (float(y[0]), float(y[1]))])
+        assert abs(Fraction(xy[0]) - ea) <= 2.0 ** -52 * abs(ea)
+        assert abs(Fraction(xy[1]) - eb) <= 2.0 ** -51 * (abs(ea) + abs(eb) + 4)
+        differ += xy != yx
+    assert differ > 90
 
 
 # --------------------------------------------------------------------------

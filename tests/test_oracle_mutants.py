@@ -34,6 +34,18 @@ MUTANTS = [
      "        uint64_t xi = (uint64_t)x[i];", "        uint64_t xi = (uint64_t)(x[i] & 0xFFFFu);"),
     ("widening: total misses the last element", "int oracle_scan_u32_u64(",
      "        *total = acc;", "        *total = n ? y[n - 1] : acc;"),
+    ("linrec: b term with swapped roles", "int oracle_scan_linrec_f32(",
+     "        pb = at * pb + bt;", "        pb = pa * bt + pb;"),
+    ("linrec: dropped additive term", "int oracle_scan_linrec_f32(",
+     "        pb = at * pb + bt;", "        pb = at * pb;"),
+    ("linrec: float accumulator", "int oracle_scan_linrec_f32(",
+     "    double pa = 1.0, pb = 0.0;", "    float pa = 1.0f, pb = 0.0f;"),
+    ("linrec: exclusive form written inclusive", "int oracle_scan_linrec_f32(",
+     "        if (inclusive) {\n            A[t] = pa;", "        if (1) {\n            A[t] = pa;"),
+    ("linrec: identity (0, 0)", "int oracle_scan_linrec_f32(",
+     "    double pa = 1.0, pb = 0.0;   /* running pair */", "    double pa = 0.0, pb = 0.0;   /* running pair */"),
+    ("linrec: magnitudes without fabs", "int oracle_scan_linrec_f32(",
+     "        qb = fabs(at) * qb + fabs(bt);", "        qb = at * qb + bt;"),
     ("sum: xor instead of add", "case ORC_SUM:", "return a + b;", "return a ^ b;"),
     ("max: picks the smaller", "case ORC_MAX:", "return (b > a) ? b : a;", "return (b > a) ? a : b;"),
     ("min: identity zero", "static uint32_t u32_identity", "    case ORC_MIN:\n        return 0xFFFFFFFFu;",
