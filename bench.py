@@ -18,6 +18,9 @@ remaining kernels on their configurations:
   segmented    segmented u32 exclusive, 2^26 values, 2^16 Zipf(1.2) segments
   compact      2^26 16-byte records, Bernoulli(0.3) keep flags
   u64x         widening u32 -> u64 exclusive sum scan, n = 2^28 (12 B/element)
+  linrec       linear recurrence h = a h + b as an inclusive fp32 pair scan,
+               n = 2^27 pairs in two planes, both outputs (16 B/pair)
+  linrec-h     the same, only B = h written (12 B/pair)
   copy         plain 1 GiB copy (the practical bandwidth ceiling)
 
 Only the cpu_baseline leg runs the oracle: the sequential C scan, one host
@@ -118,6 +121,22 @@ def build_workload(name: str):
         run = lambda: dw.ps_scan(op, True, d_in, d_out, workspace=ws)  # noqa: E731
         return dict(desc="fp32 inclusive %s scan, n=2^27, N(0,1), seed 3" % op, dtype="f32", n=n,
                     bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=True, kind="f32" + op)
+    if name in ("linrec", "linrec-h"):
+        # both planes of the scanned pair (16 B per pair), or h = B only (12 B)
+        n = wl.N_LINREC
+        a, b = wl.linrec_pairs()
+        d_a, d_b = dev(a), dev(b)
+        d_ob = torch.empty(n, dtype=torch.float32, device="cuda")
+        d_oa = torch.empty(n, dtype=torch.float32, device="cuda") if name == "linrec" else None
+        ws = torch.empty(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 1, None, None),
+                         dtype=torch.uint8, device="cuda")
+        run = lambda: dw.ps_scan_linrec_f32(d_a, d_b, d_ob, out_a=d_oa, inclusive=True,  # noqa: E731
+                                            workspace=ws)
+        both = name == "linrec"
+        return dict(desc="linear recurrence h[t] = a[t] h[t-1] + b[t] as an inclusive fp32 (a, b) pair scan, "
+                         "n=2^27, a ~ U[0.9,1), b ~ N(0,1), seed 6, %s written" % ("A and B" if both else "B = h"),
+                    dtype="f32", n=n, bytes=(16.0 if both else 12.0) * n, inputs=dict(a=a, b=b), run=run,
+                    out=(d_oa, d_ob), inclusive=True, kind="linrec")
     if name == "segmented":
         values, off = wl.zipf_segments()
         n = values.size
@@ -155,6 +174,8 @@ def tile_elements(dw, w):
         return dw.ps_compact_tile_records(16)
     if w["kind"] == "copy":
         return None
+    if w["kind"] == "linrec":
+        return dw.ps_linrec_tile_elements()
     return dw.ps_tile_elements({"f32": 1, "u64": 2}.get(w["dtype"], 0))
 
 
@@ -180,6 +201,8 @@ def cpu_baseline(w, gpu_out, min_seconds: float):
             ref = orc.segmented_scan_u32(w["inputs"]["x"], w["inputs"]["off"], False)
         elif kind == "compact":
             ref = orc.compact(w["inputs"]["rec"], w["inputs"]["flags"])
+        elif kind == "linrec":
+            ref = orc.scan_linrec_f32(np.stack([w["inputs"]["a"], w["inputs"]["b"]], axis=1), True)
         times.append(time.perf_counter() - t0)
         if len(times) >= 3 and time.perf_counter() - t_start >= min_seconds:
             break
@@ -194,6 +217,13 @@ def cpu_baseline(w, gpu_out, min_seconds: float):
         y, ab, _ = ref
         ok = bool(np.all(np.abs(gpu_out.astype(np.float64) - y) <= 1e-5 * ab))
         parity = "within 1e-5*sum|x|" if ok else "MISMATCH"
+    elif kind == "linrec":
+        A, B, SA, SB, _ = ref
+        ga, gb = gpu_out
+        ok = bool(np.all(np.abs(gb.astype(np.float64) - B) <= 1e-5 * SB + 2.0 ** -100))
+        if ga is not None:
+            ok = ok and bool(np.all(np.abs(ga.astype(np.float64) - A) <= 1e-5 * SA + 2.0 ** -100))
+        parity = "within 1e-5*magnitude scan" if ok else "MISMATCH"
     elif kind == "compact":
         out, count = ref
         parity = "bit-exact" if (count == gpu_out[1] and np.array_equal(gpu_out[0][:count], out[:count])) \
@@ -258,6 +288,8 @@ def main():
     if args.cpu_seconds > 0:
         if w["kind"] == "compact":
             gpu_out = (w["out"].cpu().numpy().view(np.uint32), int(w["count"].cpu().item()))
+        elif w["kind"] == "linrec":
+            gpu_out = tuple(None if t is None else t.cpu().numpy() for t in w["out"])
         else:
             o = w["out"].cpu().numpy()
             gpu_out = o.view(np.uint32) if o.dtype == np.int32 else (o.view(np.uint64) if o.dtype == np.int64 else o)

@@ -53,6 +53,10 @@ def lib() -> ctypes.CDLL:
                  "ps_scan_exclusive_u32_u64", "ps_scan_inclusive_u32_u64"):
         getattr(L, name).argtypes = flat
         getattr(L, name).restype = i32
+    L.ps_scan_linrec_f32.argtypes = [vp, sz, vp, vp, vp, vp, u64, i32, vp, vp]
+    L.ps_scan_linrec_f32.restype = i32
+    L.ps_linrec_tile_elements.argtypes = []
+    L.ps_linrec_tile_elements.restype = u32
     L.ps_scan.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
     L.ps_scan.restype = i32
     L.ps_segmented_scan_u32.argtypes = [vp, sz, vp, u64, vp, u32, vp, i32, vp]
@@ -199,6 +203,31 @@ def ps_scan(op, inclusive, inp, out, total=None, workspace=None, stream=None, dt
     ws, have = _workspace("ps_scan", call, inp.device, workspace)
     _check("ps_scan", call(_ptr(ws), ctypes.byref(have)))
     return out
+
+
+def ps_scan_linrec_f32(a, b, out_b, out_a=None, inclusive=True, total=None, workspace=None, stream=None):
+    """Linear recurrence h[t] = a[t] h[t-1] + b[t] as a scan of (a, b) pairs:
+    out_b receives B (= h for the inclusive form), out_a (optional) the
+    products A; total (optional) two floats, the fold (A, B) of all pairs."""
+    _dev_tensor("a", a, (torch.float32,))
+    n = a.numel()
+    _dev_tensor("b", b, (torch.float32,), n)
+    _dev_tensor("out_b", out_b, (torch.float32,), n)
+    if out_a is not None:
+        _dev_tensor("out_a", out_a, (torch.float32,), n)
+    if total is not None:
+        _dev_tensor("total", total, (torch.float32,), 2)
+    s = _stream(a, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_scan_linrec_f32(ws, wsb, _ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b),  # noqa: E731
+                                                n, int(bool(inclusive)), _ptr(total), s)
+    ws, have = _workspace("ps_scan_linrec_f32", call, a.device, workspace)
+    _check("ps_scan_linrec_f32", call(_ptr(ws), ctypes.byref(have)))
+    return out_b
+
+
+def ps_linrec_tile_elements() -> int:
+    return int(lib().ps_linrec_tile_elements())
 
 
 def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None, stream=None):

@@ -31,6 +31,23 @@ template <class T> __device__ __forceinline__ T from_bits(uint32_t b);
 template <> __device__ __forceinline__ uint32_t from_bits<uint32_t>(uint32_t b) { return b; }
 template <> __device__ __forceinline__ float from_bits<float>(uint32_t b) { return __uint_as_float(b); }
 
+// (a, b) of the map h -> a h + b, the element of the linear recurrence.
+struct F2 {
+    float a, b;
+};
+
+// 64-bit values as bits, for moving them in two 32-bit halves (DPP, lane
+// reads, two-word descriptors).
+__device__ __forceinline__ uint64_t to_bits64(uint64_t v) { return v; }
+__device__ __forceinline__ uint64_t to_bits64(F2 v) {
+    return ((uint64_t)__float_as_uint(v.b) << 32) | (uint64_t)__float_as_uint(v.a);
+}
+template <class T> __device__ __forceinline__ T from_bits64(uint64_t b);
+template <> __device__ __forceinline__ uint64_t from_bits64<uint64_t>(uint64_t b) { return b; }
+template <> __device__ __forceinline__ F2 from_bits64<F2>(uint64_t b) {
+    return F2{__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+
 struct SumU32 {
     using T = uint32_t;
     __device__ static T id() { return 0u; }
@@ -95,6 +112,17 @@ struct MinF32 {
     __device__ static T op(T a, T b) { return (b < a) ? b : a; }
 };
 
+// Linear recurrence h[t] = a[t] h[t-1] + b[t] in fp32 ("Parallel Prefix Sum
+// (Scan), in depth", section "What scan builds"): x first, then y, is
+// h -> y.a (x.a h + x.b) + y.b, i.e. (x.a y.a, y.a x.b + y.b).  Associative
+// (up to rounding), not commutative.  The identity (1, 0) is exact on
+// either side, so identity padding changes no bit.
+struct LinRecF32 {
+    using T = F2;
+    __device__ static T id() { return F2{1.0f, 0.0f}; }
+    __device__ static T op(T x, T y) { return F2{x.a * y.a, __builtin_fmaf(y.a, x.b, y.b)}; }
+};
+
 // Element type of an operator's input: Op::In when it widens, else Op::T.
 template <class Op, class = void>
 struct InputOf {
@@ -119,13 +147,13 @@ template <class Op, int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ typename Op::T dpp_from(typename Op::T x) {
     using T = typename Op::T;
     if constexpr (sizeof(T) == 8) {
-        const uint64_t id = (uint64_t)Op::id(), v = (uint64_t)x;
+        const uint64_t id = to_bits64(Op::id()), v = to_bits64(x);
         const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)id, (int)(uint32_t)v, CTRL,
                                                                   ROW_MASK, 0xF, false);
         const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(id >> 32),
                                                                   (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF,
                                                                   false);
-        return (T)(((uint64_t)hi << 32) | lo);
+        return from_bits64<T>(((uint64_t)hi << 32) | lo);
     } else {
         return from_bits<T>((uint32_t)__builtin_amdgcn_update_dpp((int)to_bits(Op::id()), (int)to_bits(x), CTRL,
                                                                   ROW_MASK, 0xF, false));
@@ -153,10 +181,10 @@ __device__ __forceinline__ typename Op::T wave_shift_right(typename Op::T x) {
 template <class T>
 __device__ __forceinline__ T read_lane(T x, int lane) {
     if constexpr (sizeof(T) == 8) {
-        const uint64_t v = (uint64_t)x;
+        const uint64_t v = to_bits64(x);
         const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
         const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-        return (T)(((uint64_t)hi << 32) | lo);
+        return from_bits64<T>(((uint64_t)hi << 32) | lo);
     } else {
         return from_bits<T>((uint32_t)__builtin_amdgcn_readlane((int)to_bits(x), lane));
     }
@@ -233,7 +261,11 @@ struct Words1 {
 // takes the tile only when both state words agree.  Every state word
 // (state and distance) is published with one payload only, so agreeing
 // words hold the two halves of one value; a read that meets a publication
-// half done sees two different state words and polls again.
+// half done sees two different state words and polls again.  The one
+// exception is a fallback's install racing the owner's own first
+// publication of the same state: a reader may then take one half from
+// each.  Both are reductions of the same tile, equal for integers and each
+// a valid fp32 evaluation for floating point.
 template <class Op>
 struct Words2 {
     using T = typename Op::T;
@@ -242,15 +274,15 @@ struct Words2 {
         const uint64_t w0 = desc_poll(desc + 2 * tile), w1 = desc_poll(desc + 2 * tile + 1);
         const uint32_t s0 = (uint32_t)(w0 >> 32), s1 = (uint32_t)(w1 >> 32);
         state = (s0 == s1) ? s0 : ST_INVALID;
-        v = (T)(((uint64_t)(uint32_t)w1 << 32) | (uint32_t)w0);
+        v = from_bits64<T>(((uint64_t)(uint32_t)w1 << 32) | (uint32_t)w0);
     }
     __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
-        const uint64_t b = (uint64_t)v, sw = (uint64_t)state << 32;
+        const uint64_t b = to_bits64(v), sw = (uint64_t)state << 32;
         desc_publish(desc + 2 * (uint64_t)tile, sw | (uint32_t)b);
         desc_publish(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32));
     }
     __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
-        const uint64_t b = (uint64_t)v, sw = (uint64_t)state << 32;
+        const uint64_t b = to_bits64(v), sw = (uint64_t)state << 32;
         const bool lo = desc_install(desc + 2 * (uint64_t)tile, sw | (uint32_t)b);
         const bool hi = desc_install(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32));
         return lo || hi;

@@ -58,7 +58,7 @@ template <class Op, int D, int Q, int G, bool INCL, bool VEC>
 __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q> &f1, int par, uint32_t &slot,
                                            PipeTiles &pt, typename Op::T (&lane_excl)[Q],
                                            typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
-                                           const typename InputOf<Op>::type *in, typename Op::T *out, uint32_t n,
+                                           typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n,
                                            uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
                                            uint64_t lane_off) {
     using T = typename Op::T;
@@ -102,7 +102,7 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
         const uint64_t bp = (uint64_t)pt.prev2 * TILE;
         const bool full = bp + TILE <= n;
         bool stored = false;
-        if constexpr (PW == 2 && VEC) {
+        if constexpr (PW == 2 && VEC && std::is_pointer<typename IoOf<Op>::Dst>::value) {
             if (full) {
                 // 8-byte outputs, read back regrouped: lane l takes elements
                 // 2l and 2l+1 of each half row of 128 (they were parked by
@@ -116,13 +116,13 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const v4u w = wp[(q * 2 + (int)(lane & 1u)) * 64 + h * 32 + (int)(lane >> 1)];
-                        const T a = Op::op(pre, (T)(((uint64_t)w.y << 32) | w.x));
-                        const T b = Op::op(pre, (T)(((uint64_t)w.w << 32) | w.z));
+                        const uint64_t a = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.y << 32) | w.x)));
+                        const uint64_t b = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.w << 32) | w.z)));
                         v4u r;
                         r.x = (uint32_t)a;
-                        r.y = (uint32_t)((uint64_t)a >> 32);
+                        r.y = (uint32_t)(a >> 32);
                         r.z = (uint32_t)b;
-                        r.w = (uint32_t)((uint64_t)b >> 32);
+                        r.w = (uint32_t)(b >> 32);
                         store16(row + q * 256 + h * 128, r);
                     }
                 stored = true;
@@ -149,8 +149,8 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
 }
 
 template <class Op, int D, int Q, int G, bool INCL, bool VEC>
-__device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, const typename InputOf<Op>::type *in,
-                                          typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+__device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, typename IoOf<Op>::Src in,
+                                          typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
                                           uint32_t lane, uint32_t d) {
     using T = typename Op::T;
     constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
@@ -178,7 +178,7 @@ __device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh
 // its owner publishes first.  Runs on the control wave, rarely.
 template <class Op, uint32_t TILE>
 struct FlatFallback {
-    const typename InputOf<Op>::type *in;
+    typename IoOf<Op>::Src in;
     uint32_t n;
     __device__ DescVal<typename Op::T> operator()(uint32_t p, uint32_t lane) const {
         using T = typename Op::T;
@@ -194,7 +194,7 @@ struct FlatFallback {
 #pragma unroll
                 for (uint32_t e = 0; e < 4; ++e) {
                     const uint64_t i = base + (uint64_t)(r + k) * 256u + e;
-                    v = Op::op(v, i < n ? (T)in[i] : Op::id());
+                    v = Op::op(v, i < n ? load_elem<T>(in, i) : Op::id());
                 }
                 part[k] = v;
             }
@@ -207,7 +207,7 @@ struct FlatFallback {
 
 template <class Op, int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
-    const typename InputOf<Op>::type *in, typename Op::T *out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+    typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
     uint64_t *desc, typename Op::T *total, uint32_t *stats, int aggregate_only, LookbackCfg cfg) {
     __shared__ ScanShared<Op, D, Q> sh;
     const uint32_t lane = threadIdx.x & 63u;
@@ -276,14 +276,47 @@ inline size_t flat_ws_bytes(uint64_t tiles) {
     return kWsHeader + round_up(tiles * 8u * (uint64_t)WordsFor<Op>::WORDS, 256);
 }
 
+// Clear the workspace and launch the flat kernel on validated arguments
+// (n > 0).  VEC: every array 16-byte aligned.  An in-place call runs without
+// the fallback: a fallback reduces a predecessor from its input, which in
+// place may already hold that predecessor's outputs.
+template <class Op, bool STATS>
+ps_status launch_flat_kernel(void *ws, size_t ws_need, typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out,
+                             uint32_t n, typename Op::T *total, bool inclusive, bool vec, bool in_place,
+                             uint32_t *stats, int aggregate_only, hipStream_t s) {
+    constexpr int Q = flat_q<Op>();
+    constexpr int K = flat_k<Op>();
+    if (launch_clear(ws, ws_need, s) != hipSuccess) return PS_ERR_HIP;
+    uint32_t *ctr = ws_counter(ws);
+    uint64_t *desc = ws_desc(ws);
+    const uint32_t nt = (uint32_t)ceil_div(n, flat_tile<Op>());
+    const LookbackCfg cfg{in_place ? 0u : lookback_fallback_after(), lookback_partial()};
+    auto launch = [&](auto kernel) -> ps_status {
+        const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kFlatThreads, nt);
+        if (!grid) return PS_ERR_HIP;
+        timing_begin(s);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFlatThreads), 0, s, in, out, n, nt, ctr, desc, total, stats,
+                           aggregate_only, cfg);
+        return PS_OK;
+    };
+    ps_status r;
+    if (inclusive)
+        r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, true, STATS>)
+                : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, false, STATS>);
+    else
+        r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, true, STATS>)
+                : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, false, STATS>);
+    if (r != PS_OK) return r;
+    timing_end(s);
+    return launch_status();
+}
+
 template <class Op, bool STATS>
 ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v, uint64_t n, void *total_v,
                       bool inclusive, uint32_t *stats, hipStream_t s, typename Op::T identity,
                       int aggregate_only = 0) {
     using T = typename Op::T;
     using In = typename InputOf<Op>::type;
-    constexpr int Q = flat_q<Op>();
-    constexpr int K = flat_k<Op>();
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
     const uint64_t tiles = ceil_div(n, flat_tile<Op>());
     const size_t ws_need = flat_ws_bytes<Op>(tiles);
@@ -306,30 +339,51 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
     // exact in-place is allowed when input and output elements have one size
     const bool in_place = sizeof(In) == sizeof(T) && in_v == (const void *)out_v;
     if (!in_place && ranges_overlap(in, n * sizeof(In), out, n * sizeof(T))) return PS_ERR_ALIAS;
-    if (launch_clear(ws, ws_need, s) != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(in, 16) && aligned(out, 16);
-    uint32_t *ctr = ws_counter(ws);
-    uint64_t *desc = ws_desc(ws);
-    const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
-    auto launch = [&](auto kernel) -> ps_status {
-        const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kFlatThreads, nt);
-        if (!grid) return PS_ERR_HIP;
-        timing_begin(s);
-        const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kFlatThreads), 0, s, in, out, n32, nt, ctr, desc, total,
-                           stats, aggregate_only, cfg);
-        return PS_OK;
-    };
-    ps_status r;
-    if (inclusive)
-        r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, true, STATS>)
-                : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, false, STATS>);
-    else
-        r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, true, STATS>)
-                : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, false, STATS>);
-    if (r != PS_OK) return r;
-    timing_end(s);
-    return launch_status();
+    return launch_flat_kernel<Op, STATS>(ws, ws_need, in, out, (uint32_t)n, total, inclusive, vec, in_place, stats,
+                                         aggregate_only, s);
+}
+
+// The recurrence pairs come in two float planes and go out in two (out_a
+// optional).  Exact in-place use of either plane is allowed; any other
+// overlap between an input and an output, or between the outputs, is not.
+ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float *b, float *out_a, float *out_b,
+                        uint64_t n, bool inclusive, float *total, hipStream_t s) {
+    if (n >= (1ull << 32)) return PS_ERR_SIZE;
+    const uint64_t tiles = ceil_div(n, flat_tile<LinRecF32>());
+    const size_t ws_need = flat_ws_bytes<LinRecF32>(tiles);
+    bool query = false;
+    ps_status st = workspace_protocol(ws, ws_bytes, ws_need, &query);
+    if (st != PS_OK || query) return st;
+    F2 *tot = reinterpret_cast<F2 *>(total);
+    if (n == 0) {
+        if (!total) return PS_OK;
+        if (!aligned(total, sizeof(float))) return PS_ERR_ALIGNMENT;
+        hipLaunchKernelGGL(write_one<F2>, dim3(1), dim3(1), 0, s, tot, F2{1.0f, 0.0f});
+        return launch_status();
+    }
+    if (!a || !b || !out_b) return PS_ERR_NULL;
+    if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out_b, 4) || (out_a && !aligned(out_a, 4)) ||
+        (total && !aligned(total, 4)))
+        return PS_ERR_ALIGNMENT;
+    const uint64_t bytes = n * sizeof(float);
+    const float *ins[2] = {a, b};
+    float *outs[2] = {out_a, out_b};
+    bool in_place = false;
+    for (int o = 0; o < 2; ++o) {
+        if (!outs[o]) continue;
+        for (int i = 0; i < 2; ++i) {
+            if (ins[i] == outs[o] && i == o) {
+                in_place = true;
+                continue;
+            }
+            if (ranges_overlap(ins[i], bytes, outs[o], bytes)) return PS_ERR_ALIAS;
+        }
+    }
+    if (out_a && ranges_overlap(out_a, bytes, out_b, bytes)) return PS_ERR_ALIAS;
+    const bool vec = aligned(a, 16) && aligned(b, 16) && aligned(out_b, 16) && (!out_a || aligned(out_a, 16));
+    return launch_flat_kernel<LinRecF32, false>(ws, ws_need, PlanesIn{a, b}, PlanesOut{out_a, out_b}, (uint32_t)n,
+                                                tot, inclusive, vec, in_place, nullptr, 0, s);
 }
 
 }  // namespace dwps
@@ -371,6 +425,14 @@ extern "C" ps_status ps_scan_inclusive_f32(void *ws, size_t *ws_bytes, const flo
     return launch_flat<SumF32, false>(ws, ws_bytes, in, out, n, total, true, nullptr,
                                       static_cast<hipStream_t>(stream), 0.0f);
 }
+
+extern "C" ps_status ps_scan_linrec_f32(void *ws, size_t *ws_bytes, const float *a, const float *b, float *out_a,
+                                        float *out_b, uint64_t n, int inclusive, float *total, void *stream) {
+    return launch_linrec(ws, ws_bytes, a, b, out_a, out_b, n, inclusive != 0, total,
+                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" uint32_t ps_linrec_tile_elements(void) { return flat_tile<LinRecF32>(); }
 
 extern "C" ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive, const void *in,
                              void *out, uint64_t n, void *total, void *stream) {

@@ -10,6 +10,8 @@
 // grid": thread-serial work first, then the warp layer, then the block layer).
 #pragma once
 
+#include <type_traits>
+
 #include "dwps_device.hpp"
 
 namespace dwps {
@@ -36,12 +38,58 @@ __device__ __forceinline__ void store16(void *p, v4u v) {
         *q = v;
 }
 
+// Where a flat scan reads and writes: one array of elements, or, for the
+// recurrence pairs, two float planes a[] and b[] (the layout in which
+// callers keep the coefficients of a linear recurrence).  Outputs go to the
+// planes of PlanesOut; its `a` may be null, then only the b plane (h[t] of
+// the inclusive scan) is written.
+struct PlanesIn {
+    const float *a, *b;
+};
+struct PlanesOut {
+    float *a, *b;
+};
+template <class Op, bool PLANES = std::is_same<typename Op::T, F2>::value>
+struct IoOf {
+    using Src = const typename InputOf<Op>::type *;
+    using Dst = typename Op::T *;
+};
+template <class Op>
+struct IoOf<Op, true> {
+    using Src = PlanesIn;
+    using Dst = PlanesOut;
+};
+
+// Four consecutive elements from a 16-byte aligned group (index g).
+template <class T, class In>
+__device__ __forceinline__ void load_group(const In *in, uint64_t g, T (&v)[4]) {
+    static_assert(sizeof(In) == 4, "16-byte loads carry four input elements");
+    const v4u r = load16(in + g);
+    v[0] = (T)from_bits<In>(r.x);
+    v[1] = (T)from_bits<In>(r.y);
+    v[2] = (T)from_bits<In>(r.z);
+    v[3] = (T)from_bits<In>(r.w);
+}
+__device__ __forceinline__ void load_group(PlanesIn in, uint64_t g, F2 (&v)[4]) {
+    const v4u ra = load16(in.a + g), rb = load16(in.b + g);
+    v[0] = F2{__uint_as_float(ra.x), __uint_as_float(rb.x)};
+    v[1] = F2{__uint_as_float(ra.y), __uint_as_float(rb.y)};
+    v[2] = F2{__uint_as_float(ra.z), __uint_as_float(rb.z)};
+    v[3] = F2{__uint_as_float(ra.w), __uint_as_float(rb.w)};
+}
+template <class T, class In>
+__device__ __forceinline__ T load_elem(const In *in, uint64_t i) {
+    return (T)in[i];
+}
+template <class T>
+__device__ __forceinline__ T load_elem(PlanesIn in, uint64_t i) {
+    return T{in.a[i], in.b[i]};
+}
+
 // Register state of one wave's span of a tile.
 template <class Op, int Q>
 struct WaveSpan {
     using T = typename Op::T;
-    using In = typename InputOf<Op>::type;  // 4-byte input elements, widened to T on load
-    static_assert(sizeof(In) == 4, "16-byte loads carry four input elements");
     T v[Q][4];  // elements, then their lane-local inclusive prefixes
 
     // Issue the loads of the span starting at element `span` (= tile base +
@@ -54,8 +102,8 @@ struct WaveSpan {
     // pad() later replaces the elements at or past n by the identity.
     // VEC: 16-byte aligned input, one 16-byte load per group; otherwise one
     // 4-byte load per element.
-    template <bool VEC>
-    __device__ __forceinline__ void load(const In *in, uint64_t span, uint32_t n, bool full, bool valid) {
+    template <bool VEC, class Src>
+    __device__ __forceinline__ void load(Src in, uint64_t span, uint32_t n, bool full, bool valid) {
         if (VEC) {
             const uint64_t last_group = ((uint64_t)n - 1u) & ~(uint64_t)3u;
 #pragma unroll
@@ -63,11 +111,7 @@ struct WaveSpan {
                 uint64_t g = span + (uint64_t)q * 256u;
                 if (!full) g = g < last_group ? g : last_group;
                 if (!valid) g = 0;
-                const v4u r = load16(in + g);
-                v[q][0] = (T)from_bits<In>(r.x);
-                v[q][1] = (T)from_bits<In>(r.y);
-                v[q][2] = (T)from_bits<In>(r.z);
-                v[q][3] = (T)from_bits<In>(r.w);
+                load_group(in, g, v[q]);
             }
         } else {
             const uint64_t last = (uint64_t)n - 1u;
@@ -78,7 +122,7 @@ struct WaveSpan {
                     uint64_t i = span + (uint64_t)q * 256u + k;
                     i = i < last ? i : last;
                     if (!valid) i = 0;
-                    v[q][k] = (T)in[i];
+                    v[q][k] = load_elem<T>(in, i);
                 }
         }
     }
@@ -150,14 +194,14 @@ __device__ __forceinline__ void finalize_span(WaveSpan<Op, Q> &s, const typename
 template <class T>
 __device__ __forceinline__ void pack16(const T (&o)[4], v4u (&w)[sizeof(T) / 4]) {
     if constexpr (sizeof(T) == 8) {
-        w[0].x = (uint32_t)o[0];
-        w[0].y = (uint32_t)(o[0] >> 32);
-        w[0].z = (uint32_t)o[1];
-        w[0].w = (uint32_t)(o[1] >> 32);
-        w[1].x = (uint32_t)o[2];
-        w[1].y = (uint32_t)(o[2] >> 32);
-        w[1].z = (uint32_t)o[3];
-        w[1].w = (uint32_t)(o[3] >> 32);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint64_t e0 = to_bits64(o[2 * h]), e1 = to_bits64(o[2 * h + 1]);
+            w[h].x = (uint32_t)e0;
+            w[h].y = (uint32_t)(e0 >> 32);
+            w[h].z = (uint32_t)e1;
+            w[h].w = (uint32_t)(e1 >> 32);
+        }
     } else {
         w[0].x = to_bits(o[0]);
         w[0].y = to_bits(o[1]);
@@ -168,10 +212,11 @@ __device__ __forceinline__ void pack16(const T (&o)[4], v4u (&w)[sizeof(T) / 4])
 template <class T>
 __device__ __forceinline__ void unpack16(const v4u (&w)[sizeof(T) / 4], T (&o)[4]) {
     if constexpr (sizeof(T) == 8) {
-        o[0] = (T)(((uint64_t)w[0].y << 32) | w[0].x);
-        o[1] = (T)(((uint64_t)w[0].w << 32) | w[0].z);
-        o[2] = (T)(((uint64_t)w[1].y << 32) | w[1].x);
-        o[3] = (T)(((uint64_t)w[1].w << 32) | w[1].z);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            o[2 * h] = from_bits64<T>(((uint64_t)w[h].y << 32) | w[h].x);
+            o[2 * h + 1] = from_bits64<T>(((uint64_t)w[h].w << 32) | w[h].z);
+        }
     } else {
         o[0] = from_bits<T>(w[0].x);
         o[1] = from_bits<T>(w[0].y);
@@ -180,27 +225,57 @@ __device__ __forceinline__ void unpack16(const v4u (&w)[sizeof(T) / 4], T (&o)[4
     }
 }
 
+// Four consecutive outputs to a 16-byte aligned group (index g), and one.
+template <class T>
+__device__ __forceinline__ void store_group(T *out, uint64_t g, const T (&o)[4]) {
+    constexpr int PW = (int)sizeof(T) / 4;  // 16-byte vectors per group of four
+    v4u w[PW];
+    pack16<T>(o, w);
+#pragma unroll
+    for (int h = 0; h < PW; ++h) store16(out + g + 4 / PW * h, w[h]);
+}
+__device__ __forceinline__ void store_group(PlanesOut out, uint64_t g, const F2 (&o)[4]) {
+    if (out.a) {
+        v4u w;
+        w.x = __float_as_uint(o[0].a);
+        w.y = __float_as_uint(o[1].a);
+        w.z = __float_as_uint(o[2].a);
+        w.w = __float_as_uint(o[3].a);
+        store16(out.a + g, w);
+    }
+    v4u w;
+    w.x = __float_as_uint(o[0].b);
+    w.y = __float_as_uint(o[1].b);
+    w.z = __float_as_uint(o[2].b);
+    w.w = __float_as_uint(o[3].b);
+    store16(out.b + g, w);
+}
+template <class T>
+__device__ __forceinline__ void store_elem(T *out, uint64_t i, T v) {
+    out[i] = v;
+}
+__device__ __forceinline__ void store_elem(PlanesOut out, uint64_t i, F2 v) {
+    if (out.a) out.a[i] = v.a;
+    out.b[i] = v.b;
+}
+
 // Store a finalized span: out = prefix (+) v.
-template <class Op, int Q, bool VEC>
-__device__ __forceinline__ void store_final(const WaveSpan<Op, Q> &s, typename Op::T prefix, typename Op::T *out,
+template <class Op, int Q, bool VEC, class Dst>
+__device__ __forceinline__ void store_final(const WaveSpan<Op, Q> &s, typename Op::T prefix, Dst out,
                                             uint64_t span, uint32_t n, bool full) {
     using T = typename Op::T;
-    constexpr int PW = (int)sizeof(T) / 4;  // 16-byte vectors per group of four
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         T o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = Op::op(prefix, s.v[q][k]);
         if (VEC && full) {
-            v4u w[PW];
-            pack16<T>(o, w);
-#pragma unroll
-            for (int h = 0; h < PW; ++h) store16(out + span + (uint64_t)q * 256u + 4 / PW * h, w[h]);
+            store_group(out, span + (uint64_t)q * 256u, o);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint64_t i = span + (uint64_t)q * 256u + k;
-                if (i < n) out[i] = o[k];
+                if (i < n) store_elem(out, i, o[k]);
             }
         }
     }

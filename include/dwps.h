@@ -12,7 +12,8 @@
  *   [P2] "Parallel Prefix Sum (Scan), in depth": "Inclusive, exclusive and
  *        associative"; "Scanning a whole array: three grid strategies";
  *        "Use the library" (size query with a null temporary buffer);
- *        "What scan builds" (compaction); "Failure modes".
+ *        "What scan builds" (compaction, recurrence pairs); "Failure
+ *        modes".
  *   [P3] "Prefix scans and compaction": "Scan as an index generator";
  *        "Worked example: Stable stream compaction".
  *   [P5] "GPUSegmentedScan": "Prefix scans and segmented scans", "Contract",
@@ -149,6 +150,37 @@ ps_status ps_scan_inclusive_u32_u64(void *ws, size_t *ws_bytes, const uint32_t *
                                     uint64_t *out, uint64_t n, uint64_t *total,
                                     void *stream);
 
+/* Linear recurrence h[t] = a[t] h[t-1] + b[t] (h[-1] = 0) as one scan of
+ * the pairs (a[t], b[t]) under (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2),
+ * identity (1, 0) ([P2] "What scan builds"; the operator is associative but
+ * not commutative, so operands keep index order, [P2] "Failure modes").
+ *   a, b         : n floats each, the coefficients as two separate arrays
+ *                  (they may be the same array).
+ *   out_a, out_b : n floats each, the two components of the scanned pair:
+ *                  inclusive  (A[t], B[t]) = (a0,b0) (+) ... (+) (at,bt),
+ *                  so B[t] = h[t] and A[t] = a[0] ... a[t];
+ *                  exclusive  (A[0], B[0]) = (1, 0), then the inclusive
+ *                  pair of t-1.  h from another start value h0 is
+ *                  A[t] h0 + B[t].  out_a may be NULL (only B is written,
+ *                  4 bytes less traffic per element); out_b is required.
+ *                  out_a == a and/or out_b == b (exact in-place) is
+ *                  allowed; any other overlap among the four arrays, or
+ *                  between out_a and out_b, returns PS_ERR_ALIAS.
+ *   total        : optional, TWO floats (A, B) of the fold of all n pairs;
+ *                  (1, 0) when n == 0.
+ * 4-byte alignment required, 16-byte alignment of every array selects the
+ * vector path.  Arithmetic is fp32: A by products, B by fused
+ * multiply-adds, in a grouping that depends on scheduling (not bitwise
+ * reproducible).  Descriptors carry the pair as two words, like the
+ * widening scan; tiles hold ps_linrec_tile_elements() pairs.  Not
+ * reachable through ps_scan, whose one input array cannot hold two
+ * planes. */
+ps_status ps_scan_linrec_f32(void *ws, size_t *ws_bytes, const float *a,
+                             const float *b, float *out_a, float *out_b,
+                             uint64_t n, int inclusive, float *total,
+                             void *stream);
+uint32_t ps_linrec_tile_elements(void);
+
 /* Generic associative-operator scan: the same pass for any (op, dtype) pair
  * listed under ps_op, and (PS_OP_SUM, PS_U64) for the widening sum.  `in`,
  * `out` and `total` point to elements of `dtype` (uint32_t or float; for
@@ -266,7 +298,10 @@ uint32_t ps_lookback_group(void);
  *                     publish; a threshold of 1 would publish on ordinary
  *                     walks, and the extra store and the short jumps it
  *                     offers slow the scans by 10-20%.
- * Results do not depend on either setting. */
+ * Calls whose output is their input (exact in-place) never fall back: the
+ * input of a stalled predecessor may already hold its outputs.  Integer
+ * results do not depend on either setting; fp32 results stay within the
+ * same bounds (a fallback changes the grouping). */
 ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows);
 void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows);
 

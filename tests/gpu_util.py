@@ -10,6 +10,11 @@ import pytest
 TILE = 12288         # elements per tile of the segmented kernel (8 data waves x 6 x 256)
 FLAT_TILE = 12288    # elements per tile of the flat scan (8 data waves x 6 x 256)
 FLAT_GROUP = 2       # consecutive flat tiles claimed per ticket
+LINREC_TILE = 6144   # pairs per tile of the recurrence scan (8 data waves x 3 x 256)
+# Absolute floor of the recurrence tolerance: products of decays below
+# 2^-100 are past any use, and an fp32 result there may be subnormal or
+# flushed (error below 2^-126).
+LINREC_FLOOR = 2.0 ** -100
 
 
 def require_gpu():
@@ -68,3 +73,25 @@ def assert_f32_sum_close(gpu, ref64, absprefix, exclusive):
     if exclusive and gpu.size:
         assert gpu[0] == 0.0 and not np.signbit(gpu[0])
     return float((err / np.maximum(tol, 1e-300)).max()) if gpu.size else 0.0
+
+
+def assert_linrec_close(gpu_a, gpu_b, ref_a, ref_b, mag_a, mag_b, exclusive):
+    """Recurrence-pair tolerance: |gpu - ref| <= 1e-5 * (the same scan over
+    (|a|, |b|)) + 2^-100 for each component at every index; the magnitude
+    scan reduces to sum |b| when a = 1, the fp32 sum scan's bound.  An
+    exclusive output 0 must be exactly (1, 0).  gpu_a may be None (B only)."""
+    worst = 0.0
+    comps = [("B", gpu_b, ref_b, mag_b)] + ([("A", gpu_a, ref_a, mag_a)] if gpu_a is not None else [])
+    for name, g, r, m in comps:
+        err = np.abs(g.astype(np.float64) - r)
+        tol = 1e-5 * m + LINREC_FLOOR
+        bad = np.nonzero(~(err <= tol))[0]  # NaN counts as bad
+        assert bad.size == 0, ("%s: tolerance broken at %d indices, first %d: gpu %r ref %r tol %r"
+                               % (name, bad.size, bad[0], g[bad[0]], r[bad[0]], tol[bad[0]]))
+        if g.size:
+            worst = max(worst, float((err / tol).max()))
+    if exclusive and gpu_b.size:
+        assert gpu_b[0] == 0.0
+        if gpu_a is not None:
+            assert gpu_a[0] == 1.0
+    return worst

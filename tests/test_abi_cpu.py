@@ -75,6 +75,13 @@ def test_size_queries():
         assert st == 0 and need == 256 + -(-tiles * 16 // 256) * 256, n
         st2, need2 = _wsq(lib, "ps_scan", 0, 2, 0, None, None, n, None, None)
         assert st2 == 0 and need2 == need
+    ltile = lib.ps_linrec_tile_elements()
+    assert ltile == 6144
+    for n in (0, 1, ltile, ltile + 1, 1 << 27):
+        st, need = _wsq(lib, "ps_scan_linrec_f32", None, None, None, None, n, 1, None, None)
+        tiles = -(-n // ltile)
+        # two descriptor words per tile for the (a, b) payload
+        assert st == 0 and need == 256 + -(-tiles * 16 // 256) * 256, n
     stile = lib.ps_segmented_tile_elements()
     assert stile == 12288
     for n in (0, 1, stile, stile + 1, 1 << 26, (1 << 32) - 1):
@@ -140,6 +147,34 @@ def test_argument_errors_widening():
         assert _call_flat(lib, fn, big, A + 48, A, 10) == PS_ERR_ALIAS   # in inside out
         assert _call_flat(lib, fn, big, A, B + 4, 10) == PS_ERR_ALIGNMENT  # out not 8-byte aligned
         assert _call_flat(lib, fn, big, A, B, 10, total=B + 4096 + 4) == PS_ERR_ALIGNMENT
+
+
+def test_argument_errors_linrec():
+    lib = _lib()
+    PS_ERR_NULL, PS_ERR_ALIAS, PS_ERR_SIZE, PS_ERR_WORKSPACE, PS_ERR_ALIGNMENT = 1, 2, 3, 4, 7
+    C, D = 0x60000000, 0x80000000
+    big = 1 << 30
+
+    def call(a, b, out_a, out_b, n, total=None, ws_bytes=big):
+        wsb = ctypes.c_size_t(ws_bytes)
+        v = lambda p: ctypes.c_void_p(p) if p else None  # noqa: E731
+        return lib.ps_scan_linrec_f32(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), v(a), v(b), v(out_a), v(out_b),
+                                      n, 1, v(total), None)
+
+    assert call(A, B, C, D, 1 << 32) == PS_ERR_SIZE
+    assert call(A, B, C, D, 100000, ws_bytes=16) == PS_ERR_WORKSPACE
+    assert call(None, B, C, D, 10) == PS_ERR_NULL
+    assert call(A, None, C, D, 10) == PS_ERR_NULL
+    assert call(A, B, C, None, 10) == PS_ERR_NULL          # out_b is required, out_a is not
+    assert call(A + 2, B, C, D, 10) == PS_ERR_ALIGNMENT
+    assert call(A, B, C + 1, D, 10) == PS_ERR_ALIGNMENT
+    assert call(A, B, C, D, 10, total=D + 4096 + 2) == PS_ERR_ALIGNMENT
+    assert call(A, B, C, A, 10) == PS_ERR_ALIAS            # B plane written over a
+    assert call(A, B, B, D, 10) == PS_ERR_ALIAS            # A plane written over b
+    assert call(A, B, None, B + 4, 10) == PS_ERR_ALIAS     # partial overlap with b
+    assert call(A, B, C, C + 36, 10) == PS_ERR_ALIAS       # the two outputs overlap
+    assert call(A, B, C, C, 10) == PS_ERR_ALIAS
+    assert call(None, None, None, None, 0) == 0             # n == 0 without a total: nothing to do
 
 
 def test_argument_errors_segmented_and_compact():

@@ -15,6 +15,8 @@ Workloads (sizes as named):
   * fp32 sum / max scan, n = 2^27, values ~ N(0, 1)               (seed 3)
   * compaction, 2^26 records of 16 bytes {u32 id, u32 key, f32 a, f32 b},
     keep flag ~ Bernoulli(0.3)                                    (seed 4)
+  * linear recurrence h[t] = a[t] h[t-1] + b[t], n = 2^27 pairs as two fp32
+    planes: decays a uniform in [0.9, 1), inputs b ~ N(0, 1)      (seed 6)
   * segmented u32 scan, 2^26 values uniform in [0, 1023], 2^16 CSR segments:
     10% empty, one holding 25% of the elements, the rest with rank-size
     Zipf(s = 1.2) lengths                                         (seed 5)
@@ -28,6 +30,7 @@ SEED_LARGE_U32 = 2
 SEED_F32 = 3
 SEED_COMPACT = 4
 SEED_SEGMENTED = 5
+SEED_LINREC = 6
 
 N_SMALL_U32 = 1 << 20
 N_LARGE_U32 = 1 << 28
@@ -36,6 +39,7 @@ N_F32 = 1 << 27
 N_COMPACT = 1 << 26
 N_SEGMENTED = 1 << 26
 NUM_SEGMENTS = 1 << 16
+N_LINREC = 1 << 27
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -76,6 +80,16 @@ def large_u32(n: int = N_LARGE_U32, seed: int = SEED_LARGE_U32) -> np.ndarray:
 def f32_normal(n: int = N_F32, seed: int = SEED_F32) -> np.ndarray:
     """fp32 scan input, n = 2^27, values ~ N(0, 1)."""
     return normal_f32(n, seed)
+
+
+def linrec_pairs(n: int = N_LINREC, seed: int = SEED_LINREC, a_lo: float = 0.9, a_hi: float = 1.0):
+    """Return (a, b), two fp32 planes of n recurrence coefficients: a uniform
+    in [a_lo, a_hi) (the per-step decay of a recurrent state; a_lo < 0 gives
+    signed multipliers), b ~ N(0, 1) (the per-step input)."""
+    g = rng(seed)
+    a = g.uniform(a_lo, a_hi, size=n).astype(np.float32)
+    b = g.standard_normal(n, dtype=np.float32)
+    return a, b
 
 
 RECORD_DTYPE = np.dtype([("id", "<u4"), ("key", "<u4"), ("a", "<f4"), ("b", "<f4")])
