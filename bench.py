@@ -18,6 +18,9 @@ remaining kernels on their configurations:
   segmented    segmented u32 exclusive, 2^26 values, 2^16 Zipf(1.2) segments
   compact      2^26 16-byte records, Bernoulli(0.3) keep flags
   u64x         widening u32 -> u64 exclusive sum scan, n = 2^28 (12 B/element)
+  u32s         the small configuration, n = 2^20 values in [0, 15] (seed 1),
+               through the default entry point (its two-level form)
+  u32s-single-pass   the same with the single-pass form forced
   linrec       linear recurrence h = a h + b as an inclusive fp32 pair scan,
                n = 2^27 pairs in two planes, both outputs (16 B/pair)
   linrec-h     the same, only B = h written (12 B/pair)
@@ -82,6 +85,26 @@ def build_workload(name: str):
             a = a.view(np.int32)
         return torch.from_numpy(a).to("cuda")
 
+    if name in ("u32s", "u32s-single-pass"):
+        # the small configuration: the flat entry point runs its two-level
+        # form here; the second name forces the single-pass form for contrast
+        n = wl.N_SMALL_U32
+        x = wl.small_u32()
+        d_in, d_out = dev(x), torch.empty(n, dtype=torch.int32, device="cuda")
+        if name == "u32s":
+            ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None),
+                             dtype=torch.uint8, device="cuda")
+            run = lambda: dw.ps_scan_exclusive_u32(d_in, d_out, workspace=ws)  # noqa: E731
+            form = "default entry point (two-level form at this size)"
+        else:
+            ws = torch.empty(dw.workspace_bytes("ps_scan_single_pass", 0, 0, 0, None, None, n, None, None),
+                             dtype=torch.uint8, device="cuda")
+            run = lambda: dw.ps_scan_single_pass("sum", False, d_in, d_out, workspace=ws)  # noqa: E731
+            form = "single-pass form forced"
+        tile = dw.ps_two_level_tile_elements() if name == "u32s" else dw.ps_tile_elements(0)
+        return dict(desc="u32 exclusive sum scan, n=2^20, values uniform in [0,15], seed 1, " + form,
+                    dtype="u32", n=n, bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=False,
+                    kind="u32", tile=tile)
     if name in ("u32x", "u32x-ragged", "u32i", "copy"):
         n = wl.N_RAGGED_U32 if name == "u32x-ragged" else wl.N_LARGE_U32
         x = wl.large_u32()[:n]
@@ -168,6 +191,8 @@ def build_workload(name: str):
 
 def tile_elements(dw, w):
     """Elements (records) per tile of the workload's main kernel."""
+    if "tile" in w:
+        return w["tile"]
     if w["kind"] == "segmented":
         return dw.ps_segmented_tile_elements()
     if w["kind"] == "compact":

@@ -59,6 +59,16 @@ def lib() -> ctypes.CDLL:
     L.ps_linrec_tile_elements.restype = u32
     L.ps_scan.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
     L.ps_scan.restype = i32
+    L.ps_scan_two_level.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
+    L.ps_scan_two_level.restype = i32
+    L.ps_scan_single_pass.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
+    L.ps_scan_single_pass.restype = i32
+    L.ps_small_n_config.argtypes = [u64]
+    L.ps_small_n_config.restype = i32
+    L.ps_small_n_config_get.argtypes = []
+    L.ps_small_n_config_get.restype = u64
+    L.ps_two_level_tile_elements.argtypes = []
+    L.ps_two_level_tile_elements.restype = u32
     L.ps_segmented_scan_u32.argtypes = [vp, sz, vp, u64, vp, u32, vp, i32, vp]
     L.ps_segmented_scan_u32.restype = i32
     L.ps_validate_offsets.argtypes = [vp, u32, u64, vp, vp]
@@ -186,6 +196,33 @@ def ps_scan_inclusive_u32_u64(inp, out, total=None, workspace=None, stream=None)
 def ps_scan(op, inclusive, inp, out, total=None, workspace=None, stream=None, dtype=None):
     """Generic associative-operator scan; ``op`` is a PS_OP_* code or a name
     ('sum', 'max', 'min', 'and', 'or', 'xor', 'affine16')."""
+    return _generic("ps_scan", op, inclusive, inp, out, total, workspace, stream, dtype)
+
+
+def ps_scan_two_level(op, inclusive, inp, out, total=None, workspace=None, stream=None, dtype=None):
+    """The two-level (reduce-then-scan, three launches) form of ps_scan."""
+    return _generic("ps_scan_two_level", op, inclusive, inp, out, total, workspace, stream, dtype)
+
+
+def ps_scan_single_pass(op, inclusive, inp, out, total=None, workspace=None, stream=None, dtype=None):
+    """The single-pass chained form of ps_scan at every n."""
+    return _generic("ps_scan_single_pass", op, inclusive, inp, out, total, workspace, stream, dtype)
+
+
+def ps_small_n_config(max_elements: int) -> None:
+    """Largest n the flat entry points hand to the two-level form (0 = never)."""
+    _check("ps_small_n_config", lib().ps_small_n_config(int(max_elements)))
+
+
+def ps_small_n_config_get() -> int:
+    return int(lib().ps_small_n_config_get())
+
+
+def ps_two_level_tile_elements() -> int:
+    return int(lib().ps_two_level_tile_elements())
+
+
+def _generic(fn, op, inclusive, inp, out, total, workspace, stream, dtype):
     opc = OPS[op] if isinstance(op, str) else int(op)
     if dtype is None:
         dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
@@ -198,10 +235,11 @@ def ps_scan(op, inclusive, inp, out, total=None, workspace=None, stream=None, dt
     n = inp.numel()
     s = _stream(inp, stream)
     L = lib()
-    call = lambda ws, wsb: L.ps_scan(ws, wsb, opc, dtype, int(bool(inclusive)), _ptr(inp),  # noqa: E731
-                                     _ptr(out), n, _ptr(total), s)
-    ws, have = _workspace("ps_scan", call, inp.device, workspace)
-    _check("ps_scan", call(_ptr(ws), ctypes.byref(have)))
+    f = getattr(L, fn)
+    call = lambda ws, wsb: f(ws, wsb, opc, dtype, int(bool(inclusive)), _ptr(inp),  # noqa: E731
+                             _ptr(out), n, _ptr(total), s)
+    ws, have = _workspace(fn, call, inp.device, workspace)
+    _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
 

@@ -175,11 +175,13 @@ extern "C" ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_s
 namespace {
 std::atomic<uint32_t> g_fallback_after{4096u};
 std::atomic<uint32_t> g_partial{4u};
+std::atomic<uint64_t> g_small_n{1ull << 23};
 }  // namespace
 
 namespace dwps {
 uint32_t lookback_fallback_after() { return g_fallback_after.load(std::memory_order_relaxed); }
 uint32_t lookback_partial() { return g_partial.load(std::memory_order_relaxed); }
+uint64_t small_n_max() { return g_small_n.load(std::memory_order_relaxed); }
 }  // namespace dwps
 
 extern "C" ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows) {
@@ -234,3 +236,11 @@ extern "C" const char *ps_status_string(ps_status status) {
 }
 
 extern "C" const char *ps_version(void) { return "dwps 0.1 (gfx950)"; }
+
+extern "C" ps_status ps_small_n_config(uint64_t max_elements) {
+    if (max_elements > dwps::kSmallNCap) return PS_ERR_SIZE;
+    g_small_n.store(max_elements, std::memory_order_relaxed);
+    return PS_OK;
+}
+
+extern "C" uint64_t ps_small_n_config_get(void) { return g_small_n.load(std::memory_order_relaxed); }

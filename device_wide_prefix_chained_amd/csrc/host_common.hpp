@@ -64,6 +64,11 @@ uint32_t persistent_grid(const void *kernel, int block_threads, uint32_t work_it
 uint32_t lookback_fallback_after();
 uint32_t lookback_partial();
 
+// Largest n that the flat entry points hand to the two-level form
+// (ps_small_n_config), and the cap of that setting.
+constexpr uint64_t kSmallNCap = 1ull << 24;
+uint64_t small_n_max();
+
 // Kernel timing hooks: when enabled (ps_kernel_timing), timing_begin/end
 // record a HIP event pair around the main kernel of the call on `stream`.
 void timing_begin(hipStream_t stream);

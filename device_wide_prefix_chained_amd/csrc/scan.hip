@@ -35,6 +35,7 @@
 #include "host_common.hpp"
 #include "pipeline.hpp"
 #include "tile_io.hpp"
+#include "twolevel.hpp"
 
 namespace dwps {
 
@@ -276,6 +277,24 @@ inline size_t flat_ws_bytes(uint64_t tiles) {
     return kWsHeader + round_up(tiles * 8u * (uint64_t)WordsFor<Op>::WORDS, 256);
 }
 
+// Which form a flat call runs: the single-pass chained scan, the two-level
+// one, or (kAuto) the two-level one for n up to the ps_small_n_config
+// setting.  Inputs up to kSmallNCap elements get a workspace that fits
+// either form, so that a size query stays valid whatever the setting.
+enum class FlatForm { kAuto, kSinglePass, kTwoLevel };
+
+template <class Op>
+inline size_t flat_form_ws_bytes(uint64_t n, FlatForm form) {
+    const size_t single = flat_ws_bytes<Op>(ceil_div(n, flat_tile<Op>()));
+    const size_t two = tl_ws_bytes<Op>(n);
+    if (form == FlatForm::kTwoLevel) return two;
+    if (form == FlatForm::kAuto && n <= kSmallNCap) return single > two ? single : two;
+    return single;
+}
+inline bool use_two_level(uint64_t n, FlatForm form) {
+    return form == FlatForm::kTwoLevel || (form == FlatForm::kAuto && n <= small_n_max());
+}
+
 // Clear the workspace and launch the flat kernel on validated arguments
 // (n > 0).  VEC: every array 16-byte aligned.  An in-place call runs without
 // the fallback: a fallback reduces a predecessor from its input, which in
@@ -314,12 +333,12 @@ ps_status launch_flat_kernel(void *ws, size_t ws_need, typename IoOf<Op>::Src in
 template <class Op, bool STATS>
 ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v, uint64_t n, void *total_v,
                       bool inclusive, uint32_t *stats, hipStream_t s, typename Op::T identity,
-                      int aggregate_only = 0) {
+                      int aggregate_only = 0, FlatForm form = FlatForm::kAuto) {
     using T = typename Op::T;
     using In = typename InputOf<Op>::type;
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
-    const uint64_t tiles = ceil_div(n, flat_tile<Op>());
-    const size_t ws_need = flat_ws_bytes<Op>(tiles);
+    if (STATS) form = FlatForm::kSinglePass;
+    const size_t ws_need = flat_form_ws_bytes<Op>(n, form);
     bool query = false;
     ps_status st = workspace_protocol(ws, ws_bytes, ws_need, &query);
     if (st != PS_OK || query) return st;
@@ -334,12 +353,14 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
     }
     if (!in || !out) return PS_ERR_NULL;
     if (STATS && !stats) return PS_ERR_NULL;
-    if (!aligned(in, sizeof(In)) || !aligned(out, sizeof(T)) || (total && !aligned(total, sizeof(T))))
+    if (!aligned(in, sizeof(In)) || !aligned(out, sizeof(T)) || (total && !aligned(total, sizeof(T))) ||
+        !aligned(ws, 16))
         return PS_ERR_ALIGNMENT;
     // exact in-place is allowed when input and output elements have one size
     const bool in_place = sizeof(In) == sizeof(T) && in_v == (const void *)out_v;
     if (!in_place && ranges_overlap(in, n * sizeof(In), out, n * sizeof(T))) return PS_ERR_ALIAS;
     const bool vec = aligned(in, 16) && aligned(out, 16);
+    if (use_two_level(n, form)) return tl_launch<Op>(ws, in, out, (uint32_t)n, total, inclusive, vec, s);
     return launch_flat_kernel<Op, STATS>(ws, ws_need, in, out, (uint32_t)n, total, inclusive, vec, in_place, stats,
                                          aggregate_only, s);
 }
@@ -350,8 +371,7 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
 ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float *b, float *out_a, float *out_b,
                         uint64_t n, bool inclusive, float *total, hipStream_t s) {
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
-    const uint64_t tiles = ceil_div(n, flat_tile<LinRecF32>());
-    const size_t ws_need = flat_ws_bytes<LinRecF32>(tiles);
+    const size_t ws_need = flat_form_ws_bytes<LinRecF32>(n, FlatForm::kAuto);
     bool query = false;
     ps_status st = workspace_protocol(ws, ws_bytes, ws_need, &query);
     if (st != PS_OK || query) return st;
@@ -364,7 +384,7 @@ ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float 
     }
     if (!a || !b || !out_b) return PS_ERR_NULL;
     if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out_b, 4) || (out_a && !aligned(out_a, 4)) ||
-        (total && !aligned(total, 4)))
+        (total && !aligned(total, 4)) || !aligned(ws, 16))
         return PS_ERR_ALIGNMENT;
     const uint64_t bytes = n * sizeof(float);
     const float *ins[2] = {a, b};
@@ -382,6 +402,8 @@ ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float 
     }
     if (out_a && ranges_overlap(out_a, bytes, out_b, bytes)) return PS_ERR_ALIAS;
     const bool vec = aligned(a, 16) && aligned(b, 16) && aligned(out_b, 16) && (!out_a || aligned(out_a, 16));
+    if (use_two_level(n, FlatForm::kAuto))
+        return tl_launch<LinRecF32>(ws, PlanesIn{a, b}, PlanesOut{out_a, out_b}, (uint32_t)n, tot, inclusive, vec, s);
     return launch_flat_kernel<LinRecF32, false>(ws, ws_need, PlanesIn{a, b}, PlanesOut{out_a, out_b}, (uint32_t)n,
                                                 tot, inclusive, vec, in_place, nullptr, 0, s);
 }
@@ -434,43 +456,65 @@ extern "C" ps_status ps_scan_linrec_f32(void *ws, size_t *ws_bytes, const float 
 
 extern "C" uint32_t ps_linrec_tile_elements(void) { return flat_tile<LinRecF32>(); }
 
-extern "C" ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive, const void *in,
-                             void *out, uint64_t n, void *total, void *stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
+
+template <class Op>
+ps_status generic(void *ws, size_t *ws_bytes, const void *in, void *out, uint64_t n, void *total, bool inc,
+                  hipStream_t s, typename Op::T identity, FlatForm form) {
+    return launch_flat<Op, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, identity, 0, form);
+}
+
+ps_status scan_any(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive, const void *in, void *out,
+                   uint64_t n, void *total, hipStream_t s, FlatForm form) {
     const bool inc = inclusive != 0;
     if (dtype == PS_U32) {
         switch (op) {
-        case PS_OP_SUM: return launch_flat<SumU32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0u);
-        case PS_OP_MAX: return launch_flat<MaxU32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0u);
-        case PS_OP_MIN:
-            return launch_flat<MinU32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0xFFFFFFFFu);
-        case PS_OP_AND:
-            return launch_flat<AndU32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0xFFFFFFFFu);
-        case PS_OP_OR: return launch_flat<OrU32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0u);
-        case PS_OP_XOR: return launch_flat<XorU32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0u);
-        case PS_OP_AFFINE16:
-            return launch_flat<Affine16, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0x00010000u);
+        case PS_OP_SUM: return generic<SumU32>(ws, ws_bytes, in, out, n, total, inc, s, 0u, form);
+        case PS_OP_MAX: return generic<MaxU32>(ws, ws_bytes, in, out, n, total, inc, s, 0u, form);
+        case PS_OP_MIN: return generic<MinU32>(ws, ws_bytes, in, out, n, total, inc, s, 0xFFFFFFFFu, form);
+        case PS_OP_AND: return generic<AndU32>(ws, ws_bytes, in, out, n, total, inc, s, 0xFFFFFFFFu, form);
+        case PS_OP_OR: return generic<OrU32>(ws, ws_bytes, in, out, n, total, inc, s, 0u, form);
+        case PS_OP_XOR: return generic<XorU32>(ws, ws_bytes, in, out, n, total, inc, s, 0u, form);
+        case PS_OP_AFFINE16: return generic<Affine16>(ws, ws_bytes, in, out, n, total, inc, s, 0x00010000u, form);
         }
         return PS_ERR_UNSUPPORTED;
     }
     if (dtype == PS_U64) {
         if (op != PS_OP_SUM) return PS_ERR_UNSUPPORTED;
-        return launch_flat<SumU32toU64, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0ull);
+        return generic<SumU32toU64>(ws, ws_bytes, in, out, n, total, inc, s, 0ull, form);
     }
     if (dtype == PS_F32) {
         switch (op) {
-        case PS_OP_SUM: return launch_flat<SumF32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s, 0.0f);
-        case PS_OP_MAX:
-            return launch_flat<MaxF32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s,
-                                              -__builtin_huge_valf());
-        case PS_OP_MIN:
-            return launch_flat<MinF32, false>(ws, ws_bytes, in, out, n, total, inc, nullptr, s,
-                                              __builtin_huge_valf());
+        case PS_OP_SUM: return generic<SumF32>(ws, ws_bytes, in, out, n, total, inc, s, 0.0f, form);
+        case PS_OP_MAX: return generic<MaxF32>(ws, ws_bytes, in, out, n, total, inc, s, -__builtin_huge_valf(), form);
+        case PS_OP_MIN: return generic<MinF32>(ws, ws_bytes, in, out, n, total, inc, s, __builtin_huge_valf(), form);
         default: return PS_ERR_UNSUPPORTED;
         }
     }
     return PS_ERR_UNSUPPORTED;
 }
+
+}  // namespace
+
+extern "C" ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive, const void *in,
+                             void *out, uint64_t n, void *total, void *stream) {
+    return scan_any(ws, ws_bytes, op, dtype, inclusive, in, out, n, total, static_cast<hipStream_t>(stream),
+                    FlatForm::kAuto);
+}
+
+extern "C" ps_status ps_scan_single_pass(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive,
+                                         const void *in, void *out, uint64_t n, void *total, void *stream) {
+    return scan_any(ws, ws_bytes, op, dtype, inclusive, in, out, n, total, static_cast<hipStream_t>(stream),
+                    FlatForm::kSinglePass);
+}
+
+extern "C" ps_status ps_scan_two_level(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive,
+                                       const void *in, void *out, uint64_t n, void *total, void *stream) {
+    return scan_any(ws, ws_bytes, op, dtype, inclusive, in, out, n, total, static_cast<hipStream_t>(stream),
+                    FlatForm::kTwoLevel);
+}
+
+extern "C" uint32_t ps_two_level_tile_elements(void) { return kTlTile; }
 
 extern "C" ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uint32_t *in, uint32_t *out,
                                            uint64_t n, uint32_t *stats, int aggregate_only, void *stream) {

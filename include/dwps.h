@@ -32,8 +32,8 @@
  *    launched, no GPU is touched); then call again with a device buffer of at
  *    least that many bytes.  The caller owns it; its contents need no
  *    initialisation (the library clears it on `stream` each call).  Two calls
- *    in flight at once must not share a workspace.  After a call its first
- *    four uint32 words hold diagnostics: [0] tiles handed out (+ one ticket
+ *    in flight at once must not share a workspace.  After a call of the
+ *    single-pass form its first four uint32 words hold diagnostics: [0] tiles handed out (+ one ticket
  *    per workgroup), [1] error word (nonzero: a look-back hit its spin limit
  *    and the results are not valid), [2] look-back fallbacks performed,
  *    [3] PARTIAL descriptors published (counted by ps_lookback_stats_u32
@@ -189,6 +189,42 @@ uint32_t ps_linrec_tile_elements(void);
 ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
                   int inclusive, const void *in, void *out, uint64_t n,
                   void *total, void *stream);
+
+/* The two forms behind every flat entry point, callable on their own.
+ *
+ * ps_scan_single_pass: the chained scan with decoupled look-back, at every
+ * n.
+ *
+ * ps_scan_two_level: the two-level (reduce-then-scan) form ([P1] the
+ * two-level form and "When not to use it"; [P2] "Scanning a whole array:
+ * three grid strategies"): fold each tile of ps_two_level_tile_elements()
+ * elements, scan the tile totals, scan each tile again from its total's
+ * prefix.  Up to 1024 tiles the tile totals are folded by the final pass
+ * itself (two launches; one launch for a single tile); beyond, one
+ * workgroup scans them in between (three launches).  It reads the input
+ * twice (12 instead of 8 bytes per 32-bit element) but has no descriptors,
+ * look-back or workspace clear, so on small inputs it finishes sooner.  Its
+ * workspace holds one tile total per tile and no diagnostics header.
+ *
+ * Both take the arguments of ps_scan and give the same results.  The flat
+ * entry points (ps_scan, ps_scan_{ex,in}clusive_{u32,f32,u32_u64},
+ * ps_scan_linrec_f32) run the two-level form for n up to the
+ * ps_small_n_config setting and the single-pass form above it. */
+ps_status ps_scan_single_pass(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
+                              int inclusive, const void *in, void *out, uint64_t n,
+                              void *total, void *stream);
+ps_status ps_scan_two_level(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
+                            int inclusive, const void *in, void *out, uint64_t n,
+                            void *total, void *stream);
+uint32_t ps_two_level_tile_elements(void);
+
+/* Largest n that the flat entry points hand to the two-level form, for
+ * every later call of this process (default 2^23, the measured crossover on
+ * MI355X; 0 = always single-pass; above 2^24 returns PS_ERR_SIZE).  The size
+ * queries of the flat entry points do not depend on it: up to 2^24
+ * elements they report a workspace that fits either form. */
+ps_status ps_small_n_config(uint64_t max_elements);
+uint64_t ps_small_n_config_get(void);
 
 /* ---------------------------------------------------------------------------
  * Segmented uint32 sum scan over CSR offsets ([P5] "Prefix scans and

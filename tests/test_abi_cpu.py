@@ -55,33 +55,57 @@ def _wsq(lib, fn, *args):
     return st, need.value
 
 
+SMALL_N_CAP = 1 << 24   # inputs up to this size get a workspace that fits both forms
+
+
+def _two_level_need(n, elem_bytes):
+    """One tile total per 4096-element tile, at least 256 bytes."""
+    return max(256, -(-(-(-n // 4096)) * elem_bytes // 256) * 256)
+
+
+def _auto_need(n, single, elem_bytes):
+    return max(single, _two_level_need(n, elem_bytes)) if n <= SMALL_N_CAP else single
+
+
 def test_size_queries():
     lib = _lib()
     tile = lib.ps_tile_elements(0)
     assert tile == 12288
-    for n in (0, 1, tile - 1, tile, tile + 1, 1 << 20, (1 << 28) - 12345, 1 << 28):
+    for n in (0, 1, tile - 1, tile, tile + 1, 1 << 20, SMALL_N_CAP, SMALL_N_CAP + 1, (1 << 28) - 12345, 1 << 28):
         st, need = _wsq(lib, "ps_scan_exclusive_u32", None, None, n, None, None)
         tiles = -(-n // tile)
-        assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256, n
+        single = 256 + -(-tiles * 8 // 256) * 256
+        assert st == 0 and need == _auto_need(n, single, 4), n
         st2, need2 = _wsq(lib, "ps_scan", 3, 0, 1, None, None, n, None, None)
         assert st2 == 0 and need2 == need
+        st3, need3 = _wsq(lib, "ps_scan_single_pass", 3, 0, 1, None, None, n, None, None)
+        assert st3 == 0 and need3 == single
         assert lib.ps_lookback_tiles(n) == tiles
     wtile = lib.ps_tile_elements(2)
     assert wtile == 6144
-    for n in (0, 1, wtile, wtile + 1, 1 << 28):
+    for n in (0, 1, wtile, wtile + 1, SMALL_N_CAP, 1 << 28):
         st, need = _wsq(lib, "ps_scan_exclusive_u32_u64", None, None, n, None, None)
         tiles = -(-n // wtile)
         # two descriptor words per tile for the 64-bit payload
-        assert st == 0 and need == 256 + -(-tiles * 16 // 256) * 256, n
+        single = 256 + -(-tiles * 16 // 256) * 256
+        assert st == 0 and need == _auto_need(n, single, 8), n
         st2, need2 = _wsq(lib, "ps_scan", 0, 2, 0, None, None, n, None, None)
         assert st2 == 0 and need2 == need
+    ttile = lib.ps_two_level_tile_elements()
+    assert ttile == 4096
+    for n in (0, 1, ttile, ttile + 1, 1 << 28):
+        tiles = -(-n // ttile)
+        for dt, size in ((0, 4), (1, 4), (2, 8)):
+            st, need = _wsq(lib, "ps_scan_two_level", 0, dt, 0, None, None, n, None, None)
+            # one tile total per tile, nothing else
+            assert st == 0 and need == max(256, -(-tiles * size // 256) * 256), (n, dt)
     ltile = lib.ps_linrec_tile_elements()
     assert ltile == 6144
-    for n in (0, 1, ltile, ltile + 1, 1 << 27):
+    for n in (0, 1, ltile, ltile + 1, SMALL_N_CAP + 1, 1 << 27):
         st, need = _wsq(lib, "ps_scan_linrec_f32", None, None, None, None, n, 1, None, None)
         tiles = -(-n // ltile)
         # two descriptor words per tile for the (a, b) payload
-        assert st == 0 and need == 256 + -(-tiles * 16 // 256) * 256, n
+        assert st == 0 and need == _auto_need(n, 256 + -(-tiles * 16 // 256) * 256, 8), n
     stile = lib.ps_segmented_tile_elements()
     assert stile == 12288
     for n in (0, 1, stile, stile + 1, 1 << 26, (1 << 32) - 1):
@@ -130,10 +154,22 @@ def test_argument_errors_flat():
     assert lib.ps_scan_exclusive_u32(None, None, None, None, 5, None, None) == PS_ERR_NULL
     # unsupported operator / dtype pairs
     wsb = ctypes.c_size_t(big)
-    for op, dt in ((3, 1), (4, 1), (5, 1), (6, 1), (7, 0), (99, 0), (0, 3), (1, 2), (6, 2)):
-        st = lib.ps_scan(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), op, dt, 0, ctypes.c_void_p(A),
-                         ctypes.c_void_p(B), 10, None, None)
-        assert st == PS_ERR_UNSUPPORTED, (op, dt)
+    for fn in (lib.ps_scan, lib.ps_scan_two_level):
+        for op, dt in ((3, 1), (4, 1), (5, 1), (6, 1), (7, 0), (99, 0), (0, 3), (1, 2), (6, 2)):
+            st = fn(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), op, dt, 0, ctypes.c_void_p(A),
+                    ctypes.c_void_p(B), 10, None, None)
+            assert st == PS_ERR_UNSUPPORTED, (op, dt)
+    # the two-level form checks its arguments like the single-pass one
+    tl = lib.ps_scan_two_level
+    for args, code in (((A, B, 1 << 32), PS_ERR_SIZE), ((None, B, 10), PS_ERR_NULL), ((A + 2, B, 10), PS_ERR_ALIGNMENT),
+                       ((A, A + 4, 10), PS_ERR_ALIAS)):
+        a, b, n = args
+        st = tl(ctypes.c_void_p(FAKE_WS), ctypes.byref(wsb), 0, 0, 0, ctypes.c_void_p(a) if a else None,
+                ctypes.c_void_p(b), n, None, None)
+        assert st == code, args
+    small = ctypes.c_size_t(16)
+    assert tl(ctypes.c_void_p(FAKE_WS), ctypes.byref(small), 0, 0, 0, ctypes.c_void_p(A), ctypes.c_void_p(B),
+              100000, None, None) == PS_ERR_WORKSPACE
 
 
 def test_argument_errors_widening():
@@ -219,6 +255,31 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(8, dtype=torch.uint32)
     with pytest.raises(ValueError):
         d.ps_scan_exclusive_u32(x, x.clone())
+
+
+def test_small_n_config_roundtrip():
+    """Host-side setting only: no GPU is touched."""
+    import device_wide_prefix_chained_amd as d
+    old = d.ps_small_n_config_get()
+    assert old == 1 << 23
+    try:
+        d.ps_small_n_config(0)
+        assert d.ps_small_n_config_get() == 0
+        d.ps_small_n_config(SMALL_N_CAP)
+        assert d.ps_small_n_config_get() == SMALL_N_CAP
+        with pytest.raises(d.DwpsError):
+            d.ps_small_n_config(SMALL_N_CAP + 1)
+        assert d.ps_small_n_config_get() == SMALL_N_CAP
+    finally:
+        d.ps_small_n_config(old)
+    # the size query of a flat entry point does not depend on the setting
+    lib = _lib()
+    sizes = []
+    for setting in (0, 1 << 23, SMALL_N_CAP):
+        d.ps_small_n_config(setting)
+        sizes.append(_wsq(lib, "ps_scan_exclusive_u32", None, None, 5_000_000, None, None)[1])
+    d.ps_small_n_config(old)
+    assert len(set(sizes)) == 1
 
 
 def test_lookback_config_roundtrip():

@@ -20,6 +20,16 @@ def dw():
     return require_gpu()
 
 
+@pytest.fixture(autouse=True, scope="module")
+def _single_pass_only(dw):
+    """Every call of this module runs the single-pass chained form, whatever
+    its size (the two-level form has its own tests)."""
+    old = dw.ps_small_n_config_get()
+    dw.ps_small_n_config(0)
+    yield
+    dw.ps_small_n_config(old)
+
+
 def _nan(n):
     import torch
     return torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
