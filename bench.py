@@ -17,6 +17,8 @@ remaining kernels on their configurations:
   f32          fp32 inclusive sum, n = 2^27, N(0,1)  f32max  fp32 inclusive max
   segmented    segmented u32 exclusive, 2^26 values, 2^16 Zipf(1.2) segments
   compact      2^26 16-byte records, Bernoulli(0.3) keep flags
+  compact-staged  the same as two passes (flag scan, then scatter): the
+               ablation of the fused kernel
   u64x         widening u32 -> u64 exclusive sum scan, n = 2^28 (12 B/element)
   u32s         the small configuration, n = 2^20 values in [0, 15] (seed 1),
                through the default entry point (its two-level form)
@@ -172,20 +174,27 @@ def build_workload(name: str):
                          "(10% empty, one with 25% of the elements, rank-size Zipf(1.2)), seed 5",
                     dtype="u32", n=n, bytes=8.0 * n + 4.0 * off.size, inputs=dict(x=values, off=off),
                     run=run, out=d_out, inclusive=False, kind="segmented")
-    if name == "compact":
+    if name in ("compact", "compact-staged"):
+        staged = name == "compact-staged"
         rec, flags = wl.compaction_records()
         n = flags.size
         kept = int(flags.sum())
         d_r, d_f = dev(rec), dev(flags)
         d_out = torch.empty_like(d_r)
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
-        ws = torch.empty(dw.workspace_bytes("ps_compact", None, 16, None, n, None, None, None),
+        fn = "ps_compact_staged" if staged else "ps_compact"
+        ws = torch.empty(dw.workspace_bytes(fn, None, 16, None, n, None, None, None),
                          dtype=torch.uint8, device="cuda")
-        run = lambda: dw.ps_compact(d_r, d_f, d_out, cnt, workspace=ws)  # noqa: E731
+        f = getattr(dw, fn)
+        run = lambda: f(d_r, d_f, d_out, cnt, workspace=ws)  # noqa: E731
+        # staged: flag scan (1 B read, 4 B written) + scatter (1 + 4 + 16 B read)
+        # on top of the 16 B written per kept record
+        per = (1.0 + 4.0 + 1.0 + 4.0 + 16.0) if staged else 17.0
         return dict(desc="stream compaction of 2^26 16-byte records {u32 id, u32 key, f32 a, f32 b}, "
-                         "keep ~ Bernoulli(0.3), seed 4", dtype="u32", n=n,
-                    bytes=17.0 * n + 16.0 * kept + 8.0, inputs=dict(rec=rec, flags=flags), run=run,
-                    out=d_out, count=cnt, inclusive=False, kind="compact")
+                         "keep ~ Bernoulli(0.3), seed 4" + (", staged: flag scan then scatter" if staged else ""),
+                    dtype="u32", n=n, bytes=per * n + 16.0 * kept + 8.0, inputs=dict(rec=rec, flags=flags),
+                    run=run, out=d_out, count=cnt, inclusive=False, kind="compact",
+                    timed_per_step=2 if staged else 1)
     raise SystemExit("unknown workload %r" % name)
 
 
@@ -300,7 +309,8 @@ def main():
     dw.ps_kernel_timing(False)
 
     ms_per_step = elapsed * 1e3 / args.steps
-    kernel_ms = kernel_ms_total / max(launches, 1)
+    # kernels timed per call: their HIP-event pairs add up to one step
+    kernel_ms = kernel_ms_total / max(launches, 1) * w.get("timed_per_step", 1)
     n = w["n"]
     value = n / (ms_per_step * 1e-3) / 1e9
     call_gbs = w["bytes"] / (ms_per_step * 1e-3) / 1e9

@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.ps_validate_offsets.restype = i32
     L.ps_compact.argtypes = [vp, sz, vp, u32, vp, u64, vp, vp, vp]
     L.ps_compact.restype = i32
+    L.ps_compact_staged.argtypes = [vp, sz, vp, u32, vp, u64, vp, vp, vp]
+    L.ps_compact_staged.restype = i32
     L.ps_copy_u32.argtypes = [vp, vp, u64, vp]
     L.ps_copy_u32.restype = i32
     L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
@@ -321,6 +323,15 @@ def ps_compact(records, flags, out, num_selected, workspace=None, stream=None):
     """records: (n,) or (n, k) tensor whose rows are the records (4, 8 or 16
     bytes); flags: (n,) uint8/bool; out: same shape as records;
     num_selected: one int64/uint64 element on the device."""
+    return _compact("ps_compact", records, flags, out, num_selected, workspace, stream)
+
+
+def ps_compact_staged(records, flags, out, num_selected, workspace=None, stream=None):
+    """ps_compact computed as a flag scan followed by a scatter (two passes)."""
+    return _compact("ps_compact_staged", records, flags, out, num_selected, workspace, stream)
+
+
+def _compact(fn, records, flags, out, num_selected, workspace, stream):
     _dev_tensor("records", records)
     _dev_tensor("flags", flags, (torch.uint8, torch.bool))
     _dev_tensor("out", out)
@@ -336,10 +347,11 @@ def ps_compact(records, flags, out, num_selected, workspace=None, stream=None):
     rb = records.element_size() * row
     s = _stream(flags, stream)
     L = lib()
-    call = lambda ws, wsb: L.ps_compact(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa: E731
-                                        _ptr(out), _ptr(num_selected), s)
-    ws, have = _workspace("ps_compact", call, flags.device, workspace)
-    _check("ps_compact", call(_ptr(ws), ctypes.byref(have)))
+    f = getattr(L, fn)
+    call = lambda ws, wsb: f(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa: E731
+                             _ptr(out), _ptr(num_selected), s)
+    ws, have = _workspace(fn, call, flags.device, workspace)
+    _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
 

@@ -123,6 +123,21 @@ struct LinRecF32 {
     __device__ static T op(T x, T y) { return F2{x.a * y.a, __builtin_fmaf(y.a, x.b, y.b)}; }
 };
 
+// A keep flag of a compaction: one byte, nonzero = keep; it converts to 1
+// or 0 ("Prefix scans and compaction", "Scan as an index generator").
+struct Flag8 {
+    uint8_t v;
+    __device__ explicit operator uint32_t() const { return v != 0 ? 1u : 0u; }
+};
+// Count of kept flags before each position: the offsets of a staged
+// compaction.
+struct CountFlags {
+    using T = uint32_t;
+    using In = Flag8;
+    __device__ static T id() { return 0u; }
+    __device__ static T op(T a, T b) { return a + b; }
+};
+
 // Element type of an operator's input: Op::In when it widens, else Op::T.
 template <class Op, class = void>
 struct InputOf {

@@ -456,6 +456,61 @@ extern "C" ps_status ps_scan_linrec_f32(void *ws, size_t *ws_bytes, const float 
 
 extern "C" uint32_t ps_linrec_tile_elements(void) { return flat_tile<LinRecF32>(); }
 
+// ---------------------------------------------------------------------------
+// Staged compaction: the ablation of the fused kernel in compact.hip.  Two
+// launches of separate passes over the whole array, the composition of
+// "Prefix scans and compaction", section "Worked example: Stable stream
+// compaction": an exclusive scan of the keep flags (uint8 -> uint32
+// offsets, the flat scan above), then a scatter of every kept record to its
+// offset.  Traffic per record: 1 + 4 bytes for the scan, 1 + 4 + R for the
+// scatter, R per kept record, against the fused kernel's 1 + R and R per
+// kept record.
+// ---------------------------------------------------------------------------
+template <class Rec>
+__global__ __launch_bounds__(256) void scatter_kept_kernel(const Rec *rec, const uint8_t *flags,
+                                                          const uint32_t *offsets, uint32_t n, Rec *out,
+                                                          const uint32_t *count, uint64_t *num_selected) {
+    const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+    if (i == 0) *num_selected = *count;
+    if (i < n && flags[i] != 0) out[offsets[i]] = rec[i];
+}
+
+__global__ void write_count_zero_staged(uint64_t *p) { *p = 0ull; }
+
+template <class Rec>
+ps_status launch_compact_staged(void *ws, size_t *ws_bytes, const void *records, const uint8_t *flags, uint64_t n,
+                                void *out, uint64_t *num_selected, hipStream_t s) {
+    // workspace: [scan workspace][offsets: n uint32][count]
+    size_t scan_bytes = flat_form_ws_bytes<CountFlags>(n, FlatForm::kAuto);
+    const size_t off_at = round_up(scan_bytes, 256), cnt_at = off_at + round_up(n * 4u, 256);
+    bool query = false;
+    ps_status st = workspace_protocol(ws, ws_bytes, cnt_at + 256, &query);
+    if (st != PS_OK || query) return st;
+    if (!num_selected) return PS_ERR_NULL;
+    if (!aligned(num_selected, 8)) return PS_ERR_ALIGNMENT;
+    if (n == 0) {
+        hipLaunchKernelGGL(write_count_zero_staged, dim3(1), dim3(1), 0, s, num_selected);
+        return launch_status();
+    }
+    if (!records || !flags || !out) return PS_ERR_NULL;
+    if (!aligned(records, sizeof(Rec)) || !aligned(out, sizeof(Rec)) || !aligned(ws, 16)) return PS_ERR_ALIGNMENT;
+    const size_t bytes = n * sizeof(Rec);
+    if (ranges_overlap(out, bytes, records, bytes) || ranges_overlap(out, bytes, flags, n) ||
+        ranges_overlap(num_selected, 8, out, bytes))
+        return PS_ERR_ALIAS;
+    char *base = static_cast<char *>(ws);
+    uint32_t *offsets = reinterpret_cast<uint32_t *>(base + off_at);
+    uint32_t *count = reinterpret_cast<uint32_t *>(base + cnt_at);
+    st = launch_flat<CountFlags, false>(ws, &scan_bytes, flags, offsets, n, count, false, nullptr, s, 0u);
+    if (st != PS_OK) return st;
+    timing_begin(s);
+    hipLaunchKernelGGL(scatter_kept_kernel<Rec>, dim3((uint32_t)ceil_div(n, 256)), dim3(256), 0, s,
+                       static_cast<const Rec *>(records), flags, offsets, (uint32_t)n, static_cast<Rec *>(out), count,
+                       num_selected);
+    timing_end(s);
+    return launch_status();
+}
+
 namespace {
 
 template <class Op>
@@ -530,4 +585,17 @@ extern "C" uint32_t ps_lookback_group(void) { return (uint32_t)kTilesPerTicket; 
 
 extern "C" uint32_t ps_tile_elements(ps_dtype dtype) {
     return dtype == PS_U64 ? flat_tile<SumU32toU64>() : kFlatTile;
+}
+
+extern "C" ps_status ps_compact_staged(void *ws, size_t *ws_bytes, const void *records, uint32_t record_bytes,
+                                       const uint8_t *flags, uint64_t n, void *out, uint64_t *num_selected,
+                                       void *stream) {
+    if (n >= (1ull << 32)) return PS_ERR_SIZE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (record_bytes) {
+    case 4: return launch_compact_staged<uint32_t>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    case 8: return launch_compact_staged<uint2>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    case 16: return launch_compact_staged<uint4>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    default: return PS_ERR_UNSUPPORTED;
+    }
 }

@@ -70,6 +70,14 @@ __device__ __forceinline__ void load_group(const In *in, uint64_t g, T (&v)[4]) 
     v[2] = (T)from_bits<In>(r.z);
     v[3] = (T)from_bits<In>(r.w);
 }
+// Four keep flags: one 4-byte load (a group never leaves the 4-byte word
+// that holds its first flag).
+template <class T>
+__device__ __forceinline__ void load_group(const Flag8 *in, uint64_t g, T (&v)[4]) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(in + g);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = ((w >> (8 * k)) & 0xFFu) != 0u ? T(1) : T(0);
+}
 __device__ __forceinline__ void load_group(PlanesIn in, uint64_t g, F2 (&v)[4]) {
     const v4u ra = load16(in.a + g), rb = load16(in.b + g);
     v[0] = F2{__uint_as_float(ra.x), __uint_as_float(rb.x)};

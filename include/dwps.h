@@ -277,6 +277,19 @@ ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_segments,
 ps_status ps_compact(void *ws, size_t *ws_bytes, const void *records,
                      uint32_t record_bytes, const uint8_t *flags, uint64_t n,
                      void *out, uint64_t *num_selected, void *stream);
+
+/* Staged compaction: the same contract and results as ps_compact, computed
+ * as two separate passes instead of one fused kernel ([P3] "Worked example:
+ * Stable stream compaction": flags -> exclusive scan -> scatter): the flat
+ * scan of the keep flags (nonzero counts as 1) into uint32 offsets in the
+ * workspace, then a scatter of every kept record to its offset.  It moves
+ * 1 + 4 + 1 + 4 + record_bytes bytes per record (plus record_bytes per kept
+ * record) against the fused kernel's 1 + record_bytes, and exists to
+ * measure what the fusion saves.  The workspace holds the scan's own, n
+ * offsets and the count. */
+ps_status ps_compact_staged(void *ws, size_t *ws_bytes, const void *records,
+                            uint32_t record_bytes, const uint8_t *flags, uint64_t n,
+                            void *out, uint64_t *num_selected, void *stream);
 /* Records per tile of the compaction kernel for a record width (4, 8 or
  * 16 bytes; 0 for any other width). */
 uint32_t ps_compact_tile_records(uint32_t record_bytes);

@@ -121,6 +121,11 @@ def test_size_queries():
             tiles = -(-n // ctile)
             assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256, (rb, n)
     assert lib.ps_compact_tile_records(12) == 0
+    for n in (0, 1, 1000, 1 << 26):
+        # the flag scan's own workspace, the n offsets, the count
+        st, scan = _wsq(lib, "ps_scan_exclusive_u32", None, None, n, None, None)
+        st2, need = _wsq(lib, "ps_compact_staged", None, 16, None, n, None, None, None)
+        assert st == st2 == 0 and need == scan + -(-n * 4 // 256) * 256 + 256, n
 
 
 FAKE_WS = 0x10000000
@@ -227,8 +232,12 @@ def test_argument_errors_segmented_and_compact():
                ctypes.c_void_p(A + (1 << 20)), 0, None) == 4
     # zero segments or n == 0: nothing to do
     assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 0, ctypes.c_void_p(B + 4096), 0, None) == 0
-    comp = lib.ps_compact
     C = 0x60000000
+    for comp in (lib.ps_compact, lib.ps_compact_staged):
+        _compact_errors(comp, ws, big, C)
+
+
+def _compact_errors(comp, ws, big, C):
     for rb in (1, 2, 3, 12, 32):
         assert comp(ws, ctypes.byref(big), ctypes.c_void_p(A), rb, ctypes.c_void_p(B), 10, ctypes.c_void_p(C),
                     ctypes.c_void_p(C + 4096), None) == 5
