@@ -27,6 +27,7 @@ remaining kernels on their configurations:
                n = 2^27 pairs in two planes, both outputs (16 B/pair)
   linrec-h     the same, only B = h written (12 B/pair)
   copy         plain 1 GiB copy (the practical bandwidth ceiling)
+  read, write  its halves: 1 GiB only read, 1 GiB only written
 
 Only the cpu_baseline leg runs the oracle: the sequential C scan, one host
 thread, timed on the same input, and its output is compared with the GPU's.
@@ -107,6 +108,20 @@ def build_workload(name: str):
         return dict(desc="u32 exclusive sum scan, n=2^20, values uniform in [0,15], seed 1, " + form,
                     dtype="u32", n=n, bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=False,
                     kind="u32", tile=tile)
+    if name in ("read", "write"):
+        # the halves of the copy: 1 GiB only read, 1 GiB only written
+        n = wl.N_LARGE_U32
+        x = wl.large_u32()
+        d_in = dev(x)
+        if name == "read":
+            sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+            run = lambda: dw.ps_read_u32(d_in, sink)  # noqa: E731
+            desc = "read-only stream of 2^28 uint32 (1 GiB read)"
+        else:
+            run = lambda: dw.ps_fill_u32(d_in, 7)  # noqa: E731
+            desc = "write-only stream of 2^28 uint32 (1 GiB written)"
+        return dict(desc=desc, dtype="u32", n=n, bytes=4.0 * n, inputs=dict(x=x), run=run, out=d_in,
+                    inclusive=False, kind="copy")
     if name in ("u32x", "u32x-ragged", "u32i", "copy"):
         n = wl.N_RAGGED_U32 if name == "u32x-ragged" else wl.N_LARGE_U32
         x = wl.large_u32()[:n]

@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
     L.ps_compact_staged.restype = i32
     L.ps_copy_u32.argtypes = [vp, vp, u64, vp]
     L.ps_copy_u32.restype = i32
+    L.ps_read_u32.argtypes = [vp, u64, vp, vp]
+    L.ps_read_u32.restype = i32
+    L.ps_fill_u32.argtypes = [vp, u64, u32, vp]
+    L.ps_fill_u32.restype = i32
     L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
     L.ps_lookback_stats_u32.restype = i32
     L.ps_lookback_tiles.argtypes = [u64]
@@ -362,6 +366,18 @@ def ps_copy_u32(inp, out, stream=None):
     _dev_tensor("inp", inp, _U32_DTYPES)
     _dev_tensor("out", out, _U32_DTYPES, inp.numel())
     _check("ps_copy_u32", lib().ps_copy_u32(_ptr(inp), _ptr(out), inp.numel(), _stream(inp, stream)))
+    return out
+
+
+def ps_read_u32(inp, sink, stream=None):
+    _dev_tensor("inp", inp, _U32_DTYPES)
+    _dev_tensor("sink", sink, _U32_DTYPES, 1)
+    _check("ps_read_u32", lib().ps_read_u32(_ptr(inp), inp.numel(), _ptr(sink), _stream(inp, stream)))
+
+
+def ps_fill_u32(out, value, stream=None):
+    _dev_tensor("out", out, _U32_DTYPES)
+    _check("ps_fill_u32", lib().ps_fill_u32(_ptr(out), out.numel(), int(value) & 0xFFFFFFFF, _stream(out, stream)))
     return out
 
 

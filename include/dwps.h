@@ -303,6 +303,15 @@ uint32_t ps_compact_tile_records(uint32_t record_bytes);
  * kernel of known size used to scale the hardware byte counters. */
 ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *stream);
 
+/* The two halves of that ceiling, with the copy's access shape: a stream
+ * that only reads n uint32 (in 16-byte aligned, n a multiple of 4, else
+ * PS_ERR_ALIGNMENT; *sink, one device word, is written only in the
+ * practically impossible case that the fold of the data hits a fixed
+ * constant) and one that only writes (fills n uint32 with `value`; also a
+ * plain fill that records no memset node when captured in a graph). */
+ps_status ps_read_u32(const uint32_t *in, uint64_t n, uint32_t *sink, void *stream);
+ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void *stream);
+
 /* Exclusive uint32 sum scan (same kernel as ps_scan_exclusive_u32, built
  * with per-tile instrumentation of the look-back of [P1] "Why the work
  * stays linear").  stats: device buffer of 4 * tiles uint32, tiles reported

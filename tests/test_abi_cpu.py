@@ -249,6 +249,18 @@ def _compact_errors(comp, ws, big, C):
                 ctypes.c_void_p(C + 4096), None) == 7
 
 
+def test_argument_errors_stream_helpers():
+    lib = _lib()
+    v = ctypes.c_void_p
+    assert lib.ps_read_u32(None, 0, None, None) == 0 and lib.ps_fill_u32(None, 0, 0, None) == 0
+    assert lib.ps_read_u32(None, 16, v(B), None) == 1 and lib.ps_read_u32(v(A), 16, None, None) == 1
+    assert lib.ps_read_u32(v(A + 4), 16, v(B), None) == 7       # 16-byte alignment
+    assert lib.ps_read_u32(v(A), 18, v(B), None) == 7           # whole 16-byte vectors only
+    assert lib.ps_fill_u32(None, 16, 0, None) == 1
+    assert lib.ps_fill_u32(v(A + 2), 16, 0, None) == 7
+    assert lib.ps_fill_u32(v(A), 1 << 32, 0, None) == 3
+
+
 def test_status_strings():
     lib = _lib()
     for code in range(8):

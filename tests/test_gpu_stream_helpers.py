@@ -1,0 +1,44 @@
+"""The measurement helpers: copy, read-only and write-only streams (the
+practical bandwidth ceilings the scans are compared with)."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from gpu_util import dev, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dw():
+    return require_gpu()
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 4096, 16384, 16385, 1_000_003])
+def test_copy_and_fill(dw, n):
+    import torch
+    x = wl.full_range_u32(n, seed=n + 60)
+    d_out = torch.zeros(n, dtype=torch.int32, device="cuda")
+    say("copy", n)
+    dw.ps_copy_u32(dev(x), d_out)
+    assert np.array_equal(host(d_out), x)
+    dw.ps_fill_u32(d_out, 0xDEADBEEF)
+    assert np.all(host(d_out) == 0xDEADBEEF)
+
+
+def test_fill_unaligned(dw):
+    import torch
+    n = 10_001
+    buf = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    dw.ps_fill_u32(buf[1:], 5)
+    h = host(buf)
+    assert h[0] == 0 and np.all(h[1:] == 5)
+
+
+@pytest.mark.parametrize("n", [4, 16384, 1 << 20])
+def test_read_leaves_sink(dw, n):
+    import torch
+    x = wl.full_range_u32(n, seed=n + 61)
+    sink = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    dw.ps_read_u32(dev(x), sink)
+    assert int(host(sink)[0]) == 12345
