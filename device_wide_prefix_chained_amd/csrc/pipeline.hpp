@@ -53,12 +53,12 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
 }
 
 // Control wave: aggregates, look-back, prefixes.  Phase k runs between
-// barriers A_k and B_k, while the data waves work on their side.  The
-// look-back of a tile runs two phases after its aggregate went out, so the
-// aggregates of its neighbours and the prefixes of the tiles one generation
-// older are already published: one poll, off the critical path.  The wave
-// issues its descriptor stores only after the poll has returned, so the only
-// thing it ever waits for is its own poll.  Shared (the workgroup's LDS
+// barriers A_k and B_k, while the data waves work on their side.  A tile's
+// aggregate goes out right after barrier B of the phase that scanned it; its
+// look-back runs two phases later, so the aggregates of its neighbours and
+// the prefixes of the tiles one generation older are already published: one
+// poll, off the critical path.  Within a phase the wave polls first and
+// publishes the prefix only after the poll has returned.  Shared (the workgroup's LDS
 // block) provides wt[2][D] (the data waves' tile totals, by phase parity),
 // prefix (the exclusive prefix of prev2, read by the data waves after B) and
 // next (the tile after f2, written by data wave 0 before A).  fb reduces a
@@ -72,12 +72,9 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
     using W = WordsFor<Op>;
     T agg_prev = Op::id(), agg_prev2 = Op::id();
     T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
+    T agg_next = Op::id();   // aggregate of cur, published at the end of the phase before
     for (int par = 0;; par ^= 1) {
-        T agg = Op::id();
-        if (pt.cur < num_tiles) {
-#pragma unroll
-            for (int w = 0; w < D; ++w) agg = Op::op(agg, sh.wt[par][w]);
-        }
+        const T agg = agg_next;
         // Only the first tile of a group looks back; the next ones of the
         // group follow it through this wave's own registers.
         LookbackStats st;
@@ -102,12 +99,22 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
             }
             if (have_prev2 && !(STATS && aggregate_only))
                 W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
-            if (pt.cur < num_tiles) W::publish(desc, pt.cur, pt.cur == 0 ? ST_PREFIX : ST_AGGREGATE, agg);
         }
         incl_last = Op::op(excl, agg_prev2);
         agg_prev2 = agg_prev;
         agg_prev = agg;
         __syncthreads();  // B: prefix of prev2 is in LDS
+        // The wave totals of f1 are complete: its aggregate goes out now,
+        // while the data waves store prev2, not after the next phase's poll.
+        // The store is then well under way when that poll is issued (the
+        // in-order vmcnt makes the poll's wait cover it), and the aggregate
+        // reaches the look-backs that depend on it most of a phase earlier.
+        agg_next = Op::id();
+        if (pt.f1 < num_tiles) {
+#pragma unroll
+            for (int w = 0; w < D; ++w) agg_next = Op::op(agg_next, sh.wt[par ^ 1][w]);
+            if (lane == 0) W::publish(desc, pt.f1, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
+        }
         if (pt.drained(num_tiles)) break;
         __syncthreads();  // A: the next tile id is in LDS
         pt.advance(uniform(sh.next), num_tiles);

@@ -240,13 +240,14 @@ struct SegFallback {
     }
 };
 
-// Control wave.  Phase k: combine the wave pairs of cur into its aggregate
-// and first start; find the carry into prev2 (a look-back only when prev2
-// heads a ticket group and its first element is not a segment start; the
-// second tile of a group takes the carry-out of the first from this wave's
-// registers); publish PREFIX for prev2 if it had no start, and cur's
-// descriptor -- PREFIX at once when cur holds a start (or is tile 0),
-// AGGREGATE otherwise.  Descriptor stores go out after the poll returned.
+// Control wave.  Phase k: find the carry into prev2 (a look-back only when
+// prev2 heads a ticket group and its first element is not a segment start;
+// the second tile of a group takes the carry-out of the first from this
+// wave's registers) and publish PREFIX for prev2 if it had no start.  After
+// barrier B: combine the wave pairs of f1 (scanned in this phase) into its
+// aggregate and first start and publish its descriptor at once -- PREFIX
+// when it holds a start (or is tile 0), AGGREGATE otherwise -- most of a
+// phase before it becomes cur (see control_loop).
 template <int D, int Q, int LB_K, int G>
 __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles,
                                                  uint32_t *ctr, uint64_t *desc, LookbackCfg cfg,
@@ -254,16 +255,11 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
     SegPair a_prev{0u, 0u}, a_prev2{0u, 0u};
     uint32_t fh_prev = kSegTile, fh_prev2 = kSegTile;
     uint32_t carry_out_last = 0;  // carry out of the tile handled one phase ago
+    SegPair agg_next{0u, 0u};     // cur's aggregate and first start, published a phase ago
+    uint32_t fh_next = kSegTile;
     for (int par = 0;; par ^= 1) {
-        SegPair agg{0u, 0u};
-        uint32_t fh = kSegTile;
-        if (pt.cur < num_tiles) {
-#pragma unroll
-            for (int w = 0; w < D; ++w) {
-                agg = seg_op(agg, SegPair{sh.wf[par][w], sh.wv[par][w]});
-                fh = min(fh, sh.wfirst[par][w]);
-            }
-        }
+        const SegPair agg = agg_next;
+        const uint32_t fh = fh_next;
         uint32_t carry = 0;
         const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
         if (have_prev2) {
@@ -280,8 +276,6 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
             sh.carry = carry;
             if (have_prev2 && !a_prev2.f)
                 desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, carry + a_prev2.v));
-            if (pt.cur < num_tiles)
-                desc_publish(desc + pt.cur, desc_word((pt.cur == 0 || agg.f) ? ST_PREFIX : ST_AGGREGATE, agg.v));
         }
         carry_out_last = a_prev2.f ? a_prev2.v : carry + a_prev2.v;
         a_prev2 = a_prev;
@@ -289,6 +283,18 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
         a_prev = agg;
         fh_prev = fh;
         __syncthreads();  // B: the carry of prev2 is in LDS
+        agg_next = SegPair{0u, 0u};
+        fh_next = kSegTile;
+        if (pt.f1 < num_tiles) {
+#pragma unroll
+            for (int w = 0; w < D; ++w) {
+                agg_next = seg_op(agg_next, SegPair{sh.wf[par ^ 1][w], sh.wv[par ^ 1][w]});
+                fh_next = min(fh_next, sh.wfirst[par ^ 1][w]);
+            }
+            if (lane == 0)
+                desc_publish(desc + pt.f1,
+                             desc_word((pt.f1 == 0 || agg_next.f) ? ST_PREFIX : ST_AGGREGATE, agg_next.v));
+        }
         if (pt.drained(num_tiles)) break;
         __syncthreads();  // A: the next tile id is in LDS
         pt.advance(uniform(sh.next), num_tiles);
