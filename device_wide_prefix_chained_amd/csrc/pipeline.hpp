@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
 // prefix (the exclusive prefix of prev2, read by the data waves after B) and
 // next (the tile after f2, written by data wave 0 before A).  fb reduces a
 // tile from its input when a look-back falls back on it (see lookback).
-template <class Op, int D, int LB_K, int G, bool STATS, class Shared, class FB>
+template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, class Shared, class FB>
 __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t num_tiles,
                                              uint32_t *ctr, uint64_t *desc, typename Op::T *total,
                                              uint32_t *stats, int aggregate_only, LookbackCfg cfg,
@@ -97,8 +97,18 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
                         make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
                 }
             }
-            if (have_prev2 && !(STATS && aggregate_only))
-                W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
+            // PAIR_PREFIX: a look-back also settles the next tile of its
+            // group (prev, one phase younger, whose aggregate is out): its
+            // inclusive prefix goes out now instead of a phase later, so
+            // later look-backs meet a prefix sooner.  Measured per kernel:
+            // it pays for the flat scans with one-word descriptors only.
+            constexpr bool kPairPrefix = PAIR_PREFIX && G > 1;
+            if (!(STATS && aggregate_only)) {
+                const bool early = kPairPrefix && pt.prev2 % G != 0u && pt.prev2 - 1u != 0u;  // went out a phase ago
+                if (have_prev2 && !early) W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
+                if (kPairPrefix && look && pt.prev == pt.prev2 + 1u && pt.prev < num_tiles)
+                    W::publish(desc, pt.prev, ST_PREFIX, Op::op(Op::op(excl, agg_prev2), agg_prev));
+            }
         }
         incl_last = Op::op(excl, agg_prev2);
         agg_prev2 = agg_prev;

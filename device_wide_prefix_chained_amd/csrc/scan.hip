@@ -222,8 +222,9 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0)
-        control_loop<Op, D, LB_K, G, STATS>(pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, cfg,
-                                            FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
+        control_loop<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
+            pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, cfg,
+            FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
     else
         data_loop<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
 }
@@ -263,6 +264,9 @@ constexpr int flat_q() {
 // with two words per tile (64-bit payloads) a poll covers half as many tiles.
 template <class Op>
 constexpr int flat_k() {
+    // the recurrence's phases are long enough for a poll of two tiles per
+    // lane (four words); the widening scan's are not
+    if (std::is_same<Op, LinRecF32>::value) return 2;
     return kLookbackK / WordsFor<Op>::WORDS > 0 ? kLookbackK / WordsFor<Op>::WORDS : 1;
 }
 template <class Op>
