@@ -39,19 +39,33 @@ constexpr int kStreamThreads = 128;
 constexpr int kStreamVecs = 8;
 constexpr uint64_t kStreamBlock = (uint64_t)kStreamThreads * kStreamVecs;  // vectors per workgroup
 
-__global__ __launch_bounds__(kStreamThreads) void copy_vec_kernel(const copy_v4u *in, copy_v4u *out, uint64_t n16) {
-    const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
+// Index of vector k of this thread; in a partial last workgroup indices past
+// the end are clamped to the last vector, so that every load is issued
+// unconditionally (a load under a branch is waited for before the next one
+// is issued) and only the stores are guarded.
+__device__ __forceinline__ uint64_t stream_index(uint64_t base, int k, uint64_t n16, bool full) {
+    const uint64_t i = base + (uint64_t)k * kStreamThreads;
+    return full ? i : (i < n16 ? i : n16 - 1u);
+}
+
+template <bool FULL>
+__device__ __forceinline__ void copy_block(const copy_v4u *in, copy_v4u *out, uint64_t base, uint64_t n16) {
     copy_v4u r[kStreamVecs];
 #pragma unroll
-    for (int k = 0; k < kStreamVecs; ++k) {
-        const uint64_t i = base + (uint64_t)k * kStreamThreads;
-        if (i < n16) r[k] = __builtin_nontemporal_load(in + i);
-    }
+    for (int k = 0; k < kStreamVecs; ++k) r[k] = __builtin_nontemporal_load(in + stream_index(base, k, n16, FULL));
 #pragma unroll
     for (int k = 0; k < kStreamVecs; ++k) {
         const uint64_t i = base + (uint64_t)k * kStreamThreads;
-        if (i < n16) __builtin_nontemporal_store(r[k], out + i);
+        if (FULL || i < n16) __builtin_nontemporal_store(r[k], out + i);
     }
+}
+
+__global__ __launch_bounds__(kStreamThreads) void copy_vec_kernel(const copy_v4u *in, copy_v4u *out, uint64_t n16) {
+    const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
+    if (((uint64_t)blockIdx.x + 1u) * kStreamBlock <= n16)
+        copy_block<true>(in, out, base, n16);
+    else
+        copy_block<false>(in, out, base, n16);
 }
 
 // Read-only stream: every vector is loaded and folded; the fold is stored
@@ -59,12 +73,10 @@ __global__ __launch_bounds__(kStreamThreads) void copy_vec_kernel(const copy_v4u
 // loads without writing anything in practice.
 __global__ __launch_bounds__(kStreamThreads) void read_vec_kernel(const copy_v4u *in, uint64_t n16, uint32_t *sink) {
     const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
+    const bool full = ((uint64_t)blockIdx.x + 1u) * kStreamBlock <= n16;
     copy_v4u acc = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < kStreamVecs; ++k) {
-        const uint64_t i = base + (uint64_t)k * kStreamThreads;
-        if (i < n16) acc ^= __builtin_nontemporal_load(in + i);
-    }
+    for (int k = 0; k < kStreamVecs; ++k) acc ^= __builtin_nontemporal_load(in + stream_index(base, k, n16, full));
     if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0xF39CC060u && acc.w == 0x5CEDC834u)
         *sink = acc.x;
 }
@@ -73,10 +85,15 @@ __global__ __launch_bounds__(kStreamThreads) void read_vec_kernel(const copy_v4u
 __global__ __launch_bounds__(kStreamThreads) void fill_vec_kernel(copy_v4u *out, uint64_t n16, uint32_t value) {
     const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
     const copy_v4u v = {value, value, value, value};
+    if (((uint64_t)blockIdx.x + 1u) * kStreamBlock <= n16) {
 #pragma unroll
-    for (int k = 0; k < kStreamVecs; ++k) {
-        const uint64_t i = base + (uint64_t)k * kStreamThreads;
-        if (i < n16) __builtin_nontemporal_store(v, out + i);
+        for (int k = 0; k < kStreamVecs; ++k) __builtin_nontemporal_store(v, out + base + (uint64_t)k * kStreamThreads);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kStreamVecs; ++k) {
+            const uint64_t i = base + (uint64_t)k * kStreamThreads;
+            if (i < n16) __builtin_nontemporal_store(v, out + i);
+        }
     }
 }
 __global__ void fill_scalar_kernel(uint32_t *out, uint64_t begin, uint64_t n, uint32_t value) {
