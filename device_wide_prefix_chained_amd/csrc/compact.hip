@@ -279,7 +279,7 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
         sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
     }
     __syncthreads();
-    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
+    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0)
         control_loop<SumU32, D, LB_K, G, false, false>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr, nullptr, 0, cfg,

@@ -385,26 +385,56 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // resident or finished ("Single-Pass Prefix Scan with Decoupled Look-Back",
 // sections "Three states in a per-block descriptor" and "Where the algorithm
 // meets the hardware").
+// One poll's worth of descriptor words: lane l holds tiles
+// nearest - 64K + 1 + lK .. + K - 1.
+template <class T, int K>
+struct Window {
+    uint32_t sw[K];  // state words
+    T val[K];
+};
+
+// Issue the loads of one window.  Every load is issued before any is used
+// (no branch around a load, so one poll costs one round trip); words before
+// tile 0 read tile 0's and are replaced by the caller.
+template <class Op, int K, class W = WordsFor<Op>>
+__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane,
+                                            Window<typename Op::T, K> &win) {
+    const int64_t first = nearest - 64 * K + 1 + (int64_t)lane * K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int64_t idx = first + j;
+        W::read(desc, idx >= 0 ? idx : 0, win.sw[j], win.val[j]);
+    }
+}
+
 template <class Op, int K, bool STATS, class FB = NoFallback<typename Op::T>, class W = WordsFor<Op>>
 __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile, uint32_t lane, LookbackStats &st,
                                                    uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u},
                                                    typename Op::T own = Op::id(), bool may_publish = false,
-                                                   const FB &fb = FB{}) {
+                                                   const FB &fb = FB{},
+                                                   const Window<typename Op::T, K> *pre = nullptr) {
     using T = typename Op::T;
     T acc = Op::id();
     int64_t nearest = (int64_t)tile - 1;
     uint32_t spins = 0, stalled = 0, walked = 0;
+    bool use_pre = pre != nullptr;  // a constant wherever lookback is inlined
     for (;;) {
         const int64_t first = nearest - 64 * K + 1 + (int64_t)lane * K;
         uint32_t sw[K];  // state words
         T val[K];
-        // every load is issued before any is used (no branch around a load,
-        // so one poll costs one round trip); words before tile 0 read
-        // tile 0's and are then replaced by a PREFIX carrying the identity
+        // the first window may have been read ahead of time (an older read
+        // of a descriptor is still a valid one: states only move forward,
+        // and an unpublished word just costs another poll)
+        Window<T, K> win;
+        if (use_pre)
+            win = *pre;
+        else
+            window_load<Op, K, W>(desc, nearest, lane, win);
+        use_pre = false;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            const int64_t idx = first + j;
-            W::read(desc, idx >= 0 ? idx : 0, sw[j], val[j]);
+            sw[j] = win.sw[j];
+            val[j] = win.val[j];
         }
 #pragma unroll
         for (int j = 0; j < K; ++j) {

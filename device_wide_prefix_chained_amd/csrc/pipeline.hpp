@@ -2,10 +2,12 @@
 // kernels (flat scan, segmented scan, compaction).
 //
 // A workgroup holds one control wave and D data waves and moves each tile
-// through three phases: loads issued (phase k-1), scanned and parked in LDS
-// with its aggregate published (phase k), looked back for two phases after
-// its aggregate went out and stored (phase k+2).  PipeTiles is the window of
-// tile ids the workgroup works on in one phase.
+// through a fixed sequence of phases: loads issued, scanned (aggregate
+// published after the phase's barrier B), parked in LDS, looked back for and
+// stored -- two phases after the park (LAG 2: segmented scan, compaction),
+// or three with the look-back resolved the phase before (LAG 3: flat
+// scan).  PipeTiles is the window of tile ids the workgroup works on in one
+// phase.
 #pragma once
 
 #include <stdint.h>
@@ -14,7 +16,7 @@
 
 namespace dwps {
 
-// LDS park slots: the tiles parked during phases k, k+1 and k+2.
+// LDS park slots: the tiles parked during the last three phases.
 constexpr int kParkSlots = 3;
 
 // Tile ids of the pipeline, identical in every wave of the workgroup
@@ -23,11 +25,26 @@ constexpr int kParkSlots = 3;
 // readfirstlane, so the compiler keeps them in scalar registers and branches
 // on them with scalar branches.
 struct PipeTiles {
-    uint32_t prev2, prev, cur, f1, f2;
-    __device__ __forceinline__ bool drained(uint32_t num_tiles) const {
-        return prev < num_tiles ? false : (cur >= num_tiles && f1 >= num_tiles && f2 >= num_tiles);
+    uint32_t prev3, prev2, prev, cur, f1, f2;
+    // LAG: phases between a tile's park and its store.  The tile stored in
+    // this phase (the one looked back for) is prev2 (LAG 2) or prev3 (LAG 3).
+    template <int LAG>
+    __device__ __forceinline__ uint32_t waiting() const {
+        return LAG == 3 ? prev3 : prev2;
     }
+    template <int LAG>
+    __device__ __forceinline__ uint32_t younger() const {  // the tile one phase behind it
+        return LAG == 3 ? prev2 : prev;
+    }
+    // nothing left after this phase's store
+    template <int LAG>
+    __device__ __forceinline__ bool drained(uint32_t num_tiles) const {
+        return (LAG == 3 ? prev2 >= num_tiles : true) && prev >= num_tiles && cur >= num_tiles &&
+               f1 >= num_tiles && f2 >= num_tiles;
+    }
+    __device__ __forceinline__ bool drained(uint32_t num_tiles) const { return drained<2>(num_tiles); }
     __device__ __forceinline__ void advance(uint32_t after, uint32_t num_tiles) {
+        prev3 = prev2;
         prev2 = prev;
         prev = cur;
         cur = f1;
@@ -63,37 +80,43 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
 // prefix (the exclusive prefix of prev2, read by the data waves after B) and
 // next (the tile after f2, written by data wave 0 before A).  fb reduces a
 // tile from its input when a look-back falls back on it (see lookback).
-template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, class Shared, class FB>
+template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, int LAG = 2, class Shared, class FB>
 __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t num_tiles,
                                              uint32_t *ctr, uint64_t *desc, typename Op::T *total,
                                              uint32_t *stats, int aggregate_only, LookbackCfg cfg,
                                              const FB &fb, uint32_t lane) {
     using T = typename Op::T;
     using W = WordsFor<Op>;
-    T agg_prev = Op::id(), agg_prev2 = Op::id();
+    // aggregates of prev, prev2 and prev3 at the start of a phase
+    T agg_prev = Op::id(), agg_prev2 = Op::id(), agg_prev3 = Op::id();
     T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
     T agg_next = Op::id();   // aggregate of cur, published at the end of the phase before
     for (int par = 0;; par ^= 1) {
         const T agg = agg_next;
+        // the tile stored this phase, its aggregate, and the one behind it
+        const uint32_t wt_tile = pt.template waiting<LAG>();
+        const uint32_t young = pt.template younger<LAG>();
+        const T agg_w = LAG == 3 ? agg_prev3 : agg_prev2;
+        const T agg_y = LAG == 3 ? agg_prev2 : agg_prev;
         // Only the first tile of a group looks back; the next ones of the
         // group follow it through this wave's own registers.
         LookbackStats st;
         uint64_t t0 = 0;
         if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
         T excl = Op::id();
-        const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
-        const bool look = have_prev2 && (pt.prev2 % G == 0u || (STATS && aggregate_only));
+        const bool have_w = wt_tile < num_tiles && wt_tile != 0;
+        const bool look = have_w && (wt_tile % G == 0u || (STATS && aggregate_only));
         if (look)
-            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb);
-        else if (have_prev2)
+            excl = lookback<Op, LB_K, STATS>(desc, wt_tile, lane, st, ctr, cfg, agg_w, true, fb);
+        else if (have_w)
             excl = incl_last;
         if (lane == 0) {
             sh.prefix = excl;
-            if (pt.prev2 < num_tiles) {
-                if (total && pt.prev2 == num_tiles - 1) *total = Op::op(excl, agg_prev2);
+            if (wt_tile < num_tiles) {
+                if (total && wt_tile == num_tiles - 1) *total = Op::op(excl, agg_w);
                 if (STATS) {
                     const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-                    reinterpret_cast<uint4 *>(stats)[pt.prev2] =
+                    reinterpret_cast<uint4 *>(stats)[wt_tile] =
                         make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
                 }
             }
@@ -104,13 +127,14 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
             // it pays for the flat scans with one-word descriptors only.
             constexpr bool kPairPrefix = PAIR_PREFIX && G > 1;
             if (!(STATS && aggregate_only)) {
-                const bool early = kPairPrefix && pt.prev2 % G != 0u && pt.prev2 - 1u != 0u;  // went out a phase ago
-                if (have_prev2 && !early) W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
-                if (kPairPrefix && look && pt.prev == pt.prev2 + 1u && pt.prev < num_tiles)
-                    W::publish(desc, pt.prev, ST_PREFIX, Op::op(Op::op(excl, agg_prev2), agg_prev));
+                const bool early = kPairPrefix && wt_tile % G != 0u && wt_tile - 1u != 0u;  // went out a phase ago
+                if (have_w && !early) W::publish(desc, wt_tile, ST_PREFIX, Op::op(excl, agg_w));
+                if (kPairPrefix && look && young == wt_tile + 1u && young < num_tiles)
+                    W::publish(desc, young, ST_PREFIX, Op::op(Op::op(excl, agg_w), agg_y));
             }
         }
-        incl_last = Op::op(excl, agg_prev2);
+        incl_last = Op::op(excl, agg_w);
+        agg_prev3 = agg_prev2;
         agg_prev2 = agg_prev;
         agg_prev = agg;
         __syncthreads();  // B: prefix of prev2 is in LDS
@@ -125,7 +149,77 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
             for (int w = 0; w < D; ++w) agg_next = Op::op(agg_next, sh.wt[par ^ 1][w]);
             if (lane == 0) W::publish(desc, pt.f1, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
         }
-        if (pt.drained(num_tiles)) break;
+        if (pt.template drained<LAG>(num_tiles)) break;
+        __syncthreads();  // A: the next tile id is in LDS
+        pt.advance(uniform(sh.next), num_tiles);
+    }
+}
+
+// Control wave of the LAG 3 pipeline (the data waves store prev3): the
+// look-back of prev2 is resolved one phase before its tile is stored, and
+// its poll straddles barrier B.  Per phase: hand the data waves prev3's
+// prefix (resolved in the phase before), issue the first poll of prev2's
+// look-back, pass barrier B at once -- the data waves store while the poll
+// is in flight -- then finish the look-back, publish prev2's prefix and
+// f1's aggregate, and meet the data waves at barrier A.  The poll is as
+// fresh as in the two-phase pipeline (issued at the start of the phase that
+// resolves it); only its round trip moves off the path to barrier B.
+template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, class Shared, class FB>
+__device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t num_tiles, uint32_t *ctr,
+                                              uint64_t *desc, typename Op::T *total, uint32_t *stats,
+                                              int aggregate_only, LookbackCfg cfg, const FB &fb, uint32_t lane) {
+    using T = typename Op::T;
+    using W = WordsFor<Op>;
+    T agg_prev = Op::id(), agg_prev2 = Op::id(), agg_prev3 = Op::id();
+    T incl_last = Op::id();   // inclusive prefix of the tile resolved one phase ago
+    T excl_next = Op::id();   // exclusive prefix of prev3, resolved one phase ago
+    T agg_next = Op::id();    // aggregate of cur, published at the end of the phase before
+    constexpr bool kPairPrefix = PAIR_PREFIX && G > 1;
+    for (int par = 0;; par ^= 1) {
+        const T agg = agg_next;
+        if (lane == 0) {
+            sh.prefix = excl_next;
+            if (total && pt.prev3 == num_tiles - 1) *total = Op::op(excl_next, agg_prev3);
+        }
+        const bool have = pt.prev2 < num_tiles && pt.prev2 != 0;
+        const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
+        Window<T, LB_K> win;
+        if (look) window_load<Op, LB_K>(desc, (int64_t)pt.prev2 - 1, lane, win);
+        __syncthreads();  // B: prev3's prefix is in LDS
+        LookbackStats st;
+        uint64_t t0 = 0;
+        if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
+        T excl = Op::id();
+        if (look)
+            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb, &win);
+        else if (have)
+            excl = incl_last;
+        if (lane == 0) {
+            if (STATS && pt.prev2 < num_tiles) {
+                const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+                reinterpret_cast<uint4 *>(stats)[pt.prev2] =
+                    make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
+            }
+            if (!(STATS && aggregate_only)) {
+                const bool early = kPairPrefix && pt.prev2 % G != 0u && pt.prev2 - 1u != 0u;
+                if (have && !early) W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
+                if (kPairPrefix && look && pt.prev == pt.prev2 + 1u && pt.prev < num_tiles)
+                    W::publish(desc, pt.prev, ST_PREFIX, Op::op(Op::op(excl, agg_prev2), agg_prev));
+            }
+        }
+        // the wave totals of f1 are complete: its aggregate goes out now
+        agg_next = Op::id();
+        if (pt.f1 < num_tiles) {
+#pragma unroll
+            for (int w = 0; w < D; ++w) agg_next = Op::op(agg_next, sh.wt[par ^ 1][w]);
+            if (lane == 0) W::publish(desc, pt.f1, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
+        }
+        excl_next = excl;
+        incl_last = Op::op(excl, agg_prev2);
+        agg_prev3 = agg_prev2;
+        agg_prev2 = agg_prev;
+        agg_prev = agg;
+        if (pt.template drained<3>(num_tiles)) break;
         __syncthreads();  // A: the next tile id is in LDS
         pt.advance(uniform(sh.next), num_tiles);
     }

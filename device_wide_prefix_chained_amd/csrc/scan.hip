@@ -5,30 +5,32 @@
 //
 // Persistent, wave-specialised workgroups.  The grid holds as many
 // workgroups as the GPU keeps resident; each one loops over tiles of
-// D * Q * 256 elements taken from the atomic tile counter.  A workgroup has
-// one control wave and D data waves.  A tile passes through three phases:
+// D * Q * 256 elements taken from the atomic tile counter (two consecutive
+// tiles per ticket).  A workgroup has one control wave and D data waves and
+// moves each tile through these phases:
 //   phase k-1  its loads are issued (into a register buffer);
-//   phase k    it is scanned, its aggregate is published, and its
-//              tile-relative outputs are parked in LDS, which frees the
-//              register buffer for the loads of the tile two ahead;
-//   phase k+1  its look-back runs -- one phase after its aggregate went out,
-//              like the aggregates of the tiles around it, so the poll
-//              normally finds every word it needs -- and the data waves add
-//              the prefix to the parked outputs and store them.
-// Control wave (per phase): publish the current tile's aggregate, take the
-// ticket of the tile three ahead, look back for the previous tile, publish
-// its inclusive prefix.  Its vector-memory queue holds only descriptor
-// traffic, so a poll never waits behind a tile load.
-// Data waves (per phase): finalize the current tile into LDS, issue the loads
-// of the tile two ahead; after the barrier, store the previous tile from LDS,
-// then scan the next tile.  Up to two tiles of loads per workgroup are in
-// flight while look-backs are resolved a phase behind (a persistent
-// grid-stride loop, as in "Where the algorithm meets the hardware", with the
-// look-back joining the tiles inside one launch).  Tickets come from an
-// atomic counter, so every tile a look-back can wait on was handed out
-// earlier to a running workgroup, which finishes it without waiting on
-// anything later ("Scanning a whole array: three grid strategies"); forward
-// progress follows by induction on the smallest unfinished tile.
+//   phase k    it is scanned; after barrier B its aggregate is published;
+//   phase k+1  it is made tile-relative and, after B, parked in LDS;
+//   phase k+3  its look-back (first tile of a ticket) polls at the start of
+//              the phase -- three phases after the aggregate went out, so
+//              the poll normally finds every word it needs -- and finishes
+//              after barrier B, while the data waves store;
+//   phase k+4  the data waves add its prefix and store it.
+// Control wave (per phase): hand the data waves the prefix resolved in the
+// phase before, issue the first poll of the next look-back, pass barrier B,
+// finish the look-back and publish its prefix, publish the aggregate of the
+// tile just scanned.  Its vector-memory queue holds only descriptor traffic,
+// so a poll never waits behind a tile load.  Data waves (per phase):
+// finalize cur in registers, issue the loads of f2, scan f1; after barrier
+// B store prev3 from LDS and park cur in its slot.  Up to two tiles of loads
+// per workgroup are in flight while look-backs are resolved two phases
+// behind (a persistent grid-stride loop, as in "Where the algorithm meets
+// the hardware", with the look-back joining the tiles inside one launch).
+// Tickets come from an atomic counter, so every tile a look-back can wait on
+// was handed out earlier to a running workgroup, which finishes it without
+// waiting on anything later ("Scanning a whole array: three grid
+// strategies"); forward progress follows by induction on the smallest
+// unfinished tile.
 #include <hip/hip_runtime.h>
 
 #include "dwps_device.hpp"
@@ -50,66 +52,55 @@ struct ScanShared {
     T prefix;
 };
 
-// One phase of a data wave: `cur` holds the scanned current tile (its wave
-// totals in wt[par]), `f1` the next tile (loads in flight).  cur is parked
-// in LDS slot `slot`; slot (slot+1) % 3 holds prev2.  Data wave 0 also takes
-// the tickets: the atomic goes out at the start of the phase, ahead of the
-// wave's tile loads, and its value is needed only after barrier B.
+// One phase of a data wave.  A tile is stored three phases after its park:
+// cur is finalized (made tile-relative) in registers at the start of the
+// phase and held until after barrier B; then the wave stores prev3 from slot
+// `slot` and parks cur in the same slot (each wave reads and writes only its
+// own part of a slot, in program order), so three slots and three register
+// buffers cover the pipeline.  Buffers: `hold` = cur, `sc` = f1 (scanned
+// now), `ld` = free, takes the loads of f2.  Straight-line code whether or
+// not the tiles exist (absent tiles are dummy loads of the first group and
+// harmless arithmetic), so that the compiler sees one fixed sequence of
+// loads and keeps two tiles in flight.  Data wave 0 also takes the tickets:
+// the atomic goes out at the start of the phase, ahead of the wave's tile
+// loads, and its value is needed only after barrier B.
 template <class Op, int D, int Q, int G, bool INCL, bool VEC>
-__device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q> &f1, int par, uint32_t &slot,
-                                           PipeTiles &pt, typename Op::T (&lane_excl)[Q],
-                                           typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
-                                           typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n,
-                                           uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
-                                           uint64_t lane_off) {
+__device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, Q> &sc, WaveSpan<Op, Q> &ld, int par,
+                                            uint32_t &slot, PipeTiles &pt, typename Op::T (&lane_excl)[Q],
+                                            typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
+                                            typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n,
+                                            uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
+                                            uint64_t lane_off) {
     using T = typename Op::T;
     constexpr uint32_t TILE = (uint32_t)D * (uint32_t)Q * 256u;
-    // the tile after f2: the next one of its group, or the first of a new
-    // group taken from the ticket counter
+    constexpr int PW = ScanShared<Op, D, Q>::PW;
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
     if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
-    constexpr int PW = ScanShared<Op, D, Q>::PW;
-    const uint32_t old_slot = next_slot(slot);
-    // group (q, lane) of wave d parks as PW vectors at ((d*Q + q)*PW + h)*64 + lane
-    v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
-    const v4u *theirs = &sh.park[old_slot][(uint32_t)d * Q * PW * 64u + lane];
-    // Straight-line code whether or not the tiles exist (absent tiles are
-    // dummy loads of the first group and harmless arithmetic), so that the
-    // compiler sees one fixed sequence of loads and keeps two tiles in flight.
-    // Make cur tile-relative and park it.
+    // cur tile-relative, in registers (its wave totals are in wt[par])
     T wave_prefix = Op::id();
 #pragma unroll
     for (int w = 0; w < D; ++w)
         if ((uint32_t)w < d) wave_prefix = Op::op(wave_prefix, sh.wt[par][w]);
-    finalize_span<Op, Q, INCL>(cur, lane_excl, row_prefix, wave_prefix);
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        v4u w[PW];
-        pack16<T>(cur.v[q], w);
-#pragma unroll
-        for (int h = 0; h < PW; ++h) mine[(q * PW + h) * 64] = w[h];
-    }
-    // the freed registers take the tile two ahead
+    finalize_span<Op, Q, INCL>(hold, lane_excl, row_prefix, wave_prefix);
+    // the free buffer takes the tile two ahead
     const uint64_t b2 = (uint64_t)pt.f2 * TILE;
-    cur.template load<VEC>(in, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
+    ld.template load<VEC>(in, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
     // scan the next tile while the control wave looks back
     const uint64_t b1 = (uint64_t)pt.f1 * TILE;
-    f1.pad(b1 + lane_off, n, b1 + TILE <= n);
-    const T wt = scan_span<Op, Q>(f1, lane_excl, row_prefix);
+    sc.pad(b1 + lane_off, n, b1 + TILE <= n);
+    const T wt = scan_span<Op, Q>(sc, lane_excl, row_prefix);
     if (lane == 0) sh.wt[par ^ 1][d] = wt;
     __syncthreads();  // B
-    if (pt.prev2 < num_tiles) {
-        const uint64_t bp = (uint64_t)pt.prev2 * TILE;
+    v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
+    if (pt.prev3 < num_tiles) {
+        const uint64_t bp = (uint64_t)pt.prev3 * TILE;
         const bool full = bp + TILE <= n;
         bool stored = false;
         if constexpr (PW == 2 && VEC && std::is_pointer<typename IoOf<Op>::Dst>::value) {
             if (full) {
-                // 8-byte outputs, read back regrouped: lane l takes elements
-                // 2l and 2l+1 of each half row of 128 (they were parked by
-                // lane l/2, in its half l%2), so every 16-byte store
-                // instruction of the wave writes 1 KiB contiguous
-                const v4u *wp = &sh.park[old_slot][(uint32_t)d * Q * PW * 64u];
+                // 8-byte outputs read back regrouped (see data_phase)
+                const v4u *wp = &sh.park[slot][(uint32_t)d * Q * PW * 64u];
                 T *row = out + bp + (uint64_t)d * Q * 256u + 2u * lane;
                 const T pre = sh.prefix;
 #pragma unroll
@@ -135,41 +126,54 @@ __device__ __forceinline__ bool data_phase(WaveSpan<Op, Q> &cur, WaveSpan<Op, Q>
             for (int q = 0; q < Q; ++q) {
                 v4u w[PW];
 #pragma unroll
-                for (int h = 0; h < PW; ++h) w[h] = theirs[(q * PW + h) * 64];
+                for (int h = 0; h < PW; ++h) w[h] = mine[(q * PW + h) * 64];
                 unpack16<T>(w, old.v[q]);
             }
             store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, full);
         }
     }
-    if (pt.drained(num_tiles)) return true;
+    // park cur where prev3 was
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        v4u w[PW];
+        pack16<T>(hold.v[q], w);
+#pragma unroll
+        for (int h = 0; h < PW; ++h) mine[(q * PW + h) * 64] = w[h];
+    }
+    if (pt.template drained<3>(num_tiles)) return true;
     if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
-    slot = old_slot;  // the slot just emptied takes the next tile
+    slot = next_slot(slot);
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);
     return false;
 }
 
 template <class Op, int D, int Q, int G, bool INCL, bool VEC>
-__device__ __forceinline__ void data_loop(PipeTiles pt, ScanShared<Op, D, Q> &sh, typename IoOf<Op>::Src in,
-                                          typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
-                                          uint32_t lane, uint32_t d) {
+__device__ __forceinline__ void data_loop3(PipeTiles pt, ScanShared<Op, D, Q> &sh, typename IoOf<Op>::Src in,
+                                           typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+                                           uint32_t lane, uint32_t d) {
     using T = typename Op::T;
     constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
     const uint64_t lane_off = (uint64_t)d * WAVE_ELEMS + 4u * lane;
-    // Two register buffers with alternating roles.  The pipeline starts
-    // empty: the first two phases only load (prev, cur and f1 are absent),
-    // so the loop is entered with no load in flight and every phase is the
-    // same instruction sequence.
-    WaveSpan<Op, Q> x, y;
+    // three register buffers in rotating roles (cur, f1, free); the phase
+    // parity alternates independently, so it stays a run-time value
+    WaveSpan<Op, Q> x, y, z;
     T lane_excl[Q], row_prefix[Q];
     uint32_t slot = 0;
+    int par = 0;
     for (;;) {
-        if (data_phase<Op, D, Q, G, INCL, VEC>(x, y, 0, slot, pt, lane_excl, row_prefix, sh, in, out, n,
-                                               num_tiles, ctr, lane, d, lane_off))
+        if (data_phase3<Op, D, Q, G, INCL, VEC>(x, y, z, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                                num_tiles, ctr, lane, d, lane_off))
             break;
-        if (data_phase<Op, D, Q, G, INCL, VEC>(y, x, 1, slot, pt, lane_excl, row_prefix, sh, in, out, n,
-                                               num_tiles, ctr, lane, d, lane_off))
+        par ^= 1;
+        if (data_phase3<Op, D, Q, G, INCL, VEC>(y, z, x, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                                num_tiles, ctr, lane, d, lane_off))
             break;
+        par ^= 1;
+        if (data_phase3<Op, D, Q, G, INCL, VEC>(z, x, y, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                                num_tiles, ctr, lane, d, lane_off))
+            break;
+        par ^= 1;
     }
 }
 
@@ -219,14 +223,14 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
         sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
     }
     __syncthreads();
-    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
+    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0)
-        control_loop<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
+        control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
             pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, cfg,
             FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
     else
-        data_loop<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
+        data_loop3<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
 }
 
 template <class T>

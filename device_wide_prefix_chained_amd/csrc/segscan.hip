@@ -476,7 +476,7 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
         sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
     }
     __syncthreads();
-    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
+    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0) {
         seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, ctr, desc, cfg, SegFallback{values, heads, n}, lane);
