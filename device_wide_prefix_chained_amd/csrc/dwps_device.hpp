@@ -348,12 +348,39 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 #define DWPS_LOOKBACK_K 2
 #endif
 
-// Decoupled look-back, executed by one full wave, reading K descriptors per
-// lane per poll, i.e. a window of 64*K predecessors.  Lane l holds tiles
-// (base + l*K) .. (base + l*K + K-1) of the window, where base =
-// nearest - 64*K + 1, so lane 63's last word is the nearest predecessor and
-// (lane, word) order is tile order.  Indices below 0 read as a PREFIX
-// carrying the identity.
+// One poll's worth of descriptor words, the 64*K predecessors from
+// base = nearest - 64K + 1 on.  Two layouts: blocked, word j of lane l is
+// tile base + 64j + l (each load instruction reads 64 consecutive
+// descriptors); interleaved, it is tile base + Kl + j (each lane reads K
+// consecutive ones, and a lane can fold its own words in tile order).
+template <class T, int K>
+struct Window {
+    uint32_t sw[K];  // state words
+    T val[K];
+};
+
+template <int K, bool BLOCKED>
+__device__ __forceinline__ int64_t window_index(int64_t base, uint32_t lane, int j) {
+    return BLOCKED ? base + 64 * j + (int64_t)lane : base + (int64_t)lane * K + j;
+}
+
+// Issue the loads of one window.  Every load is issued before any is used
+// (no branch around a load, so one poll costs one round trip); words before
+// tile 0 read tile 0's and are replaced by the caller.
+template <class Op, int K, bool BLOCKED, class W = WordsFor<Op>>
+__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane,
+                                            Window<typename Op::T, K> &win) {
+    const int64_t base = nearest - 64 * K + 1;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const int64_t idx = window_index<K, BLOCKED>(base, lane, j);
+        W::read(desc, idx >= 0 ? idx : 0, win.sw[j], win.val[j]);
+    }
+}
+
+// Decoupled look-back, executed by one full wave over windows of 64*K
+// predecessors (BLOCKED or interleaved, see Window).  Indices below 0 read
+// as a PREFIX carrying the identity.
 //
 // Walking back from the nearest predecessor, an AGGREGATE adds its payload
 // and steps one tile, a PARTIAL adds its payload and jumps over the d tiles
@@ -361,16 +388,17 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // In a window: let s be the nearest word in PREFIX or PARTIAL state; if a
 // word nearer than s is INVALID the window is polled again (each poll
 // reloads every word); otherwise the payloads from s to the nearest
-// predecessor are folded in tile order (each lane folds its own words, then
-// one wave scan joins the lanes).  At a PREFIX the fold is final; at a
-// PARTIAL the next window ends just before the tiles it covers; with neither,
-// the window slides 64*K tiles back.  Each time the walk continues, the
-// tile's own descriptor becomes a PARTIAL covering everything folded so far
-// and itself (once cfg.partial windows were walked, and when may_publish),
-// so later look-backs over
-// the same stretch jump it in one read -- the bounded-window variant of
-// "Single-Pass Prefix Scan with Decoupled Look-Back", section "Why the work
-// stays linear", with W = cfg.partial windows of 64*K predecessors.
+// predecessor are folded in tile order (blocked: one wave scan per block,
+// the blocks in order; interleaved: each lane folds its own words, one wave
+// scan joins the lanes).  At a PREFIX the fold is final; at a PARTIAL the
+// next window ends just before the tiles it covers; with neither, the
+// window slides 64*K tiles back.  Each time the walk continues, the tile's
+// own descriptor becomes a PARTIAL covering everything folded so far and
+// itself (once cfg.partial windows were walked, and when may_publish), so
+// later look-backs over the same stretch jump it in one read -- the
+// bounded-window variant of "Single-Pass Prefix Scan with Decoupled
+// Look-Back", section "Why the work stays linear", with W = cfg.partial
+// windows of 64*K predecessors.
 //
 // After cfg.fallback_after stalled polls in a row the wave reduces the
 // nearest unpublished predecessor from its input (fb(tile, lane) returns the
@@ -384,35 +412,117 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // every tile only waits on tiles that took their ticket earlier, hence are
 // resident or finished ("Single-Pass Prefix Scan with Decoupled Look-Back",
 // sections "Three states in a per-block descriptor" and "Where the algorithm
-// meets the hardware").
-// One poll's worth of descriptor words: lane l holds tiles
-// nearest - 64K + 1 + lK .. + K - 1.
-template <class T, int K>
-struct Window {
-    uint32_t sw[K];  // state words
-    T val[K];
-};
-
-// Issue the loads of one window.  Every load is issued before any is used
-// (no branch around a load, so one poll costs one round trip); words before
-// tile 0 read tile 0's and are replaced by the caller.
-template <class Op, int K, class W = WordsFor<Op>>
-__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane,
-                                            Window<typename Op::T, K> &win) {
-    const int64_t first = nearest - 64 * K + 1 + (int64_t)lane * K;
+// meets the hardware").  `pre`, when given, is the first window, read ahead
+// of time (an older read of a descriptor is still a valid one: states only
+// move forward, and an unpublished word just costs another poll).
+template <class Op, int K, bool STATS, class FB, class W>
+__device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint32_t tile, uint32_t lane,
+                                                           LookbackStats &st, uint32_t *hdr, LookbackCfg cfg,
+                                                           typename Op::T own, bool may_publish, const FB &fb,
+                                                           const Window<typename Op::T, K> *pre) {
+    using T = typename Op::T;
+    T acc = Op::id();
+    int64_t nearest = (int64_t)tile - 1;
+    uint32_t spins = 0, stalled = 0, walked = 0;
+    bool use_pre = pre != nullptr;  // a constant wherever lookback is inlined
+    for (;;) {
+        const int64_t base = nearest - 64 * K + 1;
+        Window<T, K> win;
+        if (use_pre)
+            win = *pre;
+        else
+            window_load<Op, K, true, W>(desc, nearest, lane, win);
+        use_pre = false;
+        uint32_t sw[K];  // state words
+        T val[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-        const int64_t idx = first + j;
-        W::read(desc, idx >= 0 ? idx : 0, win.sw[j], win.val[j]);
+        for (int j = 0; j < K; ++j) {
+            const bool before = window_index<K, true>(base, lane, j) < 0;
+            sw[j] = before ? ST_PREFIX : win.sw[j];
+            val[j] = before ? Op::id() : win.val[j];
+        }
+        // the nearest PREFIX/PARTIAL word: block js, lane ls (js = -1: none)
+        int js = -1;
+        uint64_t pm = 0;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint64_t m = ballot((sw[j] & 3u) >= ST_PREFIX);
+            js = m ? j : js;
+            pm = m ? m : pm;
+        }
+        const uint32_t ls = pm ? 63u - (uint32_t)__builtin_clzll(pm) : 0u;
+        bool rel[K];  // nearer than the stopper, or the stopper itself
+#pragma unroll
+        for (int j = 0; j < K; ++j) rel[j] = j > js || (j == js && lane >= ls);
+        // the nearest INVALID word among them: block ji, lane li
+        int ji = -1;
+        uint64_t imask = 0;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const uint64_t m = ballot(rel[j] && (sw[j] & 3u) == ST_INVALID);
+            ji = m ? j : ji;
+            imask = m ? m : imask;
+        }
+        if (STATS) st.polls++;
+        if (ji >= 0) {
+            if (STATS) st.stalls++;
+            if (cfg.fallback_after && ++stalled >= cfg.fallback_after) {
+                // reduce the nearest unpublished predecessor ourselves
+                const uint32_t li = 63u - (uint32_t)__builtin_clzll(imask);
+                const int64_t p = base + 64 * ji + (int64_t)li;
+                const DescVal<T> dv = fb((uint32_t)p, lane);
+                if (lane == 0 && W::install(desc, (uint32_t)p, dv.state, dv.value)) count_event(hdr + kHdrFallbacks);
+                stalled = 0;
+                continue;
+            }
+            if (++spins < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            if (lane == 0) __hip_atomic_store(hdr + kHdrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        spins = 0;
+        stalled = 0;
+        // fold the counted words in tile order: block by block, the lanes of
+        // a block by the wave scan
+        T wsum = Op::id();
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (j >= js) {
+                const T v = wave_inclusive<Op>(rel[j] ? val[j] : Op::id());
+                wsum = Op::op(wsum, read_lane(v, 63));
+            }
+        }
+        acc = Op::op(wsum, acc);
+        if (STATS) st.windows++;
+        if (js >= 0) {
+            // the stopper's state word, uniform
+            uint32_t ss = sw[0];
+#pragma unroll
+            for (int j = 1; j < K; ++j) ss = (j == js) ? sw[j] : ss;
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)ss, (int)ls);
+            if ((hi & 3u) == ST_PREFIX) break;
+            const int64_t stop = base + 64 * js + (int64_t)ls;
+            nearest = stop - (int64_t)(hi >> 2);
+        } else {
+            nearest -= 64 * K;
+        }
+        if (nearest < 0) break;  // a PARTIAL reaching back to tile 0 ends the walk
+        if (cfg.partial && ++walked >= cfg.partial && may_publish && lane == 0) {
+            W::publish(desc, tile, ((uint32_t)((int64_t)tile - nearest) << 2) | ST_PARTIAL, Op::op(acc, own));
+            // counted by the instrumented build only: an atomic on one shared
+            // word would queue ahead of this wave's next poll
+            if (STATS) count_event(hdr + kHdrPartials);
+        }
     }
+    return acc;
 }
 
-template <class Op, int K, bool STATS, class FB = NoFallback<typename Op::T>, class W = WordsFor<Op>>
-__device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile, uint32_t lane, LookbackStats &st,
-                                                   uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u},
-                                                   typename Op::T own = Op::id(), bool may_publish = false,
-                                                   const FB &fb = FB{},
-                                                   const Window<typename Op::T, K> *pre = nullptr) {
+template <class Op, int K, bool STATS, class FB, class W>
+__device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, uint32_t tile, uint32_t lane,
+                                                               LookbackStats &st, uint32_t *hdr, LookbackCfg cfg,
+                                                               typename Op::T own, bool may_publish, const FB &fb,
+                                                               const Window<typename Op::T, K> *pre) {
     using T = typename Op::T;
     T acc = Op::id();
     int64_t nearest = (int64_t)tile - 1;
@@ -429,7 +539,7 @@ __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile
         if (use_pre)
             win = *pre;
         else
-            window_load<Op, K, W>(desc, nearest, lane, win);
+            window_load<Op, K, false, W>(desc, nearest, lane, win);
         use_pre = false;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -508,6 +618,19 @@ __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile
         }
     }
     return acc;
+}
+
+template <class Op, int K, bool STATS, bool BLOCKED = false, class FB = NoFallback<typename Op::T>,
+          class W = WordsFor<Op>>
+__device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile, uint32_t lane, LookbackStats &st,
+                                                   uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u},
+                                                   typename Op::T own = Op::id(), bool may_publish = false,
+                                                   const FB &fb = FB{},
+                                                   const Window<typename Op::T, K> *pre = nullptr) {
+    if constexpr (BLOCKED)
+        return lookback_blocked<Op, K, STATS, FB, W>(desc, tile, lane, st, hdr, cfg, own, may_publish, fb, pre);
+    else
+        return lookback_interleaved<Op, K, STATS, FB, W>(desc, tile, lane, st, hdr, cfg, own, may_publish, fb, pre);
 }
 
 }  // namespace dwps

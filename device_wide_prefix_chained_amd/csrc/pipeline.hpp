@@ -184,14 +184,14 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         const bool have = pt.prev2 < num_tiles && pt.prev2 != 0;
         const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
         Window<T, LB_K> win;
-        if (look) window_load<Op, LB_K>(desc, (int64_t)pt.prev2 - 1, lane, win);
+        if (look) window_load<Op, LB_K, true>(desc, (int64_t)pt.prev2 - 1, lane, win);
         __syncthreads();  // B: prev3's prefix is in LDS
         LookbackStats st;
         uint64_t t0 = 0;
         if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
         T excl = Op::id();
         if (look)
-            excl = lookback<Op, LB_K, STATS>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb, &win);
+            excl = lookback<Op, LB_K, STATS, true>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb, &win);
         else if (have)
             excl = incl_last;
         if (lane == 0) {
