@@ -11,15 +11,15 @@
 // The flat scan's persistent, wave-specialised pipeline with a count as the
 // scanned value: a tile is D waves x Q loads of 16 bytes per lane (E = 16 /
 // record_bytes records per load), 48 KiB of records.  Per phase a data wave
-//   * parks the kept records of the current tile, compacted, at their
-//     tile-relative positions in LDS (the rank of a record is a ballot plus a
-//     lane-masked popcount, v_mbcnt, over its row of 64 lanes);
-//   * issues the loads of the tile two ahead into the freed registers;
-//   * ranks the next tile (its wave count goes to the control wave);
-//   * after the look-back of the tile parked two phases earlier has returned
-//     its output base, copies that tile's run of kept records from LDS to
-//     out[base ...] -- contiguous, so every store instruction of the wave
-//     writes 64 consecutive records.
+//   * issues the loads of the tile two ahead into the free registers;
+//   * ranks the next tile (the rank of a record is a ballot plus a
+//     lane-masked popcount, v_mbcnt, over its row of 64 lanes; the wave's
+//     count goes to the control wave);
+//   * after barrier B, copies its run of kept records of the tile parked
+//     three phases earlier, whose output base the look-back has returned,
+//     from its part of the LDS slot to out[base + offset ...] -- contiguous,
+//     so every store instruction writes 64 consecutive records -- and parks
+//     the kept records of the current tile, compacted, in the same place.
 // The control wave is the flat scan's (tile counts instead of sums).
 #include <hip/hip_runtime.h>
 
@@ -131,63 +131,54 @@ struct RecSpan {
 
 template <int D, int Q>
 struct CompactShared {
-    v4u park[kParkSlots][D * Q * 64];  // kept records of a tile, compacted
-    uint32_t park_cnt[kParkSlots];     // number of kept records of each parked tile
+    v4u park[kParkSlots][D * Q * 64];  // kept records of each wave's span, compacted, in the wave's part
+    uint2 park_wave[kParkSlots][D];    // per wave, (offset in the tile's output, count) of its parked run
     uint32_t wt[2][D];                 // wave counts, double-buffered by phase parity
     uint32_t t0;
     uint32_t next;
-    uint32_t prefix;                   // output base of prev2
+    uint32_t prefix;                   // output base of the tile stored in the phase
 };
 
-// One phase of a data wave (see the file comment).  kb[q] holds the keep
-// bits of the lane's E records of row q of cur, pos[q] the wave-relative
-// position of the first of them; both come from the ranking of the previous
-// phase.
+// One phase of a data wave (the flat scan's phase, data_phase3 in scan.hip,
+// with a count as the scanned value).  Each wave parks the kept
+// records of its own span, compacted, in its own part of the slot, so after
+// barrier B a wave can copy prev3's run out of its part and write cur's run
+// into it without waiting on the other waves.  The wave's run of a tile goes
+// to out[base + (kept records of the earlier waves of the tile) ...]; both
+// numbers travel with the parked run (park_wave).  kb/pos of `hold` come
+// from its ranking in the phase before; the ranking of `sc` fills new ones.
 template <class Rec, int D, int Q, int G, bool VEC>
-__device__ __forceinline__ bool compact_phase(RecSpan<Rec, Q> &cur, RecSpan<Rec, Q> &f1, int par, uint32_t &slot,
-                                              PipeTiles &pt, uint32_t (&kb)[Q], uint32_t (&pos)[Q],
-                                              CompactShared<D, Q> &sh, const Rec *records, const uint8_t *flags,
-                                              Rec *out, uint64_t *num_selected, uint32_t n, uint32_t num_tiles,
-                                              uint32_t *ctr, uint32_t lane, uint32_t d, uint64_t lane_off) {
+__device__ __forceinline__ bool compact_phase3(RecSpan<Rec, Q> &hold, RecSpan<Rec, Q> &sc, RecSpan<Rec, Q> &ld,
+                                               int par, uint32_t &slot, PipeTiles &pt, uint32_t (&kb)[Q],
+                                               uint32_t (&pos)[Q], CompactShared<D, Q> &sh, const Rec *records,
+                                               const uint8_t *flags, Rec *out, uint64_t *num_selected, uint32_t n,
+                                               uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
+                                               uint64_t lane_off) {
     constexpr int E = RecSpan<Rec, Q>::E;
     constexpr uint32_t TILE = (uint32_t)D * Q * 64u * E;
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
     if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
-    const uint32_t old_slot = next_slot(slot);
-
-    // park the kept records of cur at their tile-relative positions
-    uint32_t wave_prefix = 0u, count = 0u;
+    // cur: the wave's offset in the tile and its count
+    uint32_t wave_prefix = 0u;
 #pragma unroll
-    for (int w = 0; w < D; ++w) {
-        const uint32_t c = sh.wt[par][w];
-        wave_prefix += ((uint32_t)w < d) ? c : 0u;
-        count += c;
-    }
-    if (d == 0 && lane == 0) sh.park_cnt[slot] = count;
-    Rec *mine = reinterpret_cast<Rec *>(&sh.park[slot][0]);
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        const uint32_t p = wave_prefix + pos[q];
-#pragma unroll
-        for (int k = 0; k < E; ++k)
-            if ((kb[q] >> k) & 1u) mine[p + (uint32_t)__builtin_popcount(kb[q] & ((1u << k) - 1u))] =
-                record_at<Rec>(cur.raw[q], k);
-    }
-    // the freed registers take the tile two ahead
+    for (int w = 0; w < D; ++w) wave_prefix += ((uint32_t)w < d) ? sh.wt[par][w] : 0u;
+    const uint32_t wave_cnt = sh.wt[par][d];
+    // the free registers take the tile two ahead
     const uint64_t b2 = (uint64_t)pt.f2 * TILE;
-    cur.template load<VEC>(records, flags, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
+    ld.template load<VEC>(records, flags, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
     // rank the next tile while the control wave looks back
+    uint32_t kb_n[Q], pos_n[Q];
     {
         const uint64_t b1 = (uint64_t)pt.f1 * TILE;
-        f1.pad(b1 + lane_off, n, b1 + TILE <= n);
+        sc.pad(b1 + lane_off, n, b1 + TILE <= n);
         uint32_t run = 0u;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             uint32_t bits = 0u;
 #pragma unroll
-            for (int k = 0; k < E; ++k) bits |= ((f1.fw[q] >> (8 * k)) & 0xFFu) ? (1u << k) : 0u;
-            kb[q] = bits;
+            for (int k = 0; k < E; ++k) bits |= ((sc.fw[q] >> (8 * k)) & 0xFFu) ? (1u << k) : 0u;
+            kb_n[q] = bits;
             uint32_t before = 0u, total = 0u;
 #pragma unroll
             for (int k = 0; k < E; ++k) {
@@ -195,48 +186,68 @@ __device__ __forceinline__ bool compact_phase(RecSpan<Rec, Q> &cur, RecSpan<Rec,
                 before += lane_rank(m);
                 total += (uint32_t)__builtin_popcountll(m);
             }
-            pos[q] = run + before;
+            pos_n[q] = run + before;
             run += total;
         }
         if (lane == 0) sh.wt[par ^ 1][d] = run;
     }
     __syncthreads();  // B
-    if (pt.prev2 < num_tiles) {
-        const uint32_t cnt = sh.park_cnt[old_slot];
-        const uint32_t base = sh.prefix;
-        const Rec *theirs = reinterpret_cast<const Rec *>(&sh.park[old_slot][0]);
-        for (uint32_t j = d * 64u + lane; j < cnt; j += (uint32_t)D * 64u)
-            __builtin_nontemporal_store(theirs[j], out + (uint64_t)base + j);
-        if (pt.prev2 == num_tiles - 1u && d == 0 && lane == 0) *num_selected = (uint64_t)base + cnt;
+    Rec *mine = reinterpret_cast<Rec *>(&sh.park[slot][(uint32_t)d * Q * 64u]);
+    if (pt.prev3 < num_tiles) {
+        const uint2 meta = sh.park_wave[slot][d];
+        const uint64_t base = (uint64_t)sh.prefix + meta.x;
+        for (uint32_t j = lane; j < meta.y; j += 64u) __builtin_nontemporal_store(mine[j], out + base + j);
+        if (pt.prev3 == num_tiles - 1u && d == (uint32_t)D - 1u && lane == 0) *num_selected = base + meta.y;
     }
-    if (pt.drained(num_tiles)) return true;
+    // park cur's kept records where prev3's were
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            if ((kb[q] >> k) & 1u) mine[pos[q] + (uint32_t)__builtin_popcount(kb[q] & ((1u << k) - 1u))] =
+                record_at<Rec>(hold.raw[q], k);
+    }
+    if (lane == 0) sh.park_wave[slot][d] = make_uint2(wave_prefix, wave_cnt);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        kb[q] = kb_n[q];
+        pos[q] = pos_n[q];
+    }
+    if (pt.template drained<3>(num_tiles)) return true;
     if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
-    slot = old_slot;  // the slot just emptied takes the next tile
+    slot = next_slot(slot);
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);
     return false;
 }
 
 template <class Rec, int D, int Q, int G, bool VEC>
-__device__ __forceinline__ void compact_data_loop(PipeTiles pt, CompactShared<D, Q> &sh, const Rec *records,
-                                                  const uint8_t *flags, Rec *out, uint64_t *num_selected,
-                                                  uint32_t n, uint32_t num_tiles, uint32_t *ctr, uint32_t lane,
-                                                  uint32_t d) {
+__device__ __forceinline__ void compact_data_loop3(PipeTiles pt, CompactShared<D, Q> &sh, const Rec *records,
+                                                   const uint8_t *flags, Rec *out, uint64_t *num_selected,
+                                                   uint32_t n, uint32_t num_tiles, uint32_t *ctr, uint32_t lane,
+                                                   uint32_t d) {
     constexpr int E = RecSpan<Rec, Q>::E;
     const uint64_t lane_off = (uint64_t)d * Q * 64u * E + (uint64_t)lane * E;
-    RecSpan<Rec, Q> x, y;
+    RecSpan<Rec, Q> x, y, z;
     // no keep bits before the first ranking: the first phases park nothing
     uint32_t kb[Q], pos[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) kb[q] = pos[q] = 0u;
     uint32_t slot = 0;
+    int par = 0;
     for (;;) {
-        if (compact_phase<Rec, D, Q, G, VEC>(x, y, 0, slot, pt, kb, pos, sh, records, flags, out, num_selected, n,
-                                             num_tiles, ctr, lane, d, lane_off))
+        if (compact_phase3<Rec, D, Q, G, VEC>(x, y, z, par, slot, pt, kb, pos, sh, records, flags, out, num_selected,
+                                              n, num_tiles, ctr, lane, d, lane_off))
             break;
-        if (compact_phase<Rec, D, Q, G, VEC>(y, x, 1, slot, pt, kb, pos, sh, records, flags, out, num_selected, n,
-                                             num_tiles, ctr, lane, d, lane_off))
+        par ^= 1;
+        if (compact_phase3<Rec, D, Q, G, VEC>(y, z, x, par, slot, pt, kb, pos, sh, records, flags, out, num_selected,
+                                              n, num_tiles, ctr, lane, d, lane_off))
             break;
+        par ^= 1;
+        if (compact_phase3<Rec, D, Q, G, VEC>(z, x, y, par, slot, pt, kb, pos, sh, records, flags, out, num_selected,
+                                              n, num_tiles, ctr, lane, d, lane_off))
+            break;
+        par ^= 1;
     }
 }
 
@@ -281,13 +292,13 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
     __syncthreads();
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
+    using Fb = CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>;
     if (wave == 0)
-        control_loop<SumU32, D, LB_K, G, false, false>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr, nullptr, 0, cfg,
-                                                CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>{flags, n},
-                                                lane);
+        control_loop3<SumU32, D, LB_K, G, false, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
+                                                              nullptr, 0, cfg, Fb{flags, n}, lane);
     else
-        compact_data_loop<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
-                                             wave - 1);
+        compact_data_loop3<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
+                                              wave - 1);
 }
 
 __global__ void write_count_zero(uint64_t *p) { *p = 0ull; }

@@ -4,9 +4,9 @@
 // A workgroup holds one control wave and D data waves and moves each tile
 // through a fixed sequence of phases: loads issued, scanned (aggregate
 // published after the phase's barrier B), parked in LDS, looked back for and
-// stored -- two phases after the park (LAG 2: segmented scan, compaction),
-// or three with the look-back resolved the phase before (LAG 3: flat
-// scan).  PipeTiles is the window of tile ids the workgroup works on in one
+// stored -- two phases after the park (LAG 2: segmented scan), or three
+// with the look-back resolved the phase before (LAG 3: flat scan,
+// compaction).  PipeTiles is the window of tile ids the workgroup works on in one
 // phase.
 #pragma once
 
@@ -69,92 +69,6 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
     return (f2 < num_tiles && f2 + 1u < num_tiles) ? f2 + 1u : num_tiles;
 }
 
-// Control wave: aggregates, look-back, prefixes.  Phase k runs between
-// barriers A_k and B_k, while the data waves work on their side.  A tile's
-// aggregate goes out right after barrier B of the phase that scanned it; its
-// look-back runs two phases later, so the aggregates of its neighbours and
-// the prefixes of the tiles one generation older are already published: one
-// poll, off the critical path.  Within a phase the wave polls first and
-// publishes the prefix only after the poll has returned.  Shared (the workgroup's LDS
-// block) provides wt[2][D] (the data waves' tile totals, by phase parity),
-// prefix (the exclusive prefix of prev2, read by the data waves after B) and
-// next (the tile after f2, written by data wave 0 before A).  fb reduces a
-// tile from its input when a look-back falls back on it (see lookback).
-template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, int LAG = 2, class Shared, class FB>
-__device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t num_tiles,
-                                             uint32_t *ctr, uint64_t *desc, typename Op::T *total,
-                                             uint32_t *stats, int aggregate_only, LookbackCfg cfg,
-                                             const FB &fb, uint32_t lane) {
-    using T = typename Op::T;
-    using W = WordsFor<Op>;
-    // aggregates of prev, prev2 and prev3 at the start of a phase
-    T agg_prev = Op::id(), agg_prev2 = Op::id(), agg_prev3 = Op::id();
-    T incl_last = Op::id();  // inclusive prefix of the tile looked back for one phase ago
-    T agg_next = Op::id();   // aggregate of cur, published at the end of the phase before
-    for (int par = 0;; par ^= 1) {
-        const T agg = agg_next;
-        // the tile stored this phase, its aggregate, and the one behind it
-        const uint32_t wt_tile = pt.template waiting<LAG>();
-        const uint32_t young = pt.template younger<LAG>();
-        const T agg_w = LAG == 3 ? agg_prev3 : agg_prev2;
-        const T agg_y = LAG == 3 ? agg_prev2 : agg_prev;
-        // Only the first tile of a group looks back; the next ones of the
-        // group follow it through this wave's own registers.
-        LookbackStats st;
-        uint64_t t0 = 0;
-        if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
-        T excl = Op::id();
-        const bool have_w = wt_tile < num_tiles && wt_tile != 0;
-        const bool look = have_w && (wt_tile % G == 0u || (STATS && aggregate_only));
-        if (look)
-            excl = lookback<Op, LB_K, STATS>(desc, wt_tile, lane, st, ctr, cfg, agg_w, true, fb);
-        else if (have_w)
-            excl = incl_last;
-        if (lane == 0) {
-            sh.prefix = excl;
-            if (wt_tile < num_tiles) {
-                if (total && wt_tile == num_tiles - 1) *total = Op::op(excl, agg_w);
-                if (STATS) {
-                    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-                    reinterpret_cast<uint4 *>(stats)[wt_tile] =
-                        make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
-                }
-            }
-            // PAIR_PREFIX: a look-back also settles the next tile of its
-            // group (prev, one phase younger, whose aggregate is out): its
-            // inclusive prefix goes out now instead of a phase later, so
-            // later look-backs meet a prefix sooner.  Measured per kernel:
-            // it pays for the flat scans with one-word descriptors only.
-            constexpr bool kPairPrefix = PAIR_PREFIX && G > 1;
-            if (!(STATS && aggregate_only)) {
-                const bool early = kPairPrefix && wt_tile % G != 0u && wt_tile - 1u != 0u;  // went out a phase ago
-                if (have_w && !early) W::publish(desc, wt_tile, ST_PREFIX, Op::op(excl, agg_w));
-                if (kPairPrefix && look && young == wt_tile + 1u && young < num_tiles)
-                    W::publish(desc, young, ST_PREFIX, Op::op(Op::op(excl, agg_w), agg_y));
-            }
-        }
-        incl_last = Op::op(excl, agg_w);
-        agg_prev3 = agg_prev2;
-        agg_prev2 = agg_prev;
-        agg_prev = agg;
-        __syncthreads();  // B: prefix of prev2 is in LDS
-        // The wave totals of f1 are complete: its aggregate goes out now,
-        // while the data waves store prev2, not after the next phase's poll.
-        // The store is then well under way when that poll is issued (the
-        // in-order vmcnt makes the poll's wait cover it), and the aggregate
-        // reaches the look-backs that depend on it most of a phase earlier.
-        agg_next = Op::id();
-        if (pt.f1 < num_tiles) {
-#pragma unroll
-            for (int w = 0; w < D; ++w) agg_next = Op::op(agg_next, sh.wt[par ^ 1][w]);
-            if (lane == 0) W::publish(desc, pt.f1, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
-        }
-        if (pt.template drained<LAG>(num_tiles)) break;
-        __syncthreads();  // A: the next tile id is in LDS
-        pt.advance(uniform(sh.next), num_tiles);
-    }
-}
-
 // Control wave of the LAG 3 pipeline (the data waves store prev3): the
 // look-back of prev2 is resolved one phase before its tile is stored, and
 // its poll straddles barrier B.  Per phase: hand the data waves prev3's
@@ -164,7 +78,8 @@ __device__ __forceinline__ void control_loop(PipeTiles pt, Shared &sh, uint32_t 
 // f1's aggregate, and meet the data waves at barrier A.  The poll is as
 // fresh as in the two-phase pipeline (issued at the start of the phase that
 // resolves it); only its round trip moves off the path to barrier B.
-template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, class Shared, class FB>
+template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, bool BLOCKED = true, class Shared,
+          class FB>
 __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t num_tiles, uint32_t *ctr,
                                               uint64_t *desc, typename Op::T *total, uint32_t *stats,
                                               int aggregate_only, LookbackCfg cfg, const FB &fb, uint32_t lane) {
@@ -184,14 +99,14 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         const bool have = pt.prev2 < num_tiles && pt.prev2 != 0;
         const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
         Window<T, LB_K> win;
-        if (look) window_load<Op, LB_K, true>(desc, (int64_t)pt.prev2 - 1, lane, win);
+        if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, win);
         __syncthreads();  // B: prev3's prefix is in LDS
         LookbackStats st;
         uint64_t t0 = 0;
         if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
         T excl = Op::id();
         if (look)
-            excl = lookback<Op, LB_K, STATS, true>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb, &win);
+            excl = lookback<Op, LB_K, STATS, BLOCKED>(desc, pt.prev2, lane, st, ctr, cfg, agg_prev2, true, fb, &win);
         else if (have)
             excl = incl_last;
         if (lane == 0) {

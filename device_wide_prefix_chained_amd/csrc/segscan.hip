@@ -247,7 +247,7 @@ struct SegFallback {
 // barrier B: combine the wave pairs of f1 (scanned in this phase) into its
 // aggregate and first start and publish its descriptor at once -- PREFIX
 // when it holds a start (or is tile 0), AGGREGATE otherwise -- most of a
-// phase before it becomes cur (see control_loop).
+// phase before it becomes cur (as in control_loop3).
 template <int D, int Q, int LB_K, int G>
 __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles,
                                                  uint32_t *ctr, uint64_t *desc, LookbackCfg cfg,
