@@ -20,22 +20,13 @@ namespace dwps {
 constexpr int kParkSlots = 3;
 
 // Tile ids of the pipeline, identical in every wave of the workgroup
-// (num_tiles = none): prev2 waits for its prefix, prev and cur are parked or
-// being parked, f1 and f2 are in flight.  Every value comes from LDS through
-// readfirstlane, so the compiler keeps them in scalar registers and branches
-// on them with scalar branches.
+// (num_tiles = none): f2 and f1 are in flight and being scanned, cur is
+// being made tile-relative or parked, prev, prev2 (and prev3) are parked;
+// the tile stored in a phase is prev2 (LAG 2) or prev3 (LAG 3).  Every value
+// comes from LDS through readfirstlane, so the compiler keeps them in scalar
+// registers and branches on them with scalar branches.
 struct PipeTiles {
     uint32_t prev3, prev2, prev, cur, f1, f2;
-    // LAG: phases between a tile's park and its store.  The tile stored in
-    // this phase (the one looked back for) is prev2 (LAG 2) or prev3 (LAG 3).
-    template <int LAG>
-    __device__ __forceinline__ uint32_t waiting() const {
-        return LAG == 3 ? prev3 : prev2;
-    }
-    template <int LAG>
-    __device__ __forceinline__ uint32_t younger() const {  // the tile one phase behind it
-        return LAG == 3 ? prev2 : prev;
-    }
     // nothing left after this phase's store
     template <int LAG>
     __device__ __forceinline__ bool drained(uint32_t num_tiles) const {
