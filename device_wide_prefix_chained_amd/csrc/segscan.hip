@@ -24,9 +24,11 @@
 // Two launches per call:
 //   1. a pre-pass, one wave per tile (four per workgroup), clears the tile's
 //      descriptor and writes the tile's segment starts as a bitmap into the
-//      workspace: two 64-way searches of the offsets, run side by side, bound
-//      the starts inside the tile, and those starts set bits in LDS (repeated
-//      offsets -- empty segments -- set the same bit);
+//      workspace: a sample of the offsets in LDS (every 512th, loaded once
+//      per workgroup) brackets the tile's first start within 512 entries,
+//      one round of contiguous loads from there fetches the starts, and
+//      they set bits in LDS (repeated offsets -- empty segments -- set the
+//      same bit);
 //   2. the persistent, wave-specialised pipeline of the flat scan (one
 //      control wave, D data waves, look-back two phases behind the
 //      aggregate), streaming the values and their bitmap words.
@@ -39,51 +41,70 @@
 
 namespace dwps {
 
-// Lower bounds of two keys in one sorted array (first index s in [0, count)
-// with a[s] >= key, count if none), searched by one full wave: per round each
-// search probes 64 evenly spaced entries of its range and keeps the stretch
-// between the last probe below its key and the next one, so 65 537 offsets
-// take three rounds.  The probes of both searches are issued together, so a
-// round costs one memory latency.  Reads stay inside [0, count) even if `a`
-// is not sorted.
-__device__ __forceinline__ void wave_lower_bound2(const uint32_t *a, uint32_t count, uint32_t key0, uint32_t key1,
-                                                  uint32_t lane, uint32_t &r0, uint32_t &r1) {
-    // [lo, hi] brackets the answer; probes stay below hi
-    uint32_t lo0 = 0, hi0 = count, lo1 = 0, hi1 = count;
-    for (;;) {
-        const uint32_t w0 = hi0 - lo0, w1 = hi1 - lo1;
-        const uint32_t s0 = w0 > 64u ? (w0 + 63u) / 64u : 1u;
-        const uint32_t s1 = w1 > 64u ? (w1 + 63u) / 64u : 1u;
-        const uint32_t p0 = lo0 + lane * s0, p1 = lo1 + lane * s1;
-        const bool in0 = p0 < hi0, in1 = p1 < hi1;
-        const uint32_t v0 = in0 ? a[p0] : 0u;
-        const uint32_t v1 = in1 ? a[p1] : 0u;
-        const uint32_t c0 = (uint32_t)__builtin_popcountll(ballot(in0 && v0 < key0));
-        const uint32_t c1 = (uint32_t)__builtin_popcountll(ballot(in1 && v1 < key1));
-        if (w0 <= 64u) {
-            lo0 += c0;  // every entry of the range was probed
-            hi0 = lo0;
-        } else if (c0 == 0u) {
-            hi0 = lo0;  // a[lo0] >= key0
-        } else {
-            const uint32_t b = lo0;
-            lo0 = b + (c0 - 1u) * s0 + 1u;
-            hi0 = min(hi0, b + c0 * s0);
-        }
-        if (w1 <= 64u) {
-            lo1 += c1;
-            hi1 = lo1;
-        } else if (c1 == 0u) {
-            hi1 = lo1;
-        } else {
-            const uint32_t b = lo1;
-            lo1 = b + (c1 - 1u) * s1 + 1u;
-            hi1 = min(hi1, b + c1 * s1);
-        }
-        if (lo0 == hi0 && lo1 == hi1) break;
+// The segment starts inside one tile [tb, te), as bits of an LDS bitmap
+// (bit i = element tb + i), found by one wave in the sorted offsets
+// a[0, count).  `sample` (in LDS, filled by the workgroup) holds every
+// stride-th entry, a[k * stride] for k < ns; counting the sample entries
+// below tb brackets the first entry >= tb within one stride.  Rounds of
+// 64*R evenly spaced probes narrow that bracket further only while it is
+// wider than 64*R entries (more than 2^19 offsets); then batches of 64*R
+// consecutive entries are loaded from its start, and every loaded offset in
+// [tb, te) sets its bit (repeated offsets -- empty segments -- set the same
+// bit), until an entry at or past te or the end of the array.  Loads are
+// straight-line (out-of-range probes read an in-range entry and are
+// ignored), so reads stay inside [0, count) even if `a` is not sorted.
+template <int R>
+__device__ __forceinline__ void wave_tile_starts(const uint32_t *a, uint32_t count, const uint32_t *sample,
+                                                 uint32_t ns, uint32_t stride, uint32_t tb, uint32_t te,
+                                                 uint32_t lane, uint32_t *bits) {
+    constexpr uint32_t P = 64u * (uint32_t)R;
+    uint32_t c = 0;  // sample entries below tb: a prefix of the sample
+    for (uint32_t k0 = 0; k0 < ns; k0 += 64u) {
+        const uint32_t k = k0 + lane;
+        c += (uint32_t)__builtin_popcountll(ballot(k < ns && sample[k < ns ? k : 0u] < tb));
     }
-    r0 = lo0;
-    r1 = lo1;
+    // the first entry >= tb lies in [lo, hi]
+    uint32_t lo = 0, hi = 0;
+    if (c != 0u) {
+        lo = (c - 1u) * stride + 1u;  // (c - 1) * stride < count
+        hi = (uint32_t)min((uint64_t)count, (uint64_t)c * stride);
+    }
+    while (hi - lo > P) {
+        const uint32_t s = (hi - lo + P - 1u) / P;
+        uint32_t v[R];
+        bool in[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint64_t p = lo + (uint64_t)((uint32_t)j * 64u + lane) * s;
+            in[j] = p < hi;
+            v[j] = a[in[j] ? (uint32_t)p : lo];
+        }
+        uint32_t cp = 0;
+#pragma unroll
+        for (int j = 0; j < R; ++j) cp += (uint32_t)__builtin_popcountll(ballot(in[j] && v[j] < tb));
+        if (cp == 0u) {
+            hi = lo;
+        } else {
+            const uint32_t b = lo;
+            lo = b + (cp - 1u) * s + 1u;  // probe cp - 1 was in range
+            hi = (uint32_t)min((uint64_t)hi, (uint64_t)b + (uint64_t)cp * s);
+        }
+    }
+    for (uint32_t base = lo; base < count; base += P) {
+        uint32_t v[R];
+        bool in[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const uint64_t idx = (uint64_t)base + (uint32_t)j * 64u + lane;
+            in[j] = idx < count;
+            v[j] = a[in[j] ? (uint32_t)idx : base];
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            if (in[j] && v[j] >= tb && v[j] < te) atomicOr(&bits[(v[j] - tb) >> 5], 1u << ((v[j] - tb) & 31u));
+        // entry base + P - 1 is lane 63's last load
+        if (count - base <= P || (uint32_t)__builtin_amdgcn_readlane((int)v[R - 1], 63) >= te) break;
+    }
 }
 
 struct SegPair {
@@ -135,7 +156,9 @@ __global__ __launch_bounds__(W * 64) void seg_prepass_kernel(const uint32_t *off
                                                              uint32_t n, uint32_t num_tiles, uint32_t *ctr,
                                                              uint64_t *desc, uint32_t *heads) {
     constexpr uint32_t WORDS = TILE / 32u;
+    constexpr uint32_t kSampleMax = 1024u, kProbes = 8u;
     __shared__ uint32_t bits_all[W][WORDS];
+    __shared__ uint32_t sample[kSampleMax];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t w = threadIdx.x >> 6;
     uint32_t *bits = bits_all[w];
@@ -152,13 +175,13 @@ __global__ __launch_bounds__(W * 64) void seg_prepass_kernel(const uint32_t *off
         }
     }
     for (uint32_t i = lane; i < WORDS; i += 64) bits[i] = 0u;
-    uint32_t lo = 0, hi = 0;
-    if (live) wave_lower_bound2(offsets, num_segments + 1u, tb, te, lane, lo, hi);
+    // every stride-th offset, shared by the workgroup's tiles
+    const uint32_t count = num_segments + 1u;
+    const uint32_t stride = max(64u * kProbes, (uint32_t)(((uint64_t)count + kSampleMax - 1u) / kSampleMax));
+    const uint32_t ns = (uint32_t)(((uint64_t)count + stride - 1u) / stride);  // <= kSampleMax
+    for (uint32_t k = threadIdx.x; k < ns; k += W * 64u) sample[k] = offsets[(uint64_t)k * stride];
     __syncthreads();
-    for (uint32_t s = lo + lane; s < hi; s += 64) {
-        const uint32_t o = offsets[s];
-        if (o >= tb && o < te) atomicOr(&bits[(o - tb) >> 5], 1u << ((o - tb) & 31u));
-    }
+    if (live) wave_tile_starts<kProbes>(offsets, count, sample, ns, stride, tb, te, lane, bits);
     __syncthreads();
     if (live) {
         uint32_t *dst = heads + (uint64_t)t * WORDS;
@@ -498,7 +521,8 @@ using namespace dwps;
 extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uint32_t *values, uint64_t n,
                                            const uint32_t *offsets, uint32_t num_segments, uint32_t *out,
                                            int inclusive, void *stream) {
-    if (n >= (1ull << 32)) return PS_ERR_SIZE;
+    // the offsets' count, num_segments + 1, must fit 32 bits
+    if (n >= (1ull << 32) || num_segments == UINT32_MAX) return PS_ERR_SIZE;
     const uint64_t tiles = ceil_div(n, kSegTile);
     bool query = false;
     ps_status st = workspace_protocol(ws, ws_bytes, seg_ws_bytes(tiles), &query);

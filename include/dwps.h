@@ -245,7 +245,8 @@ uint64_t ps_small_n_config_get(void);
  *                  written; empty segments write nothing.
  *   inclusive    : nonzero for the inclusive form.
  * Any overlap of out with values or offsets returns PS_ERR_ALIAS.
- * num_segments may be 0 (nothing is written).
+ * num_segments may be 0 (nothing is written); num_segments = 2^32 - 1 (an
+ * offsets array of 2^32 entries) returns PS_ERR_SIZE, as does n >= 2^32.
  * Two kernels run per call: a pre-pass that writes a bitmap of the segment
  * starts of every tile into the workspace (n/8 bytes, beside the tile
  * descriptors), then the single-pass scan, which reads the values once and

@@ -223,11 +223,14 @@ def test_argument_errors_segmented_and_compact():
     big = ctypes.c_size_t(1 << 30)
     ws = ctypes.c_void_p(FAKE_WS)
     seg = lib.ps_segmented_scan_u32
+    C0 = 0x70000000
     # out overlapping values or offsets
     assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 4, ctypes.c_void_p(A), 0, None) == 2
     assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 4, ctypes.c_void_p(B - 16), 0, None) == 2
     assert seg(ws, ctypes.byref(big), None, 100, ctypes.c_void_p(B), 4, ctypes.c_void_p(A), 0, None) == 1
     assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 1 << 32, ctypes.c_void_p(B), 4, ctypes.c_void_p(A), 0, None) == 3
+    assert seg(ws, ctypes.byref(big), ctypes.c_void_p(A), 100, ctypes.c_void_p(B), 0xFFFFFFFF, ctypes.c_void_p(C0),
+               0, None) == 3
     assert seg(ws, ctypes.byref(ctypes.c_size_t(8)), ctypes.c_void_p(A), 100000, ctypes.c_void_p(B), 4,
                ctypes.c_void_p(A + (1 << 20)), 0, None) == 4
     # zero segments or n == 0: nothing to do
