@@ -21,17 +21,17 @@
 //     and only the first tile of a ticket group looks back for it -- long
 //     segments chain through start-free tiles exactly like the flat scan.
 //
-// Two launches per call:
-//   1. a pre-pass, one wave per tile (four per workgroup), clears the tile's
-//      descriptor and writes the tile's segment starts as a bitmap into the
-//      workspace: a sample of the offsets in LDS (every 512th, loaded once
-//      per workgroup) brackets the tile's first start within 512 entries,
-//      one round of contiguous loads from there fetches the starts, and
-//      they set bits in LDS (repeated offsets -- empty segments -- set the
-//      same bit);
-//   2. the persistent, wave-specialised pipeline of the flat scan (one
-//      control wave, D data waves, look-back two phases behind the
-//      aggregate), streaming the values and their bitmap words.
+// Two launches per call: the workspace clear (tile descriptors, ticket
+// counter), then the persistent, wave-specialised pipeline of the flat scan
+// (one control wave, D data waves, look-back two phases behind the
+// aggregate).  The segment starts never go through memory as flags: while
+// the data waves load a tile, the control wave reads the tile's offsets and
+// sets the starts as bits of an LDS bitmap, which the data waves read when
+// they scan the tile in the next phase.  To find those offsets, a sample of
+// the offsets (every 512th, loaded into LDS once per workgroup) brackets the
+// tile's first start within 512 entries, and one round of contiguous loads
+// from there fetches the starts (repeated offsets -- empty segments -- set
+// the same bit).
 #include <hip/hip_runtime.h>
 
 #include "dwps_device.hpp"
@@ -41,71 +41,110 @@
 
 namespace dwps {
 
-// The segment starts inside one tile [tb, te), as bits of an LDS bitmap
-// (bit i = element tb + i), found by one wave in the sorted offsets
-// a[0, count).  `sample` (in LDS, filled by the workgroup) holds every
-// stride-th entry, a[k * stride] for k < ns; counting the sample entries
-// below tb brackets the first entry >= tb within one stride.  Rounds of
-// 64*R evenly spaced probes narrow that bracket further only while it is
-// wider than 64*R entries (more than 2^19 offsets); then batches of 64*R
-// consecutive entries are loaded from its start, and every loaded offset in
-// [tb, te) sets its bit (repeated offsets -- empty segments -- set the same
-// bit), until an entry at or past te or the end of the array.  Loads are
-// straight-line (out-of-range probes read an in-range entry and are
+// Segment starts of one tile [tb, te) as bits of an LDS bitmap (bit i =
+// element tb + i), found by one wave in the sorted offsets a[0, count).
+//   * StartIndex: `sample` (LDS) holds every stride-th entry, a[k * stride]
+//     for k < ns (ns <= kSampleMax); counting the sample entries below tb
+//     brackets the first entry >= tb within one stride, and rounds of
+//     64 * kStartProbes evenly spaced probes narrow the bracket further only
+//     while it is wider than that (more than 2^19 offsets).
+//   * Then batches of 64 * kStartProbes consecutive entries are loaded from
+//     the bracket's start, and every loaded offset in [tb, te) sets its bit
+//     (repeated offsets -- empty segments -- set the same bit), until an
+//     entry at or past te or the end of the array.
+// Loads are straight-line (out-of-range lanes read an in-range entry and are
 // ignored), so reads stay inside [0, count) even if `a` is not sorted.
-template <int R>
-__device__ __forceinline__ void wave_tile_starts(const uint32_t *a, uint32_t count, const uint32_t *sample,
-                                                 uint32_t ns, uint32_t stride, uint32_t tb, uint32_t te,
-                                                 uint32_t lane, uint32_t *bits) {
-    constexpr uint32_t P = 64u * (uint32_t)R;
-    uint32_t c = 0;  // sample entries below tb: a prefix of the sample
-    for (uint32_t k0 = 0; k0 < ns; k0 += 64u) {
-        const uint32_t k = k0 + lane;
-        c += (uint32_t)__builtin_popcountll(ballot(k < ns && sample[k < ns ? k : 0u] < tb));
+constexpr uint32_t kSampleMax = 1024u;
+constexpr int kStartProbes = 8;
+constexpr uint32_t kStartBatch = 64u * (uint32_t)kStartProbes;
+
+struct StartIndex {
+    const uint32_t *a;       // offsets
+    uint32_t count;          // num_segments + 1
+    uint32_t stride;         // sample stride (>= kStartBatch)
+    uint32_t ns;             // sample entries
+    const uint32_t *sample;  // LDS
+
+    __device__ static StartIndex make(const uint32_t *offsets, uint32_t num_segments, const uint32_t *sample) {
+        const uint32_t count = num_segments + 1u;  // < 2^32: checked on the host
+        const uint32_t stride = max(kStartBatch, (uint32_t)(((uint64_t)count + kSampleMax - 1u) / kSampleMax));
+        return StartIndex{offsets, count, stride, (uint32_t)(((uint64_t)count + stride - 1u) / stride), sample};
     }
-    // the first entry >= tb lies in [lo, hi]
-    uint32_t lo = 0, hi = 0;
-    if (c != 0u) {
-        lo = (c - 1u) * stride + 1u;  // (c - 1) * stride < count
-        hi = (uint32_t)min((uint64_t)count, (uint64_t)c * stride);
+    // Fill the sample (all threads of the workgroup; a barrier must follow).
+    __device__ void load_sample(uint32_t *dst, uint32_t tid, uint32_t nthreads) const {
+        for (uint32_t k = tid; k < ns; k += nthreads) dst[k] = a[(uint64_t)k * stride];
     }
-    while (hi - lo > P) {
-        const uint32_t s = (hi - lo + P - 1u) / P;
-        uint32_t v[R];
-        bool in[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j) {
-            const uint64_t p = lo + (uint64_t)((uint32_t)j * 64u + lane) * s;
-            in[j] = p < hi;
-            v[j] = a[in[j] ? (uint32_t)p : lo];
+    // Index at or before the first entry >= tb, at most kStartBatch before it.
+    __device__ uint32_t bracket(uint32_t tb, uint32_t lane) const {
+        constexpr uint32_t P = kStartBatch;
+        uint32_t c = 0;  // sample entries below tb: a prefix of the sample
+        for (uint32_t k0 = 0; k0 < ns; k0 += 64u) {
+            const uint32_t k = k0 + lane;
+            c += (uint32_t)__builtin_popcountll(ballot(k < ns && sample[k < ns ? k : 0u] < tb));
         }
-        uint32_t cp = 0;
-#pragma unroll
-        for (int j = 0; j < R; ++j) cp += (uint32_t)__builtin_popcountll(ballot(in[j] && v[j] < tb));
-        if (cp == 0u) {
-            hi = lo;
-        } else {
-            const uint32_t b = lo;
-            lo = b + (cp - 1u) * s + 1u;  // probe cp - 1 was in range
-            hi = (uint32_t)min((uint64_t)hi, (uint64_t)b + (uint64_t)cp * s);
+        // the first entry >= tb lies in [lo, hi]
+        uint32_t lo = 0, hi = 0;
+        if (c != 0u) {
+            lo = (c - 1u) * stride + 1u;  // (c - 1) * stride < count
+            hi = (uint32_t)min((uint64_t)count, (uint64_t)c * stride);
         }
-    }
-    for (uint32_t base = lo; base < count; base += P) {
-        uint32_t v[R];
-        bool in[R];
+        while (hi - lo > P) {
+            const uint32_t s = (hi - lo + P - 1u) / P;
+            uint32_t v[kStartProbes];
+            bool in[kStartProbes];
 #pragma unroll
-        for (int j = 0; j < R; ++j) {
+            for (int j = 0; j < kStartProbes; ++j) {
+                const uint64_t p = lo + (uint64_t)((uint32_t)j * 64u + lane) * s;
+                in[j] = p < hi;
+                v[j] = a[in[j] ? (uint32_t)p : lo];
+            }
+            uint32_t cp = 0;
+#pragma unroll
+            for (int j = 0; j < kStartProbes; ++j) cp += (uint32_t)__builtin_popcountll(ballot(in[j] && v[j] < tb));
+            if (cp == 0u) {
+                hi = lo;
+            } else {
+                const uint32_t b = lo;
+                lo = b + (cp - 1u) * s + 1u;  // probe cp - 1 was in range
+                hi = (uint32_t)min((uint64_t)hi, (uint64_t)b + (uint64_t)cp * s);
+            }
+        }
+        return lo;
+    }
+    // The batch of entries from `base` (lane l, load j: entry base + 64 j + l).
+    __device__ void load_batch(uint32_t base, uint32_t lane, uint32_t (&v)[kStartProbes]) const {
+#pragma unroll
+        for (int j = 0; j < kStartProbes; ++j) {
             const uint64_t idx = (uint64_t)base + (uint32_t)j * 64u + lane;
-            in[j] = idx < count;
-            v[j] = a[in[j] ? (uint32_t)idx : base];
+            v[j] = a[idx < count ? (uint32_t)idx : count - 1u];
         }
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            if (in[j] && v[j] >= tb && v[j] < te) atomicOr(&bits[(v[j] - tb) >> 5], 1u << ((v[j] - tb) & 31u));
-        // entry base + P - 1 is lane 63's last load
-        if (count - base <= P || (uint32_t)__builtin_amdgcn_readlane((int)v[R - 1], 63) >= te) break;
     }
-}
+    // Set the bits of the batch's offsets in [tb, te); true if the entries
+    // after the batch may still hold starts of the tile.
+    __device__ bool mark(const uint32_t (&v)[kStartProbes], uint32_t base, uint32_t tb, uint32_t te, uint32_t lane,
+                         uint32_t *bits) const {
+#pragma unroll
+        for (int j = 0; j < kStartProbes; ++j) {
+            const uint64_t idx = (uint64_t)base + (uint32_t)j * 64u + lane;
+            if (idx < count && v[j] >= tb && v[j] < te) atomicOr(&bits[(v[j] - tb) >> 5], 1u << ((v[j] - tb) & 31u));
+        }
+        // entry base + kStartBatch - 1 is lane 63's last load
+        return (uint64_t)base + kStartBatch < count &&
+               (uint32_t)__builtin_amdgcn_readlane((int)v[kStartProbes - 1], 63) < te;
+    }
+    // Clear `words` bitmap words (16-byte aligned, a multiple of 4), then
+    // mark the batches from `base` on (the first batch already loaded into v).
+    __device__ void finish(uint32_t (&v)[kStartProbes], uint32_t base, uint32_t tb, uint32_t te, uint32_t lane,
+                           uint32_t *bits, uint32_t words) const {
+        // LDS operations of one wave complete in order: the clear before the marks
+        for (uint32_t i = 4u * lane; i < words; i += 256u) *reinterpret_cast<v4u *>(bits + i) = v4u{0u, 0u, 0u, 0u};
+        if (base >= count) return;
+        while (mark(v, base, tb, te, lane, bits)) {
+            base += kStartBatch;
+            load_batch(base, lane, v);
+        }
+    }
+};
 
 struct SegPair {
     uint32_t f;  // 1 if the covered range contains a segment start
@@ -148,49 +187,7 @@ constexpr uint32_t kSegTile = (uint32_t)kSegD * kSegQ * 256u;
 constexpr uint32_t kSegWords = kSegTile / 32u;  // bitmap words per tile
 
 // ---------------------------------------------------------------------------
-// 1. pre-pass: descriptors cleared, per-tile segment-start bitmaps written
-// ---------------------------------------------------------------------------
-// W waves per workgroup, one tile per wave.
-template <uint32_t TILE, int W>
-__global__ __launch_bounds__(W * 64) void seg_prepass_kernel(const uint32_t *offsets, uint32_t num_segments,
-                                                             uint32_t n, uint32_t num_tiles, uint32_t *ctr,
-                                                             uint64_t *desc, uint32_t *heads) {
-    constexpr uint32_t WORDS = TILE / 32u;
-    constexpr uint32_t kSampleMax = 1024u, kProbes = 8u;
-    __shared__ uint32_t bits_all[W][WORDS];
-    __shared__ uint32_t sample[kSampleMax];
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t w = threadIdx.x >> 6;
-    uint32_t *bits = bits_all[w];
-    const uint32_t t = blockIdx.x * W + w;
-    const bool live = t < num_tiles;  // the last workgroup may hold fewer tiles
-    const uint32_t tb = live ? t * TILE : 0u;  // t * TILE <= n - 1
-    const uint64_t tile_end = (uint64_t)tb + TILE;
-    const uint32_t te = tile_end < (uint64_t)n ? (uint32_t)tile_end : n;
-    if (live && lane == 0) {
-        desc[t] = 0ull;
-        if (t == 0) {
-            ctr[0] = 0u;  // ticket counter
-            ctr[1] = 0u;  // error word
-        }
-    }
-    for (uint32_t i = lane; i < WORDS; i += 64) bits[i] = 0u;
-    // every stride-th offset, shared by the workgroup's tiles
-    const uint32_t count = num_segments + 1u;
-    const uint32_t stride = max(64u * kProbes, (uint32_t)(((uint64_t)count + kSampleMax - 1u) / kSampleMax));
-    const uint32_t ns = (uint32_t)(((uint64_t)count + stride - 1u) / stride);  // <= kSampleMax
-    for (uint32_t k = threadIdx.x; k < ns; k += W * 64u) sample[k] = offsets[(uint64_t)k * stride];
-    __syncthreads();
-    if (live) wave_tile_starts<kProbes>(offsets, count, sample, ns, stride, tb, te, lane, bits);
-    __syncthreads();
-    if (live) {
-        uint32_t *dst = heads + (uint64_t)t * WORDS;
-        for (uint32_t i = lane; i < WORDS; i += 64) dst[i] = bits[i];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. the persistent pipeline
+// the persistent pipeline
 // ---------------------------------------------------------------------------
 template <int D, int Q>
 struct SegShared {
@@ -198,50 +195,58 @@ struct SegShared {
     uint32_t park_first[kParkSlots];   // first segment start of each parked tile (tile-local; TILE if none)
     uint32_t wf[2][D], wv[2][D];       // wave totals (pairs), double-buffered by phase parity
     uint32_t wfirst[2][D];             // first segment start in each wave's span (TILE if none)
+    alignas(16) uint32_t starts[2][kSegWords];  // start bitmaps of f2 (written) and f1 (read), by phase parity
+    alignas(16) uint32_t fb_starts[kSegWords];  // start bitmap of a tile a fallback reduces
+    uint32_t sample[kSampleMax];       // every stride-th offset (StartIndex)
     uint32_t t0;
     uint32_t next;
     uint32_t carry;                    // carry into prev2
 };
 
-// Register state of one wave's span: the values and the bitmap words that
-// cover them (one word per group-row; 8 lanes share a word).
+// Register state of one wave's span: the values.
 template <int Q>
 struct SegSpan {
     WaveSpan<SumU32, Q> x;
-    uint32_t hw[Q];
     template <bool VEC>
-    __device__ __forceinline__ void load(const uint32_t *values, const uint32_t *heads, uint32_t tile,
-                                         uint64_t lane_off, uint32_t word_off, uint32_t n, bool valid) {
+    __device__ __forceinline__ void load(const uint32_t *values, uint32_t tile, uint64_t lane_off, uint32_t n,
+                                         bool valid) {
         const uint64_t base = (uint64_t)tile * kSegTile;
         x.template load<VEC>(values, base + lane_off, n, base + kSegTile <= n, valid);
-        const uint64_t wb = valid ? (uint64_t)tile * kSegWords + word_off : (uint64_t)word_off;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) hw[q] = heads[wb + (uint64_t)q * 8u];
     }
 };
 
-// A look-back's fallback: reduce tile p from scratch -- values and start
-// bits, rows of 256 elements, lane-serial pairs of four, the DPP pair scan
-// across the lanes, rows folded in order -- and return the descriptor word
-// its owner publishes first: PREFIX with the carry-out when the tile holds a
+// A look-back's fallback: reduce tile p from scratch -- its start bitmap
+// built from the offsets into `bits` (LDS), then values and start bits in
+// rows of 256 elements, lane-serial pairs of four, the DPP pair scan across
+// the lanes, rows folded in order -- and return the descriptor word its
+// owner publishes first: PREFIX with the carry-out when the tile holds a
 // start (or is tile 0), AGGREGATE with its sum otherwise.  Control wave,
 // rarely.
 struct SegFallback {
     const uint32_t *values;
-    const uint32_t *heads;
+    StartIndex idx;
+    uint32_t *bits;
     uint32_t n;
     __device__ DescVal<uint32_t> operator()(uint32_t p, uint32_t lane) const {
         constexpr uint32_t ROWS = kSegTile / 256u, BATCH = 8u;
         static_assert(ROWS % BATCH == 0, "whole batches of rows");
+        {
+            const uint32_t tb = p * kSegTile;
+            const uint32_t te = (uint32_t)min((uint64_t)n, (uint64_t)tb + kSegTile);
+            const uint32_t lo = idx.bracket(tb, lane);
+            uint32_t v[kStartProbes];
+            idx.load_batch(lo, lane, v);
+            idx.finish(v, lo, tb, te, lane, bits, kSegWords);
+        }
         const uint64_t base = (uint64_t)p * kSegTile + 4u * lane;
-        const uint64_t wbase = (uint64_t)p * kSegWords + (lane >> 3);
+        const uint32_t wbase = lane >> 3;
         const uint32_t sh4 = 4u * (lane & 7u);
         SegPair acc{0u, 0u};
         for (uint32_t r = 0; r < ROWS; r += BATCH) {
             uint32_t x[BATCH][4], fl[BATCH];
 #pragma unroll
             for (uint32_t k = 0; k < BATCH; ++k) {
-                fl[k] = (heads[wbase + (uint64_t)(r + k) * 8u] >> sh4) & 0xFu;
+                fl[k] = (bits[wbase + (r + k) * 8u] >> sh4) & 0xFu;
 #pragma unroll
                 for (uint32_t e = 0; e < 4; ++e) {
                     const uint64_t i = base + (uint64_t)(r + k) * 256u + e;
@@ -263,18 +268,23 @@ struct SegFallback {
     }
 };
 
-// Control wave.  Phase k: find the carry into prev2 (a look-back only when
-// prev2 heads a ticket group and its first element is not a segment start;
-// the second tile of a group takes the carry-out of the first from this
-// wave's registers) and publish PREFIX for prev2 if it had no start.  After
-// barrier B: combine the wave pairs of f1 (scanned in this phase) into its
-// aggregate and first start and publish its descriptor at once -- PREFIX
-// when it holds a start (or is tile 0), AGGREGATE otherwise -- most of a
-// phase before it becomes cur (as in control_loop3).
+// Control wave.  Phase k: issue the loads of the offsets around f2's first
+// segment start (the tile the data waves load in this phase); find the carry
+// into prev2 (a look-back only when prev2 heads a ticket group and its first
+// element is not a segment start; the second tile of a group takes the
+// carry-out of the first from this wave's registers) and publish PREFIX for
+// prev2 if it had no start.  After barrier B: combine the wave pairs of f1
+// (scanned in this phase) into its aggregate and first start and publish
+// its descriptor at once -- PREFIX when it holds a start (or is tile 0),
+// AGGREGATE otherwise -- most of a phase before it becomes cur (as in
+// control_loop3).  f2's start bitmap is written before barrier B, while the
+// data waves finalize, park and scan, into the buffer of this phase's
+// parity; the data waves read it when they scan f2 in the next phase, and
+// read the other buffer in this one.
 template <int D, int Q, int LB_K, int G>
-__device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles,
+__device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles, uint32_t n,
                                                  uint32_t *ctr, uint64_t *desc, LookbackCfg cfg,
-                                                 const SegFallback &fb, uint32_t lane) {
+                                                 const StartIndex &idx, const SegFallback &fb, uint32_t lane) {
     SegPair a_prev{0u, 0u}, a_prev2{0u, 0u};
     uint32_t fh_prev = kSegTile, fh_prev2 = kSegTile;
     uint32_t carry_out_last = 0;  // carry out of the tile handled one phase ago
@@ -283,6 +293,13 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
     for (int par = 0;; par ^= 1) {
         const SegPair agg = agg_next;
         const uint32_t fh = fh_next;
+        // f2's starts: the first batch of offsets is in flight during the look-back
+        const bool build = pt.f2 < num_tiles;
+        const uint32_t tb = build ? pt.f2 * kSegTile : 0u;
+        const uint32_t te = (uint32_t)min((uint64_t)n, (uint64_t)tb + kSegTile);
+        const uint32_t s_lo = idx.bracket(tb, lane);
+        uint32_t s_v[kStartProbes];
+        idx.load_batch(s_lo, lane, s_v);
         uint32_t carry = 0;
         const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
         if (have_prev2) {
@@ -300,6 +317,7 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
             if (have_prev2 && !a_prev2.f)
                 desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, carry + a_prev2.v));
         }
+        if (build) idx.finish(s_v, s_lo, tb, te, lane, sh.starts[par], kSegWords);
         carry_out_last = a_prev2.f ? a_prev2.v : carry + a_prev2.v;
         a_prev2 = a_prev;
         fh_prev2 = fh_prev;
@@ -331,8 +349,7 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
 template <int D, int Q, int G, bool INCL, bool VEC>
 __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, int par, uint32_t &slot,
                                                PipeTiles &pt, uint32_t (&pre)[Q], uint32_t (&fl)[Q],
-                                               SegShared<D, Q> &sh, const uint32_t *values,
-                                               const uint32_t *heads, uint32_t *out, uint32_t n,
+                                               SegShared<D, Q> &sh, const uint32_t *values, uint32_t *out, uint32_t n,
                                                uint32_t row_lo, uint32_t row_hi, uint32_t num_tiles,
                                                uint32_t *ctr, uint32_t lane, uint32_t d, uint64_t lane_off,
                                                uint32_t word_off) {
@@ -380,7 +397,7 @@ __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, 
         mine[q * 64] = w;
     }
     // the freed registers take the tile two ahead
-    cur.template load<VEC>(values, heads, pt.f2, lane_off, word_off, n, pt.f2 < num_tiles);
+    cur.template load<VEC>(values, pt.f2, lane_off, n, pt.f2 < num_tiles);
     // scan the next tile while the control wave looks back
     {
         const uint64_t b1 = (uint64_t)pt.f1 * TILE;
@@ -388,7 +405,7 @@ __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, 
         const uint32_t sh4 = 4u * (lane & 7u);
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            fl[q] = (f1.hw[q] >> sh4) & 0xFu;
+            fl[q] = (sh.starts[par ^ 1][word_off + (uint32_t)q * 8u] >> sh4) & 0xFu;
             f1.x.v[q][1] = (fl[q] & 2u) ? f1.x.v[q][1] : f1.x.v[q][0] + f1.x.v[q][1];
             f1.x.v[q][2] = (fl[q] & 4u) ? f1.x.v[q][2] : f1.x.v[q][1] + f1.x.v[q][2];
             f1.x.v[q][3] = (fl[q] & 8u) ? f1.x.v[q][3] : f1.x.v[q][2] + f1.x.v[q][3];
@@ -463,7 +480,7 @@ __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, 
 
 template <int D, int Q, int G, bool INCL, bool VEC>
 __device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh, const uint32_t *values,
-                                              const uint32_t *heads, uint32_t *out, uint32_t n, uint32_t row_lo,
+                                              uint32_t *out, uint32_t n, uint32_t row_lo,
                                               uint32_t row_hi, uint32_t num_tiles, uint32_t *ctr, uint32_t lane,
                                               uint32_t d) {
     const uint64_t lane_off = (uint64_t)d * Q * 256u + 4u * lane;
@@ -474,11 +491,11 @@ __device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh,
     uint32_t pre[Q], fl[Q];
     uint32_t slot = 0;
     for (;;) {
-        if (seg_data_phase<D, Q, G, INCL, VEC>(x, y, 0, slot, pt, pre, fl, sh, values, heads,
+        if (seg_data_phase<D, Q, G, INCL, VEC>(x, y, 0, slot, pt, pre, fl, sh, values,
                                                out, n, row_lo, row_hi, num_tiles, ctr, lane, d, lane_off,
                                                word_off))
             break;
-        if (seg_data_phase<D, Q, G, INCL, VEC>(y, x, 1, slot, pt, pre, fl, sh, values, heads,
+        if (seg_data_phase<D, Q, G, INCL, VEC>(y, x, 1, slot, pt, pre, fl, sh, values,
                                                out, n, row_lo, row_hi, num_tiles, ctr, lane, d, lane_off,
                                                word_off))
             break;
@@ -486,14 +503,15 @@ __device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh,
 }
 
 template <int D, int Q, int LB_K, int G, bool INCL, bool VEC>
-__global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *values, const uint32_t *heads,
-                                                               uint32_t *out, uint32_t n,
+__global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *values, uint32_t *out, uint32_t n,
                                                                const uint32_t *offsets, uint32_t num_segments,
                                                                uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
                                                                LookbackCfg cfg) {
     __shared__ SegShared<D, Q> sh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
+    const StartIndex idx = StartIndex::make(offsets, num_segments, sh.sample);
+    idx.load_sample(sh.sample, threadIdx.x, (D + 1) * 64u);
     if (threadIdx.x == 0) {
         const uint32_t g = take_ticket(ctr);
         sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
@@ -502,17 +520,18 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0) {
-        seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, ctr, desc, cfg, SegFallback{values, heads, n}, lane);
+        seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
+                                        SegFallback{values, idx, sh.fb_starts, n}, lane);
     } else {
         // rows outside [offsets[0], offsets[N]) belong to no segment
         const uint32_t lo = offsets[0], hi = offsets[num_segments];
-        seg_data_loop<D, Q, G, INCL, VEC>(pt, sh, values, heads, out, n, uniform(lo < n ? lo : n),
+        seg_data_loop<D, Q, G, INCL, VEC>(pt, sh, values, out, n, uniform(lo < n ? lo : n),
                                           uniform(hi < n ? hi : n), num_tiles, ctr, lane, wave - 1);
     }
 }
 
-// Workspace: header and descriptors as for the flat scan, then the bitmaps.
-inline size_t seg_ws_bytes(uint64_t tiles) { return ws_bytes_for_tiles(tiles) + tiles * kSegWords * 4u; }
+// Workspace: header and descriptors as for the flat scan.
+inline size_t seg_ws_bytes(uint64_t tiles) { return ws_bytes_for_tiles(tiles); }
 
 }  // namespace dwps
 
@@ -536,19 +555,15 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t *ctr = ws_counter(ws);
     uint64_t *desc = ws_desc(ws);
-    uint32_t *heads = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + ws_bytes_for_tiles(tiles));
     const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
-    constexpr int kPreWaves = 4;
-    hipLaunchKernelGGL((seg_prepass_kernel<kSegTile, kPreWaves>), dim3((unsigned)ceil_div(nt, kPreWaves)),
-                       dim3(kPreWaves * 64), 0, s, offsets, num_segments, n32, nt, ctr, desc, heads);
-    if (hipGetLastError() != hipSuccess) return PS_ERR_HIP;
+    if (launch_clear(ws, seg_ws_bytes(tiles), s) != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(values, 16) && aligned(out, 16);
     auto launch = [&](auto kernel) -> ps_status {
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kSegThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
         const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSegThreads), 0, s, values, heads, out, n32, offsets,
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSegThreads), 0, s, values, out, n32, offsets,
                            num_segments, nt, ctr, desc, cfg);
         return PS_OK;
     };

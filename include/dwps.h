@@ -247,10 +247,11 @@ uint64_t ps_small_n_config_get(void);
  * Any overlap of out with values or offsets returns PS_ERR_ALIAS.
  * num_segments may be 0 (nothing is written); num_segments = 2^32 - 1 (an
  * offsets array of 2^32 entries) returns PS_ERR_SIZE, as does n >= 2^32.
- * Two kernels run per call: a pre-pass that writes a bitmap of the segment
- * starts of every tile into the workspace (n/8 bytes, beside the tile
- * descriptors), then the single-pass scan, which reads the values once and
- * writes every row of a segment once. */
+ * Two kernels run per call: the workspace clear (tile descriptors and
+ * counter), then the single-pass scan, which reads the values and, per tile,
+ * the offsets that fall into it (its segment starts) once, and writes every
+ * row of a segment once.  The workspace holds the header and one descriptor
+ * per tile. */
 ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes,
                                 const uint32_t *values, uint64_t n,
                                 const uint32_t *offsets, uint32_t num_segments,

@@ -111,8 +111,8 @@ def test_size_queries():
     for n in (0, 1, stile, stile + 1, 1 << 26, (1 << 32) - 1):
         st, need = _wsq(lib, "ps_segmented_scan_u32", None, n, None, 1 << 16, None, 0, None)
         tiles = -(-n // stile)
-        # header, one descriptor per tile, then a bitmap of segment starts
-        assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256 + tiles * (stile // 8), n
+        # header and one descriptor per tile (the start bitmaps stay in LDS)
+        assert st == 0 and need == 256 + -(-tiles * 8 // 256) * 256, n
     for rb in (4, 8, 16):
         ctile = lib.ps_compact_tile_records(rb)
         assert ctile == 8 * 6 * 64 * (16 // rb)

@@ -137,12 +137,25 @@ def test_unaligned_buffers(dw, orc, inclusive):
 @pytest.mark.parametrize("inclusive", [False, True])
 @pytest.mark.parametrize("nseg", [131071, 131072])
 def test_many_segments(dw, orc, inclusive, nseg):
-    """2^17 segments over 2^22 + 5 values: three-round offset searches in the
-    pre-pass, about 32 elements per segment."""
+    """2^17 segments over 2^22 + 5 values, about 32 elements per segment: a
+    257-entry sample of the offsets, 300-400 starts per tile."""
     n = 32 * 131072 + 5
     x = wl.full_range_u32(n, seed=nseg)
     off = wl.random_segments(n, nseg, seed=nseg + 1, cover=True)
     say("segmented many segments", nseg, inclusive)
+    _check(dw, orc, x, off, inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_more_offsets_than_the_sample_brackets(dw, orc, inclusive):
+    """2^20 + 7 segments (a fifth of them empty) over 2^22 + 9 values: the
+    offsets' sample is capped at 1 024 entries, so its stride exceeds 512 and
+    rounds of evenly spaced probes narrow each tile's bracket before the
+    contiguous loads; a tile holds about 2 400 starts (several batches)."""
+    n = (1 << 22) + 9
+    x = wl.full_range_u32(n, seed=91)
+    off = wl.random_segments(n, (1 << 20) + 7, seed=92, cover=True)
+    say("segmented 2^20 + 7 segments", inclusive)
     _check(dw, orc, x, off, inclusive)
 
 
