@@ -319,3 +319,29 @@ def test_lookback_config_roundtrip():
     finally:
         d.ps_lookback_config(*old)
     assert d.ps_lookback_config_get() == old
+
+
+@pytest.mark.parametrize("lang", ["c99", "c++17"])
+def test_header_and_library_from_plain_c(tmp_path, lang):
+    """tests/c/abi_from_c.c, built as C99 (and as C++17) with warnings as
+    errors against include/dwps.h and linked to libdwps.so, runs its size
+    queries and argument-error checks: the boundary needs neither Python nor
+    torch."""
+    import shutil
+    lib = _lib()
+    libdir = os.path.dirname(lib._name)
+    cc = "gcc" if lang == "c99" else "g++"
+    if shutil.which(cc) is None:
+        pytest.skip("%s not installed" % cc)
+    exe = str(tmp_path / "abi_from_c")
+    cmd = [cc, "-std=" + lang, "-Wall", "-Wextra", "-Werror", "-I" + os.path.join(ROOT, "include")]
+    if lang == "c99":
+        cmd.append("-pedantic")
+    else:
+        cmd += ["-x", "c++"]
+    cmd += [os.path.join(ROOT, "tests", "c", "abi_from_c.c"), "-L" + libdir, "-ldwps",
+            "-Wl,-rpath," + libdir, "-Wl,-rpath-link,/opt/rocm/lib", "-o", exe]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    run = subprocess.run([exe], capture_output=True, text=True)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "FAIL" not in run.stdout and run.stdout.count("ok") >= 10
