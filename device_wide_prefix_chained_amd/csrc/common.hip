@@ -164,6 +164,10 @@ thread_local hipEvent_t t_pending_start = nullptr;
 
 void timing_begin(hipStream_t stream) {
     if (!g_timing_on.load(std::memory_order_relaxed)) return;
+    if (t_pending_start) {  // a call that returned between begin and end
+        (void)hipEventDestroy(t_pending_start);
+        t_pending_start = nullptr;
+    }
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return;
     (void)hipEventRecord(e, stream);
@@ -173,7 +177,11 @@ void timing_begin(hipStream_t stream) {
 void timing_end(hipStream_t stream) {
     if (!g_timing_on.load(std::memory_order_relaxed) || !t_pending_start) return;
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipEventDestroy(t_pending_start);
+        t_pending_start = nullptr;
+        return;
+    }
     (void)hipEventRecord(e, stream);
     std::lock_guard<std::mutex> lk(g_timing_mu);
     g_timing_events.emplace_back(t_pending_start, e);
