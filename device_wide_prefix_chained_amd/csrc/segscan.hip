@@ -70,9 +70,10 @@ struct StartIndex {
         const uint32_t stride = max(kStartBatch, (uint32_t)(((uint64_t)count + kSampleMax - 1u) / kSampleMax));
         return StartIndex{offsets, count, stride, (uint32_t)(((uint64_t)count + stride - 1u) / stride), sample};
     }
-    // Fill the sample (all threads of the workgroup; a barrier must follow).
-    __device__ void load_sample(uint32_t *dst, uint32_t tid, uint32_t nthreads) const {
-        for (uint32_t k = tid; k < ns; k += nthreads) dst[k] = a[(uint64_t)k * stride];
+    // Fill the sample, by the one wave that uses it (its own LDS writes are
+    // visible to its later reads without a barrier).
+    __device__ void load_sample(uint32_t *dst, uint32_t lane) const {
+        for (uint32_t k = lane; k < ns; k += 64u) dst[k] = a[(uint64_t)k * stride];
     }
     // Index at or before the first entry >= tb, at most kStartBatch before it.
     __device__ uint32_t bracket(uint32_t tb, uint32_t lane) const {
@@ -511,7 +512,6 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const StartIndex idx = StartIndex::make(offsets, num_segments, sh.sample);
-    idx.load_sample(sh.sample, threadIdx.x, (D + 1) * 64u);
     if (threadIdx.x == 0) {
         const uint32_t g = take_ticket(ctr);
         sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
@@ -520,6 +520,9 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
     const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
     if (pt.f2 >= num_tiles) return;
     if (wave == 0) {
+        // only the control wave reads the sample: the data waves' first
+        // loads do not wait for it
+        idx.load_sample(sh.sample, lane);
         seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
                                         SegFallback{values, idx, sh.fb_starts, n}, lane);
     } else {
