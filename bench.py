@@ -308,7 +308,10 @@ def main():
     w = build_workload(args.workload)
     run = w["run"]
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
+    # the warm-up runs instrumented too: the timing events it creates are
+    # recycled by the timed steps, which then create none
+    dw.ps_kernel_timing(True)
+    for _ in range(max(args.warmup, 1)):
         run()
     torch.cuda.synchronize()
     print("[bench] warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)

@@ -159,26 +159,50 @@ namespace {
 std::mutex g_timing_mu;
 std::atomic<bool> g_timing_on{false};
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timing_events;
+std::vector<hipEvent_t> g_event_pool;  // created events not holding a record
 thread_local hipEvent_t t_pending_start = nullptr;
+// Timing-only events: recording one performs no system-scope fence (no
+// cache writeback and invalidation between the kernels it separates), so
+// instrumented calls run almost as fast as uninstrumented ones.  They are
+// created once and recycled, so a timed call creates none.
+constexpr unsigned kTimingEventFlags = hipEventDisableSystemFence;
+
+hipEvent_t take_event() {
+    {
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        if (!g_event_pool.empty()) {
+            hipEvent_t e = g_event_pool.back();
+            g_event_pool.pop_back();
+            return e;
+        }
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreateWithFlags(&e, kTimingEventFlags) == hipSuccess ? e : nullptr;
+}
+
+void give_event(hipEvent_t e) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_event_pool.push_back(e);
+}
 }  // namespace
 
 void timing_begin(hipStream_t stream) {
     if (!g_timing_on.load(std::memory_order_relaxed)) return;
     if (t_pending_start) {  // a call that returned between begin and end
-        (void)hipEventDestroy(t_pending_start);
+        give_event(t_pending_start);
         t_pending_start = nullptr;
     }
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
+    hipEvent_t e = take_event();
+    if (!e) return;
     (void)hipEventRecord(e, stream);
     t_pending_start = e;
 }
 
 void timing_end(hipStream_t stream) {
     if (!g_timing_on.load(std::memory_order_relaxed) || !t_pending_start) return;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) {
-        (void)hipEventDestroy(t_pending_start);
+    hipEvent_t e = take_event();
+    if (!e) {
+        give_event(t_pending_start);
         t_pending_start = nullptr;
         return;
     }
@@ -294,9 +318,9 @@ extern "C" void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *parti
 
 extern "C" ps_status ps_kernel_timing(int enable) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    for (auto &pr : g_timing_events) {
-        (void)hipEventDestroy(pr.first);
-        (void)hipEventDestroy(pr.second);
+    for (auto &pr : g_timing_events) {  // recycled: a later record replaces theirs
+        g_event_pool.push_back(pr.first);
+        g_event_pool.push_back(pr.second);
     }
     g_timing_events.clear();
     g_timing_on.store(enable != 0);

@@ -368,7 +368,10 @@ void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows)
 /* Kernel timing with HIP events placed around the main scan kernel of every
  * call (the workspace clear is outside the pair).  enable != 0 starts a new
  * measurement; ps_kernel_timing_read synchronises on the recorded events and
- * returns the summed milliseconds and the number of timed launches. */
+ * returns the summed milliseconds and the number of timed launches.  The
+ * events are created with hipEventDisableSystemFence (recording one writes
+ * back and invalidates no cache) and are recycled across measurements, so a
+ * timed call creates none once a first measurement has run. */
 ps_status ps_kernel_timing(int enable);
 ps_status ps_kernel_timing_read(double *total_ms, uint64_t *launches);
 
