@@ -51,6 +51,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 METRIC = "Gelem/s and % of HBM peak GB/s, 2^28 uint32 exclusive scan on 1 MI355X"
 PROFILES = os.path.join(ROOT, "profiles")
+# The kernel time comes from HIP event pairs on a sample of the timed steps:
+# every 5th main-kernel launch (odd, so the two kernels of a two-kernel step
+# are sampled alike).  Each timed launch carries two event packets (a few µs),
+# which a sample spreads over the wall-clock steps.
+TIMING_EVERY = 5
 
 
 def kernel_source_hash() -> str:
@@ -310,13 +315,13 @@ def main():
     torch.cuda.synchronize()
     # the warm-up runs instrumented too: the timing events it creates are
     # recycled by the timed steps, which then create none
-    dw.ps_kernel_timing(True)
+    dw.ps_kernel_timing(True, every=TIMING_EVERY)
     for _ in range(max(args.warmup, 1)):
         run()
     torch.cuda.synchronize()
     print("[bench] warmup done, timing %d steps" % args.steps, file=sys.stderr, flush=True)
 
-    dw.ps_kernel_timing(True)
+    dw.ps_kernel_timing(True, every=TIMING_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

@@ -381,8 +381,9 @@ def ps_fill_u32(out, value, stream=None):
     return out
 
 
-def ps_kernel_timing(enable: bool) -> None:
-    _check("ps_kernel_timing", lib().ps_kernel_timing(int(bool(enable))))
+def ps_kernel_timing(enable: bool, every: int = 1) -> None:
+    """Start (enable) or stop kernel timing; ``every`` = N times every Nth call."""
+    _check("ps_kernel_timing", lib().ps_kernel_timing(int(every) if enable else 0))
 
 
 def ps_kernel_timing_read():

@@ -157,7 +157,8 @@ uint32_t persistent_grid(const void *kernel, int block_threads, uint32_t work_it
 // ---------------------------------------------------------------------------
 namespace {
 std::mutex g_timing_mu;
-std::atomic<bool> g_timing_on{false};
+std::atomic<uint32_t> g_timing_every{0};  // 0: off; N: time every Nth call
+std::atomic<uint32_t> g_timing_calls{0};   // calls seen since timing was (re)enabled
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timing_events;
 std::vector<hipEvent_t> g_event_pool;  // created events not holding a record
 thread_local hipEvent_t t_pending_start = nullptr;
@@ -187,11 +188,13 @@ void give_event(hipEvent_t e) {
 }  // namespace
 
 void timing_begin(hipStream_t stream) {
-    if (!g_timing_on.load(std::memory_order_relaxed)) return;
+    const uint32_t every = g_timing_every.load(std::memory_order_relaxed);
+    if (!every) return;
     if (t_pending_start) {  // a call that returned between begin and end
         give_event(t_pending_start);
         t_pending_start = nullptr;
     }
+    if (g_timing_calls.fetch_add(1u, std::memory_order_relaxed) % every != 0u) return;
     hipEvent_t e = take_event();
     if (!e) return;
     (void)hipEventRecord(e, stream);
@@ -199,7 +202,7 @@ void timing_begin(hipStream_t stream) {
 }
 
 void timing_end(hipStream_t stream) {
-    if (!g_timing_on.load(std::memory_order_relaxed) || !t_pending_start) return;
+    if (!t_pending_start) return;
     hipEvent_t e = take_event();
     if (!e) {
         give_event(t_pending_start);
@@ -316,14 +319,16 @@ extern "C" void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *parti
     if (partial_windows) *partial_windows = g_partial.load(std::memory_order_relaxed);
 }
 
-extern "C" ps_status ps_kernel_timing(int enable) {
+extern "C" ps_status ps_kernel_timing(int every) {
+    if (every < 0) return PS_ERR_SIZE;
     std::lock_guard<std::mutex> lk(g_timing_mu);
     for (auto &pr : g_timing_events) {  // recycled: a later record replaces theirs
         g_event_pool.push_back(pr.first);
         g_event_pool.push_back(pr.second);
     }
     g_timing_events.clear();
-    g_timing_on.store(enable != 0);
+    g_timing_calls.store(0u);
+    g_timing_every.store((uint32_t)every);
     return PS_OK;
 }
 

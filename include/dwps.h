@@ -365,14 +365,18 @@ uint32_t ps_lookback_group(void);
 ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows);
 void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows);
 
-/* Kernel timing with HIP events placed around the main scan kernel of every
- * call (the workspace clear is outside the pair).  enable != 0 starts a new
- * measurement; ps_kernel_timing_read synchronises on the recorded events and
- * returns the summed milliseconds and the number of timed launches.  The
- * events are created with hipEventDisableSystemFence (recording one writes
- * back and invalidates no cache) and are recycled across measurements, so a
- * timed call creates none once a first measurement has run. */
-ps_status ps_kernel_timing(int enable);
+/* Kernel timing with HIP events placed around the main scan kernel of a
+ * call (the workspace clear is outside the pair).  every = 0 turns timing
+ * off; every = N >= 1 starts a new measurement that times the 1st, (N+1)th,
+ * (2N+1)th ... call from now on (1 = every call); a negative value returns
+ * PS_ERR_SIZE.  ps_kernel_timing_read synchronises on the recorded events
+ * and returns the summed milliseconds and the number of timed launches.
+ * The events are created with hipEventDisableSystemFence (recording one
+ * writes back and invalidates no cache) and are recycled across
+ * measurements, so a timed call creates none once a first measurement has
+ * run; each timed call still carries two event packets (a few µs), which
+ * timing a sample of the calls spreads thin. */
+ps_status ps_kernel_timing(int every);
 ps_status ps_kernel_timing_read(double *total_ms, uint64_t *launches);
 
 /* Elements per tile of the flat scan kernel for `dtype` (PS_U64: the

@@ -345,3 +345,9 @@ def test_header_and_library_from_plain_c(tmp_path, lang):
     run = subprocess.run([exe], capture_output=True, text=True)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "FAIL" not in run.stdout and run.stdout.count("ok") >= 10
+
+
+def test_kernel_timing_arguments():
+    lib = _lib()
+    assert lib.ps_kernel_timing(-1) == 3          # PS_ERR_SIZE
+    assert lib.ps_kernel_timing(4) == 0 and lib.ps_kernel_timing(0) == 0

@@ -42,3 +42,22 @@ def test_read_leaves_sink(dw, n):
     sink = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
     dw.ps_read_u32(dev(x), sink)
     assert int(host(sink)[0]) == 12345
+
+
+def test_kernel_timing_samples_every_nth_call(dw):
+    """ps_kernel_timing(every=N) times the 1st, (N+1)th, ... main-kernel
+    launch: 7 calls at N = 3 give 3 timed launches, each a plausible kernel
+    time; N = 1 times all of them; timing off records none."""
+    import torch
+    x = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    for every, calls, want in ((3, 7, 3), (1, 4, 4), (5, 5, 1)):
+        dw.ps_kernel_timing(True, every=every)
+        for _ in range(calls):
+            dw.ps_copy_u32(x, y)
+        ms, launches = dw.ps_kernel_timing_read()
+        assert launches == want, (every, calls, launches)
+        assert 0.0 < ms / launches < 10.0
+    dw.ps_kernel_timing(False)
+    dw.ps_copy_u32(x, y)
+    assert dw.ps_kernel_timing_read() == (0.0, 0)
