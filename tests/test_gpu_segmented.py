@@ -66,6 +66,10 @@ def test_special_segmentations(dw, orc, inclusive):
         "heads one past tile edges": np.concatenate(([0], np.arange(1, n, TILE), [n])).astype(np.uint32),
         "empties between": np.array([0, 10, 10, 10, TILE, TILE, 3 * TILE, n, n], np.uint32),
         "gap at both ends": np.array([TILE + 5, 2 * TILE, 3 * TILE + 1, n - 100], np.uint32),
+        # runs of repeated offsets longer than one 512-entry batch of the
+        # start search, inside a tile and on a tile edge
+        "long runs of empty segments": np.concatenate(
+            ([0], np.full(2000, 777), np.full(1500, TILE), [TILE + 3], np.full(600, n - 1), [n])).astype(np.uint32),
     }
     for name, off in cases.items():
         say("segmented special", name, inclusive)
