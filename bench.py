@@ -6,9 +6,9 @@
 A step is one call of the library entry point over the whole input resident
 in HBM (workspace clear + the single-pass kernel).  W untimed steps, then K
 steps timed with the wall clock between two device synchronisations; HIP
-events that the library records around its main kernel on the same stream
-give that kernel's average duration for the roofline figure.  Prints one JSON
-line.
+events that the library records around its main kernel on the same stream,
+on every 5th of those steps, give that kernel's average duration for the
+roofline figure.  Prints one JSON line.
 
 Workloads (default: u32x): the headline is the uint32 exclusive sum scan of
 2^28 elements, values uniform in [0, 255] (seed 2).  The others time the
