@@ -100,13 +100,11 @@ def build_workload(name: str):
         x = wl.small_u32()
         d_in, d_out = dev(x), torch.empty(n, dtype=torch.int32, device="cuda")
         if name == "u32s":
-            ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None),
-                             dtype=torch.uint8, device="cuda")
+            ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None))
             run = lambda: dw.ps_scan_exclusive_u32(d_in, d_out, workspace=ws)  # noqa: E731
             form = "default entry point (two-level form at this size)"
         else:
-            ws = torch.empty(dw.workspace_bytes("ps_scan_single_pass", 0, 0, 0, None, None, n, None, None),
-                             dtype=torch.uint8, device="cuda")
+            ws = dw.new_workspace(dw.workspace_bytes("ps_scan_single_pass", 0, 0, 0, None, None, n, None, None))
             run = lambda: dw.ps_scan_single_pass("sum", False, d_in, d_out, workspace=ws)  # noqa: E731
             form = "single-pass form forced"
         tile = dw.ps_two_level_tile_elements() if name == "u32s" else dw.ps_tile_elements(0)
@@ -138,7 +136,7 @@ def build_workload(name: str):
         else:
             incl = name == "u32i"
             fn = "ps_scan_inclusive_u32" if incl else "ps_scan_exclusive_u32"
-            ws = torch.empty(dw.workspace_bytes(fn, None, None, n, None, None), dtype=torch.uint8, device="cuda")
+            ws = dw.new_workspace(dw.workspace_bytes(fn, None, None, n, None, None))
             f = getattr(dw, fn)
             run = lambda: f(d_in, d_out, total, workspace=ws)  # noqa: E731
             desc = "u32 %s sum scan, n=%s, values uniform in [0,255], seed 2" % (
@@ -150,8 +148,7 @@ def build_workload(name: str):
         x = wl.large_u32()
         d_in, d_out = dev(x), torch.empty(n, dtype=torch.int64, device="cuda")
         total = torch.zeros(1, dtype=torch.int64, device="cuda")
-        ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None),
-                         dtype=torch.uint8, device="cuda")
+        ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None))
         run = lambda: dw.ps_scan_exclusive_u32_u64(d_in, d_out, total, workspace=ws)  # noqa: E731
         return dict(desc="widening u32 -> u64 exclusive sum scan, n=2^28, values uniform in [0,255], seed 2",
                     dtype="u64", n=n, bytes=12.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=False,
@@ -161,8 +158,7 @@ def build_workload(name: str):
         x = wl.f32_normal()
         d_in, d_out = dev(x), torch.empty(n, dtype=torch.float32, device="cuda")
         op = "sum" if name == "f32" else "max"
-        ws = torch.empty(dw.workspace_bytes("ps_scan", 0, 1, 1, None, None, n, None, None),
-                         dtype=torch.uint8, device="cuda")
+        ws = dw.new_workspace(dw.workspace_bytes("ps_scan", 0, 1, 1, None, None, n, None, None))
         run = lambda: dw.ps_scan(op, True, d_in, d_out, workspace=ws)  # noqa: E731
         return dict(desc="fp32 inclusive %s scan, n=2^27, N(0,1), seed 3" % op, dtype="f32", n=n,
                     bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=True, kind="f32" + op)
@@ -173,8 +169,7 @@ def build_workload(name: str):
         d_a, d_b = dev(a), dev(b)
         d_ob = torch.empty(n, dtype=torch.float32, device="cuda")
         d_oa = torch.empty(n, dtype=torch.float32, device="cuda") if name == "linrec" else None
-        ws = torch.empty(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 1, None, None),
-                         dtype=torch.uint8, device="cuda")
+        ws = dw.new_workspace(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 1, None, None))
         run = lambda: dw.ps_scan_linrec_f32(d_a, d_b, d_ob, out_a=d_oa, inclusive=True,  # noqa: E731
                                             workspace=ws)
         both = name == "linrec"
@@ -187,8 +182,7 @@ def build_workload(name: str):
         n = values.size
         d_v, d_o = dev(values), dev(off)
         d_out = torch.empty(n, dtype=torch.int32, device="cuda")
-        ws = torch.empty(dw.workspace_bytes("ps_segmented_scan_u32", None, n, None, off.size - 1, None, 0, None),
-                         dtype=torch.uint8, device="cuda")
+        ws = dw.new_workspace(dw.workspace_bytes("ps_segmented_scan_u32", None, n, None, off.size - 1, None, 0, None))
         run = lambda: dw.ps_segmented_scan_u32(d_v, d_o, d_out, inclusive=False, workspace=ws)  # noqa: E731
         return dict(desc="segmented u32 exclusive sum scan, 2^26 values U[0,1023], 2^16 CSR segments "
                          "(10% empty, one with 25% of the elements, rank-size Zipf(1.2)), seed 5",
@@ -203,8 +197,7 @@ def build_workload(name: str):
         d_out = torch.empty_like(d_r)
         cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
         fn = "ps_compact_staged" if staged else "ps_compact"
-        ws = torch.empty(dw.workspace_bytes(fn, None, 16, None, n, None, None, None),
-                         dtype=torch.uint8, device="cuda")
+        ws = dw.new_workspace(dw.workspace_bytes(fn, None, 16, None, n, None, None, None))
         f = getattr(dw, fn)
         run = lambda: f(d_r, d_f, d_out, cnt, workspace=ws)  # noqa: E731
         # staged: flag scan (1 B read, 4 B written) + scatter (1 + 4 + 16 B read)

@@ -2,10 +2,13 @@
 
 Each Python function has the name of the C entry point it wraps (see
 ``include/dwps.h`` for the contract).  Tensors are PyTorch CUDA (HIP) tensors;
-PyTorch supplies device memory (outputs and workspaces the caller does not
-pass are allocated with ``torch.empty``) and the current stream.  Every step
-of the computation runs in the library's HIP kernels; there is no fallback:
-if the library is missing or a call fails, an exception is raised.
+PyTorch supplies device memory and streams.  A call that is given no
+workspace uses one kept per (device, stream), allocated on that stream and
+prepared once with ``ps_workspace_init``, so it is one kernel launch like
+any other and its workspace is never handed to another stream while in use.
+Every step of the computation runs in the library's HIP kernels; there is
+no fallback: if the library is missing or a call fails, an exception is
+raised.
 """
 from __future__ import annotations
 
@@ -23,6 +26,13 @@ PS_U32, PS_F32, PS_U64 = 0, 1, 2
 PS_OP_SUM, PS_OP_MAX, PS_OP_MIN, PS_OP_AND, PS_OP_OR, PS_OP_XOR, PS_OP_AFFINE16 = range(7)
 OPS = {"sum": PS_OP_SUM, "max": PS_OP_MAX, "min": PS_OP_MIN, "and": PS_OP_AND,
        "or": PS_OP_OR, "xor": PS_OP_XOR, "affine16": PS_OP_AFFINE16}
+
+# workspace header words and error bits (ps_ws_word, ps_ws_error)
+PS_WS_HEADER_BYTES = 256
+(PS_WS_TICKET, PS_WS_ERROR, PS_WS_FALLBACKS, PS_WS_PARTIALS, PS_WS_TAG, PS_WS_DONE, PS_WS_MAGIC,
+ PS_WS_CAPACITY, PS_WS_HIGH, PS_WS_DIRTY_LO, PS_WS_DIRTY_HI, PS_WS_READY, PS_WS_CALLS) = range(13)
+PS_WS_ERR_SPIN, PS_WS_ERR_NOT_PREPARED, PS_WS_ERR_CAPACITY = 1, 2, 4
+PS_DEBUG_WITHHOLD_AGGREGATES = 1
 
 _U32_DTYPES = (torch.uint32, torch.int32)
 _U64_DTYPES = (torch.uint64, torch.int64)
@@ -105,6 +115,12 @@ def lib() -> ctypes.CDLL:
     L.ps_segmented_tile_elements.restype = u32
     L.ps_compact_tile_records.argtypes = [u32]
     L.ps_compact_tile_records.restype = u32
+    L.ps_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
+    L.ps_workspace_init.restype = i32
+    L.ps_lookback_debug.argtypes = [u32]
+    L.ps_lookback_debug.restype = i32
+    L.ps_lookback_debug_get.argtypes = []
+    L.ps_lookback_debug_get.restype = u32
     L.ps_version.argtypes = []
     L.ps_version.restype = ctypes.c_char_p
     L.ps_status_string.argtypes = [i32]
@@ -122,12 +138,18 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(t, stream):
+def _torch_stream(device, stream):
+    """The call's stream as a torch stream object (the current stream of
+    ``device`` when None; raw hipStream_t handles are wrapped)."""
     if stream is None:
-        stream = torch.cuda.current_stream(t.device)
+        return torch.cuda.current_stream(device)
     if isinstance(stream, torch.cuda.Stream):
-        return ctypes.c_void_p(stream.cuda_stream)
-    return ctypes.c_void_p(int(stream))
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _stream(t, stream):
+    return ctypes.c_void_p(_torch_stream(t.device, stream).cuda_stream)
 
 
 def _dev_tensor(name, t, dtypes=None, numel=None):
@@ -144,12 +166,53 @@ def _dev_tensor(name, t, dtypes=None, numel=None):
     return t
 
 
-def _workspace(fn: str, call, device, workspace):
-    """CUB-style size query, then a torch byte buffer when none is given."""
+def ps_workspace_init(workspace, stream=None):
+    """Prepare a workspace (a uint8 device tensor) for its first use."""
+    _dev_tensor("workspace", workspace)
+    _check("ps_workspace_init", lib().ps_workspace_init(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(workspace, stream)))
+    return workspace
+
+
+def new_workspace(nbytes, device="cuda", stream=None):
+    """A prepared workspace of at least ``nbytes`` bytes, allocated on the
+    stream that will use it (the current stream when None)."""
+    device = torch.device(device)
+    ts = _torch_stream(device, stream)
+    with torch.cuda.stream(ts):
+        ws = torch.empty(max(int(nbytes), PS_WS_HEADER_BYTES), dtype=torch.uint8, device=device)
+    return ps_workspace_init(ws, stream=ts)
+
+
+_WS_CACHE = {}
+
+
+def _cached_workspace(fn, need, device, stream):
+    ts = _torch_stream(device, stream)
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, ts.cuda_stream)
+    ws = _WS_CACHE.get(key)
+    if ws is not None and ws.numel() >= need:
+        return ws
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("%s: pass a workspace (new_workspace) when capturing a graph" % fn)
+    # grow geometrically; the old buffer was only ever used on this stream,
+    # so the allocator may hand it out again in this stream's order
+    size = max(int(need), 1 << 16)
+    if ws is not None:
+        size = max(size, 2 * ws.numel())
+    ws = new_workspace(size, device, ts)
+    _WS_CACHE[key] = ws
+    return ws
+
+
+def _workspace(fn: str, call, device, workspace, stream=None):
+    """CUB-style size query; the call's workspace, or the prepared one kept
+    for its device and stream when none is given."""
     need = ctypes.c_size_t(0)
     _check(fn, call(None, ctypes.byref(need)))
     if workspace is None:
-        workspace = torch.empty(max(int(need.value), 1), dtype=torch.uint8, device=device)
+        workspace = _cached_workspace(fn, int(need.value), device, stream)
     else:
         _dev_tensor("workspace", workspace)
     have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
@@ -169,7 +232,7 @@ def _flat(fn: str, inp, out, total, workspace, stream, dtypes, out_dtypes=None):
     n = inp.numel()
     s = _stream(inp, stream)
     call = lambda ws, wsb: f(ws, wsb, _ptr(inp), _ptr(out), n, _ptr(total), s)  # noqa: E731
-    ws, have = _workspace(fn, call, inp.device, workspace)
+    ws, have = _workspace(fn, call, inp.device, workspace, stream)
     _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -244,7 +307,7 @@ def _generic(fn, op, inclusive, inp, out, total, workspace, stream, dtype):
     f = getattr(L, fn)
     call = lambda ws, wsb: f(ws, wsb, opc, dtype, int(bool(inclusive)), _ptr(inp),  # noqa: E731
                              _ptr(out), n, _ptr(total), s)
-    ws, have = _workspace(fn, call, inp.device, workspace)
+    ws, have = _workspace(fn, call, inp.device, workspace, stream)
     _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -265,7 +328,7 @@ def ps_scan_linrec_f32(a, b, out_b, out_a=None, inclusive=True, total=None, work
     L = lib()
     call = lambda ws, wsb: L.ps_scan_linrec_f32(ws, wsb, _ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b),  # noqa: E731
                                                 n, int(bool(inclusive)), _ptr(total), s)
-    ws, have = _workspace("ps_scan_linrec_f32", call, a.device, workspace)
+    ws, have = _workspace("ps_scan_linrec_f32", call, a.device, workspace, stream)
     _check("ps_scan_linrec_f32", call(_ptr(ws), ctypes.byref(have)))
     return out_b
 
@@ -283,7 +346,7 @@ def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None,
     L = lib()
     call = lambda ws, wsb: L.ps_lookback_stats_u32(ws, wsb, _ptr(inp), _ptr(out), n,  # noqa: E731
                                                    _ptr(stats), int(bool(aggregate_only)), s)
-    ws, have = _workspace("ps_lookback_stats_u32", call, inp.device, workspace)
+    ws, have = _workspace("ps_lookback_stats_u32", call, inp.device, workspace, stream)
     _check("ps_lookback_stats_u32", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
@@ -307,7 +370,7 @@ def ps_segmented_scan_u32(values, offsets, out, inclusive=False, workspace=None,
     L = lib()
     call = lambda ws, wsb: L.ps_segmented_scan_u32(ws, wsb, _ptr(values), n, _ptr(offsets),  # noqa: E731
                                                    nseg, _ptr(out), int(bool(inclusive)), s)
-    ws, have = _workspace("ps_segmented_scan_u32", call, values.device, workspace)
+    ws, have = _workspace("ps_segmented_scan_u32", call, values.device, workspace, stream)
     _check("ps_segmented_scan_u32", call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -354,7 +417,7 @@ def _compact(fn, records, flags, out, num_selected, workspace, stream):
     f = getattr(L, fn)
     call = lambda ws, wsb: f(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa: E731
                              _ptr(out), _ptr(num_selected), s)
-    ws, have = _workspace(fn, call, flags.device, workspace)
+    ws, have = _workspace(fn, call, flags.device, workspace, stream)
     _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -407,6 +470,23 @@ def ps_lookback_config(fallback_polls: int, partial_windows: int) -> None:
     stalled polls (0 = never); PARTIAL descriptors after this many windows
     walked without an inclusive prefix (0 = never)."""
     _check("ps_lookback_config", lib().ps_lookback_config(int(fallback_polls), int(partial_windows)))
+
+
+def ps_lookback_debug(flags: int) -> None:
+    """Debug settings of every later single-pass call (PS_DEBUG_* bits; 0 = off)."""
+    _check("ps_lookback_debug", lib().ps_lookback_debug(int(flags)))
+
+
+def ps_lookback_debug_get() -> int:
+    return int(lib().ps_lookback_debug_get())
+
+
+def workspace_header(workspace):
+    """The header words of a workspace as Python ints (synchronises)."""
+    import numpy as np
+    torch.cuda.synchronize(workspace.device)
+    h = workspace[:PS_WS_HEADER_BYTES].cpu().numpy().view(np.uint32)
+    return [int(v) for v in h[:PS_WS_CALLS + 1]]
 
 
 def ps_lookback_config_get():

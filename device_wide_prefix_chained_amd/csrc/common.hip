@@ -1,5 +1,6 @@
-// common.hip -- workspace clearing, the calibration copy kernel, the offsets
-// validator, kernel-timing events and the status/version strings.
+// common.hip -- workspace preparation, the calibration copy kernel, the
+// offsets validator, kernel-timing events, the process-wide settings and the
+// status/version strings.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -8,21 +9,26 @@
 #include <vector>
 
 #include "host_common.hpp"
+#include "ws_state.hpp"
 
 namespace dwps {
 
-__global__ void clear_kernel(uint4 *p, uint64_t n16) {
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-        p[i] = make_uint4(0u, 0u, 0u, 0u);
+// Prepared header: nothing in flight, tag 0, every descriptor word dirty
+// (the first call zeroes the words it uses).  Only the header is written.
+__global__ void ws_init_kernel(uint32_t *hdr, uint32_t capacity) {
+    const uint32_t i = threadIdx.x;
+    if (i >= kWsHeader / 4) return;
+    uint32_t v = 0u;
+    if (i == kHdrMagic) v = kWsMagic;
+    if (i == kHdrCapacity || i == kHdrDirtyHi) v = capacity;
+    hdr[i] = v;
 }
 
-hipError_t launch_clear(void *p, size_t bytes, hipStream_t stream) {
-    const uint64_t n16 = bytes / 16;
-    if (!n16) return hipSuccess;
-    const uint64_t blocks = ceil_div(n16, 256);
-    const unsigned grid = (unsigned)(blocks < 2048 ? blocks : 2048);
-    hipLaunchKernelGGL(clear_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint4 *>(p), n16);
+hipError_t launch_ws_init(void *ws, size_t bytes, hipStream_t stream) {
+    const uint64_t words = (bytes - kWsHeader) / 8u;
+    const uint32_t capacity = words > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)words;
+    hipLaunchKernelGGL(ws_init_kernel, dim3(1), dim3(kWsHeader / 4), 0, stream, static_cast<uint32_t *>(ws),
+                       capacity);
     return hipGetLastError();
 }
 
@@ -299,14 +305,32 @@ extern "C" ps_status ps_validate_offsets(const uint32_t *offsets, uint32_t num_s
 namespace {
 std::atomic<uint32_t> g_fallback_after{4096u};
 std::atomic<uint32_t> g_partial{4u};
+std::atomic<uint32_t> g_debug{0u};
 std::atomic<uint64_t> g_small_n{1ull << 23};
 }  // namespace
 
 namespace dwps {
 uint32_t lookback_fallback_after() { return g_fallback_after.load(std::memory_order_relaxed); }
 uint32_t lookback_partial() { return g_partial.load(std::memory_order_relaxed); }
+uint32_t lookback_debug_flags() { return g_debug.load(std::memory_order_relaxed); }
 uint64_t small_n_max() { return g_small_n.load(std::memory_order_relaxed); }
 }  // namespace dwps
+
+extern "C" ps_status ps_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return PS_ERR_NULL;
+    if (!aligned(ws, 16)) return PS_ERR_ALIGNMENT;
+    if (ws_bytes < kWsHeader) return PS_ERR_WORKSPACE;
+    if (launch_ws_init(ws, ws_bytes, static_cast<hipStream_t>(stream)) != hipSuccess) return PS_ERR_HIP;
+    return PS_OK;
+}
+
+extern "C" ps_status ps_lookback_debug(uint32_t flags) {
+    if (flags & ~(uint32_t)PS_DEBUG_WITHHOLD_AGGREGATES) return PS_ERR_UNSUPPORTED;
+    g_debug.store(flags, std::memory_order_relaxed);
+    return PS_OK;
+}
+
+extern "C" uint32_t ps_lookback_debug_get(void) { return g_debug.load(std::memory_order_relaxed); }
 
 extern "C" ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows) {
     g_fallback_after.store(fallback_polls, std::memory_order_relaxed);

@@ -134,7 +134,6 @@ struct CompactShared {
     v4u park[kParkSlots][D * Q * 64];  // kept records of each wave's span, compacted, in the wave's part
     uint2 park_wave[kParkSlots][D];    // per wave, (offset in the tile's output, count) of its parked run
     uint32_t wt[2][D];                 // wave counts, double-buffered by phase parity
-    uint32_t t0;
     uint32_t next;
     uint32_t prefix;                   // output base of the tile stored in the phase
 };
@@ -283,22 +282,25 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
                                                                uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
                                                                LookbackCfg cfg) {
     __shared__ CompactShared<D, Q> sh;
+    __shared__ WsShared wsh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
-    if (threadIdx.x == 0) {
-        const uint32_t g = take_ticket(ctr);
-        sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
+    uint32_t t0;
+    const WsCall call = ws_start<G>(ctr, desc, num_tiles, num_tiles, wsh, t0);
+    cfg.tf = tag_field(call.plan.tag);
+    if (t0 < num_tiles) {
+        const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, t0};
+        using Fb = CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>;
+        if (wave == 0) {
+            ws_wait_clean(call, ctr);
+            control_loop3<SumU32, D, LB_K, G, false, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
+                                                                  nullptr, 0, cfg, Fb{flags, n}, lane);
+        } else {
+            compact_data_loop3<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
+                                                  wave - 1);
+        }
     }
-    __syncthreads();
-    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
-    if (pt.f2 >= num_tiles) return;
-    using Fb = CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>;
-    if (wave == 0)
-        control_loop3<SumU32, D, LB_K, G, false, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
-                                                              nullptr, 0, cfg, Fb{flags, n}, lane);
-    else
-        compact_data_loop3<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
-                                              wave - 1);
+    ws_finish(wsh, num_tiles, ctr);
 }
 
 __global__ void write_count_zero(uint64_t *p) { *p = 0ull; }
@@ -335,7 +337,6 @@ ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const 
     if (ranges_overlap(out, bytes, records, bytes) || ranges_overlap(out, bytes, flags, n) ||
         ranges_overlap(num_selected, 8, out, bytes))
         return PS_ERR_ALIAS;
-    if (launch_clear(ws, ws_bytes_for_tiles(tiles), s) != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(records, 16) && aligned(flags, 16 / sizeof(Rec));
     const Rec *rin = static_cast<const Rec *>(records);
     Rec *rout = static_cast<Rec *>(out);
@@ -346,7 +347,7 @@ ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const 
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kCompactThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
-        const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
+        const LookbackCfg cfg = lookback_cfg(false);
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCompactThreads), 0, s, rin, flags, n32, rout, num_selected,
                            nt, ctr, desc, cfg);
         return PS_OK;

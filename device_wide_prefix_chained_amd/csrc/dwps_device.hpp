@@ -20,6 +20,8 @@
 
 #include <type_traits>
 
+#include "ws_state.hpp"
+
 namespace dwps {
 
 // ---------------------------------------------------------------------------
@@ -208,14 +210,16 @@ __device__ __forceinline__ T read_lane(T x, int lane) {
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // ---------------------------------------------------------------------------
-// Tile descriptors: state in the high 32 bits, payload in the low 32 bits,
-// so one atomic store publishes both and one atomic load reads a consistent
-// pair.  Agent (device) scope: readers are on other XCDs of the same GPU,
-// never on the host or a peer device.  The ordering that matters -- the tile's
-// own LDS/register scan before its publication -- is program order within the
-// publishing lane after a workgroup barrier, so relaxed ordering suffices;
-// no other memory is handed over through a descriptor.
-// High word: bits 1..0 the state, bits 31..2 the distance of a PARTIAL.
+// Tile descriptors: state word in the high 32 bits, payload in the low 32
+// bits, so one atomic store publishes both and one atomic load reads a
+// consistent pair.  Agent (device) scope: readers are on other XCDs of the
+// same GPU, never on the host or a peer device.  The ordering that matters
+// -- the tile's own LDS/register scan before its publication -- is program
+// order within the publishing lane after a workgroup barrier, so relaxed
+// ordering suffices; no other memory is handed over through a descriptor.
+// State word: bits 1..0 the state, bits 10..2 the tag of the call that
+// wrote it, bits 31..11 the distance of a PARTIAL (ws_state.hpp); a word
+// carrying another call's tag reads as INVALID.
 // ---------------------------------------------------------------------------
 constexpr uint32_t ST_INVALID = 0u;    // nothing published
 constexpr uint32_t ST_AGGREGATE = 1u;  // payload = the tile's own fold
@@ -231,11 +235,14 @@ __device__ __forceinline__ void desc_publish(uint64_t *d, uint64_t w) {
 __device__ __forceinline__ uint64_t desc_poll(const uint64_t *d) {
     return __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Install a descriptor computed by another tile's fallback: only over
-// INVALID, so a word the owner (or an earlier fallback) published stays.
-__device__ __forceinline__ bool desc_install(uint64_t *d, uint64_t w) {
-    uint64_t expected = 0ull;
-    return __hip_atomic_compare_exchange_strong(d, &expected, w, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+// Install a descriptor computed by another tile's fallback: only over a
+// word that the call with tag field tf sees as INVALID (zero, or left by
+// another call), so a word the owner (or an earlier fallback) published in
+// this call stays.
+__device__ __forceinline__ bool desc_install(uint64_t *d, uint64_t w, uint32_t tf) {
+    uint64_t seen = desc_poll(d);
+    if (state_seen((uint32_t)(seen >> 32), tf) != ST_INVALID) return false;
+    return __hip_atomic_compare_exchange_strong(d, &seen, w, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr) {
@@ -246,35 +253,38 @@ __device__ __forceinline__ void count_event(uint32_t *word) {
 }
 
 // A descriptor's content: the state word (state in bits 1..0, a PARTIAL's
-// distance in bits 31..2) and the payload.
+// distance from bit kDistShift up; the tag is added on publication) and the
+// payload.
 template <class T>
 struct DescVal {
     uint32_t state;
     T value;
 };
 
-// One 64-bit word per tile: state word high, 32-bit payload low.
+// One 64-bit word per tile: state word high, 32-bit payload low.  read()
+// returns the state word as the call with tag field tf sees it (0 when
+// another call wrote it); publish() and install() add tf.
 template <class Op>
 struct Words1 {
     using T = typename Op::T;
     static constexpr int WORDS = 1;
-    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t &state, T &v) {
+    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t tf, uint32_t &state, T &v) {
         const uint64_t w = desc_poll(desc + tile);
-        state = (uint32_t)(w >> 32);
+        state = state_seen((uint32_t)(w >> 32), tf);
         v = from_bits<T>((uint32_t)w);
     }
-    __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
-        desc_publish(desc + tile, ((uint64_t)state << 32) | to_bits(v));
+    __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t tf, uint32_t state, T v) {
+        desc_publish(desc + tile, ((uint64_t)(state | tf) << 32) | to_bits(v));
     }
-    __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
-        return desc_install(desc + tile, ((uint64_t)state << 32) | to_bits(v));
+    __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t tf, uint32_t state, T v) {
+        return desc_install(desc + tile, ((uint64_t)(state | tf) << 32) | to_bits(v), tf);
     }
 };
 
 // Two 64-bit words per tile for a 64-bit payload: word 0 = state word | low
 // half, word 1 = state word | high half, each one atomic store.  A reader
 // takes the tile only when both state words agree.  Every state word
-// (state and distance) is published with one payload only, so agreeing
+// (state, tag and distance) is published with one payload only, so agreeing
 // words hold the two halves of one value; a read that meets a publication
 // half done sees two different state words and polls again.  The one
 // exception is a fallback's install racing the owner's own first
@@ -285,21 +295,21 @@ template <class Op>
 struct Words2 {
     using T = typename Op::T;
     static constexpr int WORDS = 2;
-    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t &state, T &v) {
+    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t tf, uint32_t &state, T &v) {
         const uint64_t w0 = desc_poll(desc + 2 * tile), w1 = desc_poll(desc + 2 * tile + 1);
-        const uint32_t s0 = (uint32_t)(w0 >> 32), s1 = (uint32_t)(w1 >> 32);
+        const uint32_t s0 = state_seen((uint32_t)(w0 >> 32), tf), s1 = state_seen((uint32_t)(w1 >> 32), tf);
         state = (s0 == s1) ? s0 : ST_INVALID;
         v = from_bits64<T>(((uint64_t)(uint32_t)w1 << 32) | (uint32_t)w0);
     }
-    __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
-        const uint64_t b = to_bits64(v), sw = (uint64_t)state << 32;
+    __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t tf, uint32_t state, T v) {
+        const uint64_t b = to_bits64(v), sw = (uint64_t)(state | tf) << 32;
         desc_publish(desc + 2 * (uint64_t)tile, sw | (uint32_t)b);
         desc_publish(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32));
     }
-    __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t state, T v) {
-        const uint64_t b = to_bits64(v), sw = (uint64_t)state << 32;
-        const bool lo = desc_install(desc + 2 * (uint64_t)tile, sw | (uint32_t)b);
-        const bool hi = desc_install(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32));
+    __device__ static bool install(uint64_t *desc, uint32_t tile, uint32_t tf, uint32_t state, T v) {
+        const uint64_t b = to_bits64(v), sw = (uint64_t)(state | tf) << 32;
+        const bool lo = desc_install(desc + 2 * (uint64_t)tile, sw | (uint32_t)b, tf);
+        const bool hi = desc_install(desc + 2 * (uint64_t)tile + 1, sw | (uint32_t)(b >> 32), tf);
         return lo || hi;
     }
 };
@@ -319,22 +329,24 @@ struct LookbackStats {
     uint32_t stalls = 0;   // polls that found an unpublished predecessor
 };
 
-// Workspace header words (32-bit): [0] ticket counter, [1] error word,
-// [2] fallbacks performed, [3] PARTIAL descriptors published (counted by the
-// instrumented scan only).
-constexpr int kHdrError = 1;
-constexpr int kHdrFallbacks = 2;
-constexpr int kHdrPartials = 3;
-
 // What a look-back may do besides waiting: after `fallback_after` stalled
 // polls in a row (0 = never) reduce the stalled predecessor's input itself;
 // once it has walked `partial` windows without reaching an inclusive prefix
 // (0 = never), publish a PARTIAL descriptor for its own tile after every
-// further window.
+// further window.  `flags` are debug settings of the whole kernel (kDbg*);
+// `tf` is the tag field of the call, filled in on the device.
 struct LookbackCfg {
     uint32_t fallback_after;
     uint32_t partial;
+    uint32_t flags;
+    uint32_t tf;
 };
+
+// Debug setting: tiles never publish their AGGREGATE (only PREFIX, and
+// PARTIALs), so every look-back that reaches a tile before its owner has
+// resolved its prefix stalls there -- with a fallback configured, that
+// fallback is what supplies the aggregate.
+constexpr uint32_t kDbgWithholdAggregates = PS_DEBUG_WITHHOLD_AGGREGATES;
 
 // Safety net of the spin: a wave that finds an unpublished predecessor this
 // many times in a row (seconds of waiting; a healthy chain needs a few) gives
@@ -368,13 +380,13 @@ __device__ __forceinline__ int64_t window_index(int64_t base, uint32_t lane, int
 // (no branch around a load, so one poll costs one round trip); words before
 // tile 0 read tile 0's and are replaced by the caller.
 template <class Op, int K, bool BLOCKED, class W = WordsFor<Op>>
-__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane,
+__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane, uint32_t tf,
                                             Window<typename Op::T, K> &win) {
     const int64_t base = nearest - 64 * K + 1;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const int64_t idx = window_index<K, BLOCKED>(base, lane, j);
-        W::read(desc, idx >= 0 ? idx : 0, win.sw[j], win.val[j]);
+        W::read(desc, idx >= 0 ? idx : 0, tf, win.sw[j], win.val[j]);
     }
 }
 
@@ -431,7 +443,7 @@ __device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint3
         if (use_pre)
             win = *pre;
         else
-            window_load<Op, K, true, W>(desc, nearest, lane, win);
+            window_load<Op, K, true, W>(desc, nearest, lane, cfg.tf, win);
         use_pre = false;
         uint32_t sw[K];  // state words
         T val[K];
@@ -471,7 +483,7 @@ __device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint3
                 const uint32_t li = 63u - (uint32_t)__builtin_clzll(imask);
                 const int64_t p = base + 64 * ji + (int64_t)li;
                 const DescVal<T> dv = fb((uint32_t)p, lane);
-                if (lane == 0 && W::install(desc, (uint32_t)p, dv.state, dv.value)) count_event(hdr + kHdrFallbacks);
+                if (lane == 0 && W::install(desc, (uint32_t)p, cfg.tf, dv.state, dv.value)) count_event(hdr + kHdrFallbacks);
                 stalled = 0;
                 continue;
             }
@@ -479,7 +491,7 @@ __device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint3
                 __builtin_amdgcn_s_sleep(1);
                 continue;
             }
-            if (lane == 0) __hip_atomic_store(hdr + kHdrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_fetch_or(hdr + kHdrError, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         spins = 0;
         stalled = 0;
@@ -503,13 +515,14 @@ __device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint3
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)ss, (int)ls);
             if ((hi & 3u) == ST_PREFIX) break;
             const int64_t stop = base + 64 * js + (int64_t)ls;
-            nearest = stop - (int64_t)(hi >> 2);
+            nearest = stop - (int64_t)(hi >> kDistShift);
         } else {
             nearest -= 64 * K;
         }
         if (nearest < 0) break;  // a PARTIAL reaching back to tile 0 ends the walk
         if (cfg.partial && ++walked >= cfg.partial && may_publish && lane == 0) {
-            W::publish(desc, tile, ((uint32_t)((int64_t)tile - nearest) << 2) | ST_PARTIAL, Op::op(acc, own));
+            W::publish(desc, tile, cfg.tf, ((uint32_t)((int64_t)tile - nearest) << kDistShift) | ST_PARTIAL,
+                       Op::op(acc, own));
             // counted by the instrumented build only: an atomic on one shared
             // word would queue ahead of this wave's next poll
             if (STATS) count_event(hdr + kHdrPartials);
@@ -539,7 +552,7 @@ __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, u
         if (use_pre)
             win = *pre;
         else
-            window_load<Op, K, false, W>(desc, nearest, lane, win);
+            window_load<Op, K, false, W>(desc, nearest, lane, cfg.tf, win);
         use_pre = false;
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -575,7 +588,7 @@ __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, u
                 const uint32_t li = 63u - (uint32_t)__builtin_clzll(im);
                 const int64_t p = nearest - 64 * K + 1 + (int64_t)li * K + __builtin_amdgcn_readlane(ji, (int)li);
                 const DescVal<T> dv = fb((uint32_t)p, lane);
-                if (lane == 0 && W::install(desc, (uint32_t)p, dv.state, dv.value)) count_event(hdr + kHdrFallbacks);
+                if (lane == 0 && W::install(desc, (uint32_t)p, cfg.tf, dv.state, dv.value)) count_event(hdr + kHdrFallbacks);
                 stalled = 0;
                 continue;
             }
@@ -583,7 +596,7 @@ __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, u
                 __builtin_amdgcn_s_sleep(1);
                 continue;
             }
-            if (lane == 0) __hip_atomic_store(hdr + kHdrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_fetch_or(hdr + kHdrError, kErrSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         spins = 0;
         stalled = 0;
@@ -605,13 +618,14 @@ __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, u
             const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)ss, (int)lp);
             if ((hi & 3u) == ST_PREFIX) break;
             const int64_t s = nearest - 64 * K + 1 + (int64_t)lp * K + __builtin_amdgcn_readlane(jp, (int)lp);
-            nearest = s - (int64_t)(hi >> 2);
+            nearest = s - (int64_t)(hi >> kDistShift);
         } else {
             nearest -= 64 * K;
         }
         if (nearest < 0) break;  // a PARTIAL reaching back to tile 0 ends the walk
         if (cfg.partial && ++walked >= cfg.partial && may_publish && lane == 0) {
-            W::publish(desc, tile, ((uint32_t)((int64_t)tile - nearest) << 2) | ST_PARTIAL, Op::op(acc, own));
+            W::publish(desc, tile, cfg.tf, ((uint32_t)((int64_t)tile - nearest) << kDistShift) | ST_PARTIAL,
+                       Op::op(acc, own));
             // counted by the instrumented build only: an atomic on one shared
             // word would queue ahead of this wave's next poll
             if (STATS) count_event(hdr + kHdrPartials);
@@ -623,7 +637,7 @@ __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, u
 template <class Op, int K, bool STATS, bool BLOCKED = false, class FB = NoFallback<typename Op::T>,
           class W = WordsFor<Op>>
 __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile, uint32_t lane, LookbackStats &st,
-                                                   uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u},
+                                                   uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u, 0u, 0u},
                                                    typename Op::T own = Op::id(), bool may_publish = false,
                                                    const FB &fb = FB{},
                                                    const Window<typename Op::T, K> *pre = nullptr) {

@@ -8,14 +8,16 @@
 #include <stdint.h>
 
 #include "dwps.h"
+#include "dwps_device.hpp"
+#include "ws_state.hpp"
 
 namespace dwps {
 
-// Workspace: a 256-byte header (word 0 = tile-ticket counter, word 1 = error
-// word, nonzero when a look-back hit its spin limit) followed by one 64-bit
-// descriptor per tile.  Everything is cleared to zero (counter 0, all
-// descriptors INVALID) on the caller's stream before each scan launch.
+// Workspace: a 256-byte header (ws_state.hpp) followed by the descriptor
+// words, one or two 64-bit words per tile.  Prepared once by
+// ps_workspace_init; every single-pass call leaves it ready for the next.
 constexpr size_t kWsHeader = 256;
+static_assert(kHdrWords * 4 <= (int)kWsHeader, "header words fit the header");
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
@@ -45,9 +47,9 @@ inline ps_status workspace_protocol(void *ws, size_t *ws_bytes, size_t need, boo
     return PS_OK;
 }
 
-// Zero-fill `bytes` (a multiple of 16) at `p` on `stream` with a small kernel
-// (not hipMemsetAsync, so that a caller may capture the call in a graph).
-hipError_t launch_clear(void *p, size_t bytes, hipStream_t stream);
+// Prepare the header of a workspace of `bytes` bytes on `stream` (a kernel,
+// not hipMemsetAsync, so that a caller may capture it in a graph).
+hipError_t launch_ws_init(void *ws, size_t bytes, hipStream_t stream);
 
 inline ps_status launch_status() {
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
@@ -63,6 +65,14 @@ uint32_t persistent_grid(const void *kernel, int block_threads, uint32_t work_it
 // publish PARTIAL descriptors.
 uint32_t lookback_fallback_after();
 uint32_t lookback_partial();
+uint32_t lookback_debug_flags();
+
+// The look-back settings of a launch.  An in-place call runs without the
+// fallback: a fallback reduces a predecessor from its input, which in place
+// may already hold that predecessor's outputs.
+inline LookbackCfg lookback_cfg(bool in_place) {
+    return LookbackCfg{in_place ? 0u : lookback_fallback_after(), lookback_partial(), lookback_debug_flags(), 0u};
+}
 
 // Largest n that the flat entry points hand to the two-level form
 // (ps_small_n_config), and the cap of that setting.

@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "dwps_device.hpp"
+#include "ws_device.hpp"
 
 namespace dwps {
 
@@ -90,7 +91,7 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         const bool have = pt.prev2 < num_tiles && pt.prev2 != 0;
         const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
         Window<T, LB_K> win;
-        if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, win);
+        if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, cfg.tf, win);
         __syncthreads();  // B: prev3's prefix is in LDS
         LookbackStats st;
         uint64_t t0 = 0;
@@ -108,9 +109,9 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
             }
             if (!(STATS && aggregate_only)) {
                 const bool early = kPairPrefix && pt.prev2 % G != 0u && pt.prev2 - 1u != 0u;
-                if (have && !early) W::publish(desc, pt.prev2, ST_PREFIX, Op::op(excl, agg_prev2));
+                if (have && !early) W::publish(desc, pt.prev2, cfg.tf, ST_PREFIX, Op::op(excl, agg_prev2));
                 if (kPairPrefix && look && pt.prev == pt.prev2 + 1u && pt.prev < num_tiles)
-                    W::publish(desc, pt.prev, ST_PREFIX, Op::op(Op::op(excl, agg_prev2), agg_prev));
+                    W::publish(desc, pt.prev, cfg.tf, ST_PREFIX, Op::op(Op::op(excl, agg_prev2), agg_prev));
             }
         }
         // the wave totals of f1 are complete: its aggregate goes out now
@@ -118,7 +119,11 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         if (pt.f1 < num_tiles) {
 #pragma unroll
             for (int w = 0; w < D; ++w) agg_next = Op::op(agg_next, sh.wt[par ^ 1][w]);
-            if (lane == 0) W::publish(desc, pt.f1, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
+            // (a debug setting withholds aggregates, so that look-backs
+            // reaching this tile stall and its aggregate comes from a fallback)
+            const bool withhold = pt.f1 != 0 && (cfg.flags & kDbgWithholdAggregates);
+            if (lane == 0 && !withhold)
+                W::publish(desc, pt.f1, cfg.tf, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
         }
         excl_next = excl;
         incl_last = Op::op(excl, agg_prev2);

@@ -46,7 +46,6 @@ struct ScanShared {
     using T = typename Op::T;
     static constexpr int PW = (int)sizeof(T) / 4;  // 16-byte vectors per group of four outputs
     v4u park[kParkSlots][D * Q * 64 * PW];       // tile-relative outputs
-    uint32_t t0;
     uint32_t next;
     T wt[2][D];  // wave totals, double-buffered by phase parity
     T prefix;
@@ -212,25 +211,27 @@ struct FlatFallback {
 
 template <class Op, int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
-    typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
+    typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *hdr,
     uint64_t *desc, typename Op::T *total, uint32_t *stats, int aggregate_only, LookbackCfg cfg) {
     __shared__ ScanShared<Op, D, Q> sh;
+    __shared__ WsShared wsh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
-
-    if (threadIdx.x == 0) {
-        const uint32_t g = take_ticket(ctr);
-        sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
+    uint32_t t0;
+    const WsCall call = ws_start<G>(hdr, desc, num_tiles * (uint32_t)WordsFor<Op>::WORDS, num_tiles, wsh, t0);
+    cfg.tf = tag_field(call.plan.tag);
+    if (t0 < num_tiles) {
+        const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, t0};
+        if (wave == 0) {
+            ws_wait_clean(call, hdr);
+            control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
+                pt, sh, num_tiles, hdr, desc, total, stats, aggregate_only, cfg,
+                FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
+        } else {
+            data_loop3<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, hdr, lane, wave - 1);
+        }
     }
-    __syncthreads();
-    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
-    if (pt.f2 >= num_tiles) return;
-    if (wave == 0)
-        control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
-            pt, sh, num_tiles, ctr, desc, total, stats, aggregate_only, cfg,
-            FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
-    else
-        data_loop3<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, ctr, lane, wave - 1);
+    ws_finish(wsh, num_tiles * (uint32_t)WordsFor<Op>::WORDS, hdr);
 }
 
 template <class T>
@@ -303,8 +304,8 @@ inline bool use_two_level(uint64_t n, FlatForm form) {
     return form == FlatForm::kTwoLevel || (form == FlatForm::kAuto && n <= small_n_max());
 }
 
-// Clear the workspace and launch the flat kernel on validated arguments
-// (n > 0).  VEC: every array 16-byte aligned.  An in-place call runs without
+// Launch the flat kernel on validated arguments (n > 0); the workspace is
+// prepared and keeps itself ready (ws_state.hpp).  VEC: every array 16-byte aligned.  An in-place call runs without
 // the fallback: a fallback reduces a predecessor from its input, which in
 // place may already hold that predecessor's outputs.
 template <class Op, bool STATS>
@@ -313,11 +314,11 @@ ps_status launch_flat_kernel(void *ws, size_t ws_need, typename IoOf<Op>::Src in
                              uint32_t *stats, int aggregate_only, hipStream_t s) {
     constexpr int Q = flat_q<Op>();
     constexpr int K = flat_k<Op>();
-    if (launch_clear(ws, ws_need, s) != hipSuccess) return PS_ERR_HIP;
+    (void)ws_need;
     uint32_t *ctr = ws_counter(ws);
     uint64_t *desc = ws_desc(ws);
     const uint32_t nt = (uint32_t)ceil_div(n, flat_tile<Op>());
-    const LookbackCfg cfg{in_place ? 0u : lookback_fallback_after(), lookback_partial()};
+    const LookbackCfg cfg = lookback_cfg(in_place);
     auto launch = [&](auto kernel) -> ps_status {
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kFlatThreads, nt);
         if (!grid) return PS_ERR_HIP;
@@ -477,10 +478,22 @@ extern "C" uint32_t ps_linrec_tile_elements(void) { return flat_tile<LinRecF32>(
 template <class Rec>
 __global__ __launch_bounds__(256) void scatter_kept_kernel(const Rec *rec, const uint8_t *flags,
                                                           const uint32_t *offsets, uint32_t n, Rec *out,
-                                                          const uint32_t *count, uint64_t *num_selected) {
+                                                          const uint32_t *count, uint64_t *num_selected,
+                                                          uint32_t *hdr, uint32_t dirty_a, uint32_t dirty_b) {
     const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-    if (i == 0) *num_selected = *count;
-    if (i < n && flags[i] != 0) out[offsets[i]] = rec[i];
+    if (i == 0) {
+        const uint32_t c = *count;
+        *num_selected = c < n ? c : n;
+        // the offsets and the count are plain data in descriptor words
+        uint32_t lo = hdr[kHdrDirtyLo], hi = hdr[kHdrDirtyHi];
+        ws_mark_dirty(lo, hi, dirty_a, dirty_b);
+        hdr[kHdrDirtyLo] = lo;
+        hdr[kHdrDirtyHi] = hi;
+    }
+    if (i < n && flags[i] != 0) {
+        const uint32_t o = offsets[i];
+        if (o < n) out[o] = rec[i];
+    }
 }
 
 __global__ void write_count_zero_staged(uint64_t *p) { *p = 0ull; }
@@ -512,9 +525,12 @@ ps_status launch_compact_staged(void *ws, size_t *ws_bytes, const void *records,
     st = launch_flat<CountFlags, false>(ws, &scan_bytes, flags, offsets, n, count, false, nullptr, s, 0u);
     if (st != PS_OK) return st;
     timing_begin(s);
+    // descriptor words holding the offsets and the count, left dirty
+    const uint32_t dirty_a = (uint32_t)((off_at - kWsHeader) / 8u);
+    const uint32_t dirty_b = (uint32_t)((cnt_at + 256u - kWsHeader) / 8u);
     hipLaunchKernelGGL(scatter_kept_kernel<Rec>, dim3((uint32_t)ceil_div(n, 256)), dim3(256), 0, s,
                        static_cast<const Rec *>(records), flags, offsets, (uint32_t)n, static_cast<Rec *>(out), count,
-                       num_selected);
+                       num_selected, ws_counter(ws), dirty_a, dirty_b);
     timing_end(s);
     return launch_status();
 }

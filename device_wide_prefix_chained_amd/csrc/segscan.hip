@@ -21,10 +21,9 @@
 //     and only the first tile of a ticket group looks back for it -- long
 //     segments chain through start-free tiles exactly like the flat scan.
 //
-// Two launches per call: the workspace clear (tile descriptors, ticket
-// counter), then the persistent, wave-specialised pipeline of the flat scan
-// (one control wave, D data waves, look-back two phases behind the
-// aggregate).  The segment starts never go through memory as flags: while
+// One launch per call: the persistent, wave-specialised pipeline of the
+// flat scan (one control wave, D data waves, look-back two phases behind the
+// aggregate) on a workspace that keeps itself ready between calls.  The segment starts never go through memory as flags: while
 // the data waves load a tile, the control wave reads the tile's offsets and
 // sets the starts as bits of an LDS bitmap, which the data waves read when
 // they scan the tile in the next phase.  To find those offsets, a sample of
@@ -199,7 +198,6 @@ struct SegShared {
     alignas(16) uint32_t starts[2][kSegWords];  // start bitmaps of f2 (written) and f1 (read), by phase parity
     alignas(16) uint32_t fb_starts[kSegWords];  // start bitmap of a tile a fallback reduces
     uint32_t sample[kSampleMax];       // every stride-th offset (StartIndex)
-    uint32_t t0;
     uint32_t next;
     uint32_t carry;                    // carry into prev2
 };
@@ -316,7 +314,7 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
         if (lane == 0) {
             sh.carry = carry;
             if (have_prev2 && !a_prev2.f)
-                desc_publish(desc + pt.prev2, desc_word(ST_PREFIX, carry + a_prev2.v));
+                desc_publish(desc + pt.prev2, desc_word(ST_PREFIX | cfg.tf, carry + a_prev2.v));
         }
         if (build) idx.finish(s_v, s_lo, tb, te, lane, sh.starts[par], kSegWords);
         carry_out_last = a_prev2.f ? a_prev2.v : carry + a_prev2.v;
@@ -333,9 +331,12 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
                 agg_next = seg_op(agg_next, SegPair{sh.wf[par ^ 1][w], sh.wv[par ^ 1][w]});
                 fh_next = min(fh_next, sh.wfirst[par ^ 1][w]);
             }
-            if (lane == 0)
-                desc_publish(desc + pt.f1,
-                             desc_word((pt.f1 == 0 || agg_next.f) ? ST_PREFIX : ST_AGGREGATE, agg_next.v));
+            // a tile holding a start publishes PREFIX; the aggregate of a
+            // start-free one may be withheld by a debug setting (look-backs
+            // reaching it then take it from a fallback)
+            const bool prefix = pt.f1 == 0 || agg_next.f;
+            if (lane == 0 && (prefix || !(cfg.flags & kDbgWithholdAggregates)))
+                desc_publish(desc + pt.f1, desc_word((prefix ? ST_PREFIX : ST_AGGREGATE) | cfg.tf, agg_next.v));
         }
         if (pt.drained(num_tiles)) break;
         __syncthreads();  // A: the next tile id is in LDS
@@ -509,28 +510,30 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
                                                                uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
                                                                LookbackCfg cfg) {
     __shared__ SegShared<D, Q> sh;
+    __shared__ WsShared wsh;
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = uniform(threadIdx.x >> 6);
     const StartIndex idx = StartIndex::make(offsets, num_segments, sh.sample);
-    if (threadIdx.x == 0) {
-        const uint32_t g = take_ticket(ctr);
-        sh.t0 = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
+    uint32_t t0;
+    const WsCall call = ws_start<G>(ctr, desc, num_tiles, num_tiles, wsh, t0);
+    cfg.tf = tag_field(call.plan.tag);
+    if (t0 < num_tiles) {
+        const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, t0};
+        if (wave == 0) {
+            // only the control wave reads the sample: the data waves' first
+            // loads do not wait for it
+            idx.load_sample(sh.sample, lane);
+            ws_wait_clean(call, ctr);
+            seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
+                                            SegFallback{values, idx, sh.fb_starts, n}, lane);
+        } else {
+            // rows outside [offsets[0], offsets[N]) belong to no segment
+            const uint32_t lo = offsets[0], hi = offsets[num_segments];
+            seg_data_loop<D, Q, G, INCL, VEC>(pt, sh, values, out, n, uniform(lo < n ? lo : n),
+                                              uniform(hi < n ? hi : n), num_tiles, ctr, lane, wave - 1);
+        }
     }
-    __syncthreads();
-    const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, uniform(sh.t0)};
-    if (pt.f2 >= num_tiles) return;
-    if (wave == 0) {
-        // only the control wave reads the sample: the data waves' first
-        // loads do not wait for it
-        idx.load_sample(sh.sample, lane);
-        seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
-                                        SegFallback{values, idx, sh.fb_starts, n}, lane);
-    } else {
-        // rows outside [offsets[0], offsets[N]) belong to no segment
-        const uint32_t lo = offsets[0], hi = offsets[num_segments];
-        seg_data_loop<D, Q, G, INCL, VEC>(pt, sh, values, out, n, uniform(lo < n ? lo : n),
-                                          uniform(hi < n ? hi : n), num_tiles, ctr, lane, wave - 1);
-    }
+    ws_finish(wsh, num_tiles, ctr);
 }
 
 // Workspace: header and descriptors as for the flat scan.
@@ -559,13 +562,12 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
     uint32_t *ctr = ws_counter(ws);
     uint64_t *desc = ws_desc(ws);
     const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
-    if (launch_clear(ws, seg_ws_bytes(tiles), s) != hipSuccess) return PS_ERR_HIP;
     const bool vec = aligned(values, 16) && aligned(out, 16);
     auto launch = [&](auto kernel) -> ps_status {
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kSegThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
-        const LookbackCfg cfg{lookback_fallback_after(), lookback_partial()};
+        const LookbackCfg cfg = lookback_cfg(false);
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSegThreads), 0, s, values, out, n32, offsets,
                            num_segments, nt, ctr, desc, cfg);
         return PS_OK;

@@ -34,9 +34,32 @@ constexpr uint32_t kTlTile = (uint32_t)kTlWaves * kTlQ * 256u;
 constexpr int kTlScanWaves = 16;
 constexpr uint32_t kTlScanChunk = (uint32_t)kTlScanWaves * 64u * 4u;
 
+// Tile totals live in the descriptor area of the workspace (after its
+// header, which they leave alone), one 64-bit word per 32 payload bits with
+// the upper half zero: every word reads as an unpublished descriptor, so a
+// later single-pass call on the same workspace never mistakes a total for
+// a published tile.
+template <class T>
+__device__ __forceinline__ T tl_get(const uint64_t *w, uint32_t i) {
+    if constexpr (sizeof(T) == 8)
+        return from_bits64<T>(((uint64_t)(uint32_t)w[2u * i + 1u] << 32) | (uint32_t)w[2u * i]);
+    else
+        return from_bits<T>((uint32_t)w[i]);
+}
+template <class T>
+__device__ __forceinline__ void tl_put(uint64_t *w, uint32_t i, T v) {
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t b = to_bits64(v);
+        w[2u * i] = (uint32_t)b;
+        w[2u * i + 1u] = (uint32_t)(b >> 32);
+    } else {
+        w[i] = to_bits(v);
+    }
+}
+
 template <class Op, bool VEC>
 __global__ __launch_bounds__(kTlWaves * 64) void tl_reduce_kernel(typename IoOf<Op>::Src in, uint32_t n,
-                                                                 typename Op::T *sums) {
+                                                                 uint64_t *sums) {
     using T = typename Op::T;
     __shared__ T wt[kTlWaves];
     const uint32_t lane = threadIdx.x & 63u;
@@ -55,14 +78,14 @@ __global__ __launch_bounds__(kTlWaves * 64) void tl_reduce_kernel(typename IoOf<
         T acc = Op::id();
 #pragma unroll
         for (int k = 0; k < kTlWaves; ++k) acc = Op::op(acc, wt[k]);
-        sums[blockIdx.x] = acc;
+        tl_put<T>(sums, blockIdx.x, acc);
     }
 }
 
 // Exclusive scan of `num` tile totals in place; *total (optional) gets the
 // fold of all of them.  Thread t holds totals 4t .. 4t+3 of each round.
 template <class Op>
-__global__ __launch_bounds__(kTlScanWaves * 64) void tl_scan_sums_kernel(typename Op::T *sums, uint32_t num,
+__global__ __launch_bounds__(kTlScanWaves * 64) void tl_scan_sums_kernel(uint64_t *sums, uint32_t num,
                                                                         typename Op::T *total) {
     using T = typename Op::T;
     __shared__ T wt[kTlScanWaves];
@@ -74,7 +97,7 @@ __global__ __launch_bounds__(kTlScanWaves * 64) void tl_scan_sums_kernel(typenam
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t i = c + 4u * threadIdx.x + (uint32_t)k;
-            v[k] = i < num ? sums[i] : Op::id();
+            v[k] = i < num ? tl_get<T>(sums, i) : Op::id();
         }
         T inc[4];
         inc[0] = v[0];
@@ -94,7 +117,7 @@ __global__ __launch_bounds__(kTlScanWaves * 64) void tl_scan_sums_kernel(typenam
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t i = c + 4u * threadIdx.x + (uint32_t)k;
-            if (i < num) sums[i] = k == 0 ? c0 : Op::op(c0, inc[k - 1]);
+            if (i < num) tl_put<T>(sums, i, k == 0 ? c0 : Op::op(c0, inc[k - 1]));
         }
         carry = all;
         __syncthreads();  // wt is rewritten by the next round
@@ -115,7 +138,7 @@ constexpr uint32_t kTlFoldMax = 1024;
 // Fold of totals[0 .. t) in index order by one wave: lane l folds a
 // contiguous run of them, the wave scan joins the runs.
 template <class Op>
-__device__ __forceinline__ typename Op::T fold_before(const typename Op::T *totals, uint32_t t, uint32_t lane) {
+__device__ __forceinline__ typename Op::T fold_before(const uint64_t *totals, uint32_t t, uint32_t lane) {
     using T = typename Op::T;
     constexpr uint32_t PER = kTlFoldMax / 64u;
     const uint32_t per = (t + 63u) / 64u;  // <= PER
@@ -124,7 +147,7 @@ __device__ __forceinline__ typename Op::T fold_before(const typename Op::T *tota
     for (uint32_t k = 0; k < PER; ++k) {
         const uint32_t i = lane * per + k;
         const bool in = k < per && i < t;
-        const T x = totals[in ? i : 0];
+        const T x = tl_get<T>(totals, in ? i : 0u);
         v = in ? Op::op(v, x) : v;
     }
     return read_lane(wave_inclusive<Op>(v), 63);
@@ -133,7 +156,7 @@ __device__ __forceinline__ typename Op::T fold_before(const typename Op::T *tota
 template <class Op, bool INCL, bool VEC, int PREFIX>
 __global__ __launch_bounds__(kTlWaves * 64) void tl_scan_kernel(typename IoOf<Op>::Src in,
                                                                typename IoOf<Op>::Dst out, uint32_t n,
-                                                               const typename Op::T *sums, typename Op::T *total) {
+                                                               const uint64_t *sums, typename Op::T *total) {
     using T = typename Op::T;
     __shared__ T wt[kTlWaves];
     __shared__ T tile_prefix_sh;
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(kTlWaves * 64) void tl_scan_kernel(typename IoOf<Op
     if (lane == 0) wt[w] = tot;
     __syncthreads();
     T tile_prefix = Op::id();
-    if (PREFIX == kTlFromScan) tile_prefix = sums[blockIdx.x];
+    if (PREFIX == kTlFromScan) tile_prefix = tl_get<T>(sums, blockIdx.x);
     if (PREFIX == kTlFold) tile_prefix = tile_prefix_sh;
     if (PREFIX != kTlFromScan && total && threadIdx.x == 0 && blockIdx.x == gridDim.x - 1) {
         T all = tile_prefix;
@@ -189,15 +212,15 @@ inline uint64_t tl_tiles(uint64_t n) { return ceil_div(n, kTlTile); }
 
 template <class Op>
 inline size_t tl_ws_bytes(uint64_t n) {
-    const size_t b = round_up(tl_tiles(n) * sizeof(typename Op::T), 256);
-    return b ? b : 256;
+    return kWsHeader + round_up(tl_tiles(n) * sizeof(typename Op::T) * 2u, 256);
 }
 
 // The passes on validated arguments (n > 0); `sums` is the workspace.  One
 // tile: pass 3 alone (one launch).  Up to kTlFoldMax tiles: pass 1, then
 // pass 3 folding the earlier totals itself (two launches).  More: all three.
+// The workspace needs no preparation for this form.
 template <class Op, int PREFIX>
-void tl_third(typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n, typename Op::T *sums,
+void tl_third(typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n, uint64_t *sums,
               typename Op::T *total, uint32_t tiles, bool inclusive, bool vec, hipStream_t s) {
     const dim3 grid(tiles), block(kTlWaves * 64);
     if (inclusive && vec)
@@ -213,8 +236,7 @@ void tl_third(typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n,
 template <class Op>
 ps_status tl_launch(void *ws, typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n,
                     typename Op::T *total, bool inclusive, bool vec, hipStream_t s) {
-    using T = typename Op::T;
-    T *sums = static_cast<T *>(ws);
+    uint64_t *sums = ws_desc(ws);
     const uint32_t tiles = (uint32_t)tl_tiles(n);
     timing_begin(s);
     if (tiles == 1) {

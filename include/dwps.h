@@ -30,14 +30,24 @@
  *  - Workspace (the CUB-style two-call pattern of [P2] "Use the library"):
  *    call with ws == NULL to receive the byte count in *ws_bytes (nothing is
  *    launched, no GPU is touched); then call again with a device buffer of at
- *    least that many bytes.  The caller owns it; its contents need no
- *    initialisation (the library clears it on `stream` each call).  Two calls
- *    in flight at once must not share a workspace.  After a call of the
- *    single-pass form its first four uint32 words hold diagnostics: [0] tiles handed out (+ one ticket
- *    per workgroup), [1] error word (nonzero: a look-back hit its spin limit
- *    and the results are not valid), [2] look-back fallbacks performed,
- *    [3] PARTIAL descriptors published (counted by ps_lookback_stats_u32
- *    only; see ps_lookback_config).
+ *    least that many bytes (16-byte aligned), passing its size in *ws_bytes.
+ *    The caller owns it.  A workspace is prepared ONCE, before its first use,
+ *    with ps_workspace_init (which takes its full size); every call then
+ *    leaves it ready for the next call of any entry point, so a call is a
+ *    single kernel launch with no separate clear.  One workspace may serve
+ *    calls of every size up to the size it was prepared with.  Two calls in
+ *    flight at once must not share a workspace (two streams need two), and a
+ *    call that does not complete (the process or the device fails mid-call)
+ *    leaves it to be prepared again.  Layout: a PS_WS_HEADER_BYTES header of
+ *    32-bit words (ps_ws_word), then the tile descriptors.  Diagnostics in
+ *    the header: PS_WS_ERROR holds sticky ps_ws_error bits (nonzero: some
+ *    call since preparation did not produce valid results); PS_WS_FALLBACKS
+ *    and PS_WS_PARTIALS count look-back fallbacks and PARTIAL descriptors
+ *    (the latter by the instrumented entry points only), cumulatively;
+ *    PS_WS_CALLS counts completed single-pass calls.  A call on a workspace
+ *    that was never prepared computes nothing and sets
+ *    PS_WS_ERR_NOT_PREPARED; one on a workspace prepared smaller than it
+ *    needs sets PS_WS_ERR_CAPACITY.
  *  - Argument errors are returned synchronously before anything is
  *    launched: PS_ERR_NULL (a required pointer is NULL while n > 0),
  *    PS_ERR_SIZE (n >= 2^32, or offsets beyond the supported range),
@@ -63,6 +73,29 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* 32-bit words of the workspace header. */
+#define PS_WS_HEADER_BYTES 256
+typedef enum ps_ws_word {
+    PS_WS_TICKET = 0,    /* tile tickets handed out by the call in flight (0 between calls) */
+    PS_WS_ERROR = 1,     /* sticky ps_ws_error bits */
+    PS_WS_FALLBACKS = 2, /* look-back fallbacks installed, cumulative */
+    PS_WS_PARTIALS = 3,  /* PARTIAL descriptors published (instrumented entry points), cumulative */
+    PS_WS_TAG = 4,       /* 9-bit tag of the next call; descriptors carry their call's tag */
+    PS_WS_DONE = 5,      /* workgroups of the call in flight that have finished */
+    PS_WS_MAGIC = 6,     /* set by ps_workspace_init */
+    PS_WS_CAPACITY = 7,  /* descriptor words the workspace holds */
+    PS_WS_HIGH = 8,      /* descriptor words any call has tagged */
+    PS_WS_DIRTY_LO = 9,  /* descriptor words [lo, hi) that may hold anything; */
+    PS_WS_DIRTY_HI = 10, /* the next call that uses them zeroes them first */
+    PS_WS_READY = 11,    /* nonzero once the call in flight has zeroed its dirty words */
+    PS_WS_CALLS = 12     /* single-pass calls completed, modulo 2^32 */
+} ps_ws_word;
+typedef enum ps_ws_error {
+    PS_WS_ERR_SPIN = 1,         /* a look-back hit its spin limit: results not valid */
+    PS_WS_ERR_NOT_PREPARED = 2, /* the workspace was not prepared: nothing computed */
+    PS_WS_ERR_CAPACITY = 4      /* prepared smaller than the call needs: nothing computed */
+} ps_ws_error;
 
 typedef enum ps_status {
     PS_OK = 0,
@@ -101,6 +134,17 @@ typedef enum ps_op {
     PS_OP_XOR = 5,
     PS_OP_AFFINE16 = 6
 } ps_op;
+
+/* Prepare a workspace of ws_bytes bytes (16-byte aligned, at least
+ * PS_WS_HEADER_BYTES) on `stream`: one small kernel that writes its header
+ * (no call in flight, tag 0, every descriptor word marked dirty, the
+ * capacity).  The descriptor words themselves are zeroed lazily, by the
+ * first call that uses them.  Needed once per workspace, before its first
+ * use; again only after a call failed to complete.  Calls made in the
+ * same stream order afterwards see the prepared header.  Returns
+ * PS_ERR_NULL, PS_ERR_ALIGNMENT or PS_ERR_WORKSPACE (too small) before
+ * launching anything. */
+ps_status ps_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Flat scans.  [P2] "Inclusive, exclusive and associative":
@@ -202,9 +246,11 @@ ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
  * prefix.  Up to 1024 tiles the tile totals are folded by the final pass
  * itself (two launches; one launch for a single tile); beyond, one
  * workgroup scans them in between (three launches).  It reads the input
- * twice (12 instead of 8 bytes per 32-bit element) but has no descriptors,
- * look-back or workspace clear, so on small inputs it finishes sooner.  Its
- * workspace holds one tile total per tile and no diagnostics header.
+ * twice (12 instead of 8 bytes per 32-bit element) but has no descriptors
+ * and no look-back, so on small inputs it finishes sooner.  It keeps its
+ * tile totals in the descriptor area of the workspace, as words that read
+ * as unpublished descriptors, and does not touch the header: it needs no
+ * preparation, and a prepared workspace stays ready.
  *
  * Both take the arguments of ps_scan and give the same results.  The flat
  * entry points (ps_scan, ps_scan_{ex,in}clusive_{u32,f32,u32_u64},
@@ -247,11 +293,10 @@ uint64_t ps_small_n_config_get(void);
  * Any overlap of out with values or offsets returns PS_ERR_ALIAS.
  * num_segments may be 0 (nothing is written); num_segments = 2^32 - 1 (an
  * offsets array of 2^32 entries) returns PS_ERR_SIZE, as does n >= 2^32.
- * Two kernels run per call: the workspace clear (tile descriptors and
- * counter), then the single-pass scan, which reads the values and, per tile,
- * the offsets that fall into it (its segment starts) once, and writes every
- * row of a segment once.  The workspace holds the header and one descriptor
- * per tile. */
+ * One kernel runs per call: the single-pass scan, which reads the values
+ * and, per tile, the offsets that fall into it (its segment starts) once,
+ * and writes every row of a segment once.  The workspace holds the header
+ * and one descriptor per tile. */
 ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes,
                                 const uint32_t *values, uint64_t n,
                                 const uint32_t *offsets, uint32_t num_segments,
@@ -288,7 +333,10 @@ ps_status ps_compact(void *ws, size_t *ws_bytes, const void *records,
  * 1 + 4 + 1 + 4 + record_bytes bytes per record (plus record_bytes per kept
  * record) against the fused kernel's 1 + record_bytes, and exists to
  * measure what the fusion saves.  The workspace holds the scan's own, n
- * offsets and the count. */
+ * offsets and the count; the offsets' words are left marked dirty, so the
+ * next single-pass call that needs them zeroes them first.  The scatter
+ * writes no record to a position at or past n (a guard against offsets
+ * left unwritten when the workspace was not prepared). */
 ps_status ps_compact_staged(void *ws, size_t *ws_bytes, const void *records,
                             uint32_t record_bytes, const uint8_t *flags, uint64_t n,
                             void *out, uint64_t *num_selected, void *stream);
@@ -365,8 +413,23 @@ uint32_t ps_lookback_group(void);
 ps_status ps_lookback_config(uint32_t fallback_polls, uint32_t partial_windows);
 void ps_lookback_config_get(uint32_t *fallback_polls, uint32_t *partial_windows);
 
+/* Debug settings of every later single-pass call of this process (a test
+ * aid, like ps_lookback_config; not for production use).
+ *   PS_DEBUG_WITHHOLD_AGGREGATES: no tile publishes its AGGREGATE (a tile
+ *     publishes only its inclusive PREFIX, and PARTIALs), so a look-back
+ *     that reaches a tile whose prefix is not yet known stalls there; with
+ *     a fallback configured (ps_lookback_config), the fallback reduces that
+ *     tile's input and installs the aggregate its owner withheld ([P4]
+ *     "Decoupled Fallback").  Results must be unchanged; PS_WS_FALLBACKS
+ *     shows how many were installed.  Without a fallback the chain of
+ *     prefixes still completes, only serially.
+ * Other bits return PS_ERR_UNSUPPORTED.  0 = off (default). */
+typedef enum ps_debug_flag { PS_DEBUG_WITHHOLD_AGGREGATES = 1 } ps_debug_flag;
+ps_status ps_lookback_debug(uint32_t flags);
+uint32_t ps_lookback_debug_get(void);
+
 /* Kernel timing with HIP events placed around the main scan kernel of a
- * call (the workspace clear is outside the pair).  every = 0 turns timing
+ * call.  every = 0 turns timing
  * off; every = N >= 1 starts a new measurement that times the 1st, (N+1)th,
  * (2N+1)th ... call from now on (1 = every call); a negative value returns
  * PS_ERR_SIZE.  ps_kernel_timing_read synchronises on the recorded events

@@ -75,16 +75,33 @@ def assert_f32_sum_close(gpu, ref64, absprefix, exclusive):
     return float((err / np.maximum(tol, 1e-300)).max()) if gpu.size else 0.0
 
 
-def assert_linrec_close(gpu_a, gpu_b, ref_a, ref_b, mag_a, mag_b, exclusive):
-    """Recurrence-pair tolerance: |gpu - ref| <= 1e-5 * (the same scan over
-    (|a|, |b|)) + 2^-100 for each component at every index; the magnitude
-    scan reduces to sum |b| when a = 1, the fp32 sum scan's bound.  An
-    exclusive output 0 must be exactly (1, 0).  gpu_a may be None (B only)."""
+def product_bound(n, first=0):
+    """Relative rounding bound of the A component at indices first ..
+    first + n - 1: a product of t + 1 fp32 factors, formed in any grouping,
+    is rounded t times, so it lies within gamma_t = t u / (1 - t u) of the
+    exact product (u = 2^-24; the identity pad multiplies exactly).
+    gamma_(t+1) is used for both forms (the exclusive form has one factor
+    less); past t u = 1/2 the bound says nothing and is capped at 1."""
+    u = 2.0 ** -24
+    tu = np.arange(first + 1, first + n + 1, dtype=np.float64) * u
+    return np.where(tu < 0.5, tu / (1.0 - np.minimum(tu, 0.5)), 1.0)
+
+
+def assert_linrec_close(gpu_a, gpu_b, ref_a, ref_b, mag_a, mag_b, exclusive, first=0):
+    """Recurrence-pair tolerance at every index: B within 1e-5 * (the same
+    scan over (|a|, |b|)) + 2^-100, which reduces to the fp32 sum scan's bound
+    when a = 1; A within max(1e-5, gamma_(t+1)) * prod |a| + 2^-100 (the B
+    bound, widened where the product's own rounding bound is larger).  An
+    exclusive output 0 must be exactly (1, 0).  gpu_a may be None (B only).
+    `first` is the index of the first element given (the total of n pairs is
+    index n - 1)."""
     worst = 0.0
-    comps = [("B", gpu_b, ref_b, mag_b)] + ([("A", gpu_a, ref_a, mag_a)] if gpu_a is not None else [])
-    for name, g, r, m in comps:
+    comps = [("B", gpu_b, ref_b, 1e-5 * mag_b)]
+    if gpu_a is not None:
+        comps.append(("A", gpu_a, ref_a, np.maximum(1e-5, product_bound(gpu_a.size, first)) * mag_a))
+    for name, g, r, rel in comps:
         err = np.abs(g.astype(np.float64) - r)
-        tol = 1e-5 * m + LINREC_FLOOR
+        tol = rel + LINREC_FLOOR
         bad = np.nonzero(~(err <= tol))[0]  # NaN counts as bad
         assert bad.size == 0, ("%s: tolerance broken at %d indices, first %d: gpu %r ref %r tol %r"
                                % (name, bad.size, bad[0], g[bad[0]], r[bad[0]], tol[bad[0]]))

@@ -59,8 +59,10 @@ SMALL_N_CAP = 1 << 24   # inputs up to this size get a workspace that fits both 
 
 
 def _two_level_need(n, elem_bytes):
-    """One tile total per 4096-element tile, at least 256 bytes."""
-    return max(256, -(-(-(-n // 4096)) * elem_bytes // 256) * 256)
+    """The header, then one tile total per 4096-element tile, stored as one
+    8-byte descriptor word per 4 bytes of total (a word that reads as an
+    unpublished descriptor)."""
+    return 256 + -(-(-(-n // 4096)) * 2 * elem_bytes // 256) * 256
 
 
 def _auto_need(n, single, elem_bytes):
@@ -97,8 +99,8 @@ def test_size_queries():
         tiles = -(-n // ttile)
         for dt, size in ((0, 4), (1, 4), (2, 8)):
             st, need = _wsq(lib, "ps_scan_two_level", 0, dt, 0, None, None, n, None, None)
-            # one tile total per tile, nothing else
-            assert st == 0 and need == max(256, -(-tiles * size // 256) * 256), (n, dt)
+            # the header, then one tile total per tile in descriptor words
+            assert st == 0 and need == 256 + -(-tiles * 2 * size // 256) * 256, (n, dt)
     ltile = lib.ps_linrec_tile_elements()
     assert ltile == 6144
     for n in (0, 1, ltile, ltile + 1, SMALL_N_CAP + 1, 1 << 27):

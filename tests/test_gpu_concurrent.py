@@ -26,12 +26,10 @@ def test_three_streams_interleaved(dw, orc):
     flags = wl.flag_pattern(rec.shape[0], "random", seed=404)
     dx, dv, do, dr, df = dev(x), dev(vals), dev(offs), dev(rec), dev(flags)
     streams = [torch.cuda.Stream() for _ in range(3)]
-    ws = [torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None),
-                      dtype=torch.uint8, device="cuda"),
-          torch.empty(dw.workspace_bytes("ps_segmented_scan_u32", None, vals.size, None, offs.size - 1, None, 0,
-                                         None), dtype=torch.uint8, device="cuda"),
-          torch.empty(dw.workspace_bytes("ps_compact", None, 16, None, flags.size, None, None, None),
-                      dtype=torch.uint8, device="cuda")]
+    ws = [dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None)),
+          dw.new_workspace(dw.workspace_bytes("ps_segmented_scan_u32", None, vals.size, None, offs.size - 1, None, 0,
+                                         None)),
+          dw.new_workspace(dw.workspace_bytes("ps_compact", None, 16, None, flags.size, None, None, None))]
     rounds = 4
     outs = [[torch.empty_like(dx), torch.empty_like(dv), torch.empty_like(dr),
              torch.zeros(1, dtype=torch.int64, device="cuda")] for _ in range(rounds)]

@@ -82,8 +82,7 @@ def test_workspace_fits_either_form(dw, orc):
     after the setting changed."""
     import torch
     n = 5_000_000
-    ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None))
     x = wl.full_range_u32(n, seed=47)
     ref, _ = orc.scan_u32(x, "sum", False)
     old = dw.ps_small_n_config_get()

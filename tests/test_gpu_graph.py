@@ -24,7 +24,7 @@ def dw():
 
 def _ws(dw, fn, *args):
     import torch
-    return torch.empty(max(dw.workspace_bytes(fn, *args), 1), dtype=torch.uint8, device="cuda")
+    return dw.new_workspace(dw.workspace_bytes(fn, *args))
 
 
 def _capture(fn):

@@ -54,7 +54,7 @@ def _check_total(orc, a, b, tot):
         assert tot.tolist() == [1.0, 0.0]
         return
     A, B, SA, SB, _ = _oracle(orc, a, b, True)
-    assert_linrec_close(tot[:1], tot[1:], A[-1:], B[-1:], SA[-1:], SB[-1:], False)
+    assert_linrec_close(tot[:1], tot[1:], A[-1:], B[-1:], SA[-1:], SB[-1:], False, first=a.size - 1)
 
 
 def _check(dw, orc, a, b, inclusive, with_a=True):
@@ -193,8 +193,7 @@ def test_repeated_runs_reuse_workspace(dw, orc):
     import torch
     n = 1 << 24
     a, b = wl.linrec_pairs(n, seed=29)
-    ws = torch.empty(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 1, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 1, None, None))
     A, B, SA, SB, _ = _oracle(orc, a, b, True)
     for it in range(5):
         say("linrec repeat", it)
@@ -210,8 +209,7 @@ def test_fallback_every_stall(dw, orc):
     import torch
     n = (1 << 24) + 5
     a, b = wl.linrec_pairs(n, seed=30, a_lo=-1.0, a_hi=1.0)
-    ws = torch.empty(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 0, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_linrec_f32", None, None, None, None, n, 0, None, None))
     old = dw.ps_lookback_config_get()
     dw.ps_lookback_config(1, 1)
     try:
@@ -232,3 +230,67 @@ def test_large_config(dw, orc, inclusive):
     say("linrec config 2^27", inclusive)
     worst = _check(dw, orc, a, b, inclusive)
     say("linrec config 2^27 worst error / tolerance", worst)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_decays_near_one_check_a_everywhere(dw, orc, inclusive):
+    """Decays in [1 - 2^-22, 1) over 2^22 pairs: the running product A stays
+    above 0.3 at every index, so the A plane is held to its rounding bound
+    everywhere, never to the absolute floor."""
+    n = 1 << 22
+    a, b = wl.linrec_pairs(n, seed=26, a_lo=1.0 - 2.0 ** -22, a_hi=1.0)
+    A, _, SA, _, _ = _oracle(orc, a, b, True)
+    assert A[-1] > 0.3 and np.all(1e-5 * SA > 1e6 * 2.0 ** -100)
+    say("linrec decays near one", inclusive)
+    _check(dw, orc, a, b, inclusive)
+
+
+def _power_of_two_decays(n, seed):
+    """a[t] = 2^e[t] with e in {-1, 0, +1}, the running exponent kept within
+    [-40, 40]: every product of consecutive factors is an exact power of two
+    inside the fp32 range, whatever the grouping."""
+    g = wl.rng(seed)
+    step = g.choice(np.array([-1, 0, 1]), size=n, p=[0.1, 0.8, 0.1])
+    e = np.empty(n, np.int64)
+    s = 0
+    for i in range(n):  # a bounded walk: steps that would leave [-40, 40] turn round
+        d = int(step[i])
+        if abs(s + d) > 40:
+            d = -d
+        e[i] = d
+        s += d
+    return np.ldexp(np.float32(1.0), e).astype(np.float32)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_power_of_two_decays_a_exact(dw, orc, inclusive):
+    """Decays that are powers of two: A is exact in fp32 at every one of 2^22
+    indices in any grouping, so it must equal the oracle bit for bit -- a
+    dropped or doubled factor in any cross-tile carry x.a * y.a shows."""
+    n = 1 << 22
+    a = _power_of_two_decays(n, seed=28)
+    b = wl.normal_f32(n, seed=29)
+    ga, gb, _ = _run(dw, a, b, inclusive)
+    A, B, SA, SB, _ = _oracle(orc, a, b, inclusive)
+    say("linrec power-of-two decays", inclusive)
+    assert np.all((np.abs(A) >= 2.0 ** -40) & (np.abs(A) <= 2.0 ** 40))
+    assert np.array_equal(ga.astype(np.float64), A)
+    assert_linrec_close(ga, gb, A, B, SA, SB, not inclusive)
+
+
+@pytest.mark.parametrize("inclusive", [False, True])
+def test_sign_multipliers_exact(dw, orc, inclusive):
+    """a = +-1 and small integer b: every product and every partial sum is an
+    exact fp32 integer in any grouping, so A (= +-1) and B must equal the
+    oracle bit for bit at every index -- a wrong sign anywhere in a
+    cross-tile carry shows."""
+    n = 200 * WT + 33
+    g = wl.rng(27)
+    a = np.where(g.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    b = g.integers(-4, 5, size=n).astype(np.float32)
+    ga, gb, _ = _run(dw, a, b, inclusive)
+    A, B, _, _, _ = _oracle(orc, a, b, inclusive)
+    say("linrec sign multipliers", inclusive)
+    assert np.array_equal(ga.astype(np.float64), A)
+    assert np.array_equal(gb.astype(np.float64), B)
+    assert np.all(np.abs(A) == 1.0)

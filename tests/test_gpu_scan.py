@@ -193,8 +193,7 @@ def test_workspace_reuse_and_error_word(dw, orc):
     """One workspace serves calls of different sizes; the spin-limit error
     word stays clear."""
     import torch
-    ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, 1 << 22, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, 1 << 22, None, None))
     for n in (1 << 22, 5, FT * 7 + 1, 1 << 22):
         x = wl.full_range_u32(n, seed=n + 3)
         d_in = dev(x)
@@ -242,8 +241,7 @@ def test_repeated_runs_stay_exact(dw, orc):
     ref, _ = orc.scan_u32(x, "sum", False)
     d_in = dev(x)
     d_out = torch.empty_like(d_in)
-    ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32", None, None, n, None, None))
     say("repeat x50", n)
     for it in range(50):
         d_out.fill_(-1)

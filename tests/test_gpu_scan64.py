@@ -113,8 +113,7 @@ def test_repeated_runs_reuse_workspace(dw, orc):
     import torch
     n = 1 << 24
     x = wl.full_range_u32(n, seed=79)
-    ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None))
     ref, ref_total = orc.scan_u32_u64(x, False)
     for it in range(10):
         say("u64 repeat", it)
@@ -128,8 +127,7 @@ def test_fallback_every_stall(dw, orc):
     import torch
     n = (1 << 25) + 5
     x = wl.full_range_u32(n, seed=80)
-    ws = torch.empty(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None),
-                     dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None))
     ref, _ = orc.scan_u32_u64(x, False)
     old = dw.ps_lookback_config_get()
     dw.ps_lookback_config(1, 1)

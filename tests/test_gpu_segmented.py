@@ -183,8 +183,8 @@ def test_repeated_runs_stay_exact(dw, orc):
     import torch
     values, off = wl.zipf_segments(n=1 << 22, num_segments=1 << 12, seed=12)
     ref = orc.segmented_scan_u32(values, off, False, sentinel=SENTINEL)
-    ws = torch.empty(dw.workspace_bytes("ps_segmented_scan_u32", None, values.size, None, off.size - 1,
-                                        None, 0, None), dtype=torch.uint8, device="cuda")
+    ws = dw.new_workspace(dw.workspace_bytes("ps_segmented_scan_u32", None, values.size, None, off.size - 1,
+                                        None, 0, None))
     for it in range(20):
         say("segmented repeat", it)
         got = _run(dw, values, off, False, workspace=ws)
