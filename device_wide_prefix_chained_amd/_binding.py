@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
     L.ps_segmented_tile_elements.restype = u32
     L.ps_compact_tile_records.argtypes = [u32]
     L.ps_compact_tile_records.restype = u32
+    L.ps_scan_noalloc.argtypes = [i32, i32, i32, vp, vp, u64, vp, vp]
+    L.ps_scan_noalloc.restype = i32
+    L.ps_scan_noalloc_bytes.argtypes = []
+    L.ps_scan_noalloc_bytes.restype = ctypes.c_size_t
     L.ps_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
     L.ps_workspace_init.restype = i32
     L.ps_lookback_debug.argtypes = [u32]
@@ -276,6 +280,26 @@ def ps_scan_two_level(op, inclusive, inp, out, total=None, workspace=None, strea
 def ps_scan_single_pass(op, inclusive, inp, out, total=None, workspace=None, stream=None, dtype=None):
     """The single-pass chained form of ps_scan at every n."""
     return _generic("ps_scan_single_pass", op, inclusive, inp, out, total, workspace, stream, dtype)
+
+
+def ps_scan_noalloc(op, inclusive, inp, out, total=None, stream=None, dtype=None):
+    """ps_scan on the library's own per-device workspace (no allocation)."""
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    if dtype is None:
+        dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
+    dtypes = (torch.float32,) if dtype == PS_F32 else _U32_DTYPES
+    out_dtypes = _U64_DTYPES if dtype == PS_U64 else dtypes
+    _dev_tensor("inp", inp, dtypes)
+    _dev_tensor("out", out, out_dtypes, inp.numel())
+    if total is not None:
+        _dev_tensor("total", total, out_dtypes, 1)
+    _check("ps_scan_noalloc", lib().ps_scan_noalloc(opc, dtype, int(bool(inclusive)), _ptr(inp), _ptr(out),
+                                                    inp.numel(), _ptr(total), _stream(inp, stream)))
+    return out
+
+
+def ps_scan_noalloc_bytes() -> int:
+    return int(lib().ps_scan_noalloc_bytes())
 
 
 def ps_small_n_config(max_elements: int) -> None:

@@ -33,6 +33,8 @@
 // unfinished tile.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "dwps_device.hpp"
 #include "host_common.hpp"
 #include "pipeline.hpp"
@@ -580,6 +582,52 @@ extern "C" ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtyp
     return scan_any(ws, ws_bytes, op, dtype, inclusive, in, out, n, total, static_cast<hipStream_t>(stream),
                     FlatForm::kAuto);
 }
+
+// ---------------------------------------------------------------------------
+// ps_scan_noalloc: ps_scan on a workspace that lives in the library itself,
+// for callers that cannot allocate device memory.  The array below is that
+// workspace, one copy per device; its address is looked up once per device
+// (in host code its name is not a device address) and the header is
+// prepared by the same first call, on its stream.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device; null until set up
+
+ps_status scratch_for_current_device(hipStream_t s, void **ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PS_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PS_ERR_HIP;
+        if (launch_ws_init(p, kScratchBytes, s) != hipSuccess) return PS_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PS_OK;
+}
+}  // namespace
+
+extern "C" ps_status ps_scan_noalloc(ps_op op, ps_dtype dtype, int inclusive, const void *in, void *out, uint64_t n,
+                                     void *total, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    size_t need = 0;
+    const ps_status q = scan_any(nullptr, &need, op, dtype, inclusive, in, out, n, total, s, FlatForm::kAuto);
+    if (q != PS_OK) return q;
+    if (need > kScratchBytes) return PS_ERR_SIZE;
+    void *ws = nullptr;
+    const ps_status st = scratch_for_current_device(s, &ws);
+    if (st != PS_OK) return st;
+    size_t have = kScratchBytes;
+    return scan_any(ws, &have, op, dtype, inclusive, in, out, n, total, s, FlatForm::kAuto);
+}
+
+extern "C" size_t ps_scan_noalloc_bytes(void) { return kScratchBytes; }
 
 extern "C" ps_status ps_scan_single_pass(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive,
                                          const void *in, void *out, uint64_t n, void *total, void *stream) {

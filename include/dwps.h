@@ -234,6 +234,24 @@ ps_status ps_scan(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
                   int inclusive, const void *in, void *out, uint64_t n,
                   void *total, void *stream);
 
+/* ps_scan for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, results and errors as ps_scan without ws / ws_bytes: the
+ * workspace is a fixed array of ps_scan_noalloc_bytes() bytes (4 MiB)
+ * inside the library, one per device, held until the process ends.  Its
+ * address is looked up, and its header prepared with one small kernel on
+ * `stream`, by the first call on each device; later calls launch only the
+ * scan.  Every call on a device shares that device's array, which keeps
+ * itself ready between calls: calls that overlap on one device (two
+ * streams, or the first call on one stream with a later one on another
+ * before the first has run) race and give wrong results.  An n whose
+ * workspace would exceed the array returns PS_ERR_SIZE (every 32-bit and
+ * fp32 scan fits; the widening sum fits n up to about 1.6e9).  Allocates
+ * nothing on the device or the host. */
+ps_status ps_scan_noalloc(ps_op op, ps_dtype dtype, int inclusive, const void *in,
+                          void *out, uint64_t n, void *total, void *stream);
+size_t ps_scan_noalloc_bytes(void);
+
 /* The two forms behind every flat entry point, callable on their own.
  *
  * ps_scan_single_pass: the chained scan with decoupled look-back, at every
