@@ -4,11 +4,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one call of the library entry point over the whole input resident
-in HBM (workspace clear + the single-pass kernel).  W untimed steps, then K
+in HBM (one kernel launch on a prepared workspace).  W untimed steps, then K
 steps timed with the wall clock between two device synchronisations; HIP
 events that the library records around its main kernel on the same stream,
 on every 5th of those steps, give that kernel's average duration for the
-roofline figure.  Prints one JSON line.
+roofline figure.  Then, outside those K steps: R more calls, each after a
+flush of the caches (1 GiB read and written through a scratch tensor, four
+times the 256 MB MALL), timed one by one with HIP events (median, min,
+max); and, in the same process and under both protocols, the plain copy,
+read and write streams of 1 GiB that set the practical ceiling
+(`stream_ceiling`: the workload's read bytes at the read rate plus its
+written bytes at the write rate, and the copy itself).  Prints one JSON
+line.
 
 Workloads (default: u32x): the headline is the uint32 exclusive sum scan of
 2^28 elements, values uniform in [0, 255] (seed 2).  The others time the
@@ -109,8 +116,8 @@ def build_workload(name: str):
             form = "single-pass form forced"
         tile = dw.ps_two_level_tile_elements() if name == "u32s" else dw.ps_tile_elements(0)
         return dict(desc="u32 exclusive sum scan, n=2^20, values uniform in [0,15], seed 1, " + form,
-                    dtype="u32", n=n, bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=False,
-                    kind="u32", tile=tile)
+                    dtype="u32", n=n, bytes=8.0 * n, rbytes=4.0 * n, inputs=dict(x=x), run=run, out=d_out,
+                    inclusive=False, kind="u32", tile=tile)
     if name in ("read", "write"):
         # the halves of the copy: 1 GiB only read, 1 GiB only written
         n = wl.N_LARGE_U32
@@ -123,8 +130,8 @@ def build_workload(name: str):
         else:
             run = lambda: dw.ps_fill_u32(d_in, 7)  # noqa: E731
             desc = "write-only stream of 2^28 uint32 (1 GiB written)"
-        return dict(desc=desc, dtype="u32", n=n, bytes=4.0 * n, inputs=dict(x=x), run=run, out=d_in,
-                    inclusive=False, kind="copy")
+        return dict(desc=desc, dtype="u32", n=n, bytes=4.0 * n, rbytes=4.0 * n if name == "read" else 0.0,
+                    inputs=dict(x=x), run=run, out=d_in, inclusive=False, kind="copy")
     if name in ("u32x", "u32x-ragged", "u32i", "copy"):
         n = wl.N_RAGGED_U32 if name == "u32x-ragged" else wl.N_LARGE_U32
         x = wl.large_u32()[:n]
@@ -139,10 +146,13 @@ def build_workload(name: str):
             ws = dw.new_workspace(dw.workspace_bytes(fn, None, None, n, None, None))
             f = getattr(dw, fn)
             run = lambda: f(d_in, d_out, total, workspace=ws)  # noqa: E731
+            stats_run = lambda st: dw.ps_scan_lookback_stats("sum", incl, d_in, d_out, st, workspace=ws)  # noqa
             desc = "u32 %s sum scan, n=%s, values uniform in [0,255], seed 2" % (
                 "inclusive" if incl else "exclusive", "2^28-12345" if name == "u32x-ragged" else "2^28")
-        return dict(desc=desc, dtype="u32", n=n, bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out,
-                    inclusive=(name == "u32i"), kind="copy" if name == "copy" else "u32")
+        return dict(desc=desc, dtype="u32", n=n, bytes=8.0 * n, rbytes=4.0 * n, inputs=dict(x=x), run=run,
+                    out=d_out, inclusive=(name == "u32i"), kind="copy" if name == "copy" else "u32",
+                    stats_run=None if name == "copy" else stats_run,
+                    stats_tiles=None if name == "copy" else dw.ps_lookback_tiles(n))
     if name == "u64x":
         n = wl.N_LARGE_U32
         x = wl.large_u32()
@@ -151,8 +161,8 @@ def build_workload(name: str):
         ws = dw.new_workspace(dw.workspace_bytes("ps_scan_exclusive_u32_u64", None, None, n, None, None))
         run = lambda: dw.ps_scan_exclusive_u32_u64(d_in, d_out, total, workspace=ws)  # noqa: E731
         return dict(desc="widening u32 -> u64 exclusive sum scan, n=2^28, values uniform in [0,255], seed 2",
-                    dtype="u64", n=n, bytes=12.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=False,
-                    kind="u64")
+                    dtype="u64", n=n, bytes=12.0 * n, rbytes=4.0 * n, inputs=dict(x=x), run=run, out=d_out,
+                    inclusive=False, kind="u64")
     if name in ("f32", "f32max"):
         n = wl.N_F32
         x = wl.f32_normal()
@@ -160,8 +170,10 @@ def build_workload(name: str):
         op = "sum" if name == "f32" else "max"
         ws = dw.new_workspace(dw.workspace_bytes("ps_scan", 0, 1, 1, None, None, n, None, None))
         run = lambda: dw.ps_scan(op, True, d_in, d_out, workspace=ws)  # noqa: E731
+        stats_run = lambda st: dw.ps_scan_lookback_stats(op, True, d_in, d_out, st, workspace=ws)  # noqa: E731
         return dict(desc="fp32 inclusive %s scan, n=2^27, N(0,1), seed 3" % op, dtype="f32", n=n,
-                    bytes=8.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=True, kind="f32" + op)
+                    bytes=8.0 * n, rbytes=4.0 * n, inputs=dict(x=x), run=run, out=d_out, inclusive=True,
+                    kind="f32" + op, stats_run=stats_run, stats_tiles=dw.ps_lookback_tiles(n))
     if name in ("linrec", "linrec-h"):
         # both planes of the scanned pair (16 B per pair), or h = B only (12 B)
         n = wl.N_LINREC
@@ -175,8 +187,8 @@ def build_workload(name: str):
         both = name == "linrec"
         return dict(desc="linear recurrence h[t] = a[t] h[t-1] + b[t] as an inclusive fp32 (a, b) pair scan, "
                          "n=2^27, a ~ U[0.9,1), b ~ N(0,1), seed 6, %s written" % ("A and B" if both else "B = h"),
-                    dtype="f32", n=n, bytes=(16.0 if both else 12.0) * n, inputs=dict(a=a, b=b), run=run,
-                    out=(d_oa, d_ob), inclusive=True, kind="linrec")
+                    dtype="f32", n=n, bytes=(16.0 if both else 12.0) * n, rbytes=8.0 * n, inputs=dict(a=a, b=b),
+                    run=run, out=(d_oa, d_ob), inclusive=True, kind="linrec")
     if name == "segmented":
         values, off = wl.zipf_segments()
         n = values.size
@@ -184,10 +196,12 @@ def build_workload(name: str):
         d_out = torch.empty(n, dtype=torch.int32, device="cuda")
         ws = dw.new_workspace(dw.workspace_bytes("ps_segmented_scan_u32", None, n, None, off.size - 1, None, 0, None))
         run = lambda: dw.ps_segmented_scan_u32(d_v, d_o, d_out, inclusive=False, workspace=ws)  # noqa: E731
+        stats_run = lambda st: dw.ps_segmented_lookback_stats_u32(d_v, d_o, d_out, st, workspace=ws)  # noqa
         return dict(desc="segmented u32 exclusive sum scan, 2^26 values U[0,1023], 2^16 CSR segments "
                          "(10% empty, one with 25% of the elements, rank-size Zipf(1.2)), seed 5",
-                    dtype="u32", n=n, bytes=8.0 * n + 4.0 * off.size, inputs=dict(x=values, off=off),
-                    run=run, out=d_out, inclusive=False, kind="segmented")
+                    dtype="u32", n=n, bytes=8.0 * n + 4.0 * off.size, rbytes=4.0 * n + 4.0 * off.size,
+                    inputs=dict(x=values, off=off), run=run, out=d_out, inclusive=False, kind="segmented",
+                    stats_run=stats_run, stats_tiles=-(-n // dw.ps_segmented_tile_elements()))
     if name in ("compact", "compact-staged"):
         staged = name == "compact-staged"
         rec, flags = wl.compaction_records()
@@ -200,14 +214,18 @@ def build_workload(name: str):
         ws = dw.new_workspace(dw.workspace_bytes(fn, None, 16, None, n, None, None, None))
         f = getattr(dw, fn)
         run = lambda: f(d_r, d_f, d_out, cnt, workspace=ws)  # noqa: E731
+        stats_run = None if staged else (  # noqa: E731
+            lambda st: dw.ps_compact_lookback_stats(d_r, d_f, d_out, cnt, st, workspace=ws))
         # staged: flag scan (1 B read, 4 B written) + scatter (1 + 4 + 16 B read)
         # on top of the 16 B written per kept record
         per = (1.0 + 4.0 + 1.0 + 4.0 + 16.0) if staged else 17.0
         return dict(desc="stream compaction of 2^26 16-byte records {u32 id, u32 key, f32 a, f32 b}, "
                          "keep ~ Bernoulli(0.3), seed 4" + (", staged: flag scan then scatter" if staged else ""),
-                    dtype="u32", n=n, bytes=per * n + 16.0 * kept + 8.0, inputs=dict(rec=rec, flags=flags),
+                    dtype="u32", n=n, bytes=per * n + 16.0 * kept + 8.0,
+                    rbytes=(22.0 if staged else 17.0) * n, inputs=dict(rec=rec, flags=flags),
                     run=run, out=d_out, count=cnt, inclusive=False, kind="compact",
-                    timed_per_step=2 if staged else 1)
+                    timed_per_step=2 if staged else 1, stats_run=stats_run,
+                    stats_tiles=-(-n // dw.ps_compact_tile_records(16)))
     raise SystemExit("unknown workload %r" % name)
 
 
@@ -276,8 +294,124 @@ def cpu_baseline(w, gpu_out, min_seconds: float):
         parity = "bit-exact" if (count == gpu_out[1] and np.array_equal(gpu_out[0][:count], out[:count])) \
             else "MISMATCH"
     sample = "the full %d-element input, %d repetitions (median)" % (w["n"], len(times))
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
     return {"value": round(gelems, 4), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds_per_rep": round(med, 4)}, parity
+            "sample": sample, "seconds_per_rep": round(med, 4),
+            "cores_on_box": os.cpu_count(), "cores_usable": usable,
+            "threads_note": "1 of %s host cores (%s usable by this process)" % (os.cpu_count(), usable)}, parity
+
+
+def flushed_reps(run, reps, flush):
+    """R calls, each after a cache flush (outside the timed pair), each timed
+    with HIP events on the current stream (the library's); milliseconds."""
+    import torch
+    times = []
+    for _ in range(reps):
+        flush.add_(1)  # reads and writes 1 GiB: evicts the L2s and the MALL
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        run()
+        end.record()
+        end.synchronize()
+        times.append(start.elapsed_time(end))
+    return {"reps": reps, "median_ms": round(statistics.median(times), 5), "min_ms": round(min(times), 5),
+            "max_ms": round(max(times), 5)}
+
+
+def wall_steps(run, steps, warmup):
+    """Milliseconds per call over `steps` calls between two synchronisations."""
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
+    """Copy, read and write of 1 GiB in the same process, under the same two
+    protocols as the workload; the workload's ceiling is its read bytes at
+    the read rate plus its written bytes at the write rate."""
+    import torch
+
+    import device_wide_prefix_chained_amd as dw
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.int32, device="cuda").fill_(3)
+    dst = torch.empty(n, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gib = 4.0 * n
+    streams = {"copy": lambda: dw.ps_copy_u32(src, dst), "read": lambda: dw.ps_read_u32(src, sink),
+               "write": lambda: dw.ps_fill_u32(dst, 7)}
+    out = {"bytes_each_way": int(gib)}
+    for name, run in streams.items():
+        wall = wall_steps(run, steps, 3)
+        fl = flushed_reps(run, reps, flush)
+        moved = 2 * gib if name == "copy" else gib
+        out[name] = {"wall_ms": round(wall, 5), "flushed_median_ms": fl["median_ms"],
+                     "gbs_wall": round(moved / (wall * 1e-3) / 1e9, 1),
+                     "gbs_flushed": round(moved / (fl["median_ms"] * 1e-3) / 1e9, 1)}
+    del src, dst
+    rb = w["rbytes"]
+    wb = w["bytes"] - rb
+    for proto, key in (("wall", "gbs_wall"), ("flushed", "gbs_flushed")):
+        model_ms = (rb / (out["read"][key] * 1e9) + wb / (out["write"][key] * 1e9)) * 1e3
+        mine = scan_ms if proto == "wall" else scan_flushed_ms
+        out["model_ms_" + proto] = round(model_ms, 5)
+        out["frac_of_model_" + proto] = round(model_ms / mine, 4)
+    if rb == wb:  # same bytes each way as the copy of the same size
+        scale = rb / gib
+        out["frac_of_copy_wall"] = round(out["copy"]["wall_ms"] * scale / scan_ms, 4)
+        out["frac_of_copy_flushed"] = round(out["copy"]["flushed_median_ms"] * scale / scan_flushed_ms, 4)
+    return out
+
+
+def lookback_summary(w, reps, warmup):
+    """Run the workload's instrumented kernel (same results, per-tile
+    look-back statistics) and summarise the looking tiles: polls and windows
+    per look-back, stalled polls, look-back time (the wait after the phase's
+    barrier; 100 MHz ticks), and the instrumented call's time."""
+    import torch
+    tiles = w["stats_tiles"]
+    st = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        w["stats_run"](st)
+    torch.cuda.synchronize()
+    rows, times = [], []
+    for _ in range(reps):
+        st.zero_()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        w["stats_run"](st)
+        end.record()
+        end.synchronize()
+        times.append(start.elapsed_time(end))
+        rows.append(st.cpu().numpy().view(np.uint32).reshape(tiles, 4).astype(np.int64))
+    a = np.concatenate(rows)
+    looking = a[a[:, 0] > 0]
+    polls, windows, us, stalls = looking[:, 0], looking[:, 1], looking[:, 2] / 100.0, looking[:, 3]
+
+    def hist(v, top):
+        h = {str(k): int(np.sum(v == k)) for k in range(1, top)}
+        h["%d+" % top] = int(np.sum(v >= top))
+        return h
+
+    pct = lambda q: round(float(np.percentile(us, q)), 2)  # noqa: E731
+    return {"tiles_per_call": tiles, "calls": reps, "looking_tiles_per_call": round(len(looking) / reps, 1),
+            "polls_hist": hist(polls, 5), "windows_hist": hist(windows, 4),
+            "tiles_with_a_stall_pct": round(100.0 * float(np.mean(stalls > 0)), 2),
+            "stalled_polls_per_looking_tile": round(float(stalls.mean()), 3),
+            "mean_polls": round(float(polls.mean()), 3),
+            "lookback_us": {"p50": pct(50), "p90": pct(90), "p99": pct(99), "max": round(float(us.max()), 2),
+                            "mean": round(float(us.mean()), 2)},
+            "instrumented_call_ms_median": round(statistics.median(times), 5)}
 
 
 def main():
@@ -288,6 +422,12 @@ def main():
     ap.add_argument("--workload", default="u32x")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum oracle time of the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--lookback-stats", type=int, default=0, metavar="R",
+                    help="also run the instrumented kernel R times and summarise its look-back "
+                         "statistics (u32x, u32i, f32, f32max, segmented, compact)")
+    ap.add_argument("--flushed-reps", type=int, default=20,
+                    help="calls timed one by one after a cache flush, and the same for the "
+                         "stream ceilings (0 skips both)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -325,6 +465,20 @@ def main():
     dw.ps_kernel_timing(False)
 
     ms_per_step = elapsed * 1e3 / args.steps
+    flushed = ceiling = None
+    if args.flushed_reps > 0:
+        print("[bench] %d calls after cache flushes" % args.flushed_reps, file=sys.stderr, flush=True)
+        flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+        flushed = flushed_reps(run, args.flushed_reps, flush)
+        print("[bench] stream ceilings (copy, read, write)", file=sys.stderr, flush=True)
+        ceiling = stream_ceiling(w, args.steps, args.flushed_reps, flush, ms_per_step, flushed["median_ms"])
+        del flush
+    lb = None
+    if args.lookback_stats > 0:
+        if not w.get("stats_run"):
+            raise SystemExit("no instrumented kernel for workload %r" % args.workload)
+        print("[bench] look-back statistics, %d calls" % args.lookback_stats, file=sys.stderr, flush=True)
+        lb = lookback_summary(w, args.lookback_stats, 3)
     # kernels timed per call: their HIP-event pairs add up to one step
     kernel_ms = kernel_ms_total / max(launches, 1) * w.get("timed_per_step", 1)
     n = w["n"]
@@ -371,7 +525,13 @@ def main():
                      "kernel_ms": round(kernel_ms, 5), "timed_launches": launches},
         "cpu_baseline": cpu,
         "parity": parity,
+        "timing": {"protocol": "value and ms_per_step: K calls back to back between two synchronisations; "
+                               "flushed: calls one by one, caches flushed before each, HIP events",
+                   "flushed": flushed},
+        "stream_ceiling": ceiling,
     }
+    if lb is not None:
+        line["lookback_stats"] = lb
     print(json.dumps(line), flush=True)
 
 

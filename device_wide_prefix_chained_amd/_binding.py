@@ -95,6 +95,12 @@ def lib() -> ctypes.CDLL:
     L.ps_fill_u32.restype = i32
     L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
     L.ps_lookback_stats_u32.restype = i32
+    L.ps_scan_lookback_stats.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
+    L.ps_scan_lookback_stats.restype = i32
+    L.ps_segmented_lookback_stats_u32.argtypes = [vp, sz, vp, u64, vp, u32, vp, i32, vp, vp]
+    L.ps_segmented_lookback_stats_u32.restype = i32
+    L.ps_compact_lookback_stats.argtypes = [vp, sz, vp, u32, vp, u64, vp, vp, vp, vp]
+    L.ps_compact_lookback_stats.restype = i32
     L.ps_lookback_tiles.argtypes = [u64]
     L.ps_lookback_tiles.restype = u64
     L.ps_kernel_timing.argtypes = [i32]
@@ -372,6 +378,66 @@ def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None,
                                                    _ptr(stats), int(bool(aggregate_only)), s)
     ws, have = _workspace("ps_lookback_stats_u32", call, inp.device, workspace, stream)
     _check("ps_lookback_stats_u32", call(_ptr(ws), ctypes.byref(have)))
+    return stats
+
+
+def ps_scan_lookback_stats(op, inclusive, inp, out, stats, workspace=None, stream=None, dtype=None):
+    """ps_scan (u32 sum, f32 sum, f32 max) with per-tile look-back statistics:
+    stats holds 4 uint32 per tile (polls, windows, 100 MHz ticks, stalls)."""
+    opc = OPS[op] if isinstance(op, str) else int(op)
+    if dtype is None:
+        dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
+    dtypes = (torch.float32,) if dtype == PS_F32 else _U32_DTYPES
+    _dev_tensor("inp", inp, dtypes)
+    _dev_tensor("out", out, dtypes, inp.numel())
+    n = inp.numel()
+    _dev_tensor("stats", stats, _U32_DTYPES, 4 * ps_lookback_tiles(n))
+    s = _stream(inp, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_scan_lookback_stats(ws, wsb, opc, dtype, int(bool(inclusive)),  # noqa: E731
+                                                    _ptr(inp), _ptr(out), n, _ptr(stats), s)
+    ws, have = _workspace("ps_scan_lookback_stats", call, inp.device, workspace, stream)
+    _check("ps_scan_lookback_stats", call(_ptr(ws), ctypes.byref(have)))
+    return stats
+
+
+def ps_segmented_lookback_stats_u32(values, offsets, out, stats, inclusive=False, workspace=None, stream=None):
+    """ps_segmented_scan_u32 with per-tile look-back statistics."""
+    _dev_tensor("values", values, _U32_DTYPES)
+    _dev_tensor("offsets", offsets, _U32_DTYPES)
+    _dev_tensor("out", out, _U32_DTYPES, values.numel())
+    n = values.numel()
+    tiles = -(-n // ps_segmented_tile_elements())
+    _dev_tensor("stats", stats, _U32_DTYPES, 4 * tiles)
+    nseg = offsets.numel() - 1
+    s = _stream(values, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_segmented_lookback_stats_u32(ws, wsb, _ptr(values), n, _ptr(offsets),  # noqa
+                                                             nseg, _ptr(out), int(bool(inclusive)), _ptr(stats), s)
+    ws, have = _workspace("ps_segmented_lookback_stats_u32", call, values.device, workspace, stream)
+    _check("ps_segmented_lookback_stats_u32", call(_ptr(ws), ctypes.byref(have)))
+    return stats
+
+
+def ps_compact_lookback_stats(records, flags, out, num_selected, stats, workspace=None, stream=None):
+    """ps_compact of 16-byte records with per-tile look-back statistics."""
+    _dev_tensor("records", records)
+    _dev_tensor("flags", flags, (torch.uint8, torch.bool))
+    _dev_tensor("out", out)
+    _dev_tensor("num_selected", num_selected, (torch.int64, torch.uint64), 1)
+    n = flags.numel()
+    tiles = -(-n // ps_compact_tile_records(16))
+    _dev_tensor("stats", stats, _U32_DTYPES, 4 * tiles)
+    row = 1
+    for d in records.shape[1:]:
+        row *= int(d)
+    rb = records.element_size() * row
+    s = _stream(flags, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_compact_lookback_stats(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa
+                                                       _ptr(out), _ptr(num_selected), _ptr(stats), s)
+    ws, have = _workspace("ps_compact_lookback_stats", call, flags.device, workspace, stream)
+    _check("ps_compact_lookback_stats", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
 

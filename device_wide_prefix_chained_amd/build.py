@@ -33,9 +33,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Extra hipcc flags (e.g. -D overrides of the tile shape or look-back width
+# for tuning builds); empty for the library as shipped.
+EXTRA_FLAGS = os.environ.get("DWPS_HIPCC_FLAGS", "").split()
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *EXTRA_FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, r.stdout, r.stderr))

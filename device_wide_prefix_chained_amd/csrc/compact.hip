@@ -276,11 +276,11 @@ struct CompactFallback {
     }
 };
 
-template <class Rec, int D, int Q, int LB_K, int G, bool VEC>
+template <class Rec, int D, int Q, int LB_K, int G, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *records, const uint8_t *flags,
                                                                uint32_t n, Rec *out, uint64_t *num_selected,
                                                                uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
-                                                               LookbackCfg cfg) {
+                                                               LookbackCfg cfg, uint32_t *stats) {
     __shared__ CompactShared<D, Q> sh;
     __shared__ WsShared wsh;
     const uint32_t lane = threadIdx.x & 63u;
@@ -293,14 +293,14 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
         using Fb = CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>;
         if (wave == 0) {
             ws_wait_clean(call, ctr);
-            control_loop3<SumU32, D, LB_K, G, false, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
-                                                                  nullptr, 0, cfg, Fb{flags, n}, lane);
+            control_loop3<SumU32, D, LB_K, G, STATS, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
+                                                                  stats, 0, cfg, Fb{flags, n}, lane);
         } else {
             compact_data_loop3<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
                                                   wave - 1);
         }
     }
-    ws_finish(wsh, num_tiles, ctr);
+    if (wave == 0) ws_done(wsh, num_tiles, ctr, lane);
 }
 
 __global__ void write_count_zero(uint64_t *p) { *p = 0ull; }
@@ -317,9 +317,9 @@ constexpr int kCompactQ = DWPS_COMPACT_Q;
 constexpr int kCompactG = 2;
 constexpr int kCompactThreads = (kCompactD + 1) * 64;
 
-template <class Rec>
+template <class Rec, bool STATS>
 ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const uint8_t *flags, uint64_t n,
-                         void *out, uint64_t *num_selected, hipStream_t s) {
+                         void *out, uint64_t *num_selected, uint32_t *stats, hipStream_t s) {
     constexpr uint32_t TILE = (uint32_t)kCompactD * kCompactQ * 64u * (16u / sizeof(Rec));
     const uint64_t tiles = ceil_div(n, TILE);
     bool query = false;
@@ -332,12 +332,14 @@ ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const 
         return launch_status();
     }
     if (!records || !flags || !out) return PS_ERR_NULL;
-    if (!aligned(records, sizeof(Rec)) || !aligned(out, sizeof(Rec))) return PS_ERR_ALIGNMENT;
+    if (STATS && !stats) return PS_ERR_NULL;
+    if (!aligned(records, sizeof(Rec)) || !aligned(out, sizeof(Rec)) || !aligned(ws, 16)) return PS_ERR_ALIGNMENT;
     const size_t bytes = n * sizeof(Rec);
     if (ranges_overlap(out, bytes, records, bytes) || ranges_overlap(out, bytes, flags, n) ||
         ranges_overlap(num_selected, 8, out, bytes))
         return PS_ERR_ALIAS;
     const bool vec = aligned(records, 16) && aligned(flags, 16 / sizeof(Rec));
+    if (STATS && !vec) return PS_ERR_ALIGNMENT;  // instrumented for the vector path only
     const Rec *rin = static_cast<const Rec *>(records);
     Rec *rout = static_cast<Rec *>(out);
     const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
@@ -349,11 +351,15 @@ ps_status launch_compact(void *ws, size_t *ws_bytes, const void *records, const 
         timing_begin(s);
         const LookbackCfg cfg = lookback_cfg(false);
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCompactThreads), 0, s, rin, flags, n32, rout, num_selected,
-                           nt, ctr, desc, cfg);
+                           nt, ctr, desc, cfg, stats);
         return PS_OK;
     };
-    const ps_status r = vec ? launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, true>)
-                            : launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, false>);
+    ps_status r;
+    if constexpr (STATS)
+        r = launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, true, true>);
+    else
+        r = vec ? launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, true, false>)
+                : launch(compact_kernel<Rec, kCompactD, kCompactQ, DWPS_LOOKBACK_K, kCompactG, false, false>);
     if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
@@ -369,11 +375,20 @@ extern "C" ps_status ps_compact(void *ws, size_t *ws_bytes, const void *records,
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (record_bytes) {
-    case 4: return launch_compact<uint32_t>(ws, ws_bytes, records, flags, n, out, num_selected, s);
-    case 8: return launch_compact<v2u>(ws, ws_bytes, records, flags, n, out, num_selected, s);
-    case 16: return launch_compact<v4u>(ws, ws_bytes, records, flags, n, out, num_selected, s);
+    case 4: return launch_compact<uint32_t, false>(ws, ws_bytes, records, flags, n, out, num_selected, nullptr, s);
+    case 8: return launch_compact<v2u, false>(ws, ws_bytes, records, flags, n, out, num_selected, nullptr, s);
+    case 16: return launch_compact<v4u, false>(ws, ws_bytes, records, flags, n, out, num_selected, nullptr, s);
     default: return PS_ERR_UNSUPPORTED;
     }
+}
+
+extern "C" ps_status ps_compact_lookback_stats(void *ws, size_t *ws_bytes, const void *records,
+                                               uint32_t record_bytes, const uint8_t *flags, uint64_t n, void *out,
+                                               uint64_t *num_selected, uint32_t *stats, void *stream) {
+    if (n >= (1ull << 32)) return PS_ERR_SIZE;
+    if (record_bytes != 16) return PS_ERR_UNSUPPORTED;
+    return launch_compact<v4u, true>(ws, ws_bytes, records, flags, n, out, num_selected, stats,
+                                     static_cast<hipStream_t>(stream));
 }
 
 extern "C" uint32_t ps_compact_tile_records(uint32_t record_bytes) {

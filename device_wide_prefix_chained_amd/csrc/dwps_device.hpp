@@ -268,10 +268,14 @@ template <class Op>
 struct Words1 {
     using T = typename Op::T;
     static constexpr int WORDS = 1;
-    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t tf, uint32_t &state, T &v) {
-        const uint64_t w = desc_poll(desc + tile);
-        state = state_seen((uint32_t)(w >> 32), tf);
-        v = from_bits<T>((uint32_t)w);
+    // load() only issues the read; decode() interprets it -- separately, so
+    // that a window read ahead of a barrier is not waited for before it
+    __device__ static void load(const uint64_t *desc, int64_t tile, uint64_t (&raw)[WORDS]) {
+        raw[0] = desc_poll(desc + tile);
+    }
+    __device__ static void decode(const uint64_t (&raw)[WORDS], uint32_t tf, uint32_t &state, T &v) {
+        state = state_seen((uint32_t)(raw[0] >> 32), tf);
+        v = from_bits<T>((uint32_t)raw[0]);
     }
     __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t tf, uint32_t state, T v) {
         desc_publish(desc + tile, ((uint64_t)(state | tf) << 32) | to_bits(v));
@@ -295,11 +299,14 @@ template <class Op>
 struct Words2 {
     using T = typename Op::T;
     static constexpr int WORDS = 2;
-    __device__ static void read(const uint64_t *desc, int64_t tile, uint32_t tf, uint32_t &state, T &v) {
-        const uint64_t w0 = desc_poll(desc + 2 * tile), w1 = desc_poll(desc + 2 * tile + 1);
-        const uint32_t s0 = state_seen((uint32_t)(w0 >> 32), tf), s1 = state_seen((uint32_t)(w1 >> 32), tf);
+    __device__ static void load(const uint64_t *desc, int64_t tile, uint64_t (&raw)[WORDS]) {
+        raw[0] = desc_poll(desc + 2 * tile);
+        raw[1] = desc_poll(desc + 2 * tile + 1);
+    }
+    __device__ static void decode(const uint64_t (&raw)[WORDS], uint32_t tf, uint32_t &state, T &v) {
+        const uint32_t s0 = state_seen((uint32_t)(raw[0] >> 32), tf), s1 = state_seen((uint32_t)(raw[1] >> 32), tf);
         state = (s0 == s1) ? s0 : ST_INVALID;
-        v = from_bits64<T>(((uint64_t)(uint32_t)w1 << 32) | (uint32_t)w0);
+        v = from_bits64<T>(((uint64_t)(uint32_t)raw[1] << 32) | (uint32_t)raw[0]);
     }
     __device__ static void publish(uint64_t *desc, uint32_t tile, uint32_t tf, uint32_t state, T v) {
         const uint64_t b = to_bits64(v), sw = (uint64_t)(state | tf) << 32;
@@ -365,10 +372,9 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // tile base + 64j + l (each load instruction reads 64 consecutive
 // descriptors); interleaved, it is tile base + Kl + j (each lane reads K
 // consecutive ones, and a lane can fold its own words in tile order).
-template <class T, int K>
+template <int K, int WORDS>
 struct Window {
-    uint32_t sw[K];  // state words
-    T val[K];
+    uint64_t raw[K][WORDS];  // descriptor words as read, decoded when used
 };
 
 template <int K, bool BLOCKED>
@@ -377,16 +383,18 @@ __device__ __forceinline__ int64_t window_index(int64_t base, uint32_t lane, int
 }
 
 // Issue the loads of one window.  Every load is issued before any is used
-// (no branch around a load, so one poll costs one round trip); words before
-// tile 0 read tile 0's and are replaced by the caller.
+// (no branch around a load, so one poll costs one round trip), and nothing
+// is computed from them here, so a window read ahead of a barrier is only
+// waited for where it is decoded; words before tile 0 read tile 0's and are
+// replaced by the look-back.
 template <class Op, int K, bool BLOCKED, class W = WordsFor<Op>>
-__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane, uint32_t tf,
-                                            Window<typename Op::T, K> &win) {
+__device__ __forceinline__ void window_load(const uint64_t *desc, int64_t nearest, uint32_t lane,
+                                            Window<K, W::WORDS> &win) {
     const int64_t base = nearest - 64 * K + 1;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const int64_t idx = window_index<K, BLOCKED>(base, lane, j);
-        W::read(desc, idx >= 0 ? idx : 0, tf, win.sw[j], win.val[j]);
+        W::load(desc, idx >= 0 ? idx : 0, win.raw[j]);
     }
 }
 
@@ -431,7 +439,7 @@ template <class Op, int K, bool STATS, class FB, class W>
 __device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint32_t tile, uint32_t lane,
                                                            LookbackStats &st, uint32_t *hdr, LookbackCfg cfg,
                                                            typename Op::T own, bool may_publish, const FB &fb,
-                                                           const Window<typename Op::T, K> *pre) {
+                                                           const Window<K, W::WORDS> *pre) {
     using T = typename Op::T;
     T acc = Op::id();
     int64_t nearest = (int64_t)tile - 1;
@@ -439,19 +447,20 @@ __device__ __forceinline__ typename Op::T lookback_blocked(uint64_t *desc, uint3
     bool use_pre = pre != nullptr;  // a constant wherever lookback is inlined
     for (;;) {
         const int64_t base = nearest - 64 * K + 1;
-        Window<T, K> win;
+        Window<K, W::WORDS> win;
         if (use_pre)
             win = *pre;
         else
-            window_load<Op, K, true, W>(desc, nearest, lane, cfg.tf, win);
+            window_load<Op, K, true, W>(desc, nearest, lane, win);
         use_pre = false;
         uint32_t sw[K];  // state words
         T val[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
+            W::decode(win.raw[j], cfg.tf, sw[j], val[j]);
             const bool before = window_index<K, true>(base, lane, j) < 0;
-            sw[j] = before ? ST_PREFIX : win.sw[j];
-            val[j] = before ? Op::id() : win.val[j];
+            sw[j] = before ? ST_PREFIX : sw[j];
+            val[j] = before ? Op::id() : val[j];
         }
         // the nearest PREFIX/PARTIAL word: block js, lane ls (js = -1: none)
         int js = -1;
@@ -535,7 +544,7 @@ template <class Op, int K, bool STATS, class FB, class W>
 __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, uint32_t tile, uint32_t lane,
                                                                LookbackStats &st, uint32_t *hdr, LookbackCfg cfg,
                                                                typename Op::T own, bool may_publish, const FB &fb,
-                                                               const Window<typename Op::T, K> *pre) {
+                                                               const Window<K, W::WORDS> *pre) {
     using T = typename Op::T;
     T acc = Op::id();
     int64_t nearest = (int64_t)tile - 1;
@@ -548,17 +557,14 @@ __device__ __forceinline__ typename Op::T lookback_interleaved(uint64_t *desc, u
         // the first window may have been read ahead of time (an older read
         // of a descriptor is still a valid one: states only move forward,
         // and an unpublished word just costs another poll)
-        Window<T, K> win;
+        Window<K, W::WORDS> win;
         if (use_pre)
             win = *pre;
         else
-            window_load<Op, K, false, W>(desc, nearest, lane, cfg.tf, win);
+            window_load<Op, K, false, W>(desc, nearest, lane, win);
         use_pre = false;
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            sw[j] = win.sw[j];
-            val[j] = win.val[j];
-        }
+        for (int j = 0; j < K; ++j) W::decode(win.raw[j], cfg.tf, sw[j], val[j]);
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const bool before = first + j < 0;
@@ -640,7 +646,7 @@ __device__ __forceinline__ typename Op::T lookback(uint64_t *desc, uint32_t tile
                                                    uint32_t *hdr, LookbackCfg cfg = LookbackCfg{0u, 0u, 0u, 0u},
                                                    typename Op::T own = Op::id(), bool may_publish = false,
                                                    const FB &fb = FB{},
-                                                   const Window<typename Op::T, K> *pre = nullptr) {
+                                                   const Window<K, W::WORDS> *pre = nullptr) {
     if constexpr (BLOCKED)
         return lookback_blocked<Op, K, STATS, FB, W>(desc, tile, lane, st, hdr, cfg, own, may_publish, fb, pre);
     else

@@ -90,8 +90,8 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         }
         const bool have = pt.prev2 < num_tiles && pt.prev2 != 0;
         const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
-        Window<T, LB_K> win;
-        if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, cfg.tf, win);
+        Window<LB_K, W::WORDS> win;
+        if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, win);
         __syncthreads();  // B: prev3's prefix is in LDS
         LookbackStats st;
         uint64_t t0 = 0;

@@ -233,7 +233,7 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
             data_loop3<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, hdr, lane, wave - 1);
         }
     }
-    ws_finish(wsh, num_tiles * (uint32_t)WordsFor<Op>::WORDS, hdr);
+    if (wave == 0) ws_done(wsh, num_tiles * (uint32_t)WordsFor<Op>::WORDS, hdr, lane);
 }
 
 template <class T>
@@ -647,6 +647,19 @@ extern "C" ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uin
                                            uint64_t n, uint32_t *stats, int aggregate_only, void *stream) {
     return launch_flat<SumU32, true>(ws, ws_bytes, in, out, n, nullptr, false, stats,
                                      static_cast<hipStream_t>(stream), 0u, aggregate_only);
+}
+
+extern "C" ps_status ps_scan_lookback_stats(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype, int inclusive,
+                                            const void *in, void *out, uint64_t n, uint32_t *stats, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool inc = inclusive != 0;
+    if (op == PS_OP_SUM && dtype == PS_U32)
+        return launch_flat<SumU32, true>(ws, ws_bytes, in, out, n, nullptr, inc, stats, s, 0u);
+    if (op == PS_OP_SUM && dtype == PS_F32)
+        return launch_flat<SumF32, true>(ws, ws_bytes, in, out, n, nullptr, inc, stats, s, 0.0f);
+    if (op == PS_OP_MAX && dtype == PS_F32)
+        return launch_flat<MaxF32, true>(ws, ws_bytes, in, out, n, nullptr, inc, stats, s, -__builtin_huge_valf());
+    return PS_ERR_UNSUPPORTED;
 }
 
 extern "C" uint64_t ps_lookback_tiles(uint64_t n) { return flat_tiles(n); }

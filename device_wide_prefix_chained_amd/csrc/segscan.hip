@@ -280,10 +280,11 @@ struct SegFallback {
 // data waves finalize, park and scan, into the buffer of this phase's
 // parity; the data waves read it when they scan f2 in the next phase, and
 // read the other buffer in this one.
-template <int D, int Q, int LB_K, int G>
+template <int D, int Q, int LB_K, int G, bool STATS>
 __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles, uint32_t n,
                                                  uint32_t *ctr, uint64_t *desc, LookbackCfg cfg,
-                                                 const StartIndex &idx, const SegFallback &fb, uint32_t lane) {
+                                                 const StartIndex &idx, const SegFallback &fb, uint32_t *stats,
+                                                 uint32_t lane) {
     SegPair a_prev{0u, 0u}, a_prev2{0u, 0u};
     uint32_t fh_prev = kSegTile, fh_prev2 = kSegTile;
     uint32_t carry_out_last = 0;  // carry out of the tile handled one phase ago
@@ -301,15 +302,22 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
         idx.load_batch(s_lo, lane, s_v);
         uint32_t carry = 0;
         const bool have_prev2 = pt.prev2 < num_tiles && pt.prev2 != 0;
+        LookbackStats st;
+        uint64_t t0 = 0;
+        if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
         if (have_prev2) {
             if (pt.prev2 % G != 0u) {
                 carry = carry_out_last;
             } else if (fh_prev2 != 0u) {
-                LookbackStats st;
                 // only a start-free tile's descriptor may turn PARTIAL (a
                 // tile holding a start published PREFIX already)
-                carry = lookback<SumU32, LB_K, false>(desc, pt.prev2, lane, st, ctr, cfg, a_prev2.v, !a_prev2.f, fb);
+                carry = lookback<SumU32, LB_K, STATS>(desc, pt.prev2, lane, st, ctr, cfg, a_prev2.v, !a_prev2.f, fb);
             }
+        }
+        if (STATS && lane == 0 && pt.prev2 < num_tiles) {
+            const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+            reinterpret_cast<uint4 *>(stats)[pt.prev2] = make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0),
+                                                                   st.stalls);
         }
         if (lane == 0) {
             sh.carry = carry;
@@ -504,11 +512,11 @@ __device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh,
     }
 }
 
-template <int D, int Q, int LB_K, int G, bool INCL, bool VEC>
+template <int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *values, uint32_t *out, uint32_t n,
                                                                const uint32_t *offsets, uint32_t num_segments,
                                                                uint32_t num_tiles, uint32_t *ctr, uint64_t *desc,
-                                                               LookbackCfg cfg) {
+                                                               LookbackCfg cfg, uint32_t *stats) {
     __shared__ SegShared<D, Q> sh;
     __shared__ WsShared wsh;
     const uint32_t lane = threadIdx.x & 63u;
@@ -524,8 +532,8 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
             // loads do not wait for it
             idx.load_sample(sh.sample, lane);
             ws_wait_clean(call, ctr);
-            seg_control_loop<D, Q, LB_K, G>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
-                                            SegFallback{values, idx, sh.fb_starts, n}, lane);
+            seg_control_loop<D, Q, LB_K, G, STATS>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
+                                                   SegFallback{values, idx, sh.fb_starts, n}, stats, lane);
         } else {
             // rows outside [offsets[0], offsets[N]) belong to no segment
             const uint32_t lo = offsets[0], hi = offsets[num_segments];
@@ -533,7 +541,7 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
                                               uniform(hi < n ? hi : n), num_tiles, ctr, lane, wave - 1);
         }
     }
-    ws_finish(wsh, num_tiles, ctr);
+    if (wave == 0) ws_done(wsh, num_tiles, ctr, lane);
 }
 
 // Workspace: header and descriptors as for the flat scan.
@@ -543,9 +551,11 @@ inline size_t seg_ws_bytes(uint64_t tiles) { return ws_bytes_for_tiles(tiles); }
 
 using namespace dwps;
 
-extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uint32_t *values, uint64_t n,
-                                           const uint32_t *offsets, uint32_t num_segments, uint32_t *out,
-                                           int inclusive, void *stream) {
+namespace dwps {
+
+template <bool STATS>
+ps_status launch_segmented(void *ws, size_t *ws_bytes, const uint32_t *values, uint64_t n, const uint32_t *offsets,
+                           uint32_t num_segments, uint32_t *out, int inclusive, uint32_t *stats, void *stream) {
     // the offsets' count, num_segments + 1, must fit 32 bits
     if (n >= (1ull << 32) || num_segments == UINT32_MAX) return PS_ERR_SIZE;
     const uint64_t tiles = ceil_div(n, kSegTile);
@@ -554,7 +564,9 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
     if (st != PS_OK || query) return st;
     if (n == 0 || num_segments == 0) return PS_OK;
     if (!values || !offsets || !out) return PS_ERR_NULL;
-    if (!aligned(values, 4) || !aligned(offsets, 4) || !aligned(out, 4)) return PS_ERR_ALIGNMENT;
+    if (STATS && !stats) return PS_ERR_NULL;
+    if (!aligned(values, 4) || !aligned(offsets, 4) || !aligned(out, 4) || !aligned(ws, 16))
+        return PS_ERR_ALIGNMENT;
     if (ranges_overlap(out, n * 4, values, n * 4) ||
         ranges_overlap(out, n * 4, offsets, ((size_t)num_segments + 1) * 4))
         return PS_ERR_ALIAS;
@@ -563,25 +575,44 @@ extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uin
     uint64_t *desc = ws_desc(ws);
     const uint32_t n32 = (uint32_t)n, nt = (uint32_t)tiles;
     const bool vec = aligned(values, 16) && aligned(out, 16);
+    if (STATS && !vec) return PS_ERR_ALIGNMENT;  // instrumented for the vector path only
     auto launch = [&](auto kernel) -> ps_status {
         const uint32_t grid = persistent_grid(reinterpret_cast<const void *>(kernel), kSegThreads, nt);
         if (!grid) return PS_ERR_HIP;
         timing_begin(s);
         const LookbackCfg cfg = lookback_cfg(false);
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(kSegThreads), 0, s, values, out, n32, offsets,
-                           num_segments, nt, ctr, desc, cfg);
+                           num_segments, nt, ctr, desc, cfg, stats);
         return PS_OK;
     };
     ps_status r;
-    if (inclusive)
-        r = vec ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, true>)
-                : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, false>);
-    else
-        r = vec ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, true>)
-                : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, false>);
+    if constexpr (STATS) {
+        r = inclusive ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, true, true>)
+                      : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, true, true>);
+    } else if (inclusive) {
+        r = vec ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, true, false>)
+                : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, true, false, false>);
+    } else {
+        r = vec ? launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, true, false>)
+                : launch(segscan_kernel<kSegD, kSegQ, DWPS_LOOKBACK_K, kSegG, false, false, false>);
+    }
     if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
+}
+
+}  // namespace dwps
+
+extern "C" ps_status ps_segmented_scan_u32(void *ws, size_t *ws_bytes, const uint32_t *values, uint64_t n,
+                                           const uint32_t *offsets, uint32_t num_segments, uint32_t *out,
+                                           int inclusive, void *stream) {
+    return launch_segmented<false>(ws, ws_bytes, values, n, offsets, num_segments, out, inclusive, nullptr, stream);
+}
+
+extern "C" ps_status ps_segmented_lookback_stats_u32(void *ws, size_t *ws_bytes, const uint32_t *values, uint64_t n,
+                                                     const uint32_t *offsets, uint32_t num_segments, uint32_t *out,
+                                                     int inclusive, uint32_t *stats, void *stream) {
+    return launch_segmented<true>(ws, ws_bytes, values, n, offsets, num_segments, out, inclusive, stats, stream);
 }
 
 extern "C" uint32_t ps_segmented_tile_elements(void) { return kSegTile; }

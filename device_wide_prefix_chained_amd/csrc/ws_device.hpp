@@ -5,9 +5,9 @@
 // the workgroup's first ticket; if the call needs dirty descriptor words
 // cleaned, the workgroup holding tile 0 zeroes them and raises the ready
 // word.  Before its first descriptor access the control wave of every
-// workgroup waits for that word (ws_wait_clean).  End: once every wave of
-// the workgroup is done, thread 0 counts the workgroup as finished; the
-// last one to finish writes the header for the next call.
+// workgroup waits for that word (ws_wait_clean).  End: once its last
+// descriptor access is done, the control wave counts the workgroup as
+// finished; the last one to finish writes the header for the next call.
 #pragma once
 
 #include "dwps_device.hpp"
@@ -58,13 +58,17 @@ template <int G>
 __device__ __forceinline__ WsCall ws_start(uint32_t *hdr, uint64_t *desc, uint32_t need, uint32_t num_tiles,
                                            WsShared &sh, uint32_t &t0) {
     if (threadIdx.x == 0) {
+        // the ticket is taken together with the header reads (one round
+        // trip, not two) and given back if the workspace is refused, which
+        // leaves the counter of a prepared workspace as it was
+        const uint32_t g = take_ticket(hdr + kHdrTicket);
         const WsBegin b = ws_read_begin(hdr);
         const WsPlan p = ws_plan(b, need);
         uint32_t first = num_tiles;
         if (p.ok) {
-            const uint32_t g = take_ticket(hdr + kHdrTicket);
             first = (g < (num_tiles + G - 1u) / G) ? g * G : num_tiles;
         } else {
+            __hip_atomic_fetch_sub(hdr + kHdrTicket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             hdr_raise(hdr, p.error);
         }
         sh.begin[0] = b.magic;
@@ -109,31 +113,34 @@ __device__ __forceinline__ void ws_wait_clean(const WsCall &c, uint32_t *hdr) {
     __threadfence();
 }
 
-// Called by every thread at kernel end (after the roles have finished).
-// What the call read at its start is taken again from LDS, so that nothing
-// of it stays live in registers across the pipeline.
-__device__ __forceinline__ void ws_finish(const WsShared &sh, uint32_t need, uint32_t *hdr) {
+// Counts the workgroup done; the last one writes the header for the next
+// call.  Called by ONE wave (lane 0 does the work): the control wave right
+// after its last descriptor access -- the data waves' last stores need not
+// be waited for, since no later part of this call reads them, and the last
+// ticket (taken by a data wave) was consumed before the barrier the control
+// wave passed in that phase -- or the first wave of a workgroup that got no
+// tile.  What the call read at its start is taken again from LDS, so that
+// nothing of it stays live in registers across the pipeline.  No fence: the
+// counters are atomics at agent scope, and descriptor words are read only
+// by later kernels (ordered by the kernel boundary); an agent-scope fence
+// here would write back the XCD's L2 at the exit of every workgroup.
+__device__ __forceinline__ void ws_done(const WsShared &sh, uint32_t need, uint32_t *hdr, uint32_t lane) {
     WsCall c;
     c.begin = ws_shared_begin(sh);
     c.plan = ws_plan(c.begin, need);
     c.need = need;
-    if (!c.plan.ok) return;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();  // this workgroup's tickets and descriptors come first
-        const uint32_t done = __hip_atomic_fetch_add(hdr + kHdrDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1u) {
-            __threadfence();
-            const WsEnd e = ws_end(c.begin, c.plan, c.need);
-            hdr_store(hdr, kHdrTicket, 0u);
-            hdr_store(hdr, kHdrDone, 0u);
-            hdr_store(hdr, kHdrReady, 0u);
-            hdr_store(hdr, kHdrHigh, e.high);
-            hdr_store(hdr, kHdrDirtyLo, e.dirty_lo);
-            hdr_store(hdr, kHdrDirtyHi, e.dirty_hi);
-            hdr_store(hdr, kHdrTag, e.tag);
-            __hip_atomic_fetch_add(hdr + kHdrCalls, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    if (!c.plan.ok || lane != 0u) return;
+    const uint32_t done = __hip_atomic_fetch_add(hdr + kHdrDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1u) {
+        const WsEnd e = ws_end(c.begin, c.plan, c.need);
+        hdr_store(hdr, kHdrTicket, 0u);
+        hdr_store(hdr, kHdrDone, 0u);
+        hdr_store(hdr, kHdrReady, 0u);
+        hdr_store(hdr, kHdrHigh, e.high);
+        hdr_store(hdr, kHdrDirtyLo, e.dirty_lo);
+        hdr_store(hdr, kHdrDirtyHi, e.dirty_hi);
+        hdr_store(hdr, kHdrTag, e.tag);
+        __hip_atomic_fetch_add(hdr + kHdrCalls, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -393,6 +393,34 @@ ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uint32_t *in,
                                 uint32_t *out, uint64_t n, uint32_t *stats,
                                 int aggregate_only, void *stream);
 uint64_t ps_lookback_tiles(uint64_t n);
+
+/* The same per-tile look-back statistics for the other single-pass kernels,
+ * each the kernel of its ordinary entry point built with the instrumentation
+ * (same results; a few percent slower).  `stats` holds 4 uint32 per tile of
+ * that kernel, in the layout above; tiles that do not look back (the
+ * second of a ticket group; in the segmented scan also tiles whose first
+ * element starts a segment, and tile 0) show zero polls.  Every array must
+ * be 16-byte aligned (the instrumented build has only the vector path),
+ * else PS_ERR_ALIGNMENT.
+ *   ps_scan_lookback_stats: ps_scan for (PS_OP_SUM, PS_U32), (PS_OP_SUM,
+ *     PS_F32) and (PS_OP_MAX, PS_F32), single-pass form at every n;
+ *     ps_lookback_tiles(n) tiles.  Other pairs: PS_ERR_UNSUPPORTED.
+ *   ps_segmented_lookback_stats_u32: ps_segmented_scan_u32;
+ *     ceil(n / ps_segmented_tile_elements()) tiles.
+ *   ps_compact_lookback_stats: ps_compact for 16-byte records only (else
+ *     PS_ERR_UNSUPPORTED); ceil(n / ps_compact_tile_records(16)) tiles. */
+ps_status ps_scan_lookback_stats(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
+                                 int inclusive, const void *in, void *out, uint64_t n,
+                                 uint32_t *stats, void *stream);
+ps_status ps_segmented_lookback_stats_u32(void *ws, size_t *ws_bytes,
+                                          const uint32_t *values, uint64_t n,
+                                          const uint32_t *offsets, uint32_t num_segments,
+                                          uint32_t *out, int inclusive, uint32_t *stats,
+                                          void *stream);
+ps_status ps_compact_lookback_stats(void *ws, size_t *ws_bytes, const void *records,
+                                    uint32_t record_bytes, const uint8_t *flags, uint64_t n,
+                                    void *out, uint64_t *num_selected, uint32_t *stats,
+                                    void *stream);
 /* Predecessor descriptors read per look-back poll (64 lanes x K words). */
 uint32_t ps_lookback_window(void);
 /* Tiles claimed per ticket of the flat scan: a workgroup scans that many
