@@ -378,8 +378,10 @@ def lookback_summary(w, reps, warmup):
     per look-back, stalled polls, look-back time (the wait after the phase's
     barrier; 100 MHz ticks), and the instrumented call's time."""
     import torch
+
+    import device_wide_prefix_chained_amd as dw
     tiles = w["stats_tiles"]
-    st = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+    st = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
     for _ in range(warmup):
         w["stats_run"](st)
     torch.cuda.synchronize()
@@ -393,7 +395,7 @@ def lookback_summary(w, reps, warmup):
         end.record()
         end.synchronize()
         times.append(start.elapsed_time(end))
-        rows.append(st.cpu().numpy().view(np.uint32).reshape(tiles, 4).astype(np.int64))
+        rows.append(st.cpu().numpy().view(np.uint32).reshape(tiles, dw.STATS_WORDS).astype(np.int64))
     a = np.concatenate(rows)
     looking = a[a[:, 0] > 0]
     polls, windows, us, stalls = looking[:, 0], looking[:, 1], looking[:, 2] / 100.0, looking[:, 3]
@@ -404,6 +406,44 @@ def lookback_summary(w, reps, warmup):
         return h
 
     pct = lambda q: round(float(np.percentile(us, q)), 2)  # noqa: E731
+    # the scan phase of every tile as the control wave saw it: to barrier B,
+    # waiting at B, B to barrier A, waiting at A (they add up to the phase)
+    ph = a[a[:, 4:8].sum(axis=1) > 0][:, 4:8] / 100.0
+    phase = {"phases": int(ph.shape[0]),
+             "length_us": {"p10": round(float(np.percentile(ph.sum(axis=1), 10)), 3),
+                           "p50": round(float(np.percentile(ph.sum(axis=1), 50)), 3),
+                           "p90": round(float(np.percentile(ph.sum(axis=1), 90)), 3),
+                           "mean": round(float(ph.sum(axis=1).mean()), 3)}}
+    for k, name in enumerate(("control_to_B", "control_waits_at_B", "control_B_to_A", "control_waits_at_A")):
+        phase[name + "_us"] = {"p50": round(float(np.percentile(ph[:, k], 50)), 3),
+                               "p90": round(float(np.percentile(ph[:, k], 90)), 3),
+                               "mean": round(float(ph[:, k].mean()), 3)}
+    # a barrier the control wave waits at for at most 20 ns: it came last
+    phase["control_last_at_B_pct"] = round(100.0 * float(np.mean(ph[:, 1] <= 0.02)), 1)
+    phase["control_last_at_A_pct"] = round(100.0 * float(np.mean(ph[:, 3] <= 0.02)), 1)
+    # the timeline of the last call: workgroup starts, first scan phase and
+    # end of each workgroup (microseconds from the first workgroup's start)
+    r = rows[-1]
+    t0 = int(r[:, 11].min())
+    rel = lambda v: (v - t0) / 100.0  # noqa: E731
+    wgs = {}
+    for row in r:
+        g = wgs.setdefault(int(row[10]), {"entry": int(row[11]), "first_scan": int(row[8]), "last_scan": int(row[8]),
+                                         "end": 0})
+        g["first_scan"] = min(g["first_scan"], int(row[8]))
+        g["last_scan"] = max(g["last_scan"], int(row[8]))
+        if row[12]:
+            g["end"] = int(row[12])
+    entry = np.array([rel(g["entry"]) for g in wgs.values()])
+    first = np.array([rel(g["first_scan"]) for g in wgs.values()])
+    last = np.array([rel(g["last_scan"]) for g in wgs.values()])
+    end = np.array([rel(g["end"]) for g in wgs.values() if g["end"]])
+    q = lambda v: {"min": round(float(v.min()), 2), "p50": round(float(np.median(v)), 2),  # noqa: E731
+                   "max": round(float(v.max()), 2)}
+    timeline = {"workgroups": len(wgs), "start_us": q(entry), "first_scan_phase_us": q(first),
+                "last_scan_phase_us": q(last), "end_us": q(end) if end.size else None,
+                "drain_us": q(end - np.array([rel(g["last_scan"]) for g in wgs.values() if g["end"]]))
+                if end.size else None}
     return {"tiles_per_call": tiles, "calls": reps, "looking_tiles_per_call": round(len(looking) / reps, 1),
             "polls_hist": hist(polls, 5), "windows_hist": hist(windows, 4),
             "tiles_with_a_stall_pct": round(100.0 * float(np.mean(stalls > 0)), 2),
@@ -411,7 +451,8 @@ def lookback_summary(w, reps, warmup):
             "mean_polls": round(float(polls.mean()), 3),
             "lookback_us": {"p50": pct(50), "p90": pct(90), "p99": pct(99), "max": round(float(us.max()), 2),
                             "mean": round(float(us.mean()), 2)},
-            "instrumented_call_ms_median": round(statistics.median(times), 5)}
+            "instrumented_call_ms_median": round(statistics.median(times), 5), "phase": phase,
+            "timeline": timeline}
 
 
 def main():

@@ -29,10 +29,12 @@ OPS = {"sum": PS_OP_SUM, "max": PS_OP_MAX, "min": PS_OP_MIN, "and": PS_OP_AND,
 
 # workspace header words and error bits (ps_ws_word, ps_ws_error)
 PS_WS_HEADER_BYTES = 256
-(PS_WS_TICKET, PS_WS_ERROR, PS_WS_FALLBACKS, PS_WS_PARTIALS, PS_WS_TAG, PS_WS_DONE, PS_WS_MAGIC,
- PS_WS_CAPACITY, PS_WS_HIGH, PS_WS_DIRTY_LO, PS_WS_DIRTY_HI, PS_WS_READY, PS_WS_CALLS) = range(13)
+(PS_WS_ERROR, PS_WS_FALLBACKS, PS_WS_PARTIALS, PS_WS_TAG) = range(1, 5)
+(PS_WS_MAGIC, PS_WS_CAPACITY, PS_WS_HIGH, PS_WS_DIRTY_LO, PS_WS_DIRTY_HI, PS_WS_READY, PS_WS_CALLS) = range(6, 13)
+PS_WS_TICKET, PS_WS_DONE = 32, 33
 PS_WS_ERR_SPIN, PS_WS_ERR_NOT_PREPARED, PS_WS_ERR_CAPACITY = 1, 2, 4
 PS_DEBUG_WITHHOLD_AGGREGATES = 1
+STATS_WORDS = 16  # uint32 per tile of the instrumented entry points
 
 _U32_DTYPES = (torch.uint32, torch.int32)
 _U64_DTYPES = (torch.uint64, torch.int64)
@@ -371,7 +373,7 @@ def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None,
     _dev_tensor("inp", inp, _U32_DTYPES)
     _dev_tensor("out", out, _U32_DTYPES, inp.numel())
     n = inp.numel()
-    _dev_tensor("stats", stats, _U32_DTYPES, 4 * ps_lookback_tiles(n))
+    _dev_tensor("stats", stats, _U32_DTYPES, STATS_WORDS * ps_lookback_tiles(n))
     s = _stream(inp, stream)
     L = lib()
     call = lambda ws, wsb: L.ps_lookback_stats_u32(ws, wsb, _ptr(inp), _ptr(out), n,  # noqa: E731
@@ -383,7 +385,7 @@ def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None,
 
 def ps_scan_lookback_stats(op, inclusive, inp, out, stats, workspace=None, stream=None, dtype=None):
     """ps_scan (u32 sum, f32 sum, f32 max) with per-tile look-back statistics:
-    stats holds 4 uint32 per tile (polls, windows, 100 MHz ticks, stalls)."""
+    stats holds 8 uint32 per tile (see ps_lookback_stats_u32 in dwps.h)."""
     opc = OPS[op] if isinstance(op, str) else int(op)
     if dtype is None:
         dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
@@ -391,7 +393,7 @@ def ps_scan_lookback_stats(op, inclusive, inp, out, stats, workspace=None, strea
     _dev_tensor("inp", inp, dtypes)
     _dev_tensor("out", out, dtypes, inp.numel())
     n = inp.numel()
-    _dev_tensor("stats", stats, _U32_DTYPES, 4 * ps_lookback_tiles(n))
+    _dev_tensor("stats", stats, _U32_DTYPES, STATS_WORDS * ps_lookback_tiles(n))
     s = _stream(inp, stream)
     L = lib()
     call = lambda ws, wsb: L.ps_scan_lookback_stats(ws, wsb, opc, dtype, int(bool(inclusive)),  # noqa: E731
@@ -408,7 +410,7 @@ def ps_segmented_lookback_stats_u32(values, offsets, out, stats, inclusive=False
     _dev_tensor("out", out, _U32_DTYPES, values.numel())
     n = values.numel()
     tiles = -(-n // ps_segmented_tile_elements())
-    _dev_tensor("stats", stats, _U32_DTYPES, 4 * tiles)
+    _dev_tensor("stats", stats, _U32_DTYPES, STATS_WORDS * tiles)
     nseg = offsets.numel() - 1
     s = _stream(values, stream)
     L = lib()
@@ -427,7 +429,7 @@ def ps_compact_lookback_stats(records, flags, out, num_selected, stats, workspac
     _dev_tensor("num_selected", num_selected, (torch.int64, torch.uint64), 1)
     n = flags.numel()
     tiles = -(-n // ps_compact_tile_records(16))
-    _dev_tensor("stats", stats, _U32_DTYPES, 4 * tiles)
+    _dev_tensor("stats", stats, _U32_DTYPES, STATS_WORDS * tiles)
     row = 1
     for d in records.shape[1:]:
         row *= int(d)
@@ -576,7 +578,7 @@ def workspace_header(workspace):
     import numpy as np
     torch.cuda.synchronize(workspace.device)
     h = workspace[:PS_WS_HEADER_BYTES].cpu().numpy().view(np.uint32)
-    return [int(v) for v in h[:PS_WS_CALLS + 1]]
+    return [int(v) for v in h[:PS_WS_DONE + 1]]
 
 
 def ps_lookback_config_get():

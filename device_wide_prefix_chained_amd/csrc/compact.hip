@@ -157,7 +157,7 @@ __device__ __forceinline__ bool compact_phase3(RecSpan<Rec, Q> &hold, RecSpan<Re
     constexpr uint32_t TILE = (uint32_t)D * Q * 64u * E;
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
-    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
+    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr + kHdrTicket);
     // cur: the wave's offset in the tile and its count
     uint32_t wave_prefix = 0u;
 #pragma unroll
@@ -166,9 +166,13 @@ __device__ __forceinline__ bool compact_phase3(RecSpan<Rec, Q> &hold, RecSpan<Re
     // the free registers take the tile two ahead
     const uint64_t b2 = (uint64_t)pt.f2 * TILE;
     ld.template load<VEC>(records, flags, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
-    // rank the next tile while the control wave looks back
+    // rank the next tile while the control wave looks back (work on absent
+    // tiles is skipped by uniform branches: nothing waits for their dummy
+    // loads)
     uint32_t kb_n[Q], pos_n[Q];
     {
+        // (also when f1 is absent: its flags are all padding, and a branch
+        // here measured slower than ranking the padding)
         const uint64_t b1 = (uint64_t)pt.f1 * TILE;
         sc.pad(b1 + lane_off, n, b1 + TILE <= n);
         uint32_t run = 0u;
@@ -199,14 +203,16 @@ __device__ __forceinline__ bool compact_phase3(RecSpan<Rec, Q> &hold, RecSpan<Re
         if (pt.prev3 == num_tiles - 1u && d == (uint32_t)D - 1u && lane == 0) *num_selected = base + meta.y;
     }
     // park cur's kept records where prev3's were
+    if (pt.cur < num_tiles) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
+        for (int q = 0; q < Q; ++q) {
 #pragma unroll
-        for (int k = 0; k < E; ++k)
-            if ((kb[q] >> k) & 1u) mine[pos[q] + (uint32_t)__builtin_popcount(kb[q] & ((1u << k) - 1u))] =
-                record_at<Rec>(hold.raw[q], k);
+            for (int k = 0; k < E; ++k)
+                if ((kb[q] >> k) & 1u) mine[pos[q] + (uint32_t)__builtin_popcount(kb[q] & ((1u << k) - 1u))] =
+                    record_at<Rec>(hold.raw[q], k);
+        }
+        if (lane == 0) sh.park_wave[slot][d] = make_uint2(wave_prefix, wave_cnt);
     }
-    if (lane == 0) sh.park_wave[slot][d] = make_uint2(wave_prefix, wave_cnt);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         kb[q] = kb_n[q];
@@ -235,16 +241,16 @@ __device__ __forceinline__ void compact_data_loop3(PipeTiles pt, CompactShared<D
     uint32_t slot = 0;
     int par = 0;
     for (;;) {
-        if (compact_phase3<Rec, D, Q, G, VEC>(x, y, z, par, slot, pt, kb, pos, sh, records, flags, out, num_selected,
-                                              n, num_tiles, ctr, lane, d, lane_off))
+        if (compact_phase3<Rec, D, Q, G, VEC>(x, y, z, par, slot, pt, kb, pos, sh, records, flags, out,
+                                              num_selected, n, num_tiles, ctr, lane, d, lane_off))
             break;
         par ^= 1;
-        if (compact_phase3<Rec, D, Q, G, VEC>(y, z, x, par, slot, pt, kb, pos, sh, records, flags, out, num_selected,
-                                              n, num_tiles, ctr, lane, d, lane_off))
+        if (compact_phase3<Rec, D, Q, G, VEC>(y, z, x, par, slot, pt, kb, pos, sh, records, flags, out,
+                                              num_selected, n, num_tiles, ctr, lane, d, lane_off))
             break;
         par ^= 1;
-        if (compact_phase3<Rec, D, Q, G, VEC>(z, x, y, par, slot, pt, kb, pos, sh, records, flags, out, num_selected,
-                                              n, num_tiles, ctr, lane, d, lane_off))
+        if (compact_phase3<Rec, D, Q, G, VEC>(z, x, y, par, slot, pt, kb, pos, sh, records, flags, out,
+                                              num_selected, n, num_tiles, ctr, lane, d, lane_off))
             break;
         par ^= 1;
     }
@@ -294,7 +300,8 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
         if (wave == 0) {
             ws_wait_clean(call, ctr);
             control_loop3<SumU32, D, LB_K, G, STATS, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
-                                                                  stats, 0, cfg, Fb{flags, n}, lane);
+                                                                  stats, 0, cfg, Fb{flags, n}, lane,
+                                                                  STATS ? wsh.entry : 0u);
         } else {
             compact_data_loop3<Rec, D, Q, G, VEC>(pt, sh, records, flags, out, num_selected, n, num_tiles, ctr, lane,
                                                   wave - 1);

@@ -47,6 +47,75 @@ struct PipeTiles {
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Per-tile statistics rows of the instrumented builds: kStatsWords uint32.
+// Words 0-3: the tile's look-back (polls, windows, time, stalled polls).
+// Words 4-7: the phase that scanned the tile, as the control wave saw it --
+// from the start of the phase to reaching barrier B, waiting at B, from
+// leaving B to reaching barrier A, waiting at A -- which add up to the
+// phase's length: a long wait means the data waves came later.
+// Words 8-12, a timeline (low 32 bits of the counter): [8] start of the
+// tile's scan phase, [9] start of the phase that stored it, [10] the
+// workgroup, [11] the workgroup's start, [12] (last tile a workgroup
+// stored only) the time its control wave finished.  Times in ticks of the
+// 100 MHz real-time counter.
+constexpr int kStatsWords = 16;
+
+__device__ __forceinline__ uint32_t realtime32() { return (uint32_t)__builtin_amdgcn_s_memrealtime(); }
+
+template <bool STATS>
+struct PhaseClock {
+    uint64_t start = 0, t_reach_b = 0, t_leave_b = 0, t_reach_a = 0;
+    __device__ __forceinline__ void begin() {
+        if (STATS) start = __builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ void reach_b() {
+        if (STATS) t_reach_b = __builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ void leave_b() {
+        if (STATS) t_leave_b = __builtin_amdgcn_s_memrealtime();
+    }
+    __device__ __forceinline__ void reach_a() {
+        if (STATS) t_reach_a = __builtin_amdgcn_s_memrealtime();
+    }
+    // after barrier A, by lane 0 of the control wave: the phase of the tile
+    // scanned (f1) and the start of the store phase of the tile stored (s)
+    __device__ __forceinline__ void record(uint32_t *stats, uint32_t f1, uint32_t s, uint32_t num_tiles,
+                                           uint32_t entry, bool writer) {
+        if (STATS && writer) {
+            const uint64_t t = __builtin_amdgcn_s_memrealtime();
+            if (f1 < num_tiles) {
+                uint32_t *row = stats + (uint64_t)kStatsWords * f1;
+                uint4 r;
+                r.x = (uint32_t)(t_reach_b - start);
+                r.y = (uint32_t)(t_leave_b - t_reach_b);
+                r.z = (uint32_t)(t_reach_a - t_leave_b);
+                r.w = (uint32_t)(t - t_reach_a);
+                reinterpret_cast<uint4 *>(row)[1] = r;
+                row[8] = (uint32_t)start;
+                row[10] = blockIdx.x;
+                row[11] = entry;
+            }
+            if (s < num_tiles) {
+                uint32_t *row = stats + (uint64_t)kStatsWords * s;
+                row[9] = (uint32_t)start;
+                if (f1 >= num_tiles) {
+                    // a phase that scanned nothing (the drain): its parts,
+                    // two per word (16 bits each)
+                    row[13] = (uint32_t)(t_reach_b - start) | ((uint32_t)(t_leave_b - t_reach_b) << 16);
+                    row[14] = (uint32_t)(t_reach_a - t_leave_b) | ((uint32_t)(t - t_reach_a) << 16);
+                }
+            }
+        }
+    }
+    // after the last phase: the store phase of the last tile and the end
+    __device__ __forceinline__ void finish(uint32_t *stats, uint32_t s, uint32_t num_tiles, bool writer) {
+        if (STATS && writer && s < num_tiles) {
+            stats[(uint64_t)kStatsWords * s + 9] = (uint32_t)start;
+            stats[(uint64_t)kStatsWords * s + 12] = realtime32();
+        }
+    }
+};
+
 __device__ __forceinline__ uint32_t next_slot(uint32_t slot) { return slot == kParkSlots - 1 ? 0u : slot + 1u; }
 
 // The tile after f2: the next one of its group of G, or the first tile of a
@@ -74,7 +143,8 @@ template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, bool B
           class FB>
 __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t num_tiles, uint32_t *ctr,
                                               uint64_t *desc, typename Op::T *total, uint32_t *stats,
-                                              int aggregate_only, LookbackCfg cfg, const FB &fb, uint32_t lane) {
+                                              int aggregate_only, LookbackCfg cfg, const FB &fb, uint32_t lane,
+                                              uint32_t t_entry = 0) {
     using T = typename Op::T;
     using W = WordsFor<Op>;
     T agg_prev = Op::id(), agg_prev2 = Op::id(), agg_prev3 = Op::id();
@@ -83,6 +153,8 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
     T agg_next = Op::id();    // aggregate of cur, published at the end of the phase before
     constexpr bool kPairPrefix = PAIR_PREFIX && G > 1;
     for (int par = 0;; par ^= 1) {
+        PhaseClock<STATS> clk;
+        clk.begin();
         const T agg = agg_next;
         if (lane == 0) {
             sh.prefix = excl_next;
@@ -92,7 +164,9 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
         Window<LB_K, W::WORDS> win;
         if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, win);
+        clk.reach_b();
         __syncthreads();  // B: prev3's prefix is in LDS
+        clk.leave_b();
         LookbackStats st;
         uint64_t t0 = 0;
         if (STATS) t0 = __builtin_amdgcn_s_memrealtime();
@@ -104,7 +178,7 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         if (lane == 0) {
             if (STATS && pt.prev2 < num_tiles) {
                 const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-                reinterpret_cast<uint4 *>(stats)[pt.prev2] =
+                reinterpret_cast<uint4 *>(stats)[(kStatsWords / 4) * pt.prev2] =
                     make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
             }
             if (!(STATS && aggregate_only)) {
@@ -130,8 +204,13 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         agg_prev3 = agg_prev2;
         agg_prev2 = agg_prev;
         agg_prev = agg;
-        if (pt.template drained<3>(num_tiles)) break;
+        if (pt.template drained<3>(num_tiles)) {
+            clk.finish(stats, pt.prev3, num_tiles, lane == 0);
+            break;
+        }
+        clk.reach_a();
         __syncthreads();  // A: the next tile id is in LDS
+        clk.record(stats, pt.f1, pt.prev3, num_tiles, t_entry, lane == 0);
         pt.advance(uniform(sh.next), num_tiles);
     }
 }

@@ -77,21 +77,28 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     constexpr int PW = ScanShared<Op, D, Q>::PW;
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
-    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
-    // cur tile-relative, in registers (its wave totals are in wt[par])
-    T wave_prefix = Op::id();
+    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr + kHdrTicket);
+    // cur tile-relative, in registers (its wave totals are in wt[par]).
+    // Work on absent tiles is skipped (uniform branches, taken every phase
+    // but the pipeline's last few): the loads stay straight-line, but
+    // nothing waits for the dummy loads of an absent tile.
+    if (pt.cur < num_tiles) {
+        T wave_prefix = Op::id();
 #pragma unroll
-    for (int w = 0; w < D; ++w)
-        if ((uint32_t)w < d) wave_prefix = Op::op(wave_prefix, sh.wt[par][w]);
-    finalize_span<Op, Q, INCL>(hold, lane_excl, row_prefix, wave_prefix);
+        for (int w = 0; w < D; ++w)
+            if ((uint32_t)w < d) wave_prefix = Op::op(wave_prefix, sh.wt[par][w]);
+        finalize_span<Op, Q, INCL>(hold, lane_excl, row_prefix, wave_prefix);
+    }
     // the free buffer takes the tile two ahead
     const uint64_t b2 = (uint64_t)pt.f2 * TILE;
     ld.template load<VEC>(in, b2 + lane_off, n, b2 + TILE <= n, pt.f2 < num_tiles);
     // scan the next tile while the control wave looks back
-    const uint64_t b1 = (uint64_t)pt.f1 * TILE;
-    sc.pad(b1 + lane_off, n, b1 + TILE <= n);
-    const T wt = scan_span<Op, Q>(sc, lane_excl, row_prefix);
-    if (lane == 0) sh.wt[par ^ 1][d] = wt;
+    if (pt.f1 < num_tiles) {
+        const uint64_t b1 = (uint64_t)pt.f1 * TILE;
+        sc.pad(b1 + lane_off, n, b1 + TILE <= n);
+        const T wt = scan_span<Op, Q>(sc, lane_excl, row_prefix);
+        if (lane == 0) sh.wt[par ^ 1][d] = wt;
+    }
     __syncthreads();  // B
     v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
     if (pt.prev3 < num_tiles) {
@@ -134,12 +141,14 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
         }
     }
     // park cur where prev3 was
+    if (pt.cur < num_tiles) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        v4u w[PW];
-        pack16<T>(hold.v[q], w);
+        for (int q = 0; q < Q; ++q) {
+            v4u w[PW];
+            pack16<T>(hold.v[q], w);
 #pragma unroll
-        for (int h = 0; h < PW; ++h) mine[(q * PW + h) * 64] = w[h];
+            for (int h = 0; h < PW; ++h) mine[(q * PW + h) * 64] = w[h];
+        }
     }
     if (pt.template drained<3>(num_tiles)) return true;
     if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
@@ -228,7 +237,7 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
             ws_wait_clean(call, hdr);
             control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
                 pt, sh, num_tiles, hdr, desc, total, stats, aggregate_only, cfg,
-                FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane);
+                FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane, STATS ? wsh.entry : 0u);
         } else {
             data_loop3<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, hdr, lane, wave - 1);
         }

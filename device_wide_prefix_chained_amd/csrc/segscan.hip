@@ -284,13 +284,15 @@ template <int D, int Q, int LB_K, int G, bool STATS>
 __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &sh, uint32_t num_tiles, uint32_t n,
                                                  uint32_t *ctr, uint64_t *desc, LookbackCfg cfg,
                                                  const StartIndex &idx, const SegFallback &fb, uint32_t *stats,
-                                                 uint32_t lane) {
+                                                 uint32_t lane, uint32_t t_entry) {
     SegPair a_prev{0u, 0u}, a_prev2{0u, 0u};
     uint32_t fh_prev = kSegTile, fh_prev2 = kSegTile;
     uint32_t carry_out_last = 0;  // carry out of the tile handled one phase ago
     SegPair agg_next{0u, 0u};     // cur's aggregate and first start, published a phase ago
     uint32_t fh_next = kSegTile;
     for (int par = 0;; par ^= 1) {
+        PhaseClock<STATS> clk;
+        clk.begin();
         const SegPair agg = agg_next;
         const uint32_t fh = fh_next;
         // f2's starts: the first batch of offsets is in flight during the look-back
@@ -316,8 +318,8 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
         }
         if (STATS && lane == 0 && pt.prev2 < num_tiles) {
             const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
-            reinterpret_cast<uint4 *>(stats)[pt.prev2] = make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0),
-                                                                   st.stalls);
+            reinterpret_cast<uint4 *>(stats)[(kStatsWords / 4) * pt.prev2] =
+                make_uint4(st.polls, st.windows, (uint32_t)(t1 - t0), st.stalls);
         }
         if (lane == 0) {
             sh.carry = carry;
@@ -330,7 +332,9 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
         fh_prev2 = fh_prev;
         a_prev = agg;
         fh_prev = fh;
+        clk.reach_b();
         __syncthreads();  // B: the carry of prev2 is in LDS
+        clk.leave_b();
         agg_next = SegPair{0u, 0u};
         fh_next = kSegTile;
         if (pt.f1 < num_tiles) {
@@ -346,8 +350,13 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
             if (lane == 0 && (prefix || !(cfg.flags & kDbgWithholdAggregates)))
                 desc_publish(desc + pt.f1, desc_word((prefix ? ST_PREFIX : ST_AGGREGATE) | cfg.tf, agg_next.v));
         }
-        if (pt.drained(num_tiles)) break;
+        if (pt.drained(num_tiles)) {
+            clk.finish(stats, pt.prev2, num_tiles, lane == 0);
+            break;
+        }
+        clk.reach_a();
         __syncthreads();  // A: the next tile id is in LDS
+        clk.record(stats, pt.f1, pt.prev2, num_tiles, t_entry, lane == 0);
         pt.advance(uniform(sh.next), num_tiles);
     }
 }
@@ -367,49 +376,54 @@ __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, 
     constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
-    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr);
+    if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr + kHdrTicket);
     const uint32_t old_slot = next_slot(slot);
     v4u *mine = &sh.park[slot][d * Q * 64u + lane];
     const v4u *theirs = &sh.park[old_slot][d * Q * 64u + lane];
 
-    // cur: tile-relative segmented outputs, parked
-    SegPair wave_prefix{0u, 0u};
-    uint32_t first = TILE;
+    // cur: tile-relative segmented outputs, parked.  Work on absent tiles is
+    // skipped (uniform branches, taken every phase but the pipeline's last
+    // few): the loads stay straight-line, but nothing waits for the dummy
+    // loads of an absent tile.
+    if (pt.cur < num_tiles) {
+        SegPair wave_prefix{0u, 0u};
+        uint32_t first = TILE;
 #pragma unroll
-    for (int w = 0; w < D; ++w) {
-        if ((uint32_t)w < d) wave_prefix = seg_op(wave_prefix, SegPair{sh.wf[par][w], sh.wv[par][w]});
-        first = min(first, sh.wfirst[par][w]);
-    }
-    if (d == 0 && lane == 0) sh.park_first[slot] = first;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        // the lane's prefix inside the wave, then the earlier waves' pair
-        const uint32_t c = (fl[q] & 16u) ? pre[q] : wave_prefix.v + pre[q];
-        uint32_t inc[4], o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool seen = (fl[q] & ((2u << k) - 1u)) != 0u;  // a start among elements 0..k
-            inc[k] = seen ? cur.x.v[q][k] : c + cur.x.v[q][k];
+        for (int w = 0; w < D; ++w) {
+            if ((uint32_t)w < d) wave_prefix = seg_op(wave_prefix, SegPair{sh.wf[par][w], sh.wv[par][w]});
+            first = min(first, sh.wfirst[par][w]);
         }
-        if (INCL) {
+        if (d == 0 && lane == 0) sh.park_first[slot] = first;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = inc[k];
-        } else {
-            o[0] = (fl[q] & 1u) ? 0u : c;
+        for (int q = 0; q < Q; ++q) {
+            // the lane's prefix inside the wave, then the earlier waves' pair
+            const uint32_t c = (fl[q] & 16u) ? pre[q] : wave_prefix.v + pre[q];
+            uint32_t inc[4], o[4];
 #pragma unroll
-            for (int k = 1; k < 4; ++k) o[k] = (fl[q] & (1u << k)) ? 0u : inc[k - 1];
+            for (int k = 0; k < 4; ++k) {
+                const bool seen = (fl[q] & ((2u << k) - 1u)) != 0u;  // a start among elements 0..k
+                inc[k] = seen ? cur.x.v[q][k] : c + cur.x.v[q][k];
+            }
+            if (INCL) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[k] = inc[k];
+            } else {
+                o[0] = (fl[q] & 1u) ? 0u : c;
+#pragma unroll
+                for (int k = 1; k < 4; ++k) o[k] = (fl[q] & (1u << k)) ? 0u : inc[k - 1];
+            }
+            v4u w;
+            w.x = o[0];
+            w.y = o[1];
+            w.z = o[2];
+            w.w = o[3];
+            mine[q * 64] = w;
         }
-        v4u w;
-        w.x = o[0];
-        w.y = o[1];
-        w.z = o[2];
-        w.w = o[3];
-        mine[q * 64] = w;
     }
     // the freed registers take the tile two ahead
     cur.template load<VEC>(values, pt.f2, lane_off, n, pt.f2 < num_tiles);
     // scan the next tile while the control wave looks back
-    {
+    if (pt.f1 < num_tiles) {
         const uint64_t b1 = (uint64_t)pt.f1 * TILE;
         f1.x.pad(b1 + lane_off, n, b1 + TILE <= n);
         const uint32_t sh4 = 4u * (lane & 7u);
@@ -533,7 +547,8 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
             idx.load_sample(sh.sample, lane);
             ws_wait_clean(call, ctr);
             seg_control_loop<D, Q, LB_K, G, STATS>(pt, sh, num_tiles, n, ctr, desc, cfg, idx,
-                                                   SegFallback{values, idx, sh.fb_starts, n}, stats, lane);
+                                                   SegFallback{values, idx, sh.fb_starts, n}, stats, lane,
+                                                   STATS ? wsh.entry : 0u);
         } else {
             // rows outside [offsets[0], offsets[N]) belong to no segment
             const uint32_t lo = offsets[0], hi = offsets[num_segments];

@@ -31,6 +31,7 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return (uint32_t)_
 struct WsShared {
     uint32_t begin[6];  // WsBegin
     uint32_t t0;        // the workgroup's first tile (num_tiles: none)
+    uint32_t entry;     // the real-time counter (low 32 bits) at the workgroup's start
 };
 
 // What a workgroup knows about its call's workspace, uniform across it.
@@ -58,6 +59,7 @@ template <int G>
 __device__ __forceinline__ WsCall ws_start(uint32_t *hdr, uint64_t *desc, uint32_t need, uint32_t num_tiles,
                                            WsShared &sh, uint32_t &t0) {
     if (threadIdx.x == 0) {
+        sh.entry = (uint32_t)__builtin_amdgcn_s_memrealtime();
         // the ticket is taken together with the header reads (one round
         // trip, not two) and given back if the workspace is refused, which
         // leaves the counter of a prepared workspace as it was

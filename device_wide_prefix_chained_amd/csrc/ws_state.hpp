@@ -55,7 +55,7 @@ constexpr int kHdrDirtyLo = PS_WS_DIRTY_LO;
 constexpr int kHdrDirtyHi = PS_WS_DIRTY_HI;
 constexpr int kHdrReady = PS_WS_READY;
 constexpr int kHdrCalls = PS_WS_CALLS;
-constexpr int kHdrWords = PS_WS_CALLS + 1;
+constexpr int kHdrWords = PS_WS_DONE + 1;
 
 constexpr uint32_t kWsMagic = 0x44575053u;  // "DWPS"
 

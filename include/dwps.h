@@ -77,19 +77,21 @@ extern "C" {
 /* 32-bit words of the workspace header. */
 #define PS_WS_HEADER_BYTES 256
 typedef enum ps_ws_word {
-    PS_WS_TICKET = 0,    /* tile tickets handed out by the call in flight (0 between calls) */
     PS_WS_ERROR = 1,     /* sticky ps_ws_error bits */
     PS_WS_FALLBACKS = 2, /* look-back fallbacks installed, cumulative */
     PS_WS_PARTIALS = 3,  /* PARTIAL descriptors published (instrumented entry points), cumulative */
     PS_WS_TAG = 4,       /* 9-bit tag of the next call; descriptors carry their call's tag */
-    PS_WS_DONE = 5,      /* workgroups of the call in flight that have finished */
     PS_WS_MAGIC = 6,     /* set by ps_workspace_init */
     PS_WS_CAPACITY = 7,  /* descriptor words the workspace holds */
     PS_WS_HIGH = 8,      /* descriptor words any call has tagged */
     PS_WS_DIRTY_LO = 9,  /* descriptor words [lo, hi) that may hold anything; */
     PS_WS_DIRTY_HI = 10, /* the next call that uses them zeroes them first */
     PS_WS_READY = 11,    /* nonzero once the call in flight has zeroed its dirty words */
-    PS_WS_CALLS = 12     /* single-pass calls completed, modulo 2^32 */
+    PS_WS_CALLS = 12,    /* single-pass calls completed, modulo 2^32 */
+    /* the two counters every workgroup updates, on a 128-byte line of their
+     * own, away from the words every workgroup reads at its start */
+    PS_WS_TICKET = 32,   /* tile tickets handed out by the call in flight (0 between calls) */
+    PS_WS_DONE = 33      /* workgroups of the call in flight that have finished */
 } ps_ws_word;
 typedef enum ps_ws_error {
     PS_WS_ERR_SPIN = 1,         /* a look-back hit its spin limit: results not valid */
@@ -382,10 +384,24 @@ ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void *stream);
 
 /* Exclusive uint32 sum scan (same kernel as ps_scan_exclusive_u32, built
  * with per-tile instrumentation of the look-back of [P1] "Why the work
- * stays linear").  stats: device buffer of 4 * tiles uint32, tiles reported
- * by ps_lookback_tiles(n); per tile: [0] poll rounds, [1] windows of
- * ps_lookback_window() predecessors walked, [2] look-back time in 100 MHz ticks (low 32 bits),
- * [3] number of polls that found an unpublished predecessor.
+ * stays linear").  stats: device buffer of 16 * tiles uint32, tiles
+ * reported by ps_lookback_tiles(n); per tile, times in ticks of the 100 MHz
+ * real-time counter:
+ *   [0] poll rounds of its look-back, [1] windows of ps_lookback_window()
+ *   predecessors walked, [2] look-back time after the barrier its first
+ *   poll straddles, [3] polls that found an unpublished predecessor;
+ *   [4]-[7] the phase that scanned the tile as the pipeline's control wave
+ *   saw it: from the start of the phase to its first barrier, waiting
+ *   there, from there to its second barrier, waiting there (they add up to
+ *   the phase; a long wait means the data waves came later);
+ *   [8]-[12] a timeline, low 32 bits of the counter: [8] start of the
+ *   tile's scan phase, [9] start of the phase that stored it, [10] the
+ *   workgroup (blockIdx), [11] that workgroup's start, [12] for the last
+ *   tile a workgroup stored, the time the workgroup's control wave
+ *   finished (0 for other tiles); [13], [14] when the phase that stored
+ *   the tile scanned no tile (the pipeline's drain), that phase's parts
+ *   as in [4]-[7], two 16-bit values per word (low half first); [15]
+ *   unused.
  * aggregate_only != 0 (a test of the sliding window): tiles after tile 0
  * never publish their inclusive prefix, so every look-back walks back to
  * tile 0 -- quadratic in the tile count, meant for small n only. */
@@ -394,9 +410,9 @@ ps_status ps_lookback_stats_u32(void *ws, size_t *ws_bytes, const uint32_t *in,
                                 int aggregate_only, void *stream);
 uint64_t ps_lookback_tiles(uint64_t n);
 
-/* The same per-tile look-back statistics for the other single-pass kernels,
- * each the kernel of its ordinary entry point built with the instrumentation
- * (same results; a few percent slower).  `stats` holds 4 uint32 per tile of
+/* The same per-tile statistics for the other single-pass kernels, each the
+ * kernel of its ordinary entry point built with the instrumentation (same
+ * results; a few percent slower).  `stats` holds 16 uint32 per tile of
  * that kernel, in the layout above; tiles that do not look back (the
  * second of a ticket group; in the segmented scan also tiles whose first
  * element starts a segment, and tile 0) show zero polls.  Every array must

@@ -245,13 +245,13 @@ def test_partial_descriptors_bound_the_walk(dw, orc, partial):
     ref, _ = orc.scan_u32(x, "sum", False)
     ws = _ws(dw, "ps_scan_exclusive_u32", None, None, n, None, None)
     with lookback_config(dw, 0, partial):
-        stats = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+        stats = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
         d_out = torch.empty_like(d_in)
         say("partial walk", partial)
         dw.ps_lookback_stats_u32(d_in, d_out, stats, aggregate_only=True, workspace=ws)
         assert np.array_equal(host(d_out), ref)
         h = header(dw, ws)
-    st = host(stats).reshape(tiles, 4).astype(np.int64)
+    st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     t = np.arange(1, tiles)
     full_walk = (t + win - 1) // win
     say("windows per tile", partial, float(st[1:, 1].mean()), float(full_walk.mean()), h[dw.PS_WS_PARTIALS])

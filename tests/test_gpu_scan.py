@@ -260,7 +260,7 @@ def test_lookback_instrumented(dw, orc, aggregate_only):
     n = 1100 * tile + 77
     x = wl.full_range_u32(n, seed=21)
     tiles = dw.ps_lookback_tiles(n)
-    stats = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
     d_in = dev(x)
     d_out = torch.empty_like(d_in)
     say("lookback stats", aggregate_only)
@@ -272,7 +272,7 @@ def test_lookback_instrumented(dw, orc, aggregate_only):
         dw.ps_lookback_config(*old)
     ref, _ = orc.scan_u32(x, "sum", False)
     assert np.array_equal(host(d_out), ref)
-    st = host(stats).reshape(tiles, 4).astype(np.int64)
+    st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     assert st[0, 0] == 0 and st[0, 1] == 0  # tile 0 never looks back
     assert np.all(st[1:, 0] >= st[1:, 1])
     t = np.arange(tiles)

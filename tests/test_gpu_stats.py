@@ -4,7 +4,8 @@ per-block descriptor" and "Why the work stays linear": how many polls and
 windows a look-back takes): their results are the ordinary entry points'
 (checked against the oracle), and every statistics row is consistent --
 tiles that do not look back show no polls, a looking tile polls at least
-once per window, stalls never exceed polls."""
+once per window, stalls never exceed polls, and every tile's scan phase was
+timed."""
 import numpy as np
 import pytest
 
@@ -20,8 +21,15 @@ def dw():
 
 
 def _check_rows(st, looks):
-    """st: (tiles, 4) polls, windows, ticks, stalls; looks: which tiles look back."""
+    """st: (tiles, 16) rows (polls, windows, ticks, stalls, the phase timing
+    of the tile's scan phase, the timeline); looks: which tiles look back."""
     polls, windows, stalls = st[:, 0], st[:, 1], st[:, 3]
+    # every tile is scanned in exactly one phase, which both waves timed
+    assert np.all(st[:, 4] + st[:, 5] > 0) and np.all(st[:, 6] + st[:, 7] > 0)
+    # and no phase part takes longer than a millisecond
+    assert np.all(st[:, 4:8] < 100_000)
+    # every tile was stored in some phase, its workgroup started before it
+    assert np.all(st[:, 9] != 0) and np.all(((st[:, 8] - st[:, 11]) & 0xFFFFFFFF) < 10_000_000)
     assert np.all(polls[~looks] == 0) and np.all(windows[~looks] == 0)
     assert np.all(polls[looks] >= 1) and np.all(windows[looks] >= 1)
     assert np.all(polls >= windows) and np.all(stalls <= polls)
@@ -34,7 +42,7 @@ def test_flat_stats(dw, orc, op, dtype):
     import torch
     n = 900 * FLAT_TILE + 17
     tiles = dw.ps_lookback_tiles(n)
-    stats = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
     if dtype == 0:
         x = wl.uniform_u32(n, 256, seed=701)
         d_out = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -52,7 +60,7 @@ def test_flat_stats(dw, orc, op, dtype):
             assert_f32_sum_close(got, ref, absprefix, exclusive=False)
         else:
             assert np.array_equal(got.view(np.uint32), orc.scan_f32_minmax(x, "max", True)[0].view(np.uint32))
-    st = host(stats).reshape(tiles, 4).astype(np.int64)
+    st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     t = np.arange(tiles)
     _check_rows(st, (t % dw.ps_lookback_group() == 0) & (t > 0))
 
@@ -62,12 +70,12 @@ def test_segmented_stats(dw, orc):
     values, off = wl.zipf_segments(n=1 << 24, num_segments=1 << 12, seed=703)
     n = values.size
     tiles = -(-n // TILE)
-    stats = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
     d_out = filled_dev(values, 0xDEADBEEF)
     say("segmented stats")
     dw.ps_segmented_lookback_stats_u32(dev(values), dev(off), d_out, stats)
     assert np.array_equal(host(d_out), orc.segmented_scan_u32(values, off, False, sentinel=0xDEADBEEF))
-    st = host(stats).reshape(tiles, 4).astype(np.int64)
+    st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     # a tile looks back iff it heads a ticket group, is not tile 0, and its
     # first element does not start a segment
     first_is_start = np.zeros(tiles, bool)
@@ -84,7 +92,7 @@ def test_compact_stats(dw, orc):
     rec, flags = wl.compaction_records(n=(1 << 22) + 5, seed=704)
     n = flags.size
     tiles = -(-n // dw.ps_compact_tile_records(16))
-    stats = torch.zeros(4 * tiles, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
     d_out = torch.zeros_like(dev(rec))
     cnt = torch.zeros(1, dtype=torch.int64, device="cuda")
     say("compact stats")
@@ -92,7 +100,7 @@ def test_compact_stats(dw, orc):
     ref, count = orc.compact(rec, flags)
     assert int(host(cnt)[0]) == count
     assert np.array_equal(host(d_out)[:count], ref[:count])
-    st = host(stats).reshape(tiles, 4).astype(np.int64)
+    st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     t = np.arange(tiles)
     _check_rows(st, (t % 2 == 0) & (t > 0))
 
