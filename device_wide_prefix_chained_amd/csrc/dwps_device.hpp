@@ -221,11 +221,6 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_bal
 // wrote it, bits 31..11 the distance of a PARTIAL (ws_state.hpp); a word
 // carrying another call's tag reads as INVALID.
 // ---------------------------------------------------------------------------
-constexpr uint32_t ST_INVALID = 0u;    // nothing published
-constexpr uint32_t ST_AGGREGATE = 1u;  // payload = the tile's own fold
-constexpr uint32_t ST_PREFIX = 2u;     // payload = fold of tiles 0..t (inclusive)
-constexpr uint32_t ST_PARTIAL = 3u;    // payload = fold of tiles t-d+1..t, d in the high bits
-
 __device__ __forceinline__ uint64_t desc_word(uint32_t state, uint32_t payload) {
     return ((uint64_t)state << 32) | (uint64_t)payload;
 }

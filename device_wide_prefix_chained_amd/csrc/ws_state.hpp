@@ -66,6 +66,10 @@ constexpr uint32_t kErrCapacity = PS_WS_ERR_CAPACITY;
 // Descriptor state word (the high 32 bits of a descriptor word): bits 1..0
 // the state, bits 10..2 the tag of the call that wrote it, bits 31..11 the
 // distance of a PARTIAL (up to 2^21 - 1 tiles, more than any call has).
+constexpr uint32_t ST_INVALID = 0u;    // nothing published
+constexpr uint32_t ST_AGGREGATE = 1u;  // payload = the tile's own fold
+constexpr uint32_t ST_PREFIX = 2u;     // payload = fold of tiles 0..t (inclusive)
+constexpr uint32_t ST_PARTIAL = 3u;    // payload = fold of tiles t-d+1..t, d in the high bits
 constexpr uint32_t kTagBits = 9;
 constexpr uint32_t kTagCount = 1u << kTagBits;
 constexpr uint32_t kTagShift = 2;
