@@ -185,10 +185,13 @@ def build_workload(name: str):
         run = lambda: dw.ps_scan_linrec_f32(d_a, d_b, d_ob, out_a=d_oa, inclusive=True,  # noqa: E731
                                             workspace=ws)
         both = name == "linrec"
+        stats_run = lambda st: dw.ps_linrec_lookback_stats(d_a, d_b, d_ob, st, out_a=d_oa,  # noqa: E731
+                                                           workspace=ws)
         return dict(desc="linear recurrence h[t] = a[t] h[t-1] + b[t] as an inclusive fp32 (a, b) pair scan, "
                          "n=2^27, a ~ U[0.9,1), b ~ N(0,1), seed 6, %s written" % ("A and B" if both else "B = h"),
                     dtype="f32", n=n, bytes=(16.0 if both else 12.0) * n, rbytes=8.0 * n, inputs=dict(a=a, b=b),
-                    run=run, out=(d_oa, d_ob), inclusive=True, kind="linrec")
+                    run=run, out=(d_oa, d_ob), inclusive=True, kind="linrec", stats_run=stats_run,
+                    stats_tiles=-(-n // dw.ps_linrec_tile_elements()))
     if name == "segmented":
         values, off = wl.zipf_segments()
         n = values.size
@@ -338,7 +341,9 @@ def wall_steps(run, steps, warmup):
 def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
     """Copy, read and write of 1 GiB in the same process, under the same two
     protocols as the workload; the workload's ceiling is its read bytes at
-    the read rate plus its written bytes at the write rate."""
+    the read rate plus its written bytes at the write rate.  For the
+    recurrence also a plain stream of its own shape (two planes read, one or
+    two written, ps_stream_planes_f32) and the call's fraction of it."""
     import torch
 
     import device_wide_prefix_chained_amd as dw
@@ -358,6 +363,22 @@ def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
                      "gbs_wall": round(moved / (wall * 1e-3) / 1e9, 1),
                      "gbs_flushed": round(moved / (fl["median_ms"] * 1e-3) / 1e9, 1)}
     del src, dst
+    if w["kind"] == "linrec":
+        # the recurrence's own shape: two planes read, one or two written
+        n2 = w["n"]
+        pa = torch.empty(n2, dtype=torch.float32, device="cuda").fill_(0.5)
+        pb = torch.empty(n2, dtype=torch.float32, device="cuda").fill_(2.0)
+        ob = torch.empty(n2, dtype=torch.float32, device="cuda")
+        oa = torch.empty(n2, dtype=torch.float32, device="cuda") if w["out"][0] is not None else None
+        run = lambda: dw.ps_stream_planes_f32(pa, pb, ob, out_a=oa)  # noqa: E731
+        wall = wall_steps(run, steps, 3)
+        fl = flushed_reps(run, reps, flush)
+        out["planes"] = {"bytes": int(w["bytes"]), "wall_ms": round(wall, 5), "flushed_median_ms": fl["median_ms"],
+                         "gbs_wall": round(w["bytes"] / (wall * 1e-3) / 1e9, 1),
+                         "gbs_flushed": round(w["bytes"] / (fl["median_ms"] * 1e-3) / 1e9, 1),
+                         "frac_wall": round(wall / scan_ms, 4),
+                         "frac_flushed": round(fl["median_ms"] / scan_flushed_ms, 4)}
+        del pa, pb, ob, oa
     rb = w["rbytes"]
     wb = w["bytes"] - rb
     for proto, key in (("wall", "gbs_wall"), ("flushed", "gbs_flushed")):
@@ -465,7 +486,7 @@ def main():
                     help="minimum oracle time of the cpu_baseline leg (0 skips it)")
     ap.add_argument("--lookback-stats", type=int, default=0, metavar="R",
                     help="also run the instrumented kernel R times and summarise its look-back "
-                         "statistics (u32x, u32i, f32, f32max, segmented, compact)")
+                         "statistics (u32x, u32i, f32, f32max, segmented, compact, linrec, linrec-h)")
     ap.add_argument("--flushed-reps", type=int, default=20,
                     help="calls timed one by one after a cache flush, and the same for the "
                          "stream ceilings (0 skips both)")

@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = i32
     L.ps_scan_linrec_f32.argtypes = [vp, sz, vp, vp, vp, vp, u64, i32, vp, vp]
     L.ps_scan_linrec_f32.restype = i32
+    L.ps_linrec_lookback_stats.argtypes = [vp, sz, vp, vp, vp, vp, u64, i32, vp, vp]
+    L.ps_linrec_lookback_stats.restype = i32
     L.ps_linrec_tile_elements.argtypes = []
     L.ps_linrec_tile_elements.restype = u32
     L.ps_scan.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.ps_read_u32.restype = i32
     L.ps_fill_u32.argtypes = [vp, u64, u32, vp]
     L.ps_fill_u32.restype = i32
+    L.ps_stream_planes_f32.argtypes = [vp, vp, vp, vp, u64, vp]
+    L.ps_stream_planes_f32.restype = i32
     L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
     L.ps_lookback_stats_u32.restype = i32
     L.ps_scan_lookback_stats.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
@@ -369,6 +373,27 @@ def ps_linrec_tile_elements() -> int:
     return int(lib().ps_linrec_tile_elements())
 
 
+def ps_linrec_lookback_stats(a, b, out_b, stats, out_a=None, inclusive=True, workspace=None, stream=None):
+    """ps_scan_linrec_f32 (single-pass form, no total) with per-tile look-back
+    statistics: STATS_WORDS uint32 for each of ceil(n / ps_linrec_tile_elements())
+    tiles."""
+    _dev_tensor("a", a, (torch.float32,))
+    n = a.numel()
+    _dev_tensor("b", b, (torch.float32,), n)
+    _dev_tensor("out_b", out_b, (torch.float32,), n)
+    if out_a is not None:
+        _dev_tensor("out_a", out_a, (torch.float32,), n)
+    tiles = -(-n // ps_linrec_tile_elements())
+    _dev_tensor("stats", stats, _U32_DTYPES, STATS_WORDS * tiles)
+    s = _stream(a, stream)
+    L = lib()
+    call = lambda ws, wsb: L.ps_linrec_lookback_stats(ws, wsb, _ptr(a), _ptr(b), _ptr(out_a),  # noqa: E731
+                                                      _ptr(out_b), n, int(bool(inclusive)), _ptr(stats), s)
+    ws, have = _workspace("ps_linrec_lookback_stats", call, a.device, workspace, stream)
+    _check("ps_linrec_lookback_stats", call(_ptr(ws), ctypes.byref(have)))
+    return stats
+
+
 def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None, stream=None):
     _dev_tensor("inp", inp, _U32_DTYPES)
     _dev_tensor("out", out, _U32_DTYPES, inp.numel())
@@ -385,7 +410,7 @@ def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None,
 
 def ps_scan_lookback_stats(op, inclusive, inp, out, stats, workspace=None, stream=None, dtype=None):
     """ps_scan (u32 sum, f32 sum, f32 max) with per-tile look-back statistics:
-    stats holds 8 uint32 per tile (see ps_lookback_stats_u32 in dwps.h)."""
+    stats holds STATS_WORDS uint32 per tile (the layout in dwps.h)."""
     opc = OPS[op] if isinstance(op, str) else int(op)
     if dtype is None:
         dtype = PS_F32 if inp.dtype == torch.float32 else PS_U32
@@ -534,6 +559,20 @@ def ps_fill_u32(out, value, stream=None):
     _dev_tensor("out", out, _U32_DTYPES)
     _check("ps_fill_u32", lib().ps_fill_u32(_ptr(out), out.numel(), int(value) & 0xFFFFFFFF, _stream(out, stream)))
     return out
+
+
+def ps_stream_planes_f32(a, b, out_b, out_a=None, stream=None):
+    """The recurrence's access shape as a plain stream: out_b = a * b and,
+    when given, out_a = a + b (float planes, 16-byte aligned, n % 4 == 0)."""
+    _dev_tensor("a", a, (torch.float32,))
+    n = a.numel()
+    _dev_tensor("b", b, (torch.float32,), n)
+    _dev_tensor("out_b", out_b, (torch.float32,), n)
+    if out_a is not None:
+        _dev_tensor("out_a", out_a, (torch.float32,), n)
+    _check("ps_stream_planes_f32", lib().ps_stream_planes_f32(_ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), n,
+                                                              _stream(a, stream)))
+    return out_b
 
 
 def ps_kernel_timing(enable: bool, every: int = 1) -> None:

@@ -87,6 +87,41 @@ __global__ __launch_bounds__(kStreamThreads) void read_vec_kernel(const copy_v4u
         *sink = acc.x;
 }
 
+// The recurrence's access shape: the float planes a and b read, one plane
+// (b' = a * b) or two (also a' = a + b) written, 16 bytes per vector as in
+// the copy.
+typedef float copy_v4f __attribute__((ext_vector_type(4)));
+
+template <bool FULL, bool BOTH>
+__device__ __forceinline__ void planes_block(const copy_v4u *a, const copy_v4u *b, copy_v4u *oa, copy_v4u *ob,
+                                             uint64_t base, uint64_t n16) {
+    copy_v4u ra[kStreamVecs], rb[kStreamVecs];
+#pragma unroll
+    for (int k = 0; k < kStreamVecs; ++k) {
+        ra[k] = __builtin_nontemporal_load(a + stream_index(base, k, n16, FULL));
+        rb[k] = __builtin_nontemporal_load(b + stream_index(base, k, n16, FULL));
+    }
+#pragma unroll
+    for (int k = 0; k < kStreamVecs; ++k) {
+        const uint64_t i = base + (uint64_t)k * kStreamThreads;
+        if (FULL || i < n16) {
+            const copy_v4f x = __builtin_bit_cast(copy_v4f, ra[k]), y = __builtin_bit_cast(copy_v4f, rb[k]);
+            __builtin_nontemporal_store(__builtin_bit_cast(copy_v4u, x * y), ob + i);
+            if (BOTH) __builtin_nontemporal_store(__builtin_bit_cast(copy_v4u, x + y), oa + i);
+        }
+    }
+}
+
+template <bool BOTH>
+__global__ __launch_bounds__(kStreamThreads) void planes_vec_kernel(const copy_v4u *a, const copy_v4u *b,
+                                                                    copy_v4u *oa, copy_v4u *ob, uint64_t n16) {
+    const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
+    if (((uint64_t)blockIdx.x + 1u) * kStreamBlock <= n16)
+        planes_block<true, BOTH>(a, b, oa, ob, base, n16);
+    else
+        planes_block<false, BOTH>(a, b, oa, ob, base, n16);
+}
+
 // Write-only stream: fills with one value.
 __global__ __launch_bounds__(kStreamThreads) void fill_vec_kernel(copy_v4u *out, uint64_t n16, uint32_t value) {
     const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
@@ -262,6 +297,35 @@ extern "C" ps_status ps_read_u32(const uint32_t *in, uint64_t n, uint32_t *sink,
     timing_begin(s);
     hipLaunchKernelGGL(read_vec_kernel, dim3((unsigned)ceil_div(n16, kStreamBlock)), dim3(kStreamThreads), 0, s,
                        reinterpret_cast<const copy_v4u *>(in), n16, sink);
+    timing_end(s);
+    return launch_status();
+}
+
+extern "C" ps_status ps_stream_planes_f32(const float *a, const float *b, float *out_a, float *out_b, uint64_t n,
+                                          void *stream) {
+    if (n == 0) return PS_OK;
+    if (!a || !b || !out_b) return PS_ERR_NULL;
+    if (n >= (1ull << 32)) return PS_ERR_SIZE;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out_b, 16) || (out_a && !aligned(out_a, 16)) || n % 4)
+        return PS_ERR_ALIGNMENT;
+    const uint64_t bytes = n * 4;
+    const float *ins[2] = {a, b};
+    for (const float *in : ins)
+        if (ranges_overlap(in, bytes, out_b, bytes) || (out_a && ranges_overlap(in, bytes, out_a, bytes)))
+            return PS_ERR_ALIAS;
+    if (out_a && ranges_overlap(out_a, bytes, out_b, bytes)) return PS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint64_t n16 = n / 4;
+    const dim3 grid((unsigned)ceil_div(n16, kStreamBlock));
+    const auto *va = reinterpret_cast<const copy_v4u *>(a);
+    const auto *vb = reinterpret_cast<const copy_v4u *>(b);
+    timing_begin(s);
+    if (out_a)
+        hipLaunchKernelGGL(planes_vec_kernel<true>, grid, dim3(kStreamThreads), 0, s, va, vb,
+                           reinterpret_cast<copy_v4u *>(out_a), reinterpret_cast<copy_v4u *>(out_b), n16);
+    else
+        hipLaunchKernelGGL(planes_vec_kernel<false>, grid, dim3(kStreamThreads), 0, s, va, vb, nullptr,
+                           reinterpret_cast<copy_v4u *>(out_b), n16);
     timing_end(s);
     return launch_status();
 }

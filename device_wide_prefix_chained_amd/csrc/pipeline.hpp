@@ -116,6 +116,38 @@ struct PhaseClock {
     }
 };
 
+// Data wave 0's view of a phase (instrumented flat scan), word 15 of the
+// scanned tile's row, three 10-bit fields in ticks (saturating at 1023):
+// bits 0-9 from the start of the phase (leaving barrier A of the phase
+// before) to the end of the scan, just before barrier B; bits 10-19 from
+// leaving barrier B to the last store of the stored tile issued; bits 20-29
+// from leaving barrier B to reaching barrier A (the park and the next tile's
+// id included).
+template <bool STATS>
+struct DataClock {
+    uint32_t start = 0, scanned = 0, left_b = 0, stored = 0;
+    __device__ __forceinline__ void begin() {
+        if (STATS) start = realtime32();
+    }
+    __device__ __forceinline__ void scan_done() {
+        if (STATS) scanned = realtime32();
+    }
+    __device__ __forceinline__ void leave_b() {
+        if (STATS) left_b = realtime32();
+    }
+    __device__ __forceinline__ void store_done() {
+        if (STATS) stored = realtime32();
+    }
+    __device__ __forceinline__ void reach_a(uint32_t *stats, uint32_t f1, uint32_t num_tiles, bool writer) {
+        if (STATS && writer && f1 < num_tiles) {
+            const uint32_t t = realtime32();
+            auto sat = [](uint32_t v) { return v < 1023u ? v : 1023u; };
+            stats[(uint64_t)kStatsWords * f1 + 15] =
+                sat(scanned - start) | (sat(stored - left_b) << 10) | (sat(t - left_b) << 20);
+        }
+    }
+};
+
 __device__ __forceinline__ uint32_t next_slot(uint32_t slot) { return slot == kParkSlots - 1 ? 0u : slot + 1u; }
 
 // The tile after f2: the next one of its group of G, or the first tile of a

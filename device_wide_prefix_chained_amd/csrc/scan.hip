@@ -65,16 +65,18 @@ struct ScanShared {
 // loads and keeps two tiles in flight.  Data wave 0 also takes the tickets:
 // the atomic goes out at the start of the phase, ahead of the wave's tile
 // loads, and its value is needed only after barrier B.
-template <class Op, int D, int Q, int G, bool INCL, bool VEC>
+template <class Op, int D, int Q, int G, bool INCL, bool VEC, bool STATS>
 __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, Q> &sc, WaveSpan<Op, Q> &ld, int par,
                                             uint32_t &slot, PipeTiles &pt, typename Op::T (&lane_excl)[Q],
                                             typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
                                             typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n,
                                             uint32_t num_tiles, uint32_t *ctr, uint32_t lane, uint32_t d,
-                                            uint64_t lane_off) {
+                                            uint64_t lane_off, uint32_t *stats) {
     using T = typename Op::T;
     constexpr uint32_t TILE = (uint32_t)D * (uint32_t)Q * 256u;
     constexpr int PW = ScanShared<Op, D, Q>::PW;
+    DataClock<STATS> clk;
+    clk.begin();
     const bool need_ticket = needs_ticket<G>(pt.f2, num_tiles);
     uint32_t ticket = 0;
     if (need_ticket && d == 0 && lane == 0) ticket = take_ticket(ctr + kHdrTicket);
@@ -99,7 +101,9 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
         const T wt = scan_span<Op, Q>(sc, lane_excl, row_prefix);
         if (lane == 0) sh.wt[par ^ 1][d] = wt;
     }
+    clk.scan_done();
     __syncthreads();  // B
+    clk.leave_b();
     v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
     if (pt.prev3 < num_tiles) {
         const uint64_t bp = (uint64_t)pt.prev3 * TILE;
@@ -140,6 +144,7 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
             store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, full);
         }
     }
+    clk.store_done();
     // park cur where prev3 was
     if (pt.cur < num_tiles) {
 #pragma unroll
@@ -153,15 +158,16 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     if (pt.template drained<3>(num_tiles)) return true;
     if (d == 0 && lane == 0) sh.next = tile_after<G>(pt.f2, num_tiles, need_ticket, ticket);
     slot = next_slot(slot);
+    clk.reach_a(stats, pt.f1, num_tiles, d == 0 && lane == 0);
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);
     return false;
 }
 
-template <class Op, int D, int Q, int G, bool INCL, bool VEC>
+template <class Op, int D, int Q, int G, bool INCL, bool VEC, bool STATS>
 __device__ __forceinline__ void data_loop3(PipeTiles pt, ScanShared<Op, D, Q> &sh, typename IoOf<Op>::Src in,
                                            typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
-                                           uint32_t lane, uint32_t d) {
+                                           uint32_t lane, uint32_t d, uint32_t *stats) {
     using T = typename Op::T;
     constexpr uint32_t WAVE_ELEMS = (uint32_t)Q * 256u;
     const uint64_t lane_off = (uint64_t)d * WAVE_ELEMS + 4u * lane;
@@ -172,16 +178,16 @@ __device__ __forceinline__ void data_loop3(PipeTiles pt, ScanShared<Op, D, Q> &s
     uint32_t slot = 0;
     int par = 0;
     for (;;) {
-        if (data_phase3<Op, D, Q, G, INCL, VEC>(x, y, z, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
-                                                num_tiles, ctr, lane, d, lane_off))
+        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS>(x, y, z, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                                num_tiles, ctr, lane, d, lane_off, stats))
             break;
         par ^= 1;
-        if (data_phase3<Op, D, Q, G, INCL, VEC>(y, z, x, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
-                                                num_tiles, ctr, lane, d, lane_off))
+        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS>(y, z, x, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                                num_tiles, ctr, lane, d, lane_off, stats))
             break;
         par ^= 1;
-        if (data_phase3<Op, D, Q, G, INCL, VEC>(z, x, y, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
-                                                num_tiles, ctr, lane, d, lane_off))
+        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS>(z, x, y, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+                                                num_tiles, ctr, lane, d, lane_off, stats))
             break;
         par ^= 1;
     }
@@ -239,7 +245,7 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
                 pt, sh, num_tiles, hdr, desc, total, stats, aggregate_only, cfg,
                 FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane, STATS ? wsh.entry : 0u);
         } else {
-            data_loop3<Op, D, Q, G, INCL, VEC>(pt, sh, in, out, n, num_tiles, hdr, lane, wave - 1);
+            data_loop3<Op, D, Q, G, INCL, VEC, STATS>(pt, sh, in, out, n, num_tiles, hdr, lane, wave - 1, stats);
         }
     }
     if (wave == 0) ws_done(wsh, num_tiles * (uint32_t)WordsFor<Op>::WORDS, hdr, lane);
@@ -339,12 +345,17 @@ ps_status launch_flat_kernel(void *ws, size_t ws_need, typename IoOf<Op>::Src in
         return PS_OK;
     };
     ps_status r;
-    if (inclusive)
+    if constexpr (STATS) {
+        if (!vec) return PS_ERR_ALIGNMENT;  // instrumented for the vector path only
+        r = inclusive ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, true, STATS>)
+                      : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, true, STATS>);
+    } else if (inclusive) {
         r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, true, STATS>)
                 : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, true, false, STATS>);
-    else
+    } else {
         r = vec ? launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, true, STATS>)
                 : launch(chained_scan_kernel<Op, kFlatD, Q, K, kTilesPerTicket, false, false, STATS>);
+    }
     if (r != PS_OK) return r;
     timing_end(s);
     return launch_status();
@@ -388,8 +399,9 @@ ps_status launch_flat(void *ws, size_t *ws_bytes, const void *in_v, void *out_v,
 // The recurrence pairs come in two float planes and go out in two (out_a
 // optional).  Exact in-place use of either plane is allowed; any other
 // overlap between an input and an output, or between the outputs, is not.
+template <bool STATS>
 ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float *b, float *out_a, float *out_b,
-                        uint64_t n, bool inclusive, float *total, hipStream_t s) {
+                        uint64_t n, bool inclusive, float *total, uint32_t *stats, hipStream_t s) {
     if (n >= (1ull << 32)) return PS_ERR_SIZE;
     const size_t ws_need = flat_form_ws_bytes<LinRecF32>(n, FlatForm::kAuto);
     bool query = false;
@@ -402,7 +414,7 @@ ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float 
         hipLaunchKernelGGL(write_one<F2>, dim3(1), dim3(1), 0, s, tot, F2{1.0f, 0.0f});
         return launch_status();
     }
-    if (!a || !b || !out_b) return PS_ERR_NULL;
+    if (!a || !b || !out_b || (STATS && !stats)) return PS_ERR_NULL;
     if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out_b, 4) || (out_a && !aligned(out_a, 4)) ||
         (total && !aligned(total, 4)) || !aligned(ws, 16))
         return PS_ERR_ALIGNMENT;
@@ -422,10 +434,10 @@ ps_status launch_linrec(void *ws, size_t *ws_bytes, const float *a, const float 
     }
     if (out_a && ranges_overlap(out_a, bytes, out_b, bytes)) return PS_ERR_ALIAS;
     const bool vec = aligned(a, 16) && aligned(b, 16) && aligned(out_b, 16) && (!out_a || aligned(out_a, 16));
-    if (use_two_level(n, FlatForm::kAuto))
+    if (!STATS && use_two_level(n, FlatForm::kAuto))
         return tl_launch<LinRecF32>(ws, PlanesIn{a, b}, PlanesOut{out_a, out_b}, (uint32_t)n, tot, inclusive, vec, s);
-    return launch_flat_kernel<LinRecF32, false>(ws, ws_need, PlanesIn{a, b}, PlanesOut{out_a, out_b}, (uint32_t)n,
-                                                tot, inclusive, vec, in_place, nullptr, 0, s);
+    return launch_flat_kernel<LinRecF32, STATS>(ws, ws_need, PlanesIn{a, b}, PlanesOut{out_a, out_b}, (uint32_t)n,
+                                                tot, inclusive, vec, in_place, stats, 0, s);
 }
 
 }  // namespace dwps
@@ -470,8 +482,15 @@ extern "C" ps_status ps_scan_inclusive_f32(void *ws, size_t *ws_bytes, const flo
 
 extern "C" ps_status ps_scan_linrec_f32(void *ws, size_t *ws_bytes, const float *a, const float *b, float *out_a,
                                         float *out_b, uint64_t n, int inclusive, float *total, void *stream) {
-    return launch_linrec(ws, ws_bytes, a, b, out_a, out_b, n, inclusive != 0, total,
-                         static_cast<hipStream_t>(stream));
+    return launch_linrec<false>(ws, ws_bytes, a, b, out_a, out_b, n, inclusive != 0, total, nullptr,
+                                static_cast<hipStream_t>(stream));
+}
+
+extern "C" ps_status ps_linrec_lookback_stats(void *ws, size_t *ws_bytes, const float *a, const float *b,
+                                             float *out_a, float *out_b, uint64_t n, int inclusive, uint32_t *stats,
+                                             void *stream) {
+    return launch_linrec<true>(ws, ws_bytes, a, b, out_a, out_b, n, inclusive != 0, nullptr, stats,
+                               static_cast<hipStream_t>(stream));
 }
 
 extern "C" uint32_t ps_linrec_tile_elements(void) { return flat_tile<LinRecF32>(); }

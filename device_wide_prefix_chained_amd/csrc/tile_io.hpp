@@ -242,29 +242,36 @@ __device__ __forceinline__ void store_group(T *out, uint64_t g, const T (&o)[4])
 #pragma unroll
     for (int h = 0; h < PW; ++h) store16(out + g + 4 / PW * h, w[h]);
 }
-__device__ __forceinline__ void store_group(PlanesOut out, uint64_t g, const F2 (&o)[4]) {
-    if (out.a) {
-        v4u w;
-        w.x = __float_as_uint(o[0].a);
-        w.y = __float_as_uint(o[1].a);
-        w.z = __float_as_uint(o[2].a);
-        w.w = __float_as_uint(o[3].a);
-        store16(out.a + g, w);
+// Four consecutive pairs, already split into their planes (registers, not
+// an array of pairs: one regrouped after a branch ends up in per-lane
+// scratch memory, and waiting for a scratch load also waits for every load
+// issued before it -- the next tile's, which the pipeline keeps in flight):
+// 16-byte vectors when `whole`, else the elements below n.
+__device__ __forceinline__ void store_planes(PlanesOut out, uint64_t g, v4u wa, v4u wb, bool whole, uint32_t n) {
+    if (whole) {
+        if (out.a) store16(out.a + g, wa);
+        store16(out.b + g, wb);
+        return;
     }
-    v4u w;
-    w.x = __float_as_uint(o[0].b);
-    w.y = __float_as_uint(o[1].b);
-    w.z = __float_as_uint(o[2].b);
-    w.w = __float_as_uint(o[3].b);
-    store16(out.b + g, w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (g + k < n) {
+            if (out.a) out.a[g + k] = __uint_as_float(wa[k]);
+            out.b[g + k] = __uint_as_float(wb[k]);
+        }
+    }
+}
+// A group of pairs split into the planes' vectors.
+__device__ __forceinline__ void split_planes(const F2 (&o)[4], v4u &wa, v4u &wb) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        wa[k] = __float_as_uint(o[k].a);
+        wb[k] = __float_as_uint(o[k].b);
+    }
 }
 template <class T>
 __device__ __forceinline__ void store_elem(T *out, uint64_t i, T v) {
     out[i] = v;
-}
-__device__ __forceinline__ void store_elem(PlanesOut out, uint64_t i, F2 v) {
-    if (out.a) out.a[i] = v.a;
-    out.b[i] = v.b;
 }
 
 // Store a finalized span: out = prefix (+) v.
@@ -272,18 +279,33 @@ template <class Op, int Q, bool VEC, class Dst>
 __device__ __forceinline__ void store_final(const WaveSpan<Op, Q> &s, typename Op::T prefix, Dst out,
                                             uint64_t span, uint32_t n, bool full) {
     using T = typename Op::T;
+    if constexpr (std::is_same<Dst, PlanesOut>::value) {
+        // the pairs split into their planes as they are computed (store_planes)
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-        T o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = Op::op(prefix, s.v[q][k]);
-        if (VEC && full) {
-            store_group(out, span + (uint64_t)q * 256u, o);
-        } else {
+        for (int q = 0; q < Q; ++q) {
+            v4u wa, wb;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const uint64_t i = span + (uint64_t)q * 256u + k;
-                if (i < n) store_elem(out, i, o[k]);
+                const F2 o = Op::op(prefix, s.v[q][k]);
+                wa[k] = __float_as_uint(o.a);
+                wb[k] = __float_as_uint(o.b);
+            }
+            store_planes(out, span + (uint64_t)q * 256u, wa, wb, VEC && full, n);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            T o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = Op::op(prefix, s.v[q][k]);
+            if (VEC && full) {
+                store_group(out, span + (uint64_t)q * 256u, o);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint64_t i = span + (uint64_t)q * 256u + k;
+                    if (i < n) store_elem(out, i, o[k]);
+                }
             }
         }
     }

@@ -193,7 +193,11 @@ __global__ __launch_bounds__(kTlWaves * 64) void tl_scan_kernel(typename IoOf<Op
 #pragma unroll
     for (int q = 0; q < kTlQ; ++q) {
         const uint64_t g = span + (uint64_t)q * 256u;
-        if (VEC && full) {
+        if constexpr (std::is_same<typename IoOf<Op>::Dst, PlanesOut>::value) {
+            v4u wa, wb;
+            split_planes(s.v[q], wa, wb);
+            store_planes(out, g, wa, wb, VEC && full, n);
+        } else if (VEC && full) {
             store_group(out, g, s.v[q]);
         } else {
 #pragma unroll

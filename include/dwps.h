@@ -382,6 +382,15 @@ ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *strea
 ps_status ps_read_u32(const uint32_t *in, uint64_t n, uint32_t *sink, void *stream);
 ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void *stream);
 
+/* The linear recurrence's access shape as a plain stream, the practical
+ * ceiling of ps_scan_linrec_f32: reads the float planes a and b (n each)
+ * and writes out_b[i] = a[i] * b[i] and, when out_a is not null, out_a[i] =
+ * a[i] + b[i] -- two planes read, one or two written, with the copy's
+ * 16-byte vectors.  Every array 16-byte aligned and n a multiple of 4, else
+ * PS_ERR_ALIGNMENT; overlapping arrays: PS_ERR_ALIAS. */
+ps_status ps_stream_planes_f32(const float *a, const float *b, float *out_a, float *out_b,
+                               uint64_t n, void *stream);
+
 /* Exclusive uint32 sum scan (same kernel as ps_scan_exclusive_u32, built
  * with per-tile instrumentation of the look-back of [P1] "Why the work
  * stays linear").  stats: device buffer of 16 * tiles uint32, tiles
@@ -424,7 +433,9 @@ uint64_t ps_lookback_tiles(uint64_t n);
  *   ps_segmented_lookback_stats_u32: ps_segmented_scan_u32;
  *     ceil(n / ps_segmented_tile_elements()) tiles.
  *   ps_compact_lookback_stats: ps_compact for 16-byte records only (else
- *     PS_ERR_UNSUPPORTED); ceil(n / ps_compact_tile_records(16)) tiles. */
+ *     PS_ERR_UNSUPPORTED); ceil(n / ps_compact_tile_records(16)) tiles.
+ *   ps_linrec_lookback_stats: ps_scan_linrec_f32 (no total), single-pass
+ *     form at every n; ceil(n / ps_linrec_tile_elements()) tiles. */
 ps_status ps_scan_lookback_stats(void *ws, size_t *ws_bytes, ps_op op, ps_dtype dtype,
                                  int inclusive, const void *in, void *out, uint64_t n,
                                  uint32_t *stats, void *stream);
@@ -437,6 +448,9 @@ ps_status ps_compact_lookback_stats(void *ws, size_t *ws_bytes, const void *reco
                                     uint32_t record_bytes, const uint8_t *flags, uint64_t n,
                                     void *out, uint64_t *num_selected, uint32_t *stats,
                                     void *stream);
+ps_status ps_linrec_lookback_stats(void *ws, size_t *ws_bytes, const float *a, const float *b,
+                                   float *out_a, float *out_b, uint64_t n, int inclusive,
+                                   uint32_t *stats, void *stream);
 /* Predecessor descriptors read per look-back poll (64 lanes x K words). */
 uint32_t ps_lookback_window(void);
 /* Tiles claimed per ticket of the flat scan: a workgroup scans that many

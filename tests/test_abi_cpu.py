@@ -133,6 +133,7 @@ def test_size_queries():
 FAKE_WS = 0x10000000
 A = 0x20000000          # fake, 256-byte aligned "device" addresses: never dereferenced
 B = 0x40000000
+C3 = 0x60000000
 
 
 def _call_flat(lib, fn, ws_bytes, inp, out, n, total=None):
@@ -264,6 +265,14 @@ def test_argument_errors_stream_helpers():
     assert lib.ps_fill_u32(None, 16, 0, None) == 1
     assert lib.ps_fill_u32(v(A + 2), 16, 0, None) == 7
     assert lib.ps_fill_u32(v(A), 1 << 32, 0, None) == 3
+    P = lib.ps_stream_planes_f32
+    assert P(None, None, None, None, 0, None) == 0
+    assert P(None, v(B), None, v(C3), 16, None) == 1 and P(v(A), v(B), None, None, 16, None) == 1
+    assert P(v(A + 4), v(B), None, v(C3), 16, None) == 7       # 16-byte alignment
+    assert P(v(A), v(B), None, v(C3), 18, None) == 7           # whole 16-byte vectors only
+    assert P(v(A), v(B), None, v(A), 16, None) == 2           # an output over an input
+    assert P(v(A), v(B), v(C3), v(C3), 16, None) == 2           # both outputs in one place
+    assert P(v(A), v(B), None, v(C3), 1 << 32, None) == 3
 
 
 def test_status_strings():

@@ -105,6 +105,36 @@ def test_compact_stats(dw, orc):
     _check_rows(st, (t % 2 == 0) & (t > 0))
 
 
+@pytest.mark.parametrize("with_a", [False, True])
+def test_linrec_stats(dw, with_a):
+    """The instrumented recurrence gives the ordinary single-pass call's
+    results bit for bit (the same arithmetic in the same order)."""
+    import torch
+    n = 700 * dw.ps_linrec_tile_elements() + 5
+    a, b = wl.linrec_pairs(n=n, seed=705)
+    da, db = dev(a), dev(b)
+    tiles = -(-n // dw.ps_linrec_tile_elements())
+    stats = torch.zeros(dw.STATS_WORDS * tiles, dtype=torch.int32, device="cuda")
+    got_b = torch.empty(n, dtype=torch.float32, device="cuda")
+    got_a = torch.empty(n, dtype=torch.float32, device="cuda") if with_a else None
+    ref_b = torch.empty(n, dtype=torch.float32, device="cuda")
+    ref_a = torch.empty(n, dtype=torch.float32, device="cuda") if with_a else None
+    old = dw.ps_small_n_config_get()
+    dw.ps_small_n_config(0)
+    try:
+        say("linrec stats", with_a)
+        dw.ps_linrec_lookback_stats(da, db, got_b, stats, out_a=got_a)
+        dw.ps_scan_linrec_f32(da, db, ref_b, out_a=ref_a)
+    finally:
+        dw.ps_small_n_config(old)
+    assert np.array_equal(host(got_b).view(np.uint32), host(ref_b).view(np.uint32))
+    if with_a:
+        assert np.array_equal(host(got_a).view(np.uint32), host(ref_a).view(np.uint32))
+    st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
+    t = np.arange(tiles)
+    _check_rows(st, (t % dw.ps_lookback_group() == 0) & (t > 0))
+
+
 def test_stats_argument_errors(dw):
     import ctypes
     L = dw.lib()
@@ -115,3 +145,4 @@ def test_stats_argument_errors(dw):
     assert L.ps_compact_lookback_stats(fake, ctypes.byref(wsb), fake, 8, fake, 1000, fake, fake, fake, None) == 5
     # null stats
     assert L.ps_scan_lookback_stats(fake, ctypes.byref(wsb), 0, 0, 0, fake, fake, 1000, None, None) == 1
+    assert L.ps_linrec_lookback_stats(fake, ctypes.byref(wsb), fake, fake, None, fake, 1000, 1, None, None) == 1

@@ -1,5 +1,6 @@
-"""The measurement helpers: copy, read-only and write-only streams (the
-practical bandwidth ceilings the scans are compared with)."""
+"""The measurement helpers: copy, read-only and write-only streams, and the
+recurrence's two-plane stream (the practical bandwidth ceilings the scans
+are compared with)."""
 import numpy as np
 import pytest
 
@@ -42,6 +43,25 @@ def test_read_leaves_sink(dw, n):
     sink = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
     dw.ps_read_u32(dev(x), sink)
     assert int(host(sink)[0]) == 12345
+
+
+@pytest.mark.parametrize("both", [False, True])
+@pytest.mark.parametrize("n", [4, 16384, 1_000_004])
+def test_planes_stream(dw, n, both):
+    """b' = a * b and a' = a + b element by element: one IEEE fp32 operation
+    each, so the results equal numpy's bit for bit (values in [0.5, 2):
+    no subnormals)."""
+    import torch
+    g = np.random.default_rng(n + 62)
+    a = g.uniform(0.5, 2.0, n).astype(np.float32)
+    b = g.uniform(0.5, 2.0, n).astype(np.float32)
+    ob = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    oa = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") if both else None
+    say("planes stream", n, both)
+    dw.ps_stream_planes_f32(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), ob, out_a=oa)
+    assert np.array_equal(host(ob).view(np.uint32), (a * b).view(np.uint32))
+    if both:
+        assert np.array_equal(host(oa).view(np.uint32), (a + b).view(np.uint32))
 
 
 def test_kernel_timing_samples_every_nth_call(dw):
