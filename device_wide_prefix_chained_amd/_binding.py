@@ -223,11 +223,13 @@ def _cached_workspace(fn, need, device, stream):
 
 
 def _workspace(fn: str, call, device, workspace, stream=None):
-    """CUB-style size query; the call's workspace, or the prepared one kept
-    for its device and stream when none is given."""
-    need = ctypes.c_size_t(0)
-    _check(fn, call(None, ctypes.byref(need)))
+    """The call's workspace, or the prepared one kept for its device and
+    stream when none is given (sized by a CUB-style query).  A given
+    workspace is not queried: the library itself refuses one that is too
+    small (PS_ERR_WORKSPACE) before anything runs."""
     if workspace is None:
+        need = ctypes.c_size_t(0)
+        _check(fn, call(None, ctypes.byref(need)))
         workspace = _cached_workspace(fn, int(need.value), device, stream)
     else:
         _dev_tensor("workspace", workspace)
