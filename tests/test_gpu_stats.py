@@ -20,10 +20,20 @@ def dw():
     return require_gpu()
 
 
-def _check_rows(st, looks):
+def _check_rows(st, looks, data_clock=False):
     """st: (tiles, 16) rows (polls, windows, ticks, stalls, the phase timing
-    of the tile's scan phase, the timeline); looks: which tiles look back."""
+    of the tile's scan phase, the timeline, and for the flat kernels data
+    wave 0's view of that phase); looks: which tiles look back."""
     polls, windows, stalls = st[:, 0], st[:, 1], st[:, 3]
+    w15 = st[:, 15]
+    if data_clock:
+        # every tile was scanned in a phase that data wave 0 timed: to the
+        # end of the scan (never 0 ticks), to the last store issued, to
+        # barrier A (not before the stores)
+        scanned, stored, at_a = w15 & 1023, (w15 >> 10) & 1023, (w15 >> 20) & 1023
+        assert np.all(scanned > 0) and np.all(at_a >= stored) and np.all(w15 >> 30 == 0)
+    else:
+        assert np.all(w15 == 0)
     # every tile is scanned in exactly one phase, which both waves timed
     assert np.all(st[:, 4] + st[:, 5] > 0) and np.all(st[:, 6] + st[:, 7] > 0)
     # and no phase part takes longer than a millisecond
@@ -62,7 +72,7 @@ def test_flat_stats(dw, orc, op, dtype):
             assert np.array_equal(got.view(np.uint32), orc.scan_f32_minmax(x, "max", True)[0].view(np.uint32))
     st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     t = np.arange(tiles)
-    _check_rows(st, (t % dw.ps_lookback_group() == 0) & (t > 0))
+    _check_rows(st, (t % dw.ps_lookback_group() == 0) & (t > 0), data_clock=True)
 
 
 def test_segmented_stats(dw, orc):
@@ -132,7 +142,7 @@ def test_linrec_stats(dw, with_a):
         assert np.array_equal(host(got_a).view(np.uint32), host(ref_a).view(np.uint32))
     st = host(stats).reshape(tiles, dw.STATS_WORDS).astype(np.int64)
     t = np.arange(tiles)
-    _check_rows(st, (t % dw.ps_lookback_group() == 0) & (t > 0))
+    _check_rows(st, (t % dw.ps_lookback_group() == 0) & (t > 0), data_clock=True)
 
 
 def test_stats_argument_errors(dw):
