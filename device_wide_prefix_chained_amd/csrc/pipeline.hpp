@@ -56,7 +56,10 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgc
 // Words 8-12, a timeline (low 32 bits of the counter): [8] start of the
 // tile's scan phase, [9] start of the phase that stored it, [10] the
 // workgroup, [11] the workgroup's start, [12] (last tile a workgroup
-// stored only) the time its control wave finished.  Times in ticks of the
+// stored only) the time its control wave finished.  Words 13-14: when the
+// phase that stored the tile scanned none (the drain), that phase's parts
+// as in 4-7, 16 bits each.  Word 15 (flat kernel only): data wave 0's view
+// of the phase that scanned the tile (DataClock).  Times in ticks of the
 // 100 MHz real-time counter.
 constexpr int kStatsWords = 16;
 
