@@ -12,10 +12,9 @@ roofline figure.  Then, outside those K steps: R more calls, each after a
 flush of the caches (1 GiB read and written through a scratch tensor, four
 times the 256 MB MALL), timed one by one with HIP events (median, min,
 max); and, in the same process and under both protocols, the plain copy,
-read and write streams of 1 GiB that set the practical ceiling
-(`stream_ceiling`: the workload's read bytes at the read rate plus its
-written bytes at the write rate, and the copy itself).  Prints one JSON
-line.
+read and write streams of 1 GiB, and a plain stream with the workload's
+own mix of read and written bytes, that set the practical ceiling
+(`stream_ceiling`).  Prints one JSON line.
 
 Workloads (default: u32x): the headline is the uint32 exclusive sum scan of
 2^28 elements, values uniform in [0, 255] (seed 2).  The others time the
@@ -340,10 +339,14 @@ def wall_steps(run, steps, warmup):
 
 def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
     """Copy, read and write of 1 GiB in the same process, under the same two
-    protocols as the workload; the workload's ceiling is its read bytes at
-    the read rate plus its written bytes at the write rate.  For the
-    recurrence also a plain stream of its own shape (two planes read, one or
-    two written, ps_stream_planes_f32) and the call's fraction of it."""
+    protocols as the workload, and the workload's ceiling: the copy of the
+    same bytes where it reads as many bytes as it writes, else a plain
+    stream of its own mix (ps_stream_mix_u32: its read bytes read, its
+    written bytes written, each workgroup a share of both), and for the
+    recurrence a plain stream of its own shape (two planes read, one or two
+    written, ps_stream_planes_f32).  The sum of the read time and the write
+    time (`model_ms`) is reported too; it is not a ceiling: a stream that
+    both reads and writes runs slower than that sum."""
     import torch
 
     import device_wide_prefix_chained_amd as dw
@@ -381,6 +384,21 @@ def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
         del pa, pb, ob, oa
     rb = w["rbytes"]
     wb = w["bytes"] - rb
+    if rb != wb and w["kind"] != "linrec":
+        ni, no = -(-int(rb) // 16) * 4, -(-int(wb) // 16) * 4  # words, whole 16-byte vectors
+        mi = torch.empty(ni, dtype=torch.int32, device="cuda").fill_(5)
+        mo = torch.empty(no, dtype=torch.int32, device="cuda")
+        run = lambda: dw.ps_stream_mix_u32(mi, mo)  # noqa: E731
+        wall = wall_steps(run, steps, 3)
+        fl = flushed_reps(run, reps, flush)
+        moved = 4 * (ni + no)
+        out["mix"] = {"bytes_read": 4 * ni, "bytes_written": 4 * no, "wall_ms": round(wall, 5),
+                      "flushed_median_ms": fl["median_ms"],
+                      "gbs_wall": round(moved / (wall * 1e-3) / 1e9, 1),
+                      "gbs_flushed": round(moved / (fl["median_ms"] * 1e-3) / 1e9, 1),
+                      "frac_wall": round(wall / scan_ms, 4),
+                      "frac_flushed": round(fl["median_ms"] / scan_flushed_ms, 4)}
+        del mi, mo
     for proto, key in (("wall", "gbs_wall"), ("flushed", "gbs_flushed")):
         model_ms = (rb / (out["read"][key] * 1e9) + wb / (out["write"][key] * 1e9)) * 1e3
         mine = scan_ms if proto == "wall" else scan_flushed_ms
@@ -390,6 +408,64 @@ def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
         scale = rb / gib
         out["frac_of_copy_wall"] = round(out["copy"]["wall_ms"] * scale / scan_ms, 4)
         out["frac_of_copy_flushed"] = round(out["copy"]["flushed_median_ms"] * scale / scan_flushed_ms, 4)
+    return out
+
+
+def stream_shapes(steps, rounds=7):
+    """The fill, the copy and the read of 1 GiB in every access shape of
+    ps_stream_shape (threads per workgroup, 16-byte vectors per thread,
+    non-temporal or plain accesses, one-shot or persistent grid) and in the
+    library's own ps_fill_u32 / ps_copy_u32 / ps_read_u32.  Each round times every kernel back to back
+    like the workload, in a new seeded order (the chip's clock drifts over a
+    sweep); per kernel the median over the rounds, and per stream the
+    fastest shape next to the library's."""
+    import torch
+
+    import device_wide_prefix_chained_amd as dw
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.int32, device="cuda").fill_(3)
+    dst = torch.empty(n, dtype=torch.int32, device="cuda")
+    gib = 4.0 * n
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kinds = ("write", "copy", "read")
+    shapes = [(kind, t, v, x, p) for kind in kinds for t in (64, 128, 256) for v in (4, 8, 16)
+              for x in (True, False) for p in (False, True)]
+    shapes += [(kind, "library") for kind in kinds]
+    library = {"write": lambda: dw.ps_fill_u32(dst, 7), "copy": lambda: dw.ps_copy_u32(src, dst),
+               "read": lambda: dw.ps_read_u32(src, sink)}
+
+    def runner(sh):
+        if sh[1] == "library":
+            return library[sh[0]]
+        out, inp = (sink, src) if sh[0] == "read" else (dst, src)
+        return lambda: dw.ps_stream_shape(sh[0], out, inp, threads=sh[1], vecs=sh[2], nontemporal=sh[3],
+                                          persistent=sh[4], value=7)
+
+    times = {sh: [] for sh in shapes}
+    rng = np.random.default_rng(2718)
+    for _ in range(rounds):
+        for k in rng.permutation(len(shapes)):
+            times[shapes[k]].append(wall_steps(runner(shapes[k]), steps, 2))
+    del src, dst, sink
+    rows = []
+    for sh in shapes:
+        ms = float(np.median(times[sh]))
+        moved = 2 * gib if sh[0] == "copy" else gib
+        row = {"stream": sh[0]}
+        if sh[1] == "library":
+            row["library"] = True
+        else:
+            row.update(threads=sh[1], vecs=sh[2], nontemporal=sh[3], persistent=sh[4])
+        row.update(wall_ms=round(ms, 5), spread_ms=round(float(np.max(times[sh]) - np.min(times[sh])), 5),
+                   gbs_wall=round(moved / (ms * 1e-3) / 1e9, 1))
+        rows.append(row)
+    out = {"bytes_each_way": int(gib), "rounds": rounds, "calls_per_round": steps, "rows": rows}
+    for kind in kinds:
+        mine = [r for r in rows if r["stream"] == kind and not r.get("library")]
+        best = max(mine, key=lambda r: r["gbs_wall"])
+        lib_row = next(r for r in rows if r["stream"] == kind and r.get("library"))
+        out[kind] = {"best": best, "library_gbs": lib_row["gbs_wall"],
+                     "library_frac_of_best": round(lib_row["gbs_wall"] / best["gbs_wall"], 4)}
     return out
 
 
@@ -487,6 +563,9 @@ def main():
     ap.add_argument("--lookback-stats", type=int, default=0, metavar="R",
                     help="also run the instrumented kernel R times and summarise its look-back "
                          "statistics (u32x, u32i, f32, f32max, segmented, compact, linrec, linrec-h)")
+    ap.add_argument("--stream-shapes", action="store_true",
+                    help="also time the fill, the copy and the read of 1 GiB in every access shape of "
+                         "ps_stream_shape (108 kernels) and in the library's own helpers, 7 rounds")
     ap.add_argument("--flushed-reps", type=int, default=20,
                     help="calls timed one by one after a cache flush, and the same for the "
                          "stream ceilings (0 skips both)")
@@ -535,6 +614,10 @@ def main():
         print("[bench] stream ceilings (copy, read, write)", file=sys.stderr, flush=True)
         ceiling = stream_ceiling(w, args.steps, args.flushed_reps, flush, ms_per_step, flushed["median_ms"])
         del flush
+    shapes = None
+    if args.stream_shapes:
+        print("[bench] stream shapes", file=sys.stderr, flush=True)
+        shapes = stream_shapes(min(args.steps, 20))
     lb = None
     if args.lookback_stats > 0:
         if not w.get("stats_run"):
@@ -594,6 +677,8 @@ def main():
     }
     if lb is not None:
         line["lookback_stats"] = lb
+    if shapes is not None:
+        line["stream_shapes"] = shapes
     print(json.dumps(line), flush=True)
 
 

@@ -99,6 +99,10 @@ def lib() -> ctypes.CDLL:
     L.ps_fill_u32.restype = i32
     L.ps_stream_planes_f32.argtypes = [vp, vp, vp, vp, u64, vp]
     L.ps_stream_planes_f32.restype = i32
+    L.ps_stream_mix_u32.argtypes = [vp, u64, vp, u64, vp]
+    L.ps_stream_mix_u32.restype = i32
+    L.ps_stream_shape.argtypes = [i32, i32, i32, i32, i32, vp, vp, u64, u32, vp]
+    L.ps_stream_shape.restype = i32
     L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
     L.ps_lookback_stats_u32.restype = i32
     L.ps_scan_lookback_stats.argtypes = [vp, sz, i32, i32, i32, vp, vp, u64, vp, vp]
@@ -575,6 +579,39 @@ def ps_stream_planes_f32(a, b, out_b, out_a=None, stream=None):
     _check("ps_stream_planes_f32", lib().ps_stream_planes_f32(_ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), n,
                                                               _stream(a, stream)))
     return out_b
+
+
+def ps_stream_mix_u32(inp, out, stream=None):
+    """A plain stream that reads inp and writes out, each workgroup a
+    proportional share of both (the ceiling of a kernel with that byte mix)."""
+    _dev_tensor("inp", inp, _U32_DTYPES)
+    _dev_tensor("out", out, _U32_DTYPES)
+    _check("ps_stream_mix_u32", lib().ps_stream_mix_u32(_ptr(inp), inp.numel(), _ptr(out), out.numel(),
+                                                        _stream(out, stream)))
+    return out
+
+
+def ps_stream_shape(kind, out, inp=None, *, threads=128, vecs=8, nontemporal=True, persistent=False, value=0,
+                    stream=None):
+    """One plain stream in a given access shape (the sweep behind the stream
+    ceilings): kind "write" fills out with ``value``, "copy" copies inp to
+    out, "read" reads inp (out: a one-word sink)."""
+    code = {"write": 0, "copy": 1, "read": 2}[kind]
+    if kind == "read":
+        _dev_tensor("inp", inp, _U32_DTYPES)
+        _dev_tensor("sink", out, _U32_DTYPES, 1)
+        n = inp.numel()
+    else:
+        _dev_tensor("out", out, _U32_DTYPES)
+        n = out.numel()
+        if kind == "copy":
+            _dev_tensor("inp", inp, _U32_DTYPES, n)
+        else:
+            inp = None
+    _check("ps_stream_shape", lib().ps_stream_shape(code, int(threads), int(vecs), int(bool(nontemporal)),
+                                                    int(bool(persistent)), _ptr(inp), _ptr(out), n,
+                                                    int(value) & 0xFFFFFFFF, _stream(out, stream)))
+    return out
 
 
 def ps_kernel_timing(enable: bool, every: int = 1) -> None:

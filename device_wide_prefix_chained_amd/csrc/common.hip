@@ -38,12 +38,18 @@ typedef unsigned int copy_v4u __attribute__((ext_vector_type(4)));
 
 // Streaming kernels of the measurement helpers: 128 threads x 8 vectors of
 // 16 bytes per workgroup (16 KiB), non-temporal loads and stores, one
-// workgroup per 16 KiB.  Of the shapes tried on MI355X (64-256 threads, 4-16
-// vectors per thread, persistent grids) this one copies fastest, so it is
-// the practical ceiling the scans are compared with.
+// workgroup per 16 KiB.  Of the shapes of ps_stream_shape (64-256 threads,
+// 4-16 vectors per thread, plain or non-temporal, persistent grids) this one
+// copies fastest on MI355X and reads within 1% of the fastest, so these are
+// the practical ceilings the scans are compared with.  A write-only stream
+// is fastest in small workgroups with plain stores (64 threads x 4 vectors,
+// 4 KiB): the fill has that shape of its own.
 constexpr int kStreamThreads = 128;
 constexpr int kStreamVecs = 8;
 constexpr uint64_t kStreamBlock = (uint64_t)kStreamThreads * kStreamVecs;  // vectors per workgroup
+constexpr int kFillThreads = 64;
+constexpr int kFillVecs = 4;
+constexpr uint64_t kFillBlock = (uint64_t)kFillThreads * kFillVecs;
 
 // Index of vector k of this thread; in a partial last workgroup indices past
 // the end are clamped to the last vector, so that every load is issued
@@ -122,18 +128,47 @@ __global__ __launch_bounds__(kStreamThreads) void planes_vec_kernel(const copy_v
         planes_block<false, BOTH>(a, b, oa, ob, base, n16);
 }
 
-// Write-only stream: fills with one value.
-__global__ __launch_bounds__(kStreamThreads) void fill_vec_kernel(copy_v4u *out, uint64_t n16, uint32_t value) {
-    const uint64_t base = (uint64_t)blockIdx.x * kStreamBlock + threadIdx.x;
-    const copy_v4u v = {value, value, value, value};
-    if (((uint64_t)blockIdx.x + 1u) * kStreamBlock <= n16) {
-#pragma unroll
-        for (int k = 0; k < kStreamVecs; ++k) __builtin_nontemporal_store(v, out + base + (uint64_t)k * kStreamThreads);
-    } else {
+// Stream of a given mix of read and written bytes: workgroup b of G reads
+// the vectors [b ni / G, (b + 1) ni / G) of in and writes the vectors
+// [b no / G, (b + 1) no / G) of out, each range at most one block of
+// kStreamBlock vectors.  Vector j of a workgroup's output range is vector j of
+// its input range (its last vector past the range's end, zero if the range
+// is empty), so every store waits for a load, as a scan's do.
+__global__ __launch_bounds__(kStreamThreads) void mix_vec_kernel(const copy_v4u *in, uint64_t ni, copy_v4u *out,
+                                                                 uint64_t no) {
+    const uint64_t g = gridDim.x, b = blockIdx.x;
+    const uint64_t i0 = b * ni / g, ilen = (b + 1) * ni / g - i0;
+    const uint64_t o0 = b * no / g, olen = (b + 1) * no / g - o0;
+    copy_v4u r[kStreamVecs];
+    if (ilen) {
 #pragma unroll
         for (int k = 0; k < kStreamVecs; ++k) {
-            const uint64_t i = base + (uint64_t)k * kStreamThreads;
-            if (i < n16) __builtin_nontemporal_store(v, out + i);
+            const uint64_t j = threadIdx.x + (uint64_t)k * kStreamThreads;
+            r[k] = __builtin_nontemporal_load(in + i0 + (j < ilen ? j : ilen - 1u));
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kStreamVecs; ++k) r[k] = copy_v4u{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kStreamVecs; ++k) {
+        const uint64_t j = threadIdx.x + (uint64_t)k * kStreamThreads;
+        if (j < olen) __builtin_nontemporal_store(r[k], out + o0 + j);
+    }
+}
+
+// Write-only stream: fills with one value.
+__global__ __launch_bounds__(kFillThreads) void fill_vec_kernel(copy_v4u *out, uint64_t n16, uint32_t value) {
+    const uint64_t base = (uint64_t)blockIdx.x * kFillBlock + threadIdx.x;
+    const copy_v4u v = {value, value, value, value};
+    if (((uint64_t)blockIdx.x + 1u) * kFillBlock <= n16) {
+#pragma unroll
+        for (int k = 0; k < kFillVecs; ++k) out[base + (uint64_t)k * kFillThreads] = v;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kFillVecs; ++k) {
+            const uint64_t i = base + (uint64_t)k * kFillThreads;
+            if (i < n16) out[i] = v;
         }
     }
 }
@@ -330,6 +365,24 @@ extern "C" ps_status ps_stream_planes_f32(const float *a, const float *b, float 
     return launch_status();
 }
 
+extern "C" ps_status ps_stream_mix_u32(const uint32_t *in, uint64_t n_in, uint32_t *out, uint64_t n_out,
+                                       void *stream) {
+    if (n_in == 0 && n_out == 0) return PS_OK;
+    if ((n_in && !in) || (n_out && !out)) return PS_ERR_NULL;
+    if (n_in >= (1ull << 32) || n_out >= (1ull << 32)) return PS_ERR_SIZE;
+    if ((n_in && !aligned(in, 16)) || (n_out && !aligned(out, 16)) || n_in % 4 || n_out % 4)
+        return PS_ERR_ALIGNMENT;
+    if (n_in && n_out && ranges_overlap(in, n_in * 4, out, n_out * 4)) return PS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint64_t ni = n_in / 4, no = n_out / 4;
+    const uint64_t grid = ceil_div(ni > no ? ni : no, kStreamBlock);
+    timing_begin(s);
+    hipLaunchKernelGGL(mix_vec_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0, s,
+                       reinterpret_cast<const copy_v4u *>(in), ni, reinterpret_cast<copy_v4u *>(out), no);
+    timing_end(s);
+    return launch_status();
+}
+
 extern "C" ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void *stream) {
     if (n == 0) return PS_OK;
     if (!out) return PS_ERR_NULL;
@@ -341,8 +394,8 @@ extern "C" ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void
     if (aligned(out, 16)) {
         const uint64_t n16 = n / 4;
         if (n16)
-            hipLaunchKernelGGL(fill_vec_kernel, dim3((unsigned)ceil_div(n16, kStreamBlock)), dim3(kStreamThreads), 0,
-                               s, reinterpret_cast<copy_v4u *>(out), n16, value);
+            hipLaunchKernelGGL(fill_vec_kernel, dim3((unsigned)ceil_div(n16, kFillBlock)), dim3(kFillThreads), 0, s,
+                               reinterpret_cast<copy_v4u *>(out), n16, value);
         done = n16 * 4;
     }
     if (done < n)

@@ -373,12 +373,14 @@ uint32_t ps_compact_tile_records(uint32_t record_bytes);
  * kernel of known size used to scale the hardware byte counters. */
 ps_status ps_copy_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *stream);
 
-/* The two halves of that ceiling, with the copy's access shape: a stream
- * that only reads n uint32 (in 16-byte aligned, n a multiple of 4, else
+/* The two halves of that ceiling: a stream that only reads n uint32, with
+ * the copy's access shape (in 16-byte aligned, n a multiple of 4, else
  * PS_ERR_ALIGNMENT; *sink, one device word, is written only in the
  * practically impossible case that the fold of the data hits a fixed
- * constant) and one that only writes (fills n uint32 with `value`; also a
- * plain fill that records no memset node when captured in a graph). */
+ * constant), and one that only writes (fills n uint32 with `value`, in the
+ * fastest write shape of ps_stream_shape: 64 threads x 4 vectors, plain
+ * stores; also a plain fill that records no memset node when captured in a
+ * graph). */
 ps_status ps_read_u32(const uint32_t *in, uint64_t n, uint32_t *sink, void *stream);
 ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void *stream);
 
@@ -390,6 +392,36 @@ ps_status ps_fill_u32(uint32_t *out, uint64_t n, uint32_t value, void *stream);
  * PS_ERR_ALIGNMENT; overlapping arrays: PS_ERR_ALIAS. */
 ps_status ps_stream_planes_f32(const float *a, const float *b, float *out_a, float *out_b,
                                uint64_t n, void *stream);
+
+/* A plain stream with a given mix of read and written bytes, the practical
+ * ceiling of a kernel that reads n_in uint32 and writes n_out: the grid's G
+ * = ceil(max(n_in, n_out) / 4096) workgroups each read a share of in and
+ * write the same share of out, with the copy's access shape.  Workgroup b
+ * reads the 16-byte vectors [b ni / G, (b + 1) ni / G) of in (ni = n_in / 4)
+ * and writes the vectors [b no / G, (b + 1) no / G) of out (no = n_out / 4);
+ * its output vector j is its input vector min(j, last), zero when its input
+ * range is empty.  Arrays 16-byte aligned and n_in, n_out multiples of 4,
+ * else PS_ERR_ALIGNMENT; in and out overlapping: PS_ERR_ALIAS. */
+ps_status ps_stream_mix_u32(const uint32_t *in, uint64_t n_in, uint32_t *out, uint64_t n_out,
+                            void *stream);
+
+/* The three plain streams in one of several access shapes, for a sweep that
+ * shows whether the stream helpers above run at the memory's rate:
+ * PS_STREAM_WRITE fills n uint32 of out with `value` (in unused),
+ * PS_STREAM_COPY copies in to out, PS_STREAM_READ reads n uint32 of in (out
+ * is a one-word sink, written only in the practically impossible case that
+ * the fold of the data hits a fixed constant).  Shape: `threads` per
+ * workgroup (64, 128 or 256), `vecs` 16-byte vectors per thread and block
+ * (4, 8 or 16), non-temporal or plain loads and stores, one workgroup per
+ * block of threads * vecs vectors or (persistent != 0) the resident grid
+ * striding over the blocks.  Any other kind, threads or vecs:
+ * PS_ERR_UNSUPPORTED; streamed arrays 16-byte aligned and n a multiple of 4,
+ * else PS_ERR_ALIGNMENT; n >= 2^32: PS_ERR_SIZE; overlapping copy:
+ * PS_ERR_ALIAS. */
+enum { PS_STREAM_WRITE = 0, PS_STREAM_COPY = 1, PS_STREAM_READ = 2 };
+ps_status ps_stream_shape(int kind, int threads, int vecs, int nontemporal, int persistent,
+                          const uint32_t *in, uint32_t *out, uint64_t n, uint32_t value,
+                          void *stream);
 
 /* Exclusive uint32 sum scan (same kernel as ps_scan_exclusive_u32, built
  * with per-tile instrumentation of the look-back of [P1] "Why the work

@@ -273,6 +273,27 @@ def test_argument_errors_stream_helpers():
     assert P(v(A), v(B), None, v(A), 16, None) == 2           # an output over an input
     assert P(v(A), v(B), v(C3), v(C3), 16, None) == 2           # both outputs in one place
     assert P(v(A), v(B), None, v(C3), 1 << 32, None) == 3
+    M = lib.ps_stream_mix_u32
+    assert M(None, 0, None, 0, None) == 0
+    assert M(None, 16, v(B), 16, None) == 1 and M(v(A), 16, None, 16, None) == 1
+    assert M(v(A + 4), 16, v(B), 16, None) == 7 and M(v(A), 16, v(B), 6, None) == 7
+    assert M(v(A), 16, v(A + 32), 16, None) == 2                     # overlapping
+    assert M(v(A), 1 << 32, v(B), 16, None) == 3
+    S = lib.ps_stream_shape
+    W, CP, RD = 0, 1, 2
+    assert S(CP, 128, 8, 1, 0, None, None, 0, 0, None) == 0          # n = 0: nothing to do
+    for t, k in ((32, 8), (512, 8), (128, 2), (128, 32), (96, 4)):
+        assert S(W, t, k, 1, 0, None, v(B), 16, 0, None) == 5       # shape not provided
+    assert S(3, 128, 8, 1, 0, v(A), v(B), 16, 0, None) == 5          # no such stream
+    assert S(CP, 128, 8, 1, 0, None, v(B), 16, 0, None) == 1         # a copy needs its input
+    assert S(RD, 128, 8, 1, 0, None, v(B), 16, 0, None) == 1         # a read its input
+    assert S(RD, 128, 8, 1, 0, v(A), None, 16, 0, None) == 1         # and its sink
+    assert S(W, 128, 8, 1, 0, None, None, 16, 0, None) == 1
+    assert S(CP, 256, 16, 0, 1, v(A + 4), v(B), 16, 0, None) == 7    # 16-byte alignment
+    assert S(RD, 256, 16, 0, 1, v(A + 4), v(B), 16, 0, None) == 7
+    assert S(W, 64, 4, 0, 0, None, v(B), 18, 0, None) == 7          # whole 16-byte vectors only
+    assert S(CP, 64, 4, 1, 1, v(A), v(A + 16), 16, 0, None) == 2     # overlapping copy
+    assert S(W, 64, 4, 1, 1, None, v(B), 1 << 32, 0, None) == 3
 
 
 def test_status_strings():

@@ -81,3 +81,61 @@ def test_kernel_timing_samples_every_nth_call(dw):
     dw.ps_kernel_timing(False)
     dw.ps_copy_u32(x, y)
     assert dw.ps_kernel_timing_read() == (0.0, 0)
+
+
+def _mix_expected(x, n_out):
+    """The mix stream's output from its definition: workgroup b of G reads
+    its share of the input vectors and writes its share of the output ones,
+    output vector j of the share being input vector min(j, last)."""
+    vin = x.reshape(-1, 4)
+    ni, no = len(vin), n_out // 4
+    g = -(-max(ni, no) // 1024)
+    out = np.zeros((no, 4), np.uint32)
+    for b in range(g):
+        i0, i1 = b * ni // g, (b + 1) * ni // g
+        o0, o1 = b * no // g, (b + 1) * no // g
+        if i1 > i0:
+            j = np.minimum(np.arange(o1 - o0), i1 - i0 - 1)
+            out[o0:o1] = vin[i0 + j]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("n_in,n_out", [(4, 4), (4096, 8192), (8192 * 3 + 4, 4 * 1000), (1 << 20, 3 << 19),
+                                        (12, 1 << 16), (1 << 16, 0), (0, 4096), (4 * 1_000_003, 8 * 1_000_003)])
+def test_mix_stream(dw, n_in, n_out):
+    import torch
+    x = wl.full_range_u32(n_in, seed=n_in + 63)
+    d_in = dev(x) if n_in else torch.empty(0, dtype=torch.int32, device="cuda")
+    buf = torch.full((n_out + 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    say("mix stream", n_in, n_out)
+    dw.ps_stream_mix_u32(d_in, buf[:n_out])
+    h = host(buf)
+    assert np.array_equal(h[:n_out], _mix_expected(x, n_out)) and np.all(h[n_out:] == 0x5A5A5A5A)
+
+
+@pytest.mark.parametrize("threads", [64, 128, 256])
+@pytest.mark.parametrize("vecs", [4, 8, 16])
+def test_stream_shapes(dw, threads, vecs):
+    """Every shape of the stream sweep copies and fills exactly n words and
+    nothing past them, and its read leaves the sink alone: sizes below one
+    block, between whole blocks and above the resident grid's first pass."""
+    import torch
+    for n in (4, 4 * (threads * vecs * 3 + 5), 1_000_004, 4 * 256 * 16 * 2048 + 12):
+        x = wl.full_range_u32(n, seed=n + threads + vecs)
+        d_in = dev(x)
+        sink = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+        for nt in (False, True):
+            for persistent in (False, True):
+                say("stream shape", threads, vecs, nt, persistent, n)
+                buf = torch.full((n + 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+                dw.ps_stream_shape("copy", buf[:n], d_in, threads=threads, vecs=vecs, nontemporal=nt,
+                                   persistent=persistent)
+                h = host(buf)
+                assert np.array_equal(h[:n], x) and np.all(h[n:] == 0x5A5A5A5A)
+                dw.ps_stream_shape("write", buf[:n], threads=threads, vecs=vecs, nontemporal=nt,
+                                   persistent=persistent, value=0xC0FFEE00 + n % 251)
+                h = host(buf)
+                assert np.all(h[:n] == 0xC0FFEE00 + n % 251) and np.all(h[n:] == 0x5A5A5A5A)
+                dw.ps_stream_shape("read", sink, d_in, threads=threads, vecs=vecs, nontemporal=nt,
+                                   persistent=persistent)
+                assert int(host(sink)[0]) == 12345
