@@ -64,9 +64,25 @@ PROFILES = os.path.join(ROOT, "profiles")
 TIMING_EVERY = 5
 
 
-def kernel_source_hash() -> str:
+# The source file that holds each workload's main kernel (scan.hip for the
+# rest); its hash, with every shared header, marks the counter summaries under
+# profiles/ taken on it, so that a change to one kernel leaves the others'
+# summaries valid.
+KERNEL_FILE = {"segmented": "segscan.hip", "compact": "compact.hip",
+               "copy": "common.hip", "read": "common.hip", "write": "common.hip"}
+
+
+def kernel_sources(workload: str):
+    csrc = os.path.join(ROOT, "device_wide_prefix_chained_amd", "csrc")
+    files = [os.path.join(csrc, KERNEL_FILE.get(workload, "scan.hip"))]
+    files += sorted(glob.glob(os.path.join(csrc, "*.hpp")))
+    files.append(os.path.join(ROOT, "include", "dwps.h"))
+    return files
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "device_wide_prefix_chained_amd", "csrc", "*"))):
+    for p in kernel_sources(workload):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -81,7 +97,7 @@ def load_traffic(workload: str, launch_bytes_alg: float):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return float(t["hbm_bytes_per_launch"])
 

@@ -173,11 +173,16 @@ __device__ __forceinline__ void wave_seg_inclusive(uint32_t &f, uint32_t &v) {
 }
 
 // Segmented tile shape: D data waves x Q groups of four elements per lane.
+// The segmented scan takes several times the vector instructions of the
+// flat scan per element, and a SIMD issues its waves oldest first, so the
+// last data wave on each SIMD reaches barrier B late.  Twelve data waves of
+// four groups (13 waves per workgroup) spread the same 12 288-element tile
+// over more waves than eight of six and shorten that wait.
 #ifndef DWPS_SEG_D
-#define DWPS_SEG_D 8
+#define DWPS_SEG_D 12
 #endif
 #ifndef DWPS_SEG_Q
-#define DWPS_SEG_Q 6
+#define DWPS_SEG_Q 4
 #endif
 constexpr int kSegD = DWPS_SEG_D;
 constexpr int kSegQ = DWPS_SEG_Q;
@@ -227,7 +232,9 @@ struct SegFallback {
     uint32_t *bits;
     uint32_t n;
     __device__ DescVal<uint32_t> operator()(uint32_t p, uint32_t lane) const {
-        constexpr uint32_t ROWS = kSegTile / 256u, BATCH = 8u;
+        constexpr uint32_t ROWS = kSegTile / 256u;
+        constexpr uint32_t BATCH = ROWS % 8u == 0u ? 8u : ROWS % 7u == 0u ? 7u : ROWS % 6u == 0u ? 6u
+                                                                            : ROWS % 5u == 0u ? 5u : 4u;
         static_assert(ROWS % BATCH == 0, "whole batches of rows");
         {
             const uint32_t tb = p * kSegTile;
