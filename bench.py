@@ -45,6 +45,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -80,12 +81,22 @@ def kernel_sources(workload: str):
     return files
 
 
+def _code_text(text: str) -> str:
+    """The source with its comments removed and its whitespace collapsed,
+    so that a change to comments alone keeps the hash.  A string literal is
+    kept whole, so that a comment marker inside one is not taken for a
+    comment."""
+    token = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
+    text = token.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
     for p in kernel_sources(workload):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(_code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -557,6 +568,22 @@ def lookback_summary(w, reps, warmup):
                 "last_scan_phase_us": q(last), "end_us": q(end) if end.size else None,
                 "drain_us": q(end - np.array([rel(g["last_scan"]) for g in wgs.values() if g["end"]]))
                 if end.size else None}
+    arrivals = None
+    if w["kind"] == "segmented":
+        # the data waves' arrivals at barrier B of each tile's scan phase
+        # (word 15, ticks after the control wave's start of the phase)
+        w15 = a[:, 15]
+        seen = w15 != 0
+        first, last = (w15[seen] & 1023) / 100.0, ((w15[seen] >> 10) & 1023) / 100.0
+        who = (w15[seen] >> 20) & 15
+        ctrl_b = a[seen, 4] / 100.0
+        stat = lambda v: {"p50": round(float(np.percentile(v, 50)), 3),  # noqa: E731
+                          "p90": round(float(np.percentile(v, 90)), 3), "mean": round(float(v.mean()), 3)}
+        arrivals = {"phases": int(seen.sum()), "first_data_wave_us": stat(first),
+                    "last_data_wave_us": stat(last), "control_wave_us": stat(ctrl_b),
+                    "last_data_wave_index_hist": {str(k): int(np.sum(who == k)) for k in range(16)
+                                                  if np.any(who == k)},
+                    "control_later_than_last_data_wave_pct": round(100.0 * float(np.mean(ctrl_b > last)), 1)}
     return {"tiles_per_call": tiles, "calls": reps, "looking_tiles_per_call": round(len(looking) / reps, 1),
             "polls_hist": hist(polls, 5), "windows_hist": hist(windows, 4),
             "tiles_with_a_stall_pct": round(100.0 * float(np.mean(stalls > 0)), 2),
@@ -565,7 +592,7 @@ def lookback_summary(w, reps, warmup):
             "lookback_us": {"p50": pct(50), "p90": pct(90), "p99": pct(99), "max": round(float(us.max()), 2),
                             "mean": round(float(us.mean()), 2)},
             "instrumented_call_ms_median": round(statistics.median(times), 5), "phase": phase,
-            "timeline": timeline}
+            "timeline": timeline, "barrier_b_arrivals": arrivals}
 
 
 def main():

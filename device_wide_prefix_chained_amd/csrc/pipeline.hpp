@@ -58,9 +58,10 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgc
 // workgroup, [11] the workgroup's start, [12] (last tile a workgroup
 // stored only) the time its control wave finished.  Words 13-14: when the
 // phase that stored the tile scanned none (the drain), that phase's parts
-// as in 4-7, 16 bits each.  Word 15 (flat kernel only): data wave 0's view
-// of the phase that scanned the tile (DataClock).  Times in ticks of the
-// 100 MHz real-time counter.
+// as in 4-7, 16 bits each.  Word 15: in the flat kernel data wave 0's view
+// of the phase that scanned the tile (DataClock), in the segmented kernel
+// the data waves' arrivals at barrier B of that phase (record_arrivals in
+// segscan.hip).  Times in ticks of the 100 MHz real-time counter.
 constexpr int kStatsWords = 16;
 
 __device__ __forceinline__ uint32_t realtime32() { return (uint32_t)__builtin_amdgcn_s_memrealtime(); }

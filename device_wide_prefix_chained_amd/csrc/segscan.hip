@@ -205,6 +205,7 @@ struct SegShared {
     uint32_t sample[kSampleMax];       // every stride-th offset (StartIndex)
     uint32_t next;
     uint32_t carry;                    // carry into prev2
+    uint32_t arrive[2][D];             // instrumented builds: each data wave's arrival at barrier B, by parity
 };
 
 // Register state of one wave's span: the values.
@@ -274,6 +275,34 @@ struct SegFallback {
     }
 };
 
+// Instrumented builds: when the data waves reached barrier B in the phase
+// that scanned tile f1, as word 15 of its statistics row -- bits 0-9 the
+// first data wave and bits 10-19 the last one (ticks of the real-time
+// counter after the control wave's phase start, 0 for a wave that came
+// before it, at most 1023), bits 20-23 the last data wave's index, bits
+// 24-27 the first one's.  The data waves' arrivals are spread by the order
+// in which each SIMD issues its waves (oldest first).
+template <int D>
+__device__ __forceinline__ void record_arrivals(const uint32_t *arrive, uint64_t start, uint32_t *stats, uint32_t f1) {
+    static_assert(D <= 16, "wave indices take four bits");
+    uint32_t first = 0xFFFFFFFFu, last = 0u, who_first = 0u, who_last = 0u;
+    for (int w = 0; w < D; ++w) {
+        const int32_t dt = (int32_t)(arrive[w] - (uint32_t)start);
+        const uint32_t t = dt < 0 ? 0u : (uint32_t)dt;
+        if (t < first) {
+            first = t;
+            who_first = (uint32_t)w;
+        }
+        if (t >= last) {
+            last = t;
+            who_last = (uint32_t)w;
+        }
+    }
+    first = first < 1023u ? first : 1023u;
+    last = last < 1023u ? last : 1023u;
+    stats[(uint64_t)kStatsWords * f1 + 15] = first | (last << 10) | (who_last << 20) | (who_first << 24);
+}
+
 // Control wave.  Phase k: issue the loads of the offsets around f2's first
 // segment start (the tile the data waves load in this phase); find the carry
 // into prev2 (a look-back only when prev2 heads a ticket group and its first
@@ -342,6 +371,7 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
         clk.reach_b();
         __syncthreads();  // B: the carry of prev2 is in LDS
         clk.leave_b();
+        if (STATS && lane == 0 && pt.f1 < num_tiles) record_arrivals<D>(sh.arrive[par], clk.start, stats, pt.f1);
         agg_next = SegPair{0u, 0u};
         fh_next = kSegTile;
         if (pt.f1 < num_tiles) {
@@ -372,7 +402,7 @@ __device__ __forceinline__ void seg_control_loop(PipeTiles pt, SegShared<D, Q> &
 // finalize cur into LDS slot `slot` with carry 0, load the tile two ahead
 // into the freed registers, scan f1; after barrier B add the carry to the
 // elements of prev2 before its first segment start and store prev2.
-template <int D, int Q, int G, bool INCL, bool VEC>
+template <int D, int Q, int G, bool INCL, bool VEC, bool STATS>
 __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, int par, uint32_t &slot,
                                                PipeTiles &pt, uint32_t (&pre)[Q], uint32_t (&fl)[Q],
                                                SegShared<D, Q> &sh, const uint32_t *values, uint32_t *out, uint32_t n,
@@ -471,6 +501,7 @@ __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, 
             sh.wfirst[par ^ 1][d] = wave_first;
         }
     }
+    if (STATS && lane == 0) sh.arrive[par][d] = realtime32();
     __syncthreads();  // B
     if (pt.prev2 < num_tiles) {
         const uint64_t bp = (uint64_t)pt.prev2 * TILE;
@@ -509,7 +540,7 @@ __device__ __forceinline__ bool seg_data_phase(SegSpan<Q> &cur, SegSpan<Q> &f1, 
     return false;
 }
 
-template <int D, int Q, int G, bool INCL, bool VEC>
+template <int D, int Q, int G, bool INCL, bool VEC, bool STATS>
 __device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh, const uint32_t *values,
                                               uint32_t *out, uint32_t n, uint32_t row_lo,
                                               uint32_t row_hi, uint32_t num_tiles, uint32_t *ctr, uint32_t lane,
@@ -522,11 +553,11 @@ __device__ __forceinline__ void seg_data_loop(PipeTiles pt, SegShared<D, Q> &sh,
     uint32_t pre[Q], fl[Q];
     uint32_t slot = 0;
     for (;;) {
-        if (seg_data_phase<D, Q, G, INCL, VEC>(x, y, 0, slot, pt, pre, fl, sh, values,
+        if (seg_data_phase<D, Q, G, INCL, VEC, STATS>(x, y, 0, slot, pt, pre, fl, sh, values,
                                                out, n, row_lo, row_hi, num_tiles, ctr, lane, d, lane_off,
                                                word_off))
             break;
-        if (seg_data_phase<D, Q, G, INCL, VEC>(y, x, 1, slot, pt, pre, fl, sh, values,
+        if (seg_data_phase<D, Q, G, INCL, VEC, STATS>(y, x, 1, slot, pt, pre, fl, sh, values,
                                                out, n, row_lo, row_hi, num_tiles, ctr, lane, d, lane_off,
                                                word_off))
             break;
@@ -559,7 +590,7 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
         } else {
             // rows outside [offsets[0], offsets[N]) belong to no segment
             const uint32_t lo = offsets[0], hi = offsets[num_segments];
-            seg_data_loop<D, Q, G, INCL, VEC>(pt, sh, values, out, n, uniform(lo < n ? lo : n),
+            seg_data_loop<D, Q, G, INCL, VEC, STATS>(pt, sh, values, out, n, uniform(lo < n ? lo : n),
                                               uniform(hi < n ? hi : n), num_tiles, ctr, lane, wave - 1);
         }
     }

@@ -442,12 +442,16 @@ ps_status ps_stream_shape(int kind, int threads, int vecs, int nontemporal, int 
  *   finished (0 for other tiles); [13], [14] when the phase that stored
  *   the tile scanned no tile (the pipeline's drain), that phase's parts
  *   as in [4]-[7], two 16-bit values per word (low half first); [15]
- *   (flat scan and recurrence only, else 0) the phase that scanned the
- *   tile as the first data wave saw it, three 10-bit fields in ticks
- *   (saturating at 1023), low bits first: from leaving the second barrier
- *   of the phase before to the end of the scan, from leaving the first
- *   barrier to the last store of the stored tile issued, from leaving the
- *   first barrier to reaching the second.
+ *   (flat scan and recurrence) the phase that scanned the tile as the
+ *   first data wave saw it, three 10-bit fields in ticks (saturating at
+ *   1023), low bits first: from leaving the second barrier of the phase
+ *   before to the end of the scan, from leaving the first barrier to the
+ *   last store of the stored tile issued, from leaving the first barrier to
+ *   reaching the second; (segmented scan) when the data waves reached the
+ *   first barrier of that phase, in ticks after the control wave's start of
+ *   the phase (0 for a data wave that came before it, at most 1023): bits
+ *   0-9 the first data wave, bits 10-19 the last, bits 20-23 the last
+ *   one's index, bits 24-27 the first one's; (compaction) 0.
  * aggregate_only != 0 (a test of the sliding window): tiles after tile 0
  * never publish their inclusive prefix, so every look-back walks back to
  * tile 0 -- quadratic in the tile count, meant for small n only. */

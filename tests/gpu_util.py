@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 TILE = 12288         # elements per tile of the segmented kernel (12 data waves x 4 x 256)
+SEG_DATA_WAVES = 12  # data waves per workgroup of the segmented kernel
 FLAT_TILE = 12288    # elements per tile of the flat scan (8 data waves x 6 x 256)
 FLAT_GROUP = 2       # consecutive flat tiles claimed per ticket
 LINREC_TILE = 6144   # pairs per tile of the recurrence scan (8 data waves x 3 x 256)

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from gpu_util import FLAT_TILE, TILE, assert_f32_sum_close, dev, filled_dev, host, require_gpu, say
+from gpu_util import FLAT_TILE, SEG_DATA_WAVES, TILE, assert_f32_sum_close, dev, filled_dev, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -20,10 +20,12 @@ def dw():
     return require_gpu()
 
 
-def _check_rows(st, looks, data_clock=False):
+def _check_rows(st, looks, data_clock=False, arrivals=0):
     """st: (tiles, 16) rows (polls, windows, ticks, stalls, the phase timing
-    of the tile's scan phase, the timeline, and for the flat kernels data
-    wave 0's view of that phase); looks: which tiles look back."""
+    of the tile's scan phase, the timeline, and word 15: for the flat kernels
+    data wave 0's view of that phase, for the segmented kernel the data
+    waves' arrivals at its first barrier); looks: which tiles look back;
+    arrivals: the segmented kernel's data wave count."""
     polls, windows, stalls = st[:, 0], st[:, 1], st[:, 3]
     w15 = st[:, 15]
     if data_clock:
@@ -32,6 +34,18 @@ def _check_rows(st, looks, data_clock=False):
         # barrier A (not before the stores)
         scanned, stored, at_a = w15 & 1023, (w15 >> 10) & 1023, (w15 >> 20) & 1023
         assert np.all(scanned > 0) and np.all(at_a >= stored) and np.all(w15 >> 30 == 0)
+    elif arrivals:
+        # the first data wave came no later than the last, which scanned its
+        # span after the phase began (never 0 ticks; the first may read 0:
+        # the control wave stamps its start of the phase after its own
+        # bookkeeping at the barrier before), their indices name data waves
+        first, last = w15 & 1023, (w15 >> 10) & 1023
+        who_last, who_first = (w15 >> 20) & 15, (w15 >> 24) & 15
+        assert np.all(last > 0) and np.all(first <= last) and np.all(w15 >> 28 == 0)
+        assert np.all(who_last < arrivals) and np.all(who_first < arrivals)
+        # the control wave saw every data wave arrive by the time it left
+        # the barrier (a few ticks of slack for the counter's reads)
+        assert np.all(last <= np.minimum(st[:, 4] + st[:, 5], 1023) + 5)
     else:
         assert np.all(w15 == 0)
     # every tile is scanned in exactly one phase, which both waves timed
@@ -94,7 +108,7 @@ def test_segmented_stats(dw, orc):
     t = np.arange(tiles)
     looks = (t % 2 == 0) & (t > 0) & ~first_is_start
     assert looks.sum() > 100  # the giant segment spans many tiles
-    _check_rows(st, looks)
+    _check_rows(st, looks, arrivals=SEG_DATA_WAVES)
 
 
 def test_compact_stats(dw, orc):
