@@ -168,8 +168,22 @@ def _torch_stream(device, stream):
     return torch.cuda.ExternalStream(int(stream), device=device)
 
 
+# The raw handle of a device's current stream, read without building a
+# torch stream object (which costs microseconds per call); None on a torch
+# without it, where the stream object is built instead.
+_CURRENT_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _raw_stream(t, stream) -> int:
+    """The call's stream as a raw hipStream_t (the current stream of t's
+    device when None)."""
+    if stream is None and _CURRENT_RAW_STREAM is not None:
+        return int(_CURRENT_RAW_STREAM(t.get_device()))
+    return int(_torch_stream(t.device, stream).cuda_stream)
+
+
 def _stream(t, stream):
-    return ctypes.c_void_p(_torch_stream(t.device, stream).cuda_stream)
+    return ctypes.c_void_p(_raw_stream(t, stream))
 
 
 def _dev_tensor(name, t, dtypes=None, numel=None):
@@ -207,13 +221,13 @@ def new_workspace(nbytes, device="cuda", stream=None):
 _WS_CACHE = {}
 
 
-def _cached_workspace(fn, need, device, stream):
-    ts = _torch_stream(device, stream)
-    index = device.index if device.index is not None else torch.cuda.current_device()
-    key = (index, ts.cuda_stream)
+def _cached_workspace(fn, need, t, stream):
+    key = (t.get_device(), _raw_stream(t, stream))
     ws = _WS_CACHE.get(key)
     if ws is not None and ws.numel() >= need:
         return ws
+    device = t.device
+    ts = _torch_stream(device, stream)
     if torch.cuda.is_current_stream_capturing():
         raise RuntimeError("%s: pass a workspace (new_workspace) when capturing a graph" % fn)
     # grow geometrically; the old buffer was only ever used on this stream,
@@ -226,15 +240,15 @@ def _cached_workspace(fn, need, device, stream):
     return ws
 
 
-def _workspace(fn: str, call, device, workspace, stream=None):
-    """The call's workspace, or the prepared one kept for its device and
-    stream when none is given (sized by a CUB-style query).  A given
-    workspace is not queried: the library itself refuses one that is too
-    small (PS_ERR_WORKSPACE) before anything runs."""
+def _workspace(fn: str, call, t, workspace, stream=None):
+    """The call's workspace, or the prepared one kept for the device and
+    stream of tensor t when none is given (sized by a CUB-style query).  A
+    given workspace is not queried: the library itself refuses one that is
+    too small (PS_ERR_WORKSPACE) before anything runs."""
     if workspace is None:
         need = ctypes.c_size_t(0)
         _check(fn, call(None, ctypes.byref(need)))
-        workspace = _cached_workspace(fn, int(need.value), device, stream)
+        workspace = _cached_workspace(fn, int(need.value), t, stream)
     else:
         _dev_tensor("workspace", workspace)
     have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
@@ -254,7 +268,7 @@ def _flat(fn: str, inp, out, total, workspace, stream, dtypes, out_dtypes=None):
     n = inp.numel()
     s = _stream(inp, stream)
     call = lambda ws, wsb: f(ws, wsb, _ptr(inp), _ptr(out), n, _ptr(total), s)  # noqa: E731
-    ws, have = _workspace(fn, call, inp.device, workspace, stream)
+    ws, have = _workspace(fn, call, inp, workspace, stream)
     _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -349,7 +363,7 @@ def _generic(fn, op, inclusive, inp, out, total, workspace, stream, dtype):
     f = getattr(L, fn)
     call = lambda ws, wsb: f(ws, wsb, opc, dtype, int(bool(inclusive)), _ptr(inp),  # noqa: E731
                              _ptr(out), n, _ptr(total), s)
-    ws, have = _workspace(fn, call, inp.device, workspace, stream)
+    ws, have = _workspace(fn, call, inp, workspace, stream)
     _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -370,7 +384,7 @@ def ps_scan_linrec_f32(a, b, out_b, out_a=None, inclusive=True, total=None, work
     L = lib()
     call = lambda ws, wsb: L.ps_scan_linrec_f32(ws, wsb, _ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b),  # noqa: E731
                                                 n, int(bool(inclusive)), _ptr(total), s)
-    ws, have = _workspace("ps_scan_linrec_f32", call, a.device, workspace, stream)
+    ws, have = _workspace("ps_scan_linrec_f32", call, a, workspace, stream)
     _check("ps_scan_linrec_f32", call(_ptr(ws), ctypes.byref(have)))
     return out_b
 
@@ -395,7 +409,7 @@ def ps_linrec_lookback_stats(a, b, out_b, stats, out_a=None, inclusive=True, wor
     L = lib()
     call = lambda ws, wsb: L.ps_linrec_lookback_stats(ws, wsb, _ptr(a), _ptr(b), _ptr(out_a),  # noqa: E731
                                                       _ptr(out_b), n, int(bool(inclusive)), _ptr(stats), s)
-    ws, have = _workspace("ps_linrec_lookback_stats", call, a.device, workspace, stream)
+    ws, have = _workspace("ps_linrec_lookback_stats", call, a, workspace, stream)
     _check("ps_linrec_lookback_stats", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
@@ -409,7 +423,7 @@ def ps_lookback_stats_u32(inp, out, stats, aggregate_only=False, workspace=None,
     L = lib()
     call = lambda ws, wsb: L.ps_lookback_stats_u32(ws, wsb, _ptr(inp), _ptr(out), n,  # noqa: E731
                                                    _ptr(stats), int(bool(aggregate_only)), s)
-    ws, have = _workspace("ps_lookback_stats_u32", call, inp.device, workspace, stream)
+    ws, have = _workspace("ps_lookback_stats_u32", call, inp, workspace, stream)
     _check("ps_lookback_stats_u32", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
@@ -429,7 +443,7 @@ def ps_scan_lookback_stats(op, inclusive, inp, out, stats, workspace=None, strea
     L = lib()
     call = lambda ws, wsb: L.ps_scan_lookback_stats(ws, wsb, opc, dtype, int(bool(inclusive)),  # noqa: E731
                                                     _ptr(inp), _ptr(out), n, _ptr(stats), s)
-    ws, have = _workspace("ps_scan_lookback_stats", call, inp.device, workspace, stream)
+    ws, have = _workspace("ps_scan_lookback_stats", call, inp, workspace, stream)
     _check("ps_scan_lookback_stats", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
@@ -447,7 +461,7 @@ def ps_segmented_lookback_stats_u32(values, offsets, out, stats, inclusive=False
     L = lib()
     call = lambda ws, wsb: L.ps_segmented_lookback_stats_u32(ws, wsb, _ptr(values), n, _ptr(offsets),  # noqa
                                                              nseg, _ptr(out), int(bool(inclusive)), _ptr(stats), s)
-    ws, have = _workspace("ps_segmented_lookback_stats_u32", call, values.device, workspace, stream)
+    ws, have = _workspace("ps_segmented_lookback_stats_u32", call, values, workspace, stream)
     _check("ps_segmented_lookback_stats_u32", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
@@ -469,7 +483,7 @@ def ps_compact_lookback_stats(records, flags, out, num_selected, stats, workspac
     L = lib()
     call = lambda ws, wsb: L.ps_compact_lookback_stats(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa
                                                        _ptr(out), _ptr(num_selected), _ptr(stats), s)
-    ws, have = _workspace("ps_compact_lookback_stats", call, flags.device, workspace, stream)
+    ws, have = _workspace("ps_compact_lookback_stats", call, flags, workspace, stream)
     _check("ps_compact_lookback_stats", call(_ptr(ws), ctypes.byref(have)))
     return stats
 
@@ -493,7 +507,7 @@ def ps_segmented_scan_u32(values, offsets, out, inclusive=False, workspace=None,
     L = lib()
     call = lambda ws, wsb: L.ps_segmented_scan_u32(ws, wsb, _ptr(values), n, _ptr(offsets),  # noqa: E731
                                                    nseg, _ptr(out), int(bool(inclusive)), s)
-    ws, have = _workspace("ps_segmented_scan_u32", call, values.device, workspace, stream)
+    ws, have = _workspace("ps_segmented_scan_u32", call, values, workspace, stream)
     _check("ps_segmented_scan_u32", call(_ptr(ws), ctypes.byref(have)))
     return out
 
@@ -540,7 +554,7 @@ def _compact(fn, records, flags, out, num_selected, workspace, stream):
     f = getattr(L, fn)
     call = lambda ws, wsb: f(ws, wsb, _ptr(records), rb, _ptr(flags), n,  # noqa: E731
                              _ptr(out), _ptr(num_selected), s)
-    ws, have = _workspace(fn, call, flags.device, workspace, stream)
+    ws, have = _workspace(fn, call, flags, workspace, stream)
     _check(fn, call(_ptr(ws), ctypes.byref(have)))
     return out
 

@@ -232,6 +232,27 @@ def test_non_default_stream(dw, orc):
     assert np.array_equal(host(d_out), ref)
 
 
+def test_calls_without_a_stream_use_the_current_one(dw, orc):
+    """A call given no stream runs on the current stream of its tensors'
+    device: the handle the binding passes is the one torch.cuda.current_stream
+    names, also inside a stream context, and the call's result is exact
+    there."""
+    import torch
+    from device_wide_prefix_chained_amd import _binding as B
+    x = wl.full_range_u32(100_003, seed=6)
+    d_in = dev(x)
+    assert B._raw_stream(d_in, None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        assert B._raw_stream(d_in, None) == s.cuda_stream == torch.cuda.current_stream().cuda_stream
+        d_out = torch.empty_like(d_in)
+        dw.ps_scan_exclusive_u32(d_in, d_out)
+    s.synchronize()
+    assert np.array_equal(host(d_out), orc.scan_u32(x, "sum", False)[0])
+    assert B._raw_stream(d_in, s) == s.cuda_stream
+
+
 def test_repeated_runs_stay_exact(dw, orc):
     """Ordering races show up rarely ("Parallel Prefix Sum (Scan), in depth",
     "Failure modes"): 50 back-to-back runs at 2^24 must all be bit-exact."""
