@@ -580,6 +580,12 @@ __global__ __launch_bounds__((D + 1) * 64) void segscan_kernel(const uint32_t *v
     if (t0 < num_tiles) {
         const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, t0};
         if (wave == 0) {
+            // The control wave's own work (bracketing each tile's starts,
+            // setting their bits, the look-back) is on the path to barrier
+            // B in about half the phases, and its SIMD also runs three data
+            // waves busy with the carried-flag scan: it issues first.  (The
+            // flat scan's control wave mostly waits and gains nothing.)
+            __builtin_amdgcn_s_setprio(3);
             // only the control wave reads the sample: the data waves' first
             // loads do not wait for it
             idx.load_sample(sh.sample, lane);
