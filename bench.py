@@ -368,8 +368,8 @@ def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
     """Copy, read and write of 1 GiB in the same process, under the same two
     protocols as the workload, and the workload's ceiling: the copy of the
     same bytes where it reads as many bytes as it writes, else a plain
-    stream of its own mix (ps_stream_mix_u32: its read bytes read, its
-    written bytes written, each workgroup a share of both), and for the
+    stream of its own mix (ps_stream_mix_u32: the bytes both directions
+    have moved as a copy, the rest read or written alone), and for the
     recurrence a plain stream of its own shape (two planes read, one or two
     written, ps_stream_planes_f32).  The sum of the read time and the write
     time (`model_ms`) is reported too; it is not a ceiling: a stream that

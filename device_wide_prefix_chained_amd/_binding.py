@@ -596,8 +596,9 @@ def ps_stream_planes_f32(a, b, out_b, out_a=None, stream=None):
 
 
 def ps_stream_mix_u32(inp, out, stream=None):
-    """A plain stream that reads inp and writes out, each workgroup a
-    proportional share of both (the ceiling of a kernel with that byte mix)."""
+    """A plain stream that reads inp and writes out: the words both have
+    copied, then the rest of the longer one read or written alone (the
+    ceiling of a kernel with that byte mix)."""
     _dev_tensor("inp", inp, _U32_DTYPES)
     _dev_tensor("out", out, _U32_DTYPES)
     _check("ps_stream_mix_u32", lib().ps_stream_mix_u32(_ptr(inp), inp.numel(), _ptr(out), out.numel(),

@@ -128,32 +128,43 @@ __global__ __launch_bounds__(kStreamThreads) void planes_vec_kernel(const copy_v
         planes_block<false, BOTH>(a, b, oa, ob, base, n16);
 }
 
-// Stream of a given mix of read and written bytes: workgroup b of G reads
-// the vectors [b ni / G, (b + 1) ni / G) of in and writes the vectors
-// [b no / G, (b + 1) no / G) of out, each range at most one block of
-// kStreamBlock vectors.  Vector j of a workgroup's output range is vector j of
-// its input range (its last vector past the range's end, zero if the range
-// is empty), so every store waits for a load, as a scan's do.
+// Stream of a given mix of read and written bytes, moved the fastest plain
+// way: the vectors both sides have, [0, min(ni, no)), copied in the copy's
+// shape by the first `cb` workgroups; the rest of the longer side, from
+// min(ni, no) on, read alone (folded, as in the read stream) or written alone
+// (zeros) by the workgroups after them.  A kernel that reads and writes
+// throughout is compared with this: a copy moves its common bytes at the
+// copy's rate, the excess goes at the faster one-way rate.
+__device__ uint32_t g_mix_sink;
+
 __global__ __launch_bounds__(kStreamThreads) void mix_vec_kernel(const copy_v4u *in, uint64_t ni, copy_v4u *out,
-                                                                 uint64_t no) {
-    const uint64_t g = gridDim.x, b = blockIdx.x;
-    const uint64_t i0 = b * ni / g, ilen = (b + 1) * ni / g - i0;
-    const uint64_t o0 = b * no / g, olen = (b + 1) * no / g - o0;
-    copy_v4u r[kStreamVecs];
-    if (ilen) {
+                                                                 uint64_t no, uint64_t cb) {
+    const uint64_t both = ni < no ? ni : no;
+    const uint64_t b = blockIdx.x;
+    if (b < cb) {
+        const uint64_t base = b * kStreamBlock + threadIdx.x;
+        if ((b + 1u) * kStreamBlock <= both)
+            copy_block<true>(in, out, base, both);
+        else
+            copy_block<false>(in, out, base, both);
+        return;
+    }
+    const uint64_t start = both + (b - cb) * kStreamBlock;
+    const uint64_t base = start + threadIdx.x;
+    if (ni > no) {
+        const bool full = start + kStreamBlock <= ni;
+        copy_v4u acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < kStreamVecs; ++k) acc ^= __builtin_nontemporal_load(in + stream_index(base, k, ni, full));
+        if (acc.x == 0x9E3779B9u && acc.y == 0x7F4A7C15u && acc.z == 0xF39CC060u && acc.w == 0x5CEDC834u)
+            g_mix_sink = acc.x;
+    } else {
+        const copy_v4u z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int k = 0; k < kStreamVecs; ++k) {
-            const uint64_t j = threadIdx.x + (uint64_t)k * kStreamThreads;
-            r[k] = __builtin_nontemporal_load(in + i0 + (j < ilen ? j : ilen - 1u));
+            const uint64_t i = base + (uint64_t)k * kStreamThreads;
+            if (i < no) __builtin_nontemporal_store(z, out + i);
         }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kStreamVecs; ++k) r[k] = copy_v4u{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int k = 0; k < kStreamVecs; ++k) {
-        const uint64_t j = threadIdx.x + (uint64_t)k * kStreamThreads;
-        if (j < olen) __builtin_nontemporal_store(r[k], out + o0 + j);
     }
 }
 
@@ -375,10 +386,11 @@ extern "C" ps_status ps_stream_mix_u32(const uint32_t *in, uint64_t n_in, uint32
     if (n_in && n_out && ranges_overlap(in, n_in * 4, out, n_out * 4)) return PS_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint64_t ni = n_in / 4, no = n_out / 4;
-    const uint64_t grid = ceil_div(ni > no ? ni : no, kStreamBlock);
+    const uint64_t both = ni < no ? ni : no, rest = (ni > no ? ni : no) - both;
+    const uint64_t cb = ceil_div(both, kStreamBlock), grid = cb + ceil_div(rest, kStreamBlock);
     timing_begin(s);
     hipLaunchKernelGGL(mix_vec_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0, s,
-                       reinterpret_cast<const copy_v4u *>(in), ni, reinterpret_cast<copy_v4u *>(out), no);
+                       reinterpret_cast<const copy_v4u *>(in), ni, reinterpret_cast<copy_v4u *>(out), no, cb);
     timing_end(s);
     return launch_status();
 }

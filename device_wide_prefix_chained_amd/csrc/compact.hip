@@ -136,7 +136,22 @@ struct CompactShared {
     uint32_t wt[2][D];                 // wave counts, double-buffered by phase parity
     uint32_t next;
     uint32_t prefix;                   // output base of the tile stored in the phase
+    uint32_t close_prefix[3];          // the closing phase's output bases (closing_phase in pipeline.hpp)
 };
+
+// Copy this wave's parked run of tile `tile` (slot `slot`) to its place
+// after the output base `prefix`; the last tile's last wave also writes the
+// count.
+template <class Rec, int D, int Q>
+__device__ __forceinline__ void store_run(CompactShared<D, Q> &sh, uint32_t slot, uint32_t tile, uint32_t prefix,
+                                          Rec *out, uint64_t *num_selected, uint32_t num_tiles, uint32_t lane,
+                                          uint32_t d) {
+    const Rec *run = reinterpret_cast<const Rec *>(&sh.park[slot][(uint32_t)d * Q * 64u]);
+    const uint2 meta = sh.park_wave[slot][d];
+    const uint64_t base = (uint64_t)prefix + meta.x;
+    for (uint32_t j = lane; j < meta.y; j += 64u) __builtin_nontemporal_store(run[j], out + base + j);
+    if (tile == num_tiles - 1u && d == (uint32_t)D - 1u && lane == 0) *num_selected = base + meta.y;
+}
 
 // One phase of a data wave (the flat scan's phase, data_phase3 in scan.hip,
 // with a count as the scanned value).  Each wave parks the kept
@@ -196,12 +211,8 @@ __device__ __forceinline__ bool compact_phase3(RecSpan<Rec, Q> &hold, RecSpan<Re
     }
     __syncthreads();  // B
     Rec *mine = reinterpret_cast<Rec *>(&sh.park[slot][(uint32_t)d * Q * 64u]);
-    if (pt.prev3 < num_tiles) {
-        const uint2 meta = sh.park_wave[slot][d];
-        const uint64_t base = (uint64_t)sh.prefix + meta.x;
-        for (uint32_t j = lane; j < meta.y; j += 64u) __builtin_nontemporal_store(mine[j], out + base + j);
-        if (pt.prev3 == num_tiles - 1u && d == (uint32_t)D - 1u && lane == 0) *num_selected = base + meta.y;
-    }
+    if (pt.prev3 < num_tiles)
+        store_run<Rec, D, Q>(sh, slot, pt.prev3, sh.prefix, out, num_selected, num_tiles, lane, d);
     // park cur's kept records where prev3's were
     if (pt.cur < num_tiles) {
 #pragma unroll
@@ -223,6 +234,18 @@ __device__ __forceinline__ bool compact_phase3(RecSpan<Rec, Q> &hold, RecSpan<Re
     slot = next_slot(slot);
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);
+    if (after_closing(pt, num_tiles)) {
+        // the closing phase resolved the three parked tiles: store them all
+        // now (the control wave has left the loop; no barrier follows)
+#pragma unroll 1
+        for (int i = 0; i < 3; ++i) {
+            const uint32_t t = i == 0 ? pt.prev3 : i == 1 ? pt.prev2 : pt.prev;
+            if (t < num_tiles)
+                store_run<Rec, D, Q>(sh, closing_slot(slot, i), t, sh.close_prefix[i], out, num_selected, num_tiles,
+                                     lane, d);
+        }
+        return true;
+    }
     return false;
 }
 
@@ -299,7 +322,7 @@ __global__ __launch_bounds__((D + 1) * 64) void compact_kernel(const Rec *record
         using Fb = CompactFallback<(uint32_t)D * Q * 64u * (16u / sizeof(Rec))>;
         if (wave == 0) {
             ws_wait_clean(call, ctr);
-            control_loop3<SumU32, D, LB_K, G, STATS, false, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
+            control_loop3<SumU32, D, LB_K, G, STATS, false, true, true>(pt, sh, num_tiles, ctr, desc, (uint32_t *)nullptr,
                                                                   stats, 0, cfg, Fb{flags, n}, lane,
                                                                   STATS ? wsh.entry : 0u);
         } else {

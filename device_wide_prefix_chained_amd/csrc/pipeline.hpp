@@ -6,8 +6,8 @@
 // published after the phase's barrier B), parked in LDS, looked back for and
 // stored -- two phases after the park (LAG 2: segmented scan), or three
 // with the look-back resolved the phase before (LAG 3: flat scan,
-// compaction).  PipeTiles is the window of tile ids the workgroup works on in one
-// phase.
+// compaction; their last tiles are stored together after a closing phase).
+// PipeTiles is the window of tile ids the workgroup works on in one phase.
 #pragma once
 
 #include <stdint.h>
@@ -118,6 +118,16 @@ struct PhaseClock {
             stats[(uint64_t)kStatsWords * s + 12] = realtime32();
         }
     }
+    // a tile of the closing store step (after the last barrier): its store
+    // step's start, and for the workgroup's last tile the end
+    __device__ __forceinline__ void closing(uint32_t *stats, uint32_t s, uint32_t num_tiles, bool last,
+                                            bool writer) {
+        if (STATS && writer && s < num_tiles) {
+            const uint32_t t = realtime32();
+            stats[(uint64_t)kStatsWords * s + 9] = t;
+            if (last) stats[(uint64_t)kStatsWords * s + 12] = t;
+        }
+    }
 };
 
 // Data wave 0's view of a phase (instrumented flat scan), word 15 of the
@@ -166,6 +176,28 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
     return (f2 < num_tiles && f2 + 1u < num_tiles) ? f2 + 1u : num_tiles;
 }
 
+// The closing phase of a LAG 3 pipeline (CLOSE): the first phase with no
+// tile to load or scan.  Its control wave resolves the prefixes of all three
+// tiles still waiting (prev2, prev and cur, in that order; cur was scanned
+// in the phase before, so every aggregate they need is out), publishes
+// them, and leaves their exclusive prefixes in `close_prefix`; after its
+// barrier A both kinds of wave leave the loop and the data waves store those
+// three tiles from their park slots at once (closing_slot) instead of one
+// per phase over three more phases.  The look-backs of prev and cur run one
+// and two phases earlier than in the steady state, when a predecessor is a
+// little more likely to be unpublished: a stalled poll costs a round trip.
+__device__ __forceinline__ bool closing_phase(const PipeTiles &pt, uint32_t num_tiles) {
+    return pt.f1 >= num_tiles && pt.f2 >= num_tiles && pt.cur < num_tiles;
+}
+// After barrier A of the closing phase (the tiles advanced, `slot` moved on):
+// the park slot of prev3, prev2 and prev (i = 0, 1, 2).
+__device__ __forceinline__ uint32_t closing_slot(uint32_t slot, int i) {
+    return (slot + (uint32_t)i) % (uint32_t)kParkSlots;
+}
+__device__ __forceinline__ bool after_closing(const PipeTiles &pt, uint32_t num_tiles) {
+    return pt.cur >= num_tiles && pt.f1 >= num_tiles && pt.f2 >= num_tiles;
+}
+
 // Control wave of the LAG 3 pipeline (the data waves store prev3): the
 // look-back of prev2 is resolved one phase before its tile is stored, and
 // its poll straddles barrier B.  Per phase: hand the data waves prev3's
@@ -175,8 +207,8 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
 // f1's aggregate, and meet the data waves at barrier A.  The poll is as
 // fresh as in the two-phase pipeline (issued at the start of the phase that
 // resolves it); only its round trip moves off the path to barrier B.
-template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, bool BLOCKED = true, class Shared,
-          class FB>
+template <class Op, int D, int LB_K, int G, bool STATS, bool PAIR_PREFIX, bool BLOCKED = true, bool CLOSE = false,
+          class Shared, class FB>
 __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t num_tiles, uint32_t *ctr,
                                               uint64_t *desc, typename Op::T *total, uint32_t *stats,
                                               int aggregate_only, LookbackCfg cfg, const FB &fb, uint32_t lane,
@@ -198,6 +230,7 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
         }
         const bool have = pt.prev2 < num_tiles && pt.prev2 != 0;
         const bool look = have && (pt.prev2 % G == 0u || (STATS && aggregate_only));
+        const bool closing = CLOSE && closing_phase(pt, num_tiles);
         Window<LB_K, W::WORDS> win;
         if (look) window_load<Op, LB_K, BLOCKED>(desc, (int64_t)pt.prev2 - 1, lane, win);
         clk.reach_b();
@@ -234,6 +267,62 @@ __device__ __forceinline__ void control_loop3(PipeTiles pt, Shared &sh, uint32_t
             const bool withhold = pt.f1 != 0 && (cfg.flags & kDbgWithholdAggregates);
             if (lane == 0 && !withhold)
                 W::publish(desc, pt.f1, cfg.tf, pt.f1 == 0 ? ST_PREFIX : ST_AGGREGATE, agg_next);
+        }
+        if constexpr (CLOSE) {
+          if (closing) {
+            // prev and cur resolved now as well (see closing_phase), in one
+            // loop, so that the look-back is not inlined twice
+            T ex1 = Op::id(), ex2 = Op::id();
+            T incl = Op::op(excl, agg_prev2);  // prev2's inclusive prefix, when it exists
+#pragma unroll 1
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t u = i == 0 ? pt.prev : pt.cur;
+                const T au = i == 0 ? agg_prev : agg;
+                if (u >= num_tiles) continue;
+                const bool u_look = u != 0 && (u % G == 0u || (STATS && aggregate_only));
+                LookbackStats su;
+                uint64_t u0 = 0;
+                if (STATS) u0 = __builtin_amdgcn_s_memrealtime();
+                // a tile that is not the first of its group follows its
+                // group's previous tile in this workgroup
+                T e = Op::id();
+                if (u_look)
+                    e = lookback<Op, LB_K, STATS, BLOCKED>(desc, u, lane, su, ctr, cfg, au, true, fb);
+                else if (u != 0)
+                    e = incl;
+                if (i == 0)
+                    ex1 = e;
+                else
+                    ex2 = e;
+                incl = Op::op(e, au);
+                if (lane == 0) {
+                    if (STATS) {
+                        const uint64_t u1 = __builtin_amdgcn_s_memrealtime();
+                        reinterpret_cast<uint4 *>(stats)[(kStatsWords / 4) * u] =
+                            make_uint4(su.polls, su.windows, (uint32_t)(u1 - u0), su.stalls);
+                    }
+                    // prev's prefix went out already with prev2's (pair prefix)
+                    const bool sent = i == 0 && kPairPrefix && look && pt.prev == pt.prev2 + 1u;
+                    if (u != 0 && !sent && !(STATS && aggregate_only))
+                        W::publish(desc, u, cfg.tf, ST_PREFIX, incl);
+                    if (total && u == num_tiles - 1u) *total = incl;
+                }
+            }
+            if (total && lane == 0 && pt.prev2 == num_tiles - 1u) *total = Op::op(excl, agg_prev2);
+            if (lane == 0) {
+                sh.close_prefix[0] = excl;
+                sh.close_prefix[1] = ex1;
+                sh.close_prefix[2] = ex2;
+            }
+            clk.reach_a();
+            __syncthreads();  // A: the closing prefixes are in LDS
+            clk.record(stats, pt.f1, pt.prev3, num_tiles, t_entry, lane == 0);
+            // cur is the workgroup's last tile
+            clk.closing(stats, pt.prev2, num_tiles, false, lane == 0);
+            clk.closing(stats, pt.prev, num_tiles, false, lane == 0);
+            clk.closing(stats, pt.cur, num_tiles, true, lane == 0);
+            break;
+          }
         }
         excl_next = excl;
         incl_last = Op::op(excl, agg_prev2);

@@ -26,6 +26,9 @@
 // per workgroup are in flight while look-backs are resolved two phases
 // behind (a persistent grid-stride loop, as in "Where the algorithm meets
 // the hardware", with the look-back joining the tiles inside one launch).
+// When a workgroup runs out of tiles, its closing phase resolves the
+// prefixes of the three tiles still parked and they are stored together
+// (closing_phase in pipeline.hpp) rather than one per phase.
 // Tickets come from an atomic counter, so every tile a look-back can wait on
 // was handed out earlier to a running workgroup, which finishes it without
 // waiting on anything later ("Scanning a whole array: three grid
@@ -51,7 +54,53 @@ struct ScanShared {
     uint32_t next;
     T wt[2][D];  // wave totals, double-buffered by phase parity
     T prefix;
+    T close_prefix[3];  // the closing phase's prefixes (closing_phase in pipeline.hpp)
 };
+
+// Store tile `tile`, parked in slot `slot`, with its exclusive prefix `pre`:
+// each wave its own part of the slot.
+template <class Op, int D, int Q, bool VEC>
+__device__ __forceinline__ void store_parked(ScanShared<Op, D, Q> &sh, uint32_t slot, uint32_t tile,
+                                             typename Op::T pre, typename IoOf<Op>::Dst out, uint32_t n,
+                                             uint32_t lane, uint32_t d, uint64_t lane_off) {
+    using T = typename Op::T;
+    constexpr uint32_t TILE = (uint32_t)D * (uint32_t)Q * 256u;
+    constexpr int PW = ScanShared<Op, D, Q>::PW;
+    const v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
+    const uint64_t bp = (uint64_t)tile * TILE;
+    const bool full = bp + TILE <= n;
+    if constexpr (PW == 2 && VEC && std::is_pointer<typename IoOf<Op>::Dst>::value) {
+        if (full) {
+            // 8-byte outputs read back regrouped (see data_phase)
+            const v4u *wp = &sh.park[slot][(uint32_t)d * Q * PW * 64u];
+            T *row = out + bp + (uint64_t)d * Q * 256u + 2u * lane;
+#pragma unroll
+            for (int q = 0; q < Q; ++q)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const v4u w = wp[(q * 2 + (int)(lane & 1u)) * 64 + h * 32 + (int)(lane >> 1)];
+                    const uint64_t a = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.y << 32) | w.x)));
+                    const uint64_t b = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.w << 32) | w.z)));
+                    v4u r;
+                    r.x = (uint32_t)a;
+                    r.y = (uint32_t)(a >> 32);
+                    r.z = (uint32_t)b;
+                    r.w = (uint32_t)(b >> 32);
+                    store16(row + q * 256 + h * 128, r);
+                }
+            return;
+        }
+    }
+    WaveSpan<Op, Q> old;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        v4u w[PW];
+#pragma unroll
+        for (int h = 0; h < PW; ++h) w[h] = mine[(q * PW + h) * 64];
+        unpack16<T>(w, old.v[q]);
+    }
+    store_final<Op, Q, VEC>(old, pre, out, bp + lane_off, n, full);
+}
 
 // One phase of a data wave.  A tile is stored three phases after its park:
 // cur is finalized (made tile-relative) in registers at the start of the
@@ -105,45 +154,7 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     __syncthreads();  // B
     clk.leave_b();
     v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
-    if (pt.prev3 < num_tiles) {
-        const uint64_t bp = (uint64_t)pt.prev3 * TILE;
-        const bool full = bp + TILE <= n;
-        bool stored = false;
-        if constexpr (PW == 2 && VEC && std::is_pointer<typename IoOf<Op>::Dst>::value) {
-            if (full) {
-                // 8-byte outputs read back regrouped (see data_phase)
-                const v4u *wp = &sh.park[slot][(uint32_t)d * Q * PW * 64u];
-                T *row = out + bp + (uint64_t)d * Q * 256u + 2u * lane;
-                const T pre = sh.prefix;
-#pragma unroll
-                for (int q = 0; q < Q; ++q)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const v4u w = wp[(q * 2 + (int)(lane & 1u)) * 64 + h * 32 + (int)(lane >> 1)];
-                        const uint64_t a = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.y << 32) | w.x)));
-                        const uint64_t b = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.w << 32) | w.z)));
-                        v4u r;
-                        r.x = (uint32_t)a;
-                        r.y = (uint32_t)(a >> 32);
-                        r.z = (uint32_t)b;
-                        r.w = (uint32_t)(b >> 32);
-                        store16(row + q * 256 + h * 128, r);
-                    }
-                stored = true;
-            }
-        }
-        if (!stored) {
-            WaveSpan<Op, Q> old;
-#pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                v4u w[PW];
-#pragma unroll
-                for (int h = 0; h < PW; ++h) w[h] = mine[(q * PW + h) * 64];
-                unpack16<T>(w, old.v[q]);
-            }
-            store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, full);
-        }
-    }
+    if (pt.prev3 < num_tiles) store_parked<Op, D, Q, VEC>(sh, slot, pt.prev3, sh.prefix, out, n, lane, d, lane_off);
     clk.store_done();
     // park cur where prev3 was
     if (pt.cur < num_tiles) {
@@ -161,6 +172,18 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     clk.reach_a(stats, pt.f1, num_tiles, d == 0 && lane == 0);
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);
+    if (after_closing(pt, num_tiles)) {
+        // the closing phase resolved the three parked tiles: store them all
+        // now (the control wave has left the loop; no barrier follows)
+#pragma unroll 1
+        for (int i = 0; i < 3; ++i) {
+            const uint32_t t = i == 0 ? pt.prev3 : i == 1 ? pt.prev2 : pt.prev;
+            if (t < num_tiles)
+                store_parked<Op, D, Q, VEC>(sh, closing_slot(slot, i), t, sh.close_prefix[i], out, n, lane, d,
+                                            lane_off);
+        }
+        return true;
+    }
     return false;
 }
 
@@ -241,7 +264,7 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
         const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, t0};
         if (wave == 0) {
             ws_wait_clean(call, hdr);
-            control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1>(
+            control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1, true, true>(
                 pt, sh, num_tiles, hdr, desc, total, stats, aggregate_only, cfg,
                 FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane, STATS ? wsh.entry : 0u);
         } else {

@@ -186,7 +186,10 @@ __device__ __forceinline__ void wave_seg_inclusive(uint32_t &f, uint32_t &v) {
 #endif
 constexpr int kSegD = DWPS_SEG_D;
 constexpr int kSegQ = DWPS_SEG_Q;
-constexpr int kSegG = 2;  // tiles claimed per ticket
+#ifndef DWPS_SEG_G
+#define DWPS_SEG_G 2
+#endif
+constexpr int kSegG = DWPS_SEG_G;  // tiles claimed per ticket
 constexpr int kSegThreads = (kSegD + 1) * 64;
 constexpr uint32_t kSegTile = (uint32_t)kSegD * kSegQ * 256u;
 constexpr uint32_t kSegWords = kSegTile / 32u;  // bitmap words per tile

@@ -394,13 +394,11 @@ ps_status ps_stream_planes_f32(const float *a, const float *b, float *out_a, flo
                                uint64_t n, void *stream);
 
 /* A plain stream with a given mix of read and written bytes, the practical
- * ceiling of a kernel that reads n_in uint32 and writes n_out: the grid's G
- * = ceil(max(n_in, n_out) / 4096) workgroups each read a share of in and
- * write the same share of out, with the copy's access shape.  Workgroup b
- * reads the 16-byte vectors [b ni / G, (b + 1) ni / G) of in (ni = n_in / 4)
- * and writes the vectors [b no / G, (b + 1) no / G) of out (no = n_out / 4);
- * its output vector j is its input vector min(j, last), zero when its input
- * range is empty.  Arrays 16-byte aligned and n_in, n_out multiples of 4,
+ * ceiling of a kernel that reads n_in uint32 and writes n_out: the 16-byte
+ * vectors both sides have (the first min(n_in, n_out) / 4) are copied in the
+ * copy's access shape, then the rest of the longer side is read alone or
+ * written alone.  out receives in's first min(n_in, n_out) words, then
+ * zeros up to n_out.  Arrays 16-byte aligned and n_in, n_out multiples of 4,
  * else PS_ERR_ALIGNMENT; in and out overlapping: PS_ERR_ALIAS. */
 ps_status ps_stream_mix_u32(const uint32_t *in, uint64_t n_in, uint32_t *out, uint64_t n_out,
                             void *stream);
