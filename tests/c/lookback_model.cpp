@@ -29,7 +29,10 @@
 // row the wave reduces the stalled predecessor itself and installs its
 // descriptor with a compare-and-swap over a word it read as unpublished.
 // The segmented form: a tile holding a segment start publishes PREFIX at
-// once and looks back only if its first element starts no segment.
+// once and looks back only if its first element starts no segment.  With
+// close=1 a workgroup that has no tile left to scan resolves the three
+// tiles still waiting (prev2, prev and cur) in one step, in order, and
+// stops -- the closing phase of the three-phase kernels.
 //
 // Checked: every descriptor a look-back accepts states a true fact about
 // its tile (its payload is the fold its state claims), every exclusive
@@ -40,7 +43,7 @@
 // words hold what earlier calls left: other tags, any state, any payload.
 //
 // Arguments key=value: words op tiles wgs resident G win partial fallback
-// pair persistent tickets withhold order(asc|desc|random) p_fresh seeds seed
+// pair persistent tickets withhold close order(asc|desc|random) p_fresh seeds seed
 // broken(torn|no_tag|partial_distance|skip_invalid) expect(ok|deadlock|
 // violation).  Exit 0 when the outcome is the expected one.
 #include <stdint.h>
@@ -95,7 +98,7 @@ struct Config {
     int words = 1;
     OpKind op = OpKind::Affine16;
     uint32_t tiles = 300, wgs = 12, resident = 12, G = 2, win = 4, partial = 1, fallback = 0;
-    bool pair = true, persistent = true, tickets = true, withhold = false;
+    bool pair = true, persistent = true, tickets = true, withhold = false, close = false;
     std::string order = "random";
     double p_fresh = 0.5;
     uint64_t seed = 1;
@@ -105,12 +108,14 @@ struct Config {
 
 struct Counts {
     long steps = 0, loads = 0, stale = 0, stale_tag = 0, torn = 0, mixed = 0, partial_pubs = 0, partial_jumps = 0,
-         fallbacks = 0, cas_won = 0, cas_lost = 0, skipped_install = 0, stalls = 0, windows = 0, deadlocks = 0;
+         fallbacks = 0, cas_won = 0, cas_lost = 0, skipped_install = 0, stalls = 0, windows = 0, deadlocks = 0,
+         closings = 0, closing_lookbacks = 0;
     void add(const Counts &o) {
         steps += o.steps, loads += o.loads, stale += o.stale, stale_tag += o.stale_tag, torn += o.torn;
         mixed += o.mixed, partial_pubs += o.partial_pubs, partial_jumps += o.partial_jumps;
         fallbacks += o.fallbacks, cas_won += o.cas_won, cas_lost += o.cas_lost;
         skipped_install += o.skipped_install, stalls += o.stalls, windows += o.windows, deadlocks += o.deadlocks;
+        closings += o.closings, closing_lookbacks += o.closing_lookbacks;
     }
 };
 
@@ -291,155 +296,163 @@ Proc workgroup(Model &m, uint32_t w) {
                 after = head(group);
             }
         }
-        // prev2: its exclusive prefix, by look-back or from the tile before
-        const bool have = prev2 < N && prev2 != 0;
-        const bool sp2 = have && op.self_prefix(m.agg[prev2]);
-        const bool look = have && prev2 % G == 0u && !(sp2 && m.first_start[prev2]);
-        uint64_t excl = op.id();
-        bool known = prev2 < N;
-        if (look) {
-            const uint32_t t = prev2;
-            const uint64_t own = m.agg[t];
-            const bool may_publish = !sp2;
-            uint64_t acc = op.id();
-            int64_t nearest = (int64_t)t - 1;
-            uint32_t stalled = 0, walked = 0;
-            long spins = 0;
-            for (;;) {
-                const int64_t base = nearest - (int64_t)c.win + 1;
-                for (uint32_t j = 0; j < c.win; ++j) {
-                    const int64_t i = base + (int64_t)j;
-                    if (i < 0) {
-                        sw[j] = ST_PREFIX;
-                        val[j] = op.id();
+        // the closing step: nothing left to scan, so prev and cur are
+        // resolved now as well, in order, after prev2
+        const bool closing = c.close && f1 >= N && f2 >= N && cur < N;
+        if (closing) m.n.closings++;
+        for (int r = 0; r < (closing ? 3 : 1); ++r) {
+            const uint32_t t = r == 0 ? prev2 : r == 1 ? prev : cur;
+            const uint32_t nxt = r == 0 ? prev : r == 1 ? cur : f1;  // the workgroup's next tile
+            // t: its exclusive prefix, by look-back or from the tile before
+            const bool have = t < N && t != 0;
+            const bool sp2 = have && op.self_prefix(m.agg[t]);
+            const bool look = have && t % G == 0u && !(sp2 && m.first_start[t]);
+            if (look && r > 0) m.n.closing_lookbacks++;
+            uint64_t excl = op.id();
+            bool known = t < N;
+            if (look) {
+                const uint64_t own = m.agg[t];
+                const bool may_publish = !sp2;
+                uint64_t acc = op.id();
+                int64_t nearest = (int64_t)t - 1;
+                uint32_t stalled = 0, walked = 0;
+                long spins = 0;
+                for (;;) {
+                    const int64_t base = nearest - (int64_t)c.win + 1;
+                    for (uint32_t j = 0; j < c.win; ++j) {
+                        const int64_t i = base + (int64_t)j;
+                        if (i < 0) {
+                            sw[j] = ST_PREFIX;
+                            val[j] = op.id();
+                            continue;
+                        }
+                        YIELD;
+                        uint32_t s0 = 0, s1 = 0;
+                        const uint64_t r0 = m.load(w, m.word((uint32_t)i, 0), &s0);
+                        uint64_t r1 = 0;
+                        if (c.words == 2) {
+                            YIELD;
+                            r1 = m.load(w, m.word((uint32_t)i, 1), &s1);
+                        }
+                        const uint32_t a0 = m.seen_state(r0);
+                        uint32_t st = a0;
+                        uint64_t v = r0 & 0xFFFFFFFFu;
+                        if (c.words == 2) {
+                            const uint32_t a1 = m.seen_state(r1);
+                            if (a0 != a1) {
+                                m.n.torn++;
+                                if (c.broken != "torn") st = ST_INVALID;
+                            } else if (a0 != ST_INVALID && s0 != s1) {
+                                m.n.mixed++;  // halves of two publications of one state word
+                            }
+                            v |= (r1 & 0xFFFFFFFFu) << 32;
+                        }
+                        if ((st & 3u) != ST_INVALID && !m.fact((uint32_t)i, st, v)) m.violation("false descriptor read", i, t);
+                        sw[j] = st;
+                        val[j] = v;
+                    }
+                    // the nearest PREFIX/PARTIAL word, and an INVALID one nearer than it
+                    int js = -1, ji = -1;
+                    for (int j = 0; j < (int)c.win; ++j)
+                        if ((sw[j] & 3u) >= ST_PREFIX) js = j;
+                    for (int j = js + 1; j < (int)c.win; ++j)
+                        if ((sw[j] & 3u) == ST_INVALID) ji = j;
+                    if (c.broken == "skip_invalid") ji = -1;
+                    if (ji >= 0) {
+                        m.n.stalls++;
+                        m.waiting[w] = 1;
+                        if (c.fallback && ++stalled >= c.fallback) {
+                            // reduce the predecessor from its input, install over a word read as unpublished
+                            m.waiting[w] = 0;
+                            const uint32_t p = (uint32_t)(base + ji);
+                            const bool pre = p == 0 || op.self_prefix(m.agg[p]);
+                            const uint32_t dsw = pre ? ST_PREFIX : ST_AGGREGATE;
+                            const uint64_t dv = pre ? m.incl[p] : m.agg[p];
+                            const uint32_t pub = ++m.pubs;
+                            m.n.fallbacks++;
+                            for (int k = 0; k < c.words; ++k) {
+                                YIELD;
+                                const uint64_t old = m.load(w, m.word(p, k), nullptr);
+                                if (state_seen((uint32_t)(old >> 32), m.tf) != ST_INVALID) {
+                                    m.n.skipped_install++;
+                                    continue;
+                                }
+                                YIELD;
+                                if (m.cas(w, m.word(p, k), old, m.encode(dsw, dv, k), pub))
+                                    m.n.cas_won++;
+                                else
+                                    m.n.cas_lost++;
+                            }
+                            stalled = 0;
+                            continue;
+                        }
+                        if (++spins > 2000000) {
+                            m.violation("spin limit", t, nearest);
+                            break;
+                        }
                         continue;
                     }
-                    YIELD;
-                    uint32_t s0 = 0, s1 = 0;
-                    const uint64_t r0 = m.load(w, m.word((uint32_t)i, 0), &s0);
-                    uint64_t r1 = 0;
-                    if (c.words == 2) {
-                        YIELD;
-                        r1 = m.load(w, m.word((uint32_t)i, 1), &s1);
+                    m.waiting[w] = 0;
+                    stalled = 0;
+                    spins = 0;
+                    uint64_t f = op.id();
+                    for (int j = js >= 0 ? js : 0; j < (int)c.win; ++j) f = op.op(f, val[j]);
+                    acc = op.op(f, acc);
+                    m.n.windows++;
+                    if (js >= 0) {
+                        if ((sw[js] & 3u) == ST_PREFIX) break;
+                        uint32_t d = sw[js] >> kDistShift;
+                        if (c.broken == "partial_distance") d -= 1u;
+                        nearest = base + js - (int64_t)d;
+                        m.n.partial_jumps++;
+                    } else {
+                        nearest = base - 1;
                     }
-                    const uint32_t a0 = m.seen_state(r0);
-                    uint32_t st = a0;
-                    uint64_t v = r0 & 0xFFFFFFFFu;
-                    if (c.words == 2) {
-                        const uint32_t a1 = m.seen_state(r1);
-                        if (a0 != a1) {
-                            m.n.torn++;
-                            if (c.broken != "torn") st = ST_INVALID;
-                        } else if (a0 != ST_INVALID && s0 != s1) {
-                            m.n.mixed++;  // halves of two publications of one state word
-                        }
-                        v |= (r1 & 0xFFFFFFFFu) << 32;
-                    }
-                    if ((st & 3u) != ST_INVALID && !m.fact((uint32_t)i, st, v)) m.violation("false descriptor read", i, t);
-                    sw[j] = st;
-                    val[j] = v;
-                }
-                // the nearest PREFIX/PARTIAL word, and an INVALID one nearer than it
-                int js = -1, ji = -1;
-                for (int j = 0; j < (int)c.win; ++j)
-                    if ((sw[j] & 3u) >= ST_PREFIX) js = j;
-                for (int j = js + 1; j < (int)c.win; ++j)
-                    if ((sw[j] & 3u) == ST_INVALID) ji = j;
-                if (c.broken == "skip_invalid") ji = -1;
-                if (ji >= 0) {
-                    m.n.stalls++;
-                    m.waiting[w] = 1;
-                    if (c.fallback && ++stalled >= c.fallback) {
-                        // reduce the predecessor from its input, install over a word read as unpublished
-                        m.waiting[w] = 0;
-                        const uint32_t p = (uint32_t)(base + ji);
-                        const bool pre = p == 0 || op.self_prefix(m.agg[p]);
-                        const uint32_t dsw = pre ? ST_PREFIX : ST_AGGREGATE;
-                        const uint64_t dv = pre ? m.incl[p] : m.agg[p];
+                    if (nearest < 0) break;
+                    if (c.partial && ++walked >= c.partial && may_publish) {
+                        const uint32_t psw = ((uint32_t)((int64_t)t - nearest) << kDistShift) | ST_PARTIAL;
+                        const uint64_t pv = op.op(acc, own);
+                        if (!m.fact(t, psw, pv)) m.violation("false PARTIAL published", t, nearest);
                         const uint32_t pub = ++m.pubs;
-                        m.n.fallbacks++;
                         for (int k = 0; k < c.words; ++k) {
                             YIELD;
-                            const uint64_t old = m.load(w, m.word(p, k), nullptr);
-                            if (state_seen((uint32_t)(old >> 32), m.tf) != ST_INVALID) {
-                                m.n.skipped_install++;
-                                continue;
-                            }
-                            YIELD;
-                            if (m.cas(w, m.word(p, k), old, m.encode(dsw, dv, k), pub))
-                                m.n.cas_won++;
-                            else
-                                m.n.cas_lost++;
+                            m.store(w, m.word(t, k), m.encode(psw, pv, k), pub);
                         }
-                        stalled = 0;
-                        continue;
+                        m.n.partial_pubs++;
                     }
-                    if (++spins > 2000000) {
-                        m.violation("spin limit", t, nearest);
-                        break;
-                    }
-                    continue;
                 }
-                m.waiting[w] = 0;
-                stalled = 0;
-                spins = 0;
-                uint64_t f = op.id();
-                for (int j = js >= 0 ? js : 0; j < (int)c.win; ++j) f = op.op(f, val[j]);
-                acc = op.op(f, acc);
-                m.n.windows++;
-                if (js >= 0) {
-                    if ((sw[js] & 3u) == ST_PREFIX) break;
-                    uint32_t d = sw[js] >> kDistShift;
-                    if (c.broken == "partial_distance") d -= 1u;
-                    nearest = base + js - (int64_t)d;
-                    m.n.partial_jumps++;
-                } else {
-                    nearest = base - 1;
+                excl = acc;
+            } else if (have && t % G != 0u) {
+                excl = incl_last;  // the tile before, resolved a phase (or a moment) ago
+            } else if (have) {
+                known = false;  // a head whose first element starts a segment needs no carry
+            }
+            if (t < N) {
+                if (known) {
+                    m.result[t] = excl;
+                    m.has_result[t] = 1;
                 }
-                if (nearest < 0) break;
-                if (c.partial && ++walked >= c.partial && may_publish) {
-                    const uint32_t psw = ((uint32_t)((int64_t)t - nearest) << kDistShift) | ST_PARTIAL;
-                    const uint64_t pv = op.op(acc, own);
-                    if (!m.fact(t, psw, pv)) m.violation("false PARTIAL published", t, nearest);
+                if (have && !sp2) {
+                    // its inclusive prefix (the second of a pair may have gone out a phase ago)
+                    const bool early = c.pair && t % G != 0u && t - 1u != 0u;
                     const uint32_t pub = ++m.pubs;
-                    for (int k = 0; k < c.words; ++k) {
-                        YIELD;
-                        m.store(w, m.word(t, k), m.encode(psw, pv, k), pub);
-                    }
-                    m.n.partial_pubs++;
-                }
-            }
-            excl = acc;
-        } else if (have && prev2 % G != 0u) {
-            excl = incl_last;  // the tile before, resolved a phase ago
-        } else if (have) {
-            known = false;  // a head whose first element starts a segment needs no carry
-        }
-        if (prev2 < N) {
-            if (known) {
-                m.result[prev2] = excl;
-                m.has_result[prev2] = 1;
-            }
-            if (have && !sp2) {
-                // its inclusive prefix (the second of a pair may have gone out a phase ago)
-                const bool early = c.pair && prev2 % G != 0u && prev2 - 1u != 0u;
-                const uint32_t pub = ++m.pubs;
-                const uint64_t p2 = op.op(excl, m.agg[prev2]);
-                if (!early)
-                    for (int k = 0; k < c.words; ++k) {
-                        YIELD;
-                        m.store(w, m.word(prev2, k), m.encode(ST_PREFIX, p2, k), pub);
-                    }
-                if (c.pair && look && prev == prev2 + 1u && prev < N) {
-                    const uint32_t pub2 = ++m.pubs;
-                    const uint64_t p1 = op.op(p2, m.agg[prev]);
-                    for (int k = 0; k < c.words; ++k) {
-                        YIELD;
-                        m.store(w, m.word(prev, k), m.encode(ST_PREFIX, p1, k), pub2);
+                    const uint64_t p2 = op.op(excl, m.agg[t]);
+                    if (!early)
+                        for (int k = 0; k < c.words; ++k) {
+                            YIELD;
+                            m.store(w, m.word(t, k), m.encode(ST_PREFIX, p2, k), pub);
+                        }
+                    if (c.pair && look && nxt == t + 1u && nxt < N) {
+                        const uint32_t pub2 = ++m.pubs;
+                        const uint64_t p1 = op.op(p2, m.agg[nxt]);
+                        for (int k = 0; k < c.words; ++k) {
+                            YIELD;
+                            m.store(w, m.word(nxt, k), m.encode(ST_PREFIX, p1, k), pub2);
+                        }
                     }
                 }
+                incl_last = op.op(excl, m.agg[t]);
             }
-            incl_last = op.op(excl, m.agg[prev2]);
         }
         // f1's aggregate (a tile with its own prefix publishes that)
         if (f1 < N) {
@@ -453,7 +466,7 @@ Proc workgroup(Model &m, uint32_t w) {
                 }
             }
         }
-        if (prev2 >= N && prev >= N && cur >= N && f1 >= N && f2 >= N) break;
+        if (closing || (prev2 >= N && prev >= N && cur >= N && f1 >= N && f2 >= N)) break;
         prev2 = prev;
         prev = cur;
         cur = f1;
@@ -552,6 +565,7 @@ bool parse(Config &c, const char *a) {
     else if (k == "persistent") c.persistent = x != 0;
     else if (k == "tickets") c.tickets = x != 0;
     else if (k == "withhold") c.withhold = x != 0;
+    else if (k == "close") c.close = x != 0;
     else if (k == "order") c.order = v;
     else if (k == "p_fresh") c.p_fresh = atof(v.c_str());
     else if (k == "seed") c.seed = (uint64_t)x;
@@ -590,10 +604,11 @@ int main(int argc, char **argv) {
     }
     printf("schedules %d: ok %d, deadlock %d, violation %d | steps %ld, loads %ld (stale %ld), words of "
            "earlier calls %ld, torn reads %ld, mixed reads %ld, stalls %ld, windows %ld, PARTIAL published %ld, "
-           "PARTIAL jumps %ld, fallbacks %ld (installs won %ld, lost %ld, skipped %ld)\n",
+           "PARTIAL jumps %ld, fallbacks %ld (installs won %ld, lost %ld, skipped %ld), closing steps %ld, "
+           "closing lookbacks %ld\n",
            c.seeds, ok, dead, bad, total.steps, total.loads, total.stale, total.stale_tag, total.torn, total.mixed,
            total.stalls, total.windows, total.partial_pubs, total.partial_jumps, total.fallbacks, total.cas_won,
-           total.cas_lost, total.skipped_install);
+           total.cas_lost, total.skipped_install, total.closings, total.closing_lookbacks);
     if (c.expect == "ok") return (ok == c.seeds) ? 0 : 1;
     if (c.expect == "deadlock") return (dead == c.seeds) ? 0 : 1;
     return bad > 0 ? 0 : 1;  // expect=violation: a broken rule must be caught

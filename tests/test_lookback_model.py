@@ -10,7 +10,8 @@ one seen ("Single-Pass Prefix Scan with Decoupled Look-Back", sections
 
 With ticket-ordered tiles every schedule terminates with every exclusive
 prefix exact, for one-word and two-word descriptors, PARTIAL jumps,
-fallbacks racing the owners' own stores, and words left by earlier calls.
+fallbacks racing the owners' own stores, words left by earlier calls, and
+the closing step in which a workgroup resolves its last three tiles.
 With tiles in a fixed order and fewer resident slots than workgroups,
 dispatched highest index first, every schedule deadlocks unless the
 fallback is on.  Each rule of the protocol, broken on purpose in the model,
@@ -115,6 +116,18 @@ def test_tickets_terminate_with_few_slots(model):
     # belong to workgroups that started earlier
     rc, c = run(model, *ONE, "persistent=0", "tickets=1", "wgs=150", "resident=8", "order=desc", "seeds=5")
     assert rc == 0 and c["ok"] == 5 and c["fallbacks"] == 0
+
+
+@pytest.mark.parametrize("base", [ONE, TWO, ["words=1", "op=affine16", "pair=0"]])
+def test_closing_step_keeps_prefixes_exact(model, base):
+    # the closing phase of the three-phase kernels (flat scans with and
+    # without pair prefixes, two-word descriptors, compaction): a workgroup
+    # with nothing left to scan resolves prev2, prev and cur in one step,
+    # the look-backs of prev and cur earlier than in the steady state
+    for extra in ([], ["fallback=1", "withhold=1"]):
+        rc, c = run(model, *base, "close=1", "seeds=20", *extra)
+        assert rc == 0 and c["ok"] == 20 and c["violation"] == 0, extra
+        assert c["closing steps"] > 0 and c["closing lookbacks"] > 0
 
 
 @pytest.mark.parametrize("broken,base", [("torn", TWO), ("no_tag", ONE), ("partial_distance", ONE),
