@@ -6,7 +6,8 @@
 // published after the phase's barrier B), parked in LDS, looked back for and
 // stored -- two phases after the park (LAG 2: segmented scan), or three
 // with the look-back resolved the phase before (LAG 3: flat scan,
-// compaction; their last tiles are stored together after a closing phase).
+// compaction; in compaction and the two-word flat kernels the last tiles
+// are stored together after a closing phase).
 // PipeTiles is the window of tile ids the workgroup works on in one phase.
 #pragma once
 
@@ -176,8 +177,10 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
     return (f2 < num_tiles && f2 + 1u < num_tiles) ? f2 + 1u : num_tiles;
 }
 
-// The closing phase of a LAG 3 pipeline (CLOSE): the first phase with no
-// tile to load or scan.  Its control wave resolves the prefixes of all three
+// The closing phase of a LAG 3 pipeline built with CLOSE (its data waves
+// must be built to match: they store after it when after_closing holds):
+// the first phase with no tile to load or scan.  Its control wave resolves
+// the prefixes of all three
 // tiles still waiting (prev2, prev and cur, in that order; cur was scanned
 // in the phase before, so every aggregate they need is out), publishes
 // them, and leaves their exclusive prefixes in `close_prefix`; after its

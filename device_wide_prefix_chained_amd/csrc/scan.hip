@@ -26,9 +26,10 @@
 // per workgroup are in flight while look-backs are resolved two phases
 // behind (a persistent grid-stride loop, as in "Where the algorithm meets
 // the hardware", with the look-back joining the tiles inside one launch).
-// When a workgroup runs out of tiles, its closing phase resolves the
-// prefixes of the three tiles still parked and they are stored together
-// (closing_phase in pipeline.hpp) rather than one per phase.
+// In the two-word kernels, a workgroup that runs out of tiles ends with a
+// closing phase that resolves the prefixes of the three tiles still parked,
+// and they are stored together (closing_phase in pipeline.hpp) rather than
+// one per phase.
 // Tickets come from an atomic counter, so every tile a look-back can wait on
 // was handed out earlier to a running workgroup, which finishes it without
 // waiting on anything later ("Scanning a whole array: three grid
@@ -58,7 +59,8 @@ struct ScanShared {
 };
 
 // Store tile `tile`, parked in slot `slot`, with its exclusive prefix `pre`:
-// each wave its own part of the slot.
+// each wave its own part of the slot (the closing phase's stores; the
+// steady-state store in data_phase3 is the same code inline).
 template <class Op, int D, int Q, bool VEC>
 __device__ __forceinline__ void store_parked(ScanShared<Op, D, Q> &sh, uint32_t slot, uint32_t tile,
                                              typename Op::T pre, typename IoOf<Op>::Dst out, uint32_t n,
@@ -114,7 +116,7 @@ __device__ __forceinline__ void store_parked(ScanShared<Op, D, Q> &sh, uint32_t 
 // loads and keeps two tiles in flight.  Data wave 0 also takes the tickets:
 // the atomic goes out at the start of the phase, ahead of the wave's tile
 // loads, and its value is needed only after barrier B.
-template <class Op, int D, int Q, int G, bool INCL, bool VEC, bool STATS>
+template <class Op, int D, int Q, int G, bool INCL, bool VEC, bool STATS, bool CLOSE>
 __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, Q> &sc, WaveSpan<Op, Q> &ld, int par,
                                             uint32_t &slot, PipeTiles &pt, typename Op::T (&lane_excl)[Q],
                                             typename Op::T (&row_prefix)[Q], ScanShared<Op, D, Q> &sh,
@@ -154,7 +156,45 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     __syncthreads();  // B
     clk.leave_b();
     v4u *mine = &sh.park[slot][(uint32_t)d * Q * PW * 64u + lane];
-    if (pt.prev3 < num_tiles) store_parked<Op, D, Q, VEC>(sh, slot, pt.prev3, sh.prefix, out, n, lane, d, lane_off);
+    if (pt.prev3 < num_tiles) {
+        const uint64_t bp = (uint64_t)pt.prev3 * TILE;
+        const bool full = bp + TILE <= n;
+        bool stored = false;
+        if constexpr (PW == 2 && VEC && std::is_pointer<typename IoOf<Op>::Dst>::value) {
+            if (full) {
+                // 8-byte outputs read back regrouped (see data_phase)
+                const v4u *wp = &sh.park[slot][(uint32_t)d * Q * PW * 64u];
+                T *row = out + bp + (uint64_t)d * Q * 256u + 2u * lane;
+                const T pre = sh.prefix;
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const v4u w = wp[(q * 2 + (int)(lane & 1u)) * 64 + h * 32 + (int)(lane >> 1)];
+                        const uint64_t a = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.y << 32) | w.x)));
+                        const uint64_t b = to_bits64(Op::op(pre, from_bits64<T>(((uint64_t)w.w << 32) | w.z)));
+                        v4u r;
+                        r.x = (uint32_t)a;
+                        r.y = (uint32_t)(a >> 32);
+                        r.z = (uint32_t)b;
+                        r.w = (uint32_t)(b >> 32);
+                        store16(row + q * 256 + h * 128, r);
+                    }
+                stored = true;
+            }
+        }
+        if (!stored) {
+            WaveSpan<Op, Q> old;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                v4u w[PW];
+#pragma unroll
+                for (int h = 0; h < PW; ++h) w[h] = mine[(q * PW + h) * 64];
+                unpack16<T>(w, old.v[q]);
+            }
+            store_final<Op, Q, VEC>(old, sh.prefix, out, bp + lane_off, n, full);
+        }
+    }
     clk.store_done();
     // park cur where prev3 was
     if (pt.cur < num_tiles) {
@@ -172,7 +212,7 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     clk.reach_a(stats, pt.f1, num_tiles, d == 0 && lane == 0);
     __syncthreads();  // A
     pt.advance(uniform(sh.next), num_tiles);
-    if (after_closing(pt, num_tiles)) {
+    if (CLOSE && after_closing(pt, num_tiles)) {
         // the closing phase resolved the three parked tiles: store them all
         // now (the control wave has left the loop; no barrier follows)
 #pragma unroll 1
@@ -187,7 +227,7 @@ __device__ __forceinline__ bool data_phase3(WaveSpan<Op, Q> &hold, WaveSpan<Op, 
     return false;
 }
 
-template <class Op, int D, int Q, int G, bool INCL, bool VEC, bool STATS>
+template <class Op, int D, int Q, int G, bool INCL, bool VEC, bool STATS, bool CLOSE>
 __device__ __forceinline__ void data_loop3(PipeTiles pt, ScanShared<Op, D, Q> &sh, typename IoOf<Op>::Src in,
                                            typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *ctr,
                                            uint32_t lane, uint32_t d, uint32_t *stats) {
@@ -201,15 +241,15 @@ __device__ __forceinline__ void data_loop3(PipeTiles pt, ScanShared<Op, D, Q> &s
     uint32_t slot = 0;
     int par = 0;
     for (;;) {
-        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS>(x, y, z, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS, CLOSE>(x, y, z, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
                                                 num_tiles, ctr, lane, d, lane_off, stats))
             break;
         par ^= 1;
-        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS>(y, z, x, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS, CLOSE>(y, z, x, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
                                                 num_tiles, ctr, lane, d, lane_off, stats))
             break;
         par ^= 1;
-        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS>(z, x, y, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
+        if (data_phase3<Op, D, Q, G, INCL, VEC, STATS, CLOSE>(z, x, y, par, slot, pt, lane_excl, row_prefix, sh, in, out, n,
                                                 num_tiles, ctr, lane, d, lane_off, stats))
             break;
         par ^= 1;
@@ -249,6 +289,17 @@ struct FlatFallback {
     }
 };
 
+// Whether a flat kernel ends with the closing phase (closing_phase in
+// pipeline.hpp).  Two-word kernels (the widening scan, the recurrence) do:
+// 528.3 -> 526.7 us for the widening scan at 2^28.  One-word ones do not:
+// their last stores are bound by the write bandwidth, and the u32 scan at
+// 2^28 ran about 1 us slower with the closing code in the kernel, also with
+// the closing switched off at run time.
+template <class Op>
+constexpr bool flat_close() {
+    return WordsFor<Op>::WORDS == 2;
+}
+
 template <class Op, int D, int Q, int LB_K, int G, bool INCL, bool VEC, bool STATS>
 __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
     typename IoOf<Op>::Src in, typename IoOf<Op>::Dst out, uint32_t n, uint32_t num_tiles, uint32_t *hdr,
@@ -264,11 +315,12 @@ __global__ __launch_bounds__((D + 1) * 64) void chained_scan_kernel(
         const PipeTiles pt{num_tiles, num_tiles, num_tiles, num_tiles, num_tiles, t0};
         if (wave == 0) {
             ws_wait_clean(call, hdr);
-            control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1, true, true>(
+            control_loop3<Op, D, LB_K, G, STATS, WordsFor<Op>::WORDS == 1, true, flat_close<Op>()>(
                 pt, sh, num_tiles, hdr, desc, total, stats, aggregate_only, cfg,
                 FlatFallback<Op, (uint32_t)D * Q * 256u>{in, n}, lane, STATS ? wsh.entry : 0u);
         } else {
-            data_loop3<Op, D, Q, G, INCL, VEC, STATS>(pt, sh, in, out, n, num_tiles, hdr, lane, wave - 1, stats);
+            data_loop3<Op, D, Q, G, INCL, VEC, STATS, flat_close<Op>()>(pt, sh, in, out, n, num_tiles, hdr, lane,
+                                                                        wave - 1, stats);
         }
     }
     if (wave == 0) ws_done(wsh, num_tiles * (uint32_t)WordsFor<Op>::WORDS, hdr, lane);
