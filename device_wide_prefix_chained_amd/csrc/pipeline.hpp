@@ -180,15 +180,15 @@ __device__ __forceinline__ uint32_t tile_after(uint32_t f2, uint32_t num_tiles, 
 // The closing phase of a LAG 3 pipeline built with CLOSE (its data waves
 // must be built to match: they store after it when after_closing holds):
 // the first phase with no tile to load or scan.  Its control wave resolves
-// the prefixes of all three
-// tiles still waiting (prev2, prev and cur, in that order; cur was scanned
-// in the phase before, so every aggregate they need is out), publishes
-// them, and leaves their exclusive prefixes in `close_prefix`; after its
-// barrier A both kinds of wave leave the loop and the data waves store those
-// three tiles from their park slots at once (closing_slot) instead of one
-// per phase over three more phases.  The look-backs of prev and cur run one
-// and two phases earlier than in the steady state, when a predecessor is a
-// little more likely to be unpublished: a stalled poll costs a round trip.
+// the prefixes of all three tiles still waiting (prev2, prev and cur, in
+// that order; cur was scanned in the phase before, so every aggregate they
+// need is out), publishes them, and leaves their exclusive prefixes in
+// `close_prefix`; after its barrier A both kinds of wave leave the loop and
+// the data waves store those three tiles from their park slots at once
+// (closing_slot) instead of one per phase over three more phases.  The
+// look-backs of prev and cur run one and two phases earlier than in the
+// steady state, when a predecessor is a little more likely to be
+// unpublished: a stalled poll costs a round trip.
 __device__ __forceinline__ bool closing_phase(const PipeTiles &pt, uint32_t num_tiles) {
     return pt.f1 >= num_tiles && pt.f2 >= num_tiles && pt.cur < num_tiles;
 }
