@@ -369,7 +369,9 @@ def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
     protocols as the workload, and the workload's ceiling: the copy of the
     same bytes where it reads as many bytes as it writes, else a plain
     stream of its own mix (ps_stream_mix_u32: the bytes both directions
-    have moved as a copy, the rest read or written alone), and for the
+    have moved as a copy, the rest read or written alone; for a read-heavy
+    mix also ps_stream_mix_even_u32, the same bytes spread evenly over the
+    workgroups, reported beside it), and for the
     recurrence a plain stream of its own shape (two planes read, one or two
     written, ps_stream_planes_f32).  The sum of the read time and the write
     time (`model_ms`) is reported too; it is not a ceiling: a stream that
@@ -425,6 +427,17 @@ def stream_ceiling(w, steps, reps, flush, scan_ms, scan_flushed_ms):
                       "gbs_flushed": round(moved / (fl["median_ms"] * 1e-3) / 1e9, 1),
                       "frac_wall": round(wall / scan_ms, 4),
                       "frac_flushed": round(fl["median_ms"] / scan_flushed_ms, 4)}
+        if no <= ni:
+            # the same mix spread evenly over the workgroups, as a kernel
+            # that stores between its loads in every workgroup moves it
+            run = lambda: dw.ps_stream_mix_even_u32(mi, mo)  # noqa: E731
+            wall = wall_steps(run, steps, 3)
+            fl = flushed_reps(run, reps, flush)
+            out["mix_even"] = {"wall_ms": round(wall, 5), "flushed_median_ms": fl["median_ms"],
+                               "gbs_wall": round(moved / (wall * 1e-3) / 1e9, 1),
+                               "gbs_flushed": round(moved / (fl["median_ms"] * 1e-3) / 1e9, 1),
+                               "frac_wall": round(wall / scan_ms, 4),
+                               "frac_flushed": round(fl["median_ms"] / scan_flushed_ms, 4)}
         del mi, mo
     for proto, key in (("wall", "gbs_wall"), ("flushed", "gbs_flushed")):
         model_ms = (rb / (out["read"][key] * 1e9) + wb / (out["write"][key] * 1e9)) * 1e3

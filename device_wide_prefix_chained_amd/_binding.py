@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
     L.ps_stream_planes_f32.restype = i32
     L.ps_stream_mix_u32.argtypes = [vp, u64, vp, u64, vp]
     L.ps_stream_mix_u32.restype = i32
+    L.ps_stream_mix_even_u32.argtypes = [vp, u64, vp, u64, vp]
+    L.ps_stream_mix_even_u32.restype = i32
     L.ps_stream_shape.argtypes = [i32, i32, i32, i32, i32, vp, vp, u64, u32, vp]
     L.ps_stream_shape.restype = i32
     L.ps_lookback_stats_u32.argtypes = [vp, sz, vp, vp, u64, vp, i32, vp]
@@ -603,6 +605,17 @@ def ps_stream_mix_u32(inp, out, stream=None):
     _dev_tensor("out", out, _U32_DTYPES)
     _check("ps_stream_mix_u32", lib().ps_stream_mix_u32(_ptr(inp), inp.numel(), _ptr(out), out.numel(),
                                                         _stream(out, stream)))
+    return out
+
+
+def ps_stream_mix_even_u32(inp, out, stream=None):
+    """The same byte mix spread evenly over the workgroups (read-heavy mixes:
+    out no longer than inp): each workgroup reads a block of inp and writes
+    its proportional share of out."""
+    _dev_tensor("inp", inp, _U32_DTYPES)
+    _dev_tensor("out", out, _U32_DTYPES)
+    _check("ps_stream_mix_even_u32", lib().ps_stream_mix_even_u32(_ptr(inp), inp.numel(), _ptr(out), out.numel(),
+                                                                  _stream(out, stream)))
     return out
 
 

@@ -168,6 +168,28 @@ __global__ __launch_bounds__(kStreamThreads) void mix_vec_kernel(const copy_v4u 
     }
 }
 
+// The same mix spread evenly (read-heavy mixes): workgroup b reads the
+// vectors [b B, (b + 1) B) of in (B = kStreamBlock) and writes vectors
+// [b oc, (b + 1) oc) of out, oc = ceil(no B / ni), each output vector the
+// input vector read by the same thread at the same offset, so every
+// workgroup stores a share of the output between its loads, as a kernel
+// that compacts its input does.
+__global__ __launch_bounds__(kStreamThreads) void mix_even_kernel(const copy_v4u *in, uint64_t ni, copy_v4u *out,
+                                                                  uint64_t no, uint64_t oc) {
+    const uint64_t b = blockIdx.x;
+    const uint64_t i0 = b * kStreamBlock, o0 = b * oc;
+    const bool full = i0 + kStreamBlock <= ni;
+    copy_v4u r[kStreamVecs];
+#pragma unroll
+    for (int k = 0; k < kStreamVecs; ++k)
+        r[k] = __builtin_nontemporal_load(in + stream_index(i0 + threadIdx.x, k, ni, full));
+#pragma unroll
+    for (int k = 0; k < kStreamVecs; ++k) {
+        const uint64_t j = threadIdx.x + (uint64_t)k * kStreamThreads;
+        if (j < oc && o0 + j < no) __builtin_nontemporal_store(r[k], out + o0 + j);
+    }
+}
+
 // Write-only stream: fills with one value.
 __global__ __launch_bounds__(kFillThreads) void fill_vec_kernel(copy_v4u *out, uint64_t n16, uint32_t value) {
     const uint64_t base = (uint64_t)blockIdx.x * kFillBlock + threadIdx.x;
@@ -391,6 +413,25 @@ extern "C" ps_status ps_stream_mix_u32(const uint32_t *in, uint64_t n_in, uint32
     timing_begin(s);
     hipLaunchKernelGGL(mix_vec_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0, s,
                        reinterpret_cast<const copy_v4u *>(in), ni, reinterpret_cast<copy_v4u *>(out), no, cb);
+    timing_end(s);
+    return launch_status();
+}
+
+extern "C" ps_status ps_stream_mix_even_u32(const uint32_t *in, uint64_t n_in, uint32_t *out, uint64_t n_out,
+                                            void *stream) {
+    if (n_in == 0 && n_out == 0) return PS_OK;
+    if (n_out > n_in) return PS_ERR_UNSUPPORTED;  // read-heavy mixes only
+    if (!in || (n_out && !out)) return PS_ERR_NULL;
+    if (n_in >= (1ull << 32)) return PS_ERR_SIZE;
+    if (!aligned(in, 16) || (n_out && !aligned(out, 16)) || n_in % 4 || n_out % 4) return PS_ERR_ALIGNMENT;
+    if (n_out && ranges_overlap(in, n_in * 4, out, n_out * 4)) return PS_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint64_t ni = n_in / 4, no = n_out / 4;
+    const uint64_t grid = ceil_div(ni, kStreamBlock);
+    const uint64_t oc = ceil_div(no * kStreamBlock, ni);  // <= kStreamBlock since no <= ni
+    timing_begin(s);
+    hipLaunchKernelGGL(mix_even_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0, s,
+                       reinterpret_cast<const copy_v4u *>(in), ni, reinterpret_cast<copy_v4u *>(out), no, oc);
     timing_end(s);
     return launch_status();
 }

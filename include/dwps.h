@@ -403,6 +403,18 @@ ps_status ps_stream_planes_f32(const float *a, const float *b, float *out_a, flo
 ps_status ps_stream_mix_u32(const uint32_t *in, uint64_t n_in, uint32_t *out, uint64_t n_out,
                             void *stream);
 
+/* The same byte mix spread evenly, for read-heavy mixes (n_out <= n_in, else
+ * PS_ERR_UNSUPPORTED): workgroup b of ceil(n_in / 4096) reads the 16-byte
+ * vectors [1024 b, 1024 (b + 1)) of in and writes the vectors [oc b,
+ * oc (b + 1)) of out, oc = ceil(1024 (n_out / 4) / (n_in / 4)); output
+ * vector oc b + j is input vector min(1024 b + j, n_in / 4 - 1).  It shows
+ * what a kernel that
+ * stores between its loads in every workgroup can reach.  Arrays 16-byte
+ * aligned and n_in, n_out multiples of 4, else PS_ERR_ALIGNMENT; in and out
+ * overlapping: PS_ERR_ALIAS. */
+ps_status ps_stream_mix_even_u32(const uint32_t *in, uint64_t n_in, uint32_t *out, uint64_t n_out,
+                                 void *stream);
+
 /* The three plain streams in one of several access shapes, for a sweep that
  * shows whether the stream helpers above run at the memory's rate:
  * PS_STREAM_WRITE fills n uint32 of out with `value` (in unused),

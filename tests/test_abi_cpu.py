@@ -279,6 +279,13 @@ def test_argument_errors_stream_helpers():
     assert M(v(A + 4), 16, v(B), 16, None) == 7 and M(v(A), 16, v(B), 6, None) == 7
     assert M(v(A), 16, v(A + 32), 16, None) == 2                     # overlapping
     assert M(v(A), 1 << 32, v(B), 16, None) == 3
+    E = lib.ps_stream_mix_even_u32
+    assert E(None, 0, None, 0, None) == 0
+    assert E(v(A), 16, v(B), 32, None) == 5                          # more written than read
+    assert E(None, 16, v(B), 16, None) == 1 and E(v(A), 16, None, 16, None) == 1
+    assert E(v(A + 4), 16, v(B), 16, None) == 7 and E(v(A), 16, v(B), 6, None) == 7
+    assert E(v(A), 32, v(A + 32), 16, None) == 2                     # overlapping
+    assert E(v(A), 1 << 32, v(B), 16, None) == 3
     S = lib.ps_stream_shape
     W, CP, RD = 0, 1, 2
     assert S(CP, 128, 8, 1, 0, None, None, 0, 0, None) == 0          # n = 0: nothing to do

@@ -105,6 +105,33 @@ def test_mix_stream(dw, n_in, n_out):
     assert np.array_equal(h[:n_out], _mix_expected(x, n_out)) and np.all(h[n_out:] == 0x5A5A5A5A)
 
 
+def _mix_even_expected(x, n_out):
+    """The even mix stream's output from its definition: workgroup b writes
+    its share of oc output vectors, each the input vector at the same offset
+    of its block of 1024 (the last input vector past the end)."""
+    vin = x.reshape(-1, 4)
+    ni, no = len(vin), n_out // 4
+    oc = -(-(no * 1024) // ni)
+    out = np.zeros((no, 4), np.uint32)
+    for b in range(-(-ni // 1024)):
+        for j in range(oc):
+            if b * oc + j < no:
+                out[b * oc + j] = vin[min(b * 1024 + j, ni - 1)]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("n_in,n_out", [(4, 4), (4096, 4096), (8192 * 3 + 4, 4 * 1000), (1 << 20, 3 << 18),
+                                        (4 * 1_000_003, 4 * 285_715), (1 << 16, 0)])
+def test_mix_even_stream(dw, n_in, n_out):
+    import torch
+    x = wl.full_range_u32(n_in, seed=n_in + 65)
+    buf = torch.full((n_out + 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    say("mix even stream", n_in, n_out)
+    dw.ps_stream_mix_even_u32(dev(x), buf[:n_out])
+    h = host(buf)
+    assert np.array_equal(h[:n_out], _mix_even_expected(x, n_out)) and np.all(h[n_out:] == 0x5A5A5A5A)
+
+
 @pytest.mark.parametrize("threads", [64, 128, 256])
 @pytest.mark.parametrize("vecs", [4, 8, 16])
 def test_stream_shapes(dw, threads, vecs):
