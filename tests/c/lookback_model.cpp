@@ -44,7 +44,7 @@
 //
 // Arguments key=value: words op tiles wgs resident G win partial fallback
 // pair persistent tickets withhold close order(asc|desc|random) p_fresh seeds seed
-// broken(torn|no_tag|partial_distance|skip_invalid) expect(ok|deadlock|
+// broken(torn|no_tag|partial_distance|skip_invalid|close_order) expect(ok|deadlock|
 // violation).  Exit 0 when the outcome is the expected one.
 #include <stdint.h>
 #include <stdio.h>
@@ -300,7 +300,9 @@ Proc workgroup(Model &m, uint32_t w) {
         // resolved now as well, in order, after prev2
         const bool closing = c.close && f1 >= N && f2 >= N && cur < N;
         if (closing) m.n.closings++;
-        for (int r = 0; r < (closing ? 3 : 1); ++r) {
+        for (int step = 0; step < (closing ? 3 : 1); ++step) {
+            // broken=close_order resolves cur before prev
+            const int r = (c.broken == "close_order" && step > 0) ? 3 - step : step;
             const uint32_t t = r == 0 ? prev2 : r == 1 ? prev : cur;
             const uint32_t nxt = r == 0 ? prev : r == 1 ? cur : f1;  // the workgroup's next tile
             // t: its exclusive prefix, by look-back or from the tile before

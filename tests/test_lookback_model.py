@@ -130,6 +130,13 @@ def test_closing_step_keeps_prefixes_exact(model, base):
         assert c["closing steps"] > 0 and c["closing lookbacks"] > 0
 
 
+def test_closing_step_order_is_checked(model):
+    # resolving cur before prev in the closing step hands a group's second
+    # tile the prefix of the wrong tile: caught
+    rc, c = run(model, *ONE, "close=1", "seeds=20", "broken=close_order", "expect=violation")
+    assert rc == 0 and c["violation"] > 0
+
+
 @pytest.mark.parametrize("broken,base", [("torn", TWO), ("no_tag", ONE), ("partial_distance", ONE),
                                          ("skip_invalid", ONE)])
 def test_broken_rules_are_caught(model, broken, base):
